@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs for the selective-scan forward and state update.
+
+This module holds only input generation: it draws random tensors and builds
+the parameter tensors of the workloads below.  It performs none of the scan's
+arithmetic, and it is the one module that both the HIP path's callers and the
+fp64 oracle's callers share.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order, each
+in its storage shape, in float32):
+    u ~ N(0, 1);  delta_raw ~ N(0, 0.1^2);  z ~ N(0, 1);  B ~ N(0, 1);  C ~ N(0, 1)
+then per channel d: dt_d = exp(U(log 1e-3, log 0.1)) and
+dt_bias_d = log(expm1(dt_d)) (the value whose softplus is dt_d), float32;
+A_log[d, n] = log(n + 1); D = 1.
+Storage shapes: u, delta_raw, z are [B, D, L] and B, C are [B, N, L] in the
+"bdl" layout; [B, L, D] and [B, L, N] in the "bld" (channel-last) layout.
+Arrays are returned in logical index order (u as [b, d, t], B as [b, n, t]),
+as views over the storage layout.  bfloat16 copies are made with torch's
+round-to-nearest-even conversion; callers hand the same rounded values to
+both the GPU and the oracle.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    layout: str = "bdl"          # "bdl" ([B,D,L] / [B,N,L]) or "bld" ([B,L,D] / [B,L,N])
+    decode_steps: int = 0        # extra timesteps drawn for a decode hand-off
+
+    @property
+    def elems(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+
+# The five workload shapes: a tiny scan, a mamba-130m-shaped layer, a
+# mamba-2.8b-shaped layer, a 32k-token sequence followed by 64 decode steps,
+# and a channel-last audio-length sequence (5 s at 44.1 kHz).
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 64, 256, 16),
+    "mamba130m_layer": Workload("mamba130m_layer", 1, 1536, 2048, 16),
+    "mamba2p8b_layer": Workload("mamba2p8b_layer", 8, 5120, 4096, 16),
+    "long_handoff": Workload("long_handoff", 1, 1536, 32768, 16, decode_steps=64),
+    "audio_channel_last": Workload("audio_channel_last", 1, 256, 220500, 16, layout="bld"),
+}
+
+
+def generate(batch: int, dim: int, seqlen: int, dstate: int, layout: str = "bdl",
+             seed: int = 0, a_log: str = "ladder", d_skip: str = "ones") -> dict:
+    """Draw one problem.  Returns numpy float32 arrays in logical index order.
+
+    a_log="ladder" gives A_log[d, n] = log(n + 1); a_log="normal" draws
+    A_log ~ N(0, 1) instead (after everything else, same stream).
+    d_skip="ones" gives D = 1; "normal" draws D ~ N(0, 1); "zeros" gives D = 0.
+    """
+    if layout not in ("bdl", "bld"):
+        raise ValueError("layout must be 'bdl' or 'bld'")
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    if layout == "bdl":
+        x_shape, bc_shape = (batch, dim, seqlen), (batch, dstate, seqlen)
+    else:
+        x_shape, bc_shape = (batch, seqlen, dim), (batch, seqlen, dstate)
+
+    def draw(shape, scale=1.0):
+        a = rng.standard_normal(shape, dtype=f32)
+        if scale != 1.0:
+            a *= f32(scale)
+        return a
+
+    u = draw(x_shape)
+    delta_raw = draw(x_shape, 0.1)
+    z = draw(x_shape)
+    Bm = draw(bc_shape)
+    Cm = draw(bc_shape)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), size=dim))
+    dt_bias = np.log(np.expm1(dt)).astype(f32)
+    if a_log == "ladder":
+        A_log = np.tile(np.log(np.arange(1, dstate + 1, dtype=np.float64)), (dim, 1)).astype(f32)
+    elif a_log == "normal":
+        A_log = rng.standard_normal((dim, dstate)).astype(f32)
+    else:
+        raise ValueError(a_log)
+    if d_skip == "ones":
+        D = np.ones(dim, dtype=f32)
+    elif d_skip == "normal":
+        D = rng.standard_normal(dim).astype(f32)
+    elif d_skip == "zeros":
+        D = np.zeros(dim, dtype=f32)
+    else:
+        raise ValueError(d_skip)
+
+    if layout == "bld":
+        u, delta_raw, z = (a.transpose(0, 2, 1) for a in (u, delta_raw, z))
+        Bm, Cm = (a.transpose(0, 2, 1) for a in (Bm, Cm))
+    return {"u": u, "delta_raw": delta_raw, "z": z, "B": Bm, "C": Cm,
+            "A_log": A_log, "D": D, "dt_bias": dt_bias, "layout": layout}
+
+
+def generate_workload(w: Workload, seed: int = 0, **kw) -> dict:
+    """Draw a named workload (with its extra decode timesteps, if any)."""
+    return generate(w.batch, w.dim, w.seqlen + w.decode_steps, w.dstate, w.layout,
+                    seed=seed, **kw)
+
+
+def to_torch(inputs: dict, device, io_dtype: str = "f32") -> dict:
+    """Move a generated problem to ``device``.
+
+    u, delta_raw, z, B and C take ``io_dtype`` ("f32" or "bf16", converted with
+    round-to-nearest-even); A_log, D and dt_bias stay float32.  The storage
+    layout is kept: logical-order views over it are returned.
+    """
+    import torch
+
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[io_dtype]
+    out = {"layout": inputs["layout"]}
+    for k in ("u", "delta_raw", "z", "B", "C"):
+        a = inputs[k]
+        if inputs["layout"] == "bld":
+            t = torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1)))
+            t = t.to(device=device, dtype=dt).transpose(1, 2)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
+        out[k] = t
+    for k in ("A_log", "D", "dt_bias"):
+        out[k] = torch.from_numpy(np.ascontiguousarray(inputs[k])).to(device)
+    return out
+
+
+def slice_time(inputs: dict, start: int, stop: int) -> dict:
+    """Sub-range of timesteps [start, stop) of a problem (views, any backend)."""
+    out = dict(inputs)
+    for k in ("u", "delta_raw", "z", "B", "C"):
+        out[k] = inputs[k][:, :, start:stop]
+    return out
+
+
+def algorithmic_bytes(batch: int, dim: int, seqlen: int, dstate: int, io_bytes: int,
+                      final_state: bool = False, has_z: bool = True, has_D: bool = True,
+                      has_dt_bias: bool = True) -> int:
+    """Bytes the forward must move: each input read once, each output written once."""
+    per_bdl = 3 + int(has_z)          # u, delta_raw, out (+ z)
+    n = batch * dim * seqlen * per_bdl * io_bytes
+    n += 2 * batch * seqlen * dstate * io_bytes   # B, C
+    n += dim * dstate * 4                          # A_log
+    n += dim * 4 * (int(has_D) + int(has_dt_bias))
+    if final_state:
+        n += batch * dim * dstate * 4
+    return n

@@ -1,0 +1,197 @@
+"""fp64 CPU oracle for the Mamba selective-scan forward and state update.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The product package
+(``mamba_selective_scan_amd``) never imports this module, and this module
+imports nothing from the product package.
+
+The arithmetic lives in ``mss_oracle.c`` (plain C, fp64, sequential in time,
+OpenMP across independent channels).  This wrapper only marshals numpy arrays:
+every input is converted exactly to float64 and laid out contiguously as
+
+    u, delta_raw, z, out : [batch, dim, seqlen]
+    B, C                 : [batch, dstate, seqlen]
+    A_log                : [dim, dstate]
+    D, dt_bias           : [dim]
+    h0, final_state      : [batch, dim, dstate]
+
+Values stored in float32 or bfloat16 upcast to float64 without rounding, so the
+oracle consumes exactly the bytes the GPU consumes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mss_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libmss_oracle.so")
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.mss_oracle_softplus.argtypes = [ctypes.c_double]
+    lib.mss_oracle_softplus.restype = ctypes.c_double
+    lib.mss_oracle_silu.argtypes = [ctypes.c_double]
+    lib.mss_oracle_silu.restype = ctypes.c_double
+    lib.mss_oracle_max_threads.argtypes = []
+    lib.mss_oracle_max_threads.restype = ctypes.c_int
+    lib.mss_oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [
+        ctypes.c_int, dp, dp, ctypes.c_int]
+    lib.mss_oracle_scan_fwd.restype = ctypes.c_int
+    lib.mss_oracle_state_update.argtypes = [i64, i64, i64, dp] + [dp] * 8 + [
+        ctypes.c_int, dp]
+    lib.mss_oracle_state_update.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path != LIB_PATH:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _f64(x, shape=None):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor: exact upcast on the CPU
+        import torch
+        x = x.detach().to("cpu", torch.float64).numpy()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def softplus(x: float, lib=None) -> float:
+    return (lib or load()).mss_oracle_softplus(float(x))
+
+
+def silu(x: float, lib=None) -> float:
+    return (lib or load()).mss_oracle_silu(float(x))
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).mss_oracle_max_threads()
+
+
+def scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, h0=None,
+             delta_softplus=True, threads=0, lib=None):
+    """Selective-scan forward in fp64.  Returns (out [b,d,l], final_state [b,d,n])."""
+    u = _f64(u)
+    batch, dim, seqlen = u.shape
+    A_log = _f64(A_log)
+    dstate = A_log.shape[1]
+    delta_raw = _f64(delta_raw, (batch, dim, seqlen))
+    A_log = _f64(A_log, (dim, dstate))
+    B = _f64(B, (batch, dstate, seqlen))
+    C = _f64(C, (batch, dstate, seqlen))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim, seqlen))
+    dt_bias = _f64(dt_bias, (dim,))
+    h0 = _f64(h0, (batch, dim, dstate))
+    out = np.empty((batch, dim, seqlen), dtype=np.float64)
+    final = np.empty((batch, dim, dstate), dtype=np.float64)
+    rc = (lib or load()).mss_oracle_scan_fwd(
+        batch, dim, seqlen, dstate, _ptr(u), _ptr(delta_raw), _ptr(A_log), _ptr(B),
+        _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), int(bool(delta_softplus)),
+        _ptr(out), _ptr(final), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle scan_fwd rejected its arguments (rc={rc})")
+    return out, final
+
+
+def state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None,
+                 delta_softplus=True, lib=None):
+    """One decode step in fp64.  Returns (out [b,d], new_state [b,d,n]); the
+    input ``state`` is not modified."""
+    new_state = _f64(state).copy()
+    batch, dim, dstate = new_state.shape
+    u = _f64(u, (batch, dim))
+    delta_raw = _f64(delta_raw, (batch, dim))
+    A_log = _f64(A_log, (dim, dstate))
+    B = _f64(B, (batch, dstate))
+    C = _f64(C, (batch, dstate))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim))
+    dt_bias = _f64(dt_bias, (dim,))
+    out = np.empty((batch, dim), dtype=np.float64)
+    rc = (lib or load()).mss_oracle_state_update(
+        batch, dim, dstate, _ptr(new_state), _ptr(u), _ptr(delta_raw), _ptr(A_log),
+        _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(delta_softplus)),
+        _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle state_update rejected its arguments (rc={rc})")
+    return out, new_state
+
+
+def scan_channels(inputs: dict, channels, delta_softplus=True, use_h0=False, threads=0):
+    """Run the oracle on selected channels only.
+
+    ``inputs`` holds arrays in logical index order (u [b,d,l], B [b,n,l], ...),
+    any numpy/torch layout.  ``channels`` is a list of (b, d) pairs.  Returns
+    (out [k, seqlen], final_state [k, dstate]) in the order given.
+    """
+    ch = list(channels)
+    out = [None] * len(ch)
+    fin = [None] * len(ch)
+    by_b: dict[int, list[tuple[int, int]]] = {}
+    for i, (b, d) in enumerate(ch):
+        by_b.setdefault(int(b), []).append((i, int(d)))
+
+    def pick(name, idx):
+        x = inputs.get(name)
+        if x is None:
+            return None
+        if hasattr(x, "detach"):
+            import torch
+            return x[idx].detach().to("cpu", torch.float64).numpy()
+        return np.asarray(x[idx], dtype=np.float64)
+
+    for b, items in by_b.items():
+        ds = np.array([d for _, d in items], dtype=np.int64)
+        sub = {
+            "u": pick("u", (slice(b, b + 1), ds)),
+            "delta_raw": pick("delta_raw", (slice(b, b + 1), ds)),
+            "z": pick("z", (slice(b, b + 1), ds)),
+            "B": pick("B", slice(b, b + 1)),
+            "C": pick("C", slice(b, b + 1)),
+            "A_log": pick("A_log", ds),
+            "D": pick("D", ds),
+            "dt_bias": pick("dt_bias", ds),
+            "h0": pick("h0", (slice(b, b + 1), ds)) if use_h0 else None,
+        }
+        o, f = scan_fwd(sub["u"], sub["delta_raw"], sub["A_log"], sub["B"], sub["C"],
+                        D=sub["D"], z=sub["z"], dt_bias=sub["dt_bias"], h0=sub["h0"],
+                        delta_softplus=delta_softplus, threads=threads)
+        for j, (i, _) in enumerate(items):
+            out[i] = o[0, j]
+            fin[i] = f[0, j]
+    return np.stack(out), np.stack(fin)

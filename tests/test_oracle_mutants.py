@@ -1,0 +1,93 @@
+"""The pins have teeth: each plausible mistake planted in a copy of the oracle
+makes at least one pin fail.
+
+Every mutant below is a one-line edit of oracle/mss_oracle.c (a dropped term,
+a wrong sign or index, a transposed or swapped operand, exp2 for exp, ...).
+The copy is compiled into a temporary library and the pins are run against
+it; the real oracle source is never modified.
+"""
+
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mss_oracle.c")
+
+MUTANTS = {
+    "A_sign": ("A[n] = -exp(A_log[d * dstate + n]);", "A[n] = exp(A_log[d * dstate + n]);"),
+    "A_no_exp": ("A[n] = -exp(A_log[d * dstate + n]);", "A[n] = -A_log[d * dstate + n];"),
+    "decay_exp2": ("double a = exp(delta * A[n]);", "double a = exp2(delta * A[n]);"),
+    "decay_no_delta": ("double a = exp(delta * A[n]);", "double a = exp(A[n]);"),
+    "b_no_delta": ("double bt = delta * B_b[n * seqlen + t] * ut;",
+                   "double bt = B_b[n * seqlen + t] * ut;"),
+    "b_no_u": ("double bt = delta * B_b[n * seqlen + t] * ut;",
+               "double bt = delta * B_b[n * seqlen + t];"),
+    "b_uses_C": ("double bt = delta * B_b[n * seqlen + t] * ut;",
+                 "double bt = delta * C_b[n * seqlen + t] * ut;"),
+    "B_transposed": ("double bt = delta * B_b[n * seqlen + t] * ut;",
+                     "double bt = delta * B_b[t * dstate + n] * ut;"),
+    "B_time_shift": ("double bt = delta * B_b[n * seqlen + t] * ut;",
+                     "double bt = delta * B_b[n * seqlen + (t > 0 ? t - 1 : 0)] * ut;"),
+    "C_transposed": ("y += C_b[n * seqlen + t] * h[n];", "y += C_b[t * dstate + n] * h[n];"),
+    "y_before_update": ("h[n] = a * h[n] + bt;\n                y += C_b[n * seqlen + t] * h[n];",
+                        "y += C_b[n * seqlen + t] * h[n];\n                h[n] = a * h[n] + bt;"),
+    "h_plus_not_times": ("h[n] = a * h[n] + bt;", "h[n] = a + h[n] + bt;"),
+    "no_skip": ("y += skip * ut;", "y += 0.0 * skip * ut;"),
+    "skip_uses_z": ("y += skip * ut;", "y += skip * (z_row ? z_row[t] : ut);"),
+    "skip_after_gate": ("y += skip * ut;\n            if (z_row) y *= mss_oracle_silu(z_row[t]);",
+                        "if (z_row) y *= mss_oracle_silu(z_row[t]);\n            y += skip * ut;"),
+    "no_dt_bias": ("double x = delta_raw + bias;", "double x = delta_raw;"),
+    "softplus_ignored": ("return delta_softplus ? mss_oracle_softplus(x) : x;", "return x;"),
+    "softplus_always": ("return delta_softplus ? mss_oracle_softplus(x) : x;",
+                        "return mss_oracle_softplus(x);"),
+    "softplus_naive_log": ("return m + log1p(exp(-fabs(x)));", "return m + log(exp(-fabs(x)));"),
+    "softplus_no_max": ("return m + log1p(exp(-fabs(x)));", "return log1p(exp(-fabs(x)));"),
+    "gate_sigmoid_only": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "gate_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "h0_ignored": ("h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;", "h[n] = 0.0;"),
+    "h0_transposed": ("h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;",
+                      "h[n] = h0 ? h0[(b * dstate + n) * dim + d] : 0.0;"),
+    "final_state_stale": ("final_state[(b * dim + d) * dstate + n] = h[n];",
+                          "final_state[(b * dim + d) * dstate + n] = h[n] * 0.5;"),
+    "step_decay_sign": ("double decay = exp(delta * -exp(A_log[d * dstate + n]));",
+                        "double decay = exp(delta * exp(A_log[d * dstate + n]));"),
+    "step_b_no_u": ("h[n] = decay * h[n] + delta * x * B[b * dstate + n];",
+                    "h[n] = decay * h[n] + delta * B[b * dstate + n];"),
+    "step_y_uses_B": ("y += h[n] * C[b * dstate + n];", "y += h[n] * B[b * dstate + n];"),
+    "step_no_skip": ("y += (D ? D[d] : 0.0) * x;", "y += 0.0 * x;"),
+    "step_no_bias": ("dt_bias ? dt_bias[d] : 0.0, delta_softplus);", "0.0, delta_softplus);"),
+}
+
+
+def _run_pins(lib):
+    failures = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            failures.append((pin.__name__, str(e)[:120]))
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    oracle.build(str(mutated), str(so))
+    # The library stays loaded: unloading a library whose OpenMP worker
+    # threads are still parked is unsafe, and each mutant is small.
+    failures = _run_pins(oracle.load(str(so)))
+    assert failures, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    so = tmp_path / "libcopy.so"
+    oracle.build(SRC, str(so))
+    assert _run_pins(oracle.load(str(so))) == []
