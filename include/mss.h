@@ -1,0 +1,180 @@
+/*
+ * mss.h -- C ABI of libmss, the MI355X (gfx950) Mamba selective-scan library.
+ *
+ * Two operations:
+ *
+ *  1. mss_selective_scan_fwd: the selective-scan forward over whole sequences.
+ *     For every channel (b, d) and time step t, with n over the dstate
+ *     diagonal state entries:
+ *        delta_t = softplus(delta_raw[b,d,t] + dt_bias[d])   (or without softplus)
+ *        A[n]    = -exp(A_log[d,n])
+ *        h_t[n]  = exp(delta_t * A[n]) * h_{t-1}[n] + delta_t * B[b,n,t] * u[b,d,t]
+ *        y_t     = sum_n C[b,n,t] * h_t[n] + D[d] * u[b,d,t]
+ *        out[b,d,t] = y_t * z[b,d,t] * sigmoid(z[b,d,t])      (if z is given)
+ *     with h_{-1} = initial_state (or 0), and optionally exporting the state
+ *     after the last step.
+ *     Sources: the recurrence and its diagonal discretisation
+ *     ("mamba-metal: Apple Silicon で Mamba を動かす", section
+ *     "Selective scan の本質"; createcentury's reading of the official CUDA
+ *     kernel, sections "なぜ「scan」か" and "1チャンク内の処理フロー");
+ *     softplus and -exp(A_log) fused into the scan, tensor roles and the
+ *     fixed 16-entry state (SpeechLens kernel-optimization notes, selective-scan
+ *     contract table); the final-state hand-off ("mamba-metal", section
+ *     "残り課題").
+ *
+ *  2. mss_selective_state_update: one decode step, O(1) per token: the loop
+ *     body above applied once to a caller-held state, updated in place
+ *     ("mamba-metal", section "O(L) インクリメンタルデコード", per-step
+ *     equation, closed by the z gate).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains caller memory and keeps no per-call
+ *    state; it caches nothing but compiled kernels.
+ *  - Tensors are described by element strides in LOGICAL index order:
+ *    u / delta_raw / z / out as (b, d, t), B / C as (b, n, t), A_log as (d, n).
+ *    u, delta_raw, z and out must share a unit-stride axis, t or d (for
+ *    example [B,D,L] or channel-last [B,L,D] buffers); B and C must share one,
+ *    t or n.  Other strides are free (views into larger buffers are fine).
+ *    A dimension of size 1 may have any stride.  D, dt_bias and the states
+ *    are contiguous.
+ *  - io_dtype selects the element type of u, delta_raw, z, B, C and out
+ *    (fp32 or bf16).  A_log, D, dt_bias and every state are always fp32;
+ *    arithmetic is fp32 throughout and bf16 outputs are rounded to nearest even.
+ *  - Execution is asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *    the null stream).  Functions return once the work is enqueued.  Nothing
+ *    synchronises the device.
+ *  - Errors are reported by return value, never by exceptions or aborts.  All
+ *    argument checks run before any HIP call: on an error nothing is launched
+ *    and no memory is touched.  MSS_ERR_HIP reports a failure that the HIP
+ *    runtime returned while enqueuing.
+ *  - out and final_state must not overlap any input (the scan reads its inputs
+ *    after it has started writing); the state of a state update is the only
+ *    in/out buffer.
+ *  - Thread-safe: concurrent calls on different streams are independent.
+ */
+#ifndef MSS_H
+#define MSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSS_ABI_VERSION 1
+#define MSS_MAX_DSTATE 16
+
+typedef enum mss_status {
+    MSS_OK = 0,
+    MSS_ERR_NULL_POINTER = 1,       /* a required pointer is NULL                      */
+    MSS_ERR_BAD_SHAPE = 2,          /* batch, dim or seqlen < 1, or sizes overflow     */
+    MSS_ERR_BAD_STRIDE = 3,         /* negative, overlapping or no unit-stride axis    */
+    MSS_ERR_UNSUPPORTED_DTYPE = 4,  /* io_dtype is not MSS_F32 or MSS_BF16             */
+    MSS_ERR_UNSUPPORTED_DSTATE = 5, /* dstate outside [1, MSS_MAX_DSTATE]              */
+    MSS_ERR_MISALIGNED = 6,         /* a pointer is not aligned to its element size    */
+    MSS_ERR_WORKSPACE_TOO_SMALL = 7,/* workspace_bytes below the required size         */
+    MSS_ERR_ALIASING = 8,           /* an output overlaps an input                     */
+    MSS_ERR_BAD_STRUCT = 9,         /* args is NULL or struct_size does not match      */
+    MSS_ERR_HIP = 10                /* the HIP runtime reported an error               */
+} mss_status;
+
+typedef enum mss_dtype {
+    MSS_F32 = 0,
+    MSS_BF16 = 1
+} mss_dtype;
+
+/* Arguments of mss_selective_scan_fwd.  Set struct_size = sizeof(mss_scan_args). */
+typedef struct mss_scan_args {
+    uint32_t struct_size;
+    int32_t io_dtype;            /* mss_dtype of u, delta_raw, z, B, C, out              */
+    int64_t batch;               /* B >= 1                                               */
+    int64_t dim;                 /* D >= 1 (d_inner channels)                            */
+    int64_t seqlen;              /* 1 <= L <= 2^30                                       */
+    int64_t dstate;              /* N, 1..MSS_MAX_DSTATE                                 */
+
+    const void *u;               /* [b,d,t] input activation                            */
+    int64_t u_stride[3];
+    const void *delta_raw;       /* [b,d,t] time step before bias and softplus           */
+    int64_t delta_stride[3];
+    const float *A_log;          /* [d,n] fp32, A = -exp(A_log)                          */
+    int64_t A_log_stride[2];
+    const void *B;               /* [b,n,t] input coefficients                           */
+    int64_t B_stride[3];
+    const void *C;               /* [b,n,t] output coefficients                          */
+    int64_t C_stride[3];
+    const float *D;              /* [d] fp32 skip, contiguous; NULL means 0              */
+    const void *z;               /* [b,d,t] gate; NULL means no gate                     */
+    int64_t z_stride[3];
+    const float *dt_bias;        /* [d] fp32, contiguous; NULL means 0                   */
+    const float *initial_state;  /* [b,d,n] fp32 contiguous h_{-1}; NULL means 0         */
+
+    void *out;                   /* [b,d,t] result, io_dtype                             */
+    int64_t out_stride[3];
+    float *final_state;          /* [b,d,n] fp32 contiguous h_{L-1}; NULL: not written   */
+
+    int32_t delta_softplus;      /* nonzero: delta = softplus(delta_raw + dt_bias)       */
+    int32_t reserved0;           /* must be 0                                            */
+
+    void *workspace;             /* device scratch, 256-byte aligned, of at least        */
+    size_t workspace_bytes;      /* mss_selective_scan_workspace_size bytes (may be 0)   */
+} mss_scan_args;
+
+/* Arguments of mss_selective_state_update.  Set struct_size = sizeof(mss_step_args). */
+typedef struct mss_step_args {
+    uint32_t struct_size;
+    int32_t io_dtype;            /* mss_dtype of u, delta_raw, z, B, C, out              */
+    int64_t batch;
+    int64_t dim;
+    int64_t dstate;              /* 1..MSS_MAX_DSTATE                                    */
+
+    float *state;                /* [b,d,n] fp32 contiguous, read and updated in place   */
+    const void *u;               /* [b,d]                                                */
+    int64_t u_stride[2];
+    const void *delta_raw;       /* [b,d]                                                */
+    int64_t delta_stride[2];
+    const float *A_log;          /* [d,n] fp32                                           */
+    int64_t A_log_stride[2];
+    const void *B;               /* [b,n]                                                */
+    int64_t B_stride[2];
+    const void *C;               /* [b,n]                                                */
+    int64_t C_stride[2];
+    const float *D;              /* [d] fp32 contiguous; NULL means 0                    */
+    const void *z;               /* [b,d]; NULL means no gate                            */
+    int64_t z_stride[2];
+    const float *dt_bias;        /* [d] fp32 contiguous; NULL means 0                    */
+    void *out;                   /* [b,d] result, io_dtype                               */
+    int64_t out_stride[2];
+    int32_t delta_softplus;
+    int32_t reserved0;           /* must be 0                                            */
+} mss_step_args;
+
+/* ABI version of the loaded library (MSS_ABI_VERSION of its build). */
+int mss_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *mss_status_string(mss_status status);
+
+/* Bytes of device workspace mss_selective_scan_fwd needs for these arguments.
+ * It is 0 unless the shape is split into time segments (few channels, long
+ * sequence), in which case it holds the per-segment state carries.  Depends
+ * only on the shapes, so it can be called before any pointer is set.  Returns 0
+ * and sets *status (if non-NULL) to an error code when the shapes are
+ * invalid. */
+size_t mss_selective_scan_workspace_size(const mss_scan_args *args, mss_status *status);
+
+/* Selective-scan forward (see the top of this file).  `stream` is a
+ * hipStream_t.  The workspace, when needed, is overwritten; it carries no
+ * state between calls, and calls that share one workspace on different
+ * streams race. */
+mss_status mss_selective_scan_fwd(const mss_scan_args *args, void *stream);
+
+/* One-token state update (see the top of this file). */
+mss_status mss_selective_state_update(const mss_step_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSS_H */

@@ -1,0 +1,226 @@
+"""mamba_selective_scan_amd -- Mamba selective-scan forward and state update on
+MI355X (gfx950), through the C ABI of libmss (include/mss.h).
+
+This module marshals arguments only: it reads tensor pointers, logical strides
+and torch's current HIP stream and calls libmss, whose HIP kernels do every
+step of the computation.  PyTorch supplies device memory and streams.  There
+is no CPU or PyTorch fallback; without the built library every call raises.
+
+    out = selective_scan_fwd(u, delta_raw, A_log, B, C, D, z, dt_bias)
+    out, h = selective_scan_fwd(..., return_final_state=True)
+    y = selective_state_update(state, u_t, delta_raw_t, A_log, B_t, C_t, D, z_t, dt_bias)
+
+Shapes (logical index order, any strides): u, delta_raw, z, out [B, D, L];
+B, C [B, N, L]; A_log [D, N]; D, dt_bias [D]; states [B, D, N] (fp32,
+contiguous).  A channel-last [B, L, D] buffer is passed as its transpose(1, 2)
+view.  u, delta_raw, z, B, C share one dtype (float32 or bfloat16); A_log, D,
+dt_bias and the states are float32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import MSS_MAX_DSTATE, MssError
+
+__all__ = ["selective_scan_fwd", "selective_state_update", "scan_workspace_size",
+           "MssError", "MSS_MAX_DSTATE", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return _lib.MSS_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.MSS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: expected float32 or bfloat16")
+
+
+def _need(t, name, ndim, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t, n):
+    arr = (ctypes.c_int64 * n)()
+    if t is not None:
+        for i, s in enumerate(t.stride()):
+            arr[i] = s
+    return arr
+
+
+def _contig_f32(t, name, shape, device):
+    torch = _torch()
+    if t is None:
+        return None
+    _need(t, name, len(shape), torch.float32, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_handle(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
+               delta_softplus):
+    torch = _torch()
+    dev = u.device
+    _need(u, "u", 3)
+    bsz, dim, seqlen = u.shape
+    dt = u.dtype
+    _need(delta_raw, "delta_raw", 3, dt, dev)
+    _need(B, "B", 3, dt, dev)
+    _need(C, "C", 3, dt, dev)
+    _need(A_log, "A_log", 2, torch.float32, dev)
+    dstate = A_log.shape[1]
+    if tuple(delta_raw.shape) != (bsz, dim, seqlen):
+        raise ValueError("delta_raw must have the shape of u")
+    if tuple(B.shape) != (bsz, dstate, seqlen) or tuple(C.shape) != (bsz, dstate, seqlen):
+        raise ValueError(f"B and C must have shape {(bsz, dstate, seqlen)}")
+    if tuple(A_log.shape) != (dim, dstate):
+        raise ValueError(f"A_log must have shape {(dim, dstate)}")
+    if z is not None:
+        _need(z, "z", 3, dt, dev)
+        if tuple(z.shape) != (bsz, dim, seqlen):
+            raise ValueError("z must have the shape of u")
+    _contig_f32(D, "D", (dim,), dev)
+    _contig_f32(dt_bias, "dt_bias", (dim,), dev)
+    _contig_f32(initial_state, "initial_state", (bsz, dim, dstate), dev)
+    a = _lib.new_scan_args()
+    a.io_dtype = _io_dtype(u)
+    a.batch, a.dim, a.seqlen, a.dstate = bsz, dim, seqlen, dstate
+    a.u, a.u_stride = _ptr(u), _strides(u, 3)
+    a.delta_raw, a.delta_stride = _ptr(delta_raw), _strides(delta_raw, 3)
+    a.A_log, a.A_log_stride = _ptr(A_log), _strides(A_log, 2)
+    a.B, a.B_stride = _ptr(B), _strides(B, 3)
+    a.C, a.C_stride = _ptr(C), _strides(C, 3)
+    a.D = _ptr(D)
+    a.z, a.z_stride = _ptr(z), _strides(z, 3)
+    a.dt_bias = _ptr(dt_bias)
+    a.initial_state = _ptr(initial_state)
+    a.out, a.out_stride = _ptr(out), _strides(out, 3)
+    a.final_state = _ptr(final_state)
+    a.delta_softplus = 1 if delta_softplus else 0
+    return a
+
+
+def scan_workspace_size(u, A_log) -> int:
+    """Workspace bytes selective_scan_fwd needs for u [B, D, L] and A_log [D, N]."""
+    a = _lib.new_scan_args()
+    a.io_dtype = _io_dtype(u)
+    a.batch, a.dim, a.seqlen = u.shape
+    a.dstate = A_log.shape[1]
+    st = ctypes.c_int(0)
+    n = _lib.lib().mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    _lib.check(st.value)
+    return int(n)
+
+
+def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
+                       delta_softplus=True, initial_state=None, return_final_state=False,
+                       out=None, final_state=None, workspace=None):
+    """Selective-scan forward on u's device, ordered on torch's current stream.
+
+    Returns ``out`` (shape and layout of u), or ``(out, final_state)`` with the
+    fp32 state [B, D, N] after the last step when ``return_final_state``.
+    ``out``, ``final_state`` and ``workspace`` (uint8, at least
+    scan_workspace_size bytes) may be supplied to avoid allocation.
+    """
+    torch = _torch()
+    lib = _lib.lib()
+    if out is None:
+        out = torch.empty_like(u)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((u.shape[0], u.shape[1], A_log.shape[1]), dtype=torch.float32,
+                                  device=u.device)
+    if final_state is not None:
+        _contig_f32(final_state, "final_state", (u.shape[0], u.shape[1], A_log.shape[1]), u.device)
+    a = _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
+                   delta_softplus)
+    if tuple(out.shape) != tuple(u.shape) or out.dtype != u.dtype or out.device != u.device:
+        raise ValueError("out must match u in shape, dtype and device")
+    st = ctypes.c_int(0)
+    need = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    _lib.check(st.value)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.mss_selective_scan_fwd(ctypes.byref(a), _stream_handle(u.device)))
+    if return_final_state:
+        return out, final_state
+    return out
+
+
+def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
+                           delta_softplus=True, out=None):
+    """One decode step: updates ``state`` [B, D, N] (fp32, contiguous) in place and
+    returns out [B, D].  u, delta_raw, z are [B, D]; B, C are [B, N]."""
+    torch = _torch()
+    lib = _lib.lib()
+    dev = state.device
+    _need(state, "state", 3, torch.float32, dev)
+    if not state.is_contiguous():
+        raise ValueError("state must be contiguous")
+    bsz, dim, dstate = state.shape
+    _need(u, "u", 2, None, dev)
+    dt = u.dtype
+    _need(delta_raw, "delta_raw", 2, dt, dev)
+    _need(B, "B", 2, dt, dev)
+    _need(C, "C", 2, dt, dev)
+    _need(A_log, "A_log", 2, torch.float32, dev)
+    if tuple(u.shape) != (bsz, dim) or tuple(delta_raw.shape) != (bsz, dim):
+        raise ValueError(f"u and delta_raw must have shape {(bsz, dim)}")
+    if tuple(B.shape) != (bsz, dstate) or tuple(C.shape) != (bsz, dstate):
+        raise ValueError(f"B and C must have shape {(bsz, dstate)}")
+    if tuple(A_log.shape) != (dim, dstate):
+        raise ValueError(f"A_log must have shape {(dim, dstate)}")
+    if z is not None:
+        _need(z, "z", 2, dt, dev)
+    _contig_f32(D, "D", (dim,), dev)
+    _contig_f32(dt_bias, "dt_bias", (dim,), dev)
+    if out is None:
+        out = torch.empty_like(u)
+    a = _lib.new_step_args()
+    a.io_dtype = _io_dtype(u)
+    a.batch, a.dim, a.dstate = bsz, dim, dstate
+    a.state = _ptr(state)
+    a.u, a.u_stride = _ptr(u), _strides(u, 2)
+    a.delta_raw, a.delta_stride = _ptr(delta_raw), _strides(delta_raw, 2)
+    a.A_log, a.A_log_stride = _ptr(A_log), _strides(A_log, 2)
+    a.B, a.B_stride = _ptr(B), _strides(B, 2)
+    a.C, a.C_stride = _ptr(C), _strides(C, 2)
+    a.D = _ptr(D)
+    a.z, a.z_stride = _ptr(z), _strides(z, 2)
+    a.dt_bias = _ptr(dt_bias)
+    a.out, a.out_stride = _ptr(out), _strides(out, 2)
+    a.delta_softplus = 1 if delta_softplus else 0
+    _lib.check(lib.mss_selective_state_update(ctypes.byref(a), _stream_handle(dev)))
+    return out

@@ -1,0 +1,356 @@
+// mss_api.hip -- the C ABI of libmss: argument checks, launch planning and
+// stream-ordered enqueue.  Every check runs on the host before any HIP call,
+// so an invalid call launches nothing and touches no memory.  There is one
+// execution path per operation and no fallback.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "mss.h"
+#include "mss_internal.hpp"
+
+namespace {
+
+using mss::kCh;
+using mss::kMaxState;
+using mss::kT;
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxSeqlen = int64_t{1} << 30;  // time indices, padded, stay in int32
+// Time segments: a shape whose channel tiles alone give fewer workgroups than
+// this is split along time until it reaches it (the plan depends only on the
+// shape, so results do not depend on the device).
+constexpr int64_t kSplitBelowTiles = 2048;
+constexpr int64_t kTargetTiles = 4096;
+
+struct Extent {
+  uintptr_t lo = 0, hi = 0;  // byte range [lo, hi)
+  bool valid = false;
+};
+
+Extent extent_of(const void* p, const int64_t* sizes, const int64_t* strides, int rank,
+                 int64_t elem) {
+  Extent e;
+  if (p == nullptr) return e;
+  int64_t span = 0;
+  for (int i = 0; i < rank; ++i) span += (sizes[i] - 1) * strides[i];
+  e.lo = reinterpret_cast<uintptr_t>(p);
+  e.hi = e.lo + static_cast<uintptr_t>((span + 1) * elem);
+  e.valid = true;
+  return e;
+}
+
+bool overlaps(const Extent& a, const Extent& b) {
+  return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, int64_t a) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(a)) == 0;
+}
+
+void norm_strides(int64_t* out, const int64_t* st, const int64_t* sizes) {
+  for (int i = 0; i < 3; ++i) out[i] = sizes[i] == 1 ? 1 : st[i];
+}
+
+bool strides_nonneg(const int64_t* st, int rank) {
+  for (int i = 0; i < rank; ++i)
+    if (st[i] < 0) return false;
+  return true;
+}
+
+// Distinct indices map to distinct elements (needed for outputs only).
+bool non_overlapping(const int64_t* sizes, const int64_t* strides, int rank) {
+  int idx[3] = {0, 1, 2};
+  std::sort(idx, idx + rank, [&](int a, int b) { return strides[a] < strides[b]; });
+  int64_t need = 1;
+  for (int k = 0; k < rank; ++k) {
+    const int i = idx[k];
+    if (sizes[i] == 1) continue;
+    if (strides[i] < need) return false;
+    need = strides[i] * sizes[i];
+  }
+  return true;
+}
+
+// Each 16-channel x 32-step tile (16-state x 32-step for B and C) is
+// addressed with 32-bit byte offsets from a per-tile base.
+bool tile_offsets_fit(const int64_t* st, int64_t elem, int64_t rows = kCh) {
+  const int64_t span = ((rows - 1) * st[1] + (kT - 1) * st[2] + 1) * elem;
+  return span < (int64_t{1} << 31);
+}
+
+struct ScanPlan {
+  mss::ScanShape shape;
+  size_t agg_bytes = 0, carry_bytes = 0, tail_bytes = 0, workspace = 0;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// elements per 16-byte vector of the io type
+int vec_elems(int32_t io_dtype) { return io_dtype == MSS_BF16 ? 8 : 4; }
+
+mss_status check_shape(const mss_scan_args* a) {
+  if (a == nullptr || a->struct_size != sizeof(mss_scan_args) || a->reserved0 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
+  if (a->batch < 1 || a->dim < 1 || a->seqlen < 1) return MSS_ERR_BAD_SHAPE;
+  if (a->batch > kMaxDim || a->dim > kMaxDim || a->seqlen > kMaxSeqlen) return MSS_ERR_BAD_SHAPE;
+  if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
+  // batch * ceil(dim/64) workgroups in grid x; batch * dim * dstate states
+  const int64_t groups = (a->dim + kCh - 1) / kCh;
+  if (a->batch * groups > kMaxDim) return MSS_ERR_BAD_SHAPE;
+  if (a->batch * a->dim > kMaxDim) return MSS_ERR_BAD_SHAPE;
+  return MSS_OK;
+}
+
+ScanPlan make_plan(const mss_scan_args* a) {
+  ScanPlan p;
+  mss::ScanShape& s = p.shape;
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.seqlen = static_cast<int>(a->seqlen);
+  s.dstate = static_cast<int>(a->dstate);
+  s.groups = static_cast<int>((a->dim + kCh - 1) / kCh);
+  const int64_t tiles = a->batch * s.groups;
+  const int64_t chunks = (a->seqlen + kT - 1) / kT;
+  int64_t nseg = 1;
+  if (tiles < kSplitBelowTiles) nseg = std::min<int64_t>((kTargetTiles + tiles - 1) / tiles, chunks);
+  nseg = std::min<int64_t>(nseg, 65535);
+  const int64_t seg_chunks = (chunks + nseg - 1) / nseg;
+  s.seg_len = static_cast<int>(seg_chunks * kT);
+  s.nseg = static_cast<int>((a->seqlen + s.seg_len - 1) / s.seg_len);
+  s.nchan_pad = tiles * kCh;
+  s.softplus = a->delta_softplus ? 1 : 0;
+  s.t_first = 0;
+  s.t_stop = s.seqlen;
+  if (s.nseg > 1) {
+    p.agg_bytes = round_up(static_cast<size_t>(s.nseg - 1) * s.nchan_pad * kMaxState * sizeof(float2), 256);
+    p.carry_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float), 256);
+  }
+  // a sequence that does not end on a 16-byte vector boundary ends with an
+  // element-wise pass that starts from a state handed over in the workspace
+  if (a->seqlen % vec_elems(a->io_dtype) != 0)
+    p.tail_bytes = round_up(static_cast<size_t>(a->batch * a->dim * a->dstate) * sizeof(float), 256);
+  p.workspace = p.agg_bytes + p.carry_bytes + p.tail_bytes;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mss_abi_version(void) { return MSS_ABI_VERSION; }
+
+const char* mss_status_string(mss_status status) {
+  switch (status) {
+    case MSS_OK: return "ok";
+    case MSS_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MSS_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 1 and fit the grid)";
+    case MSS_ERR_BAD_STRIDE: return "invalid stride (negative, overlapping output, or a tile spans >= 2 GiB)";
+    case MSS_ERR_UNSUPPORTED_DTYPE: return "unsupported io dtype (expected MSS_F32 or MSS_BF16)";
+    case MSS_ERR_UNSUPPORTED_DSTATE: return "dstate must be between 1 and 16";
+    case MSS_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
+    case MSS_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or smaller than mss_selective_scan_workspace_size";
+    case MSS_ERR_ALIASING: return "an output overlaps an input";
+    case MSS_ERR_BAD_STRUCT: return "arguments struct is NULL, of the wrong size, or has reserved fields set";
+    case MSS_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
+  }
+  return "unknown status";
+}
+
+size_t mss_selective_scan_workspace_size(const mss_scan_args* a, mss_status* status) {
+  const mss_status st = check_shape(a);
+  if (status != nullptr) *status = st;
+  if (st != MSS_OK) return 0;
+  return make_plan(a).workspace;
+}
+
+mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
+  mss_status st = check_shape(a);
+  if (st != MSS_OK) return st;
+  if (a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr || a->B == nullptr ||
+      a->C == nullptr || a->out == nullptr)
+    return MSS_ERR_NULL_POINTER;
+  const int64_t es = a->io_dtype == MSS_BF16 ? 2 : 4;
+  const int64_t xs[3] = {a->batch, a->dim, a->seqlen};
+  const int64_t bcs[3] = {a->batch, a->dstate, a->seqlen};
+  const int64_t as[2] = {a->dim, a->dstate};
+  const int64_t vs[1] = {a->dim};
+  const int64_t ss[3] = {a->batch, a->dim, a->dstate};
+  const int64_t unit[3] = {a->dim * a->dstate, a->dstate, 1};
+  const int64_t one[1] = {1};
+  // strides
+  if (!strides_nonneg(a->u_stride, 3) || !strides_nonneg(a->delta_stride, 3) ||
+      !strides_nonneg(a->B_stride, 3) || !strides_nonneg(a->C_stride, 3) ||
+      !strides_nonneg(a->out_stride, 3) || !strides_nonneg(a->A_log_stride, 2) ||
+      (a->z != nullptr && !strides_nonneg(a->z_stride, 3)))
+    return MSS_ERR_BAD_STRIDE;
+  if (!non_overlapping(xs, a->out_stride, 3)) return MSS_ERR_BAD_STRIDE;
+  if (!tile_offsets_fit(a->u_stride, es) || !tile_offsets_fit(a->delta_stride, es) ||
+      !tile_offsets_fit(a->out_stride, es) || (a->z != nullptr && !tile_offsets_fit(a->z_stride, es)) ||
+      !tile_offsets_fit(a->B_stride, es, kMaxState) || !tile_offsets_fit(a->C_stride, es, kMaxState))
+    return MSS_ERR_BAD_STRIDE;
+  // alignment
+  if (!aligned(a->u, es) || !aligned(a->delta_raw, es) || !aligned(a->B, es) ||
+      !aligned(a->C, es) || !aligned(a->z, es) || !aligned(a->out, es) || !aligned(a->A_log, 4) ||
+      !aligned(a->D, 4) || !aligned(a->dt_bias, 4) || !aligned(a->initial_state, 4) ||
+      !aligned(a->final_state, 4))
+    return MSS_ERR_MISALIGNED;
+  // aliasing: outputs against every input and each other
+  const Extent ins[] = {
+      extent_of(a->u, xs, a->u_stride, 3, es),
+      extent_of(a->delta_raw, xs, a->delta_stride, 3, es),
+      extent_of(a->z, xs, a->z_stride, 3, es),
+      extent_of(a->B, bcs, a->B_stride, 3, es),
+      extent_of(a->C, bcs, a->C_stride, 3, es),
+      extent_of(a->A_log, as, a->A_log_stride, 2, 4),
+      extent_of(a->D, vs, one, 1, 4),
+      extent_of(a->dt_bias, vs, one, 1, 4),
+      extent_of(a->initial_state, ss, unit, 3, 4),
+  };
+  const Extent eo = extent_of(a->out, xs, a->out_stride, 3, es);
+  const Extent ef = extent_of(a->final_state, ss, unit, 3, 4);
+  for (const Extent& e : ins)
+    if (overlaps(eo, e) || overlaps(ef, e)) return MSS_ERR_ALIASING;
+  if (overlaps(eo, ef)) return MSS_ERR_ALIASING;
+
+  const ScanPlan plan = make_plan(a);
+  mss::ScanPtrs p{};
+  if (plan.workspace > 0) {
+    if (a->workspace == nullptr || a->workspace_bytes < plan.workspace)
+      return MSS_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(a->workspace, 256)) return MSS_ERR_MISALIGNED;
+    const Extent ew{reinterpret_cast<uintptr_t>(a->workspace),
+                    reinterpret_cast<uintptr_t>(a->workspace) + plan.workspace, true};
+    for (const Extent& e : ins)
+      if (overlaps(ew, e)) return MSS_ERR_ALIASING;
+    if (overlaps(ew, eo) || overlaps(ew, ef)) return MSS_ERR_ALIASING;
+    char* ws = static_cast<char*>(a->workspace);
+    if (plan.agg_bytes > 0) {
+      p.agg = reinterpret_cast<float2*>(ws);
+      p.carry = reinterpret_cast<float*>(ws + plan.agg_bytes);
+    }
+    if (plan.tail_bytes > 0)
+      p.tail_h0 = reinterpret_cast<float*>(ws + plan.agg_bytes + plan.carry_bytes);
+  }
+  mss::ScanShape s = plan.shape;
+  // A dimension of size 1 is never stepped, so its stride is free: use 1.
+  norm_strides(s.su, a->u_stride, xs);
+  norm_strides(s.sd, a->delta_stride, xs);
+  norm_strides(s.so, a->out_stride, xs);
+  norm_strides(s.sB, a->B_stride, bcs);
+  norm_strides(s.sC, a->C_stride, bcs);
+  std::memcpy(s.sA, a->A_log_stride, sizeof(s.sA));
+  if (a->z != nullptr) norm_strides(s.sz, a->z_stride, xs);
+  else std::memcpy(s.sz, s.su, sizeof(s.sz));
+  // Layouts: u/delta_raw/z/out share a unit-stride axis (t or d), and so do
+  // B and C (t or n); loads move 16-byte vectors along that axis.
+  const bool x_tfast = s.su[2] == 1 && s.sd[2] == 1 && s.sz[2] == 1 && s.so[2] == 1;
+  const bool x_dfast = s.su[1] == 1 && s.sd[1] == 1 && s.sz[1] == 1 && s.so[1] == 1;
+  const bool bc_tfast = s.sB[2] == 1 && s.sC[2] == 1;
+  const bool bc_nfast = s.sB[1] == 1 && s.sC[1] == 1;
+  if (!(x_tfast || x_dfast) || !(bc_tfast || bc_nfast)) return MSS_ERR_BAD_STRIDE;
+  const bool xt = x_tfast;
+  const bool bt = bc_tfast;
+  const int V = vec_elems(a->io_dtype);
+  // bf16 vectors start at 4-byte aligned addresses only if every base pointer
+  // is 4-byte aligned and every stride other than the unit one is even.
+  s.vec_ok = 1;
+  if (es == 2) {
+    auto even = [](int64_t v) { return (v % 2) == 0; };
+    const int64_t* xsts[4] = {s.su, s.sd, s.sz, s.so};
+    const void* xps[4] = {a->u, a->delta_raw, a->z != nullptr ? a->z : a->u, a->out};
+    for (int i = 0; i < 4; ++i)
+      if (!aligned(xps[i], 4) || !even(xsts[i][0]) || !even(xsts[i][xt ? 1 : 2])) s.vec_ok = 0;
+    const int64_t* bsts[2] = {s.sB, s.sC};
+    const void* bps[2] = {a->B, a->C};
+    for (int i = 0; i < 2; ++i)
+      if (!aligned(bps[i], 4) || !even(bsts[i][0]) || !even(bsts[i][bt ? 1 : 2])) s.vec_ok = 0;
+  }
+  p.u = a->u;
+  p.delta_raw = a->delta_raw;
+  p.A_log = a->A_log;
+  p.B = a->B;
+  p.C = a->C;
+  p.D = a->D;
+  p.z = a->z;
+  p.dt_bias = a->dt_bias;
+  p.h0 = a->initial_state;
+  p.out = a->out;
+  p.final_state = a->final_state;
+  // 16-byte vectors along the unit-stride axes need the channel count (for
+  // d-fast data) and dstate (for n-fast B/C) to be whole vectors; a time axis
+  // that is not a whole number of vectors gets an element-wise tail pass.
+  s.use_vec = s.vec_ok && (xt || a->dim % V == 0) && (bt || a->dstate % V == 0);
+  if (s.use_vec && (xt || bt)) s.t_stop = static_cast<int>(a->seqlen / V * V);
+  if (s.use_vec && s.t_stop < s.seqlen && s.t_stop > 0 && p.tail_h0 == nullptr)
+    return MSS_ERR_WORKSPACE_TOO_SMALL;  // unreachable: the plan reserves it
+  if (s.use_vec) s.nseg = std::max(1, (s.t_stop + s.seg_len - 1) / s.seg_len);
+  const hipError_t e = mss::launch_scan(s, p, a->io_dtype == MSS_BF16, xt, bt,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
+mss_status mss_selective_state_update(const mss_step_args* a, void* stream) {
+  if (a == nullptr || a->struct_size != sizeof(mss_step_args) || a->reserved0 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
+  if (a->batch < 1 || a->dim < 1 || a->batch > kMaxDim || a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->batch * ((a->dim + 63) / 64) > kMaxDim || a->batch * a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
+  if (a->state == nullptr || a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr ||
+      a->B == nullptr || a->C == nullptr || a->out == nullptr)
+    return MSS_ERR_NULL_POINTER;
+  const int64_t es = a->io_dtype == MSS_BF16 ? 2 : 4;
+  if (!strides_nonneg(a->u_stride, 2) || !strides_nonneg(a->delta_stride, 2) ||
+      !strides_nonneg(a->B_stride, 2) || !strides_nonneg(a->C_stride, 2) ||
+      !strides_nonneg(a->out_stride, 2) || !strides_nonneg(a->A_log_stride, 2) ||
+      (a->z != nullptr && !strides_nonneg(a->z_stride, 2)))
+    return MSS_ERR_BAD_STRIDE;
+  const int64_t xs[2] = {a->batch, a->dim};
+  if (!non_overlapping(xs, a->out_stride, 2)) return MSS_ERR_BAD_STRIDE;
+  if (!aligned(a->state, 4) || !aligned(a->u, es) || !aligned(a->delta_raw, es) ||
+      !aligned(a->B, es) || !aligned(a->C, es) || !aligned(a->z, es) || !aligned(a->out, es) ||
+      !aligned(a->A_log, 4) || !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
+    return MSS_ERR_MISALIGNED;
+  const int64_t bcs[2] = {a->batch, a->dstate};
+  const int64_t as[2] = {a->dim, a->dstate};
+  const int64_t vs[1] = {a->dim};
+  const int64_t one[1] = {1};
+  const int64_t ss[3] = {a->batch, a->dim, a->dstate};
+  const int64_t unit[3] = {a->dim * a->dstate, a->dstate, 1};
+  const Extent ins[] = {
+      extent_of(a->u, xs, a->u_stride, 2, es),      extent_of(a->delta_raw, xs, a->delta_stride, 2, es),
+      extent_of(a->z, xs, a->z_stride, 2, es),      extent_of(a->B, bcs, a->B_stride, 2, es),
+      extent_of(a->C, bcs, a->C_stride, 2, es),     extent_of(a->A_log, as, a->A_log_stride, 2, 4),
+      extent_of(a->D, vs, one, 1, 4),               extent_of(a->dt_bias, vs, one, 1, 4),
+  };
+  const Extent eo = extent_of(a->out, xs, a->out_stride, 2, es);
+  const Extent est = extent_of(a->state, ss, unit, 3, 4);
+  for (const Extent& e : ins)
+    if (overlaps(eo, e) || overlaps(est, e)) return MSS_ERR_ALIASING;
+  if (overlaps(eo, est)) return MSS_ERR_ALIASING;
+
+  mss::StepShape s{};
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.dstate = static_cast<int>(a->dstate);
+  std::memcpy(s.su, a->u_stride, sizeof(s.su));
+  std::memcpy(s.sd, a->delta_stride, sizeof(s.sd));
+  std::memcpy(s.sz, a->z_stride, sizeof(s.sz));
+  std::memcpy(s.so, a->out_stride, sizeof(s.so));
+  std::memcpy(s.sB, a->B_stride, sizeof(s.sB));
+  std::memcpy(s.sC, a->C_stride, sizeof(s.sC));
+  std::memcpy(s.sA, a->A_log_stride, sizeof(s.sA));
+  if (a->z == nullptr) std::memset(s.sz, 0, sizeof(s.sz));
+  s.softplus = a->delta_softplus ? 1 : 0;
+  mss::StepPtrs p{a->state, a->u, a->delta_raw, a->A_log, a->B, a->C, a->D, a->z, a->dt_bias, a->out};
+  const hipError_t e = mss::launch_step(s, p, a->io_dtype == MSS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
+}  // extern "C"

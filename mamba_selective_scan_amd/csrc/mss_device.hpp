@@ -1,0 +1,97 @@
+// mss_device.hpp -- device-side helpers shared by the libmss kernels (gfx950).
+//
+// Element conversion, the stable softplus, the SiLU gate and the hardware
+// exp2.  Everything here is fp32 arithmetic on wave64 lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage types: fp32 and bf16 (raw 16-bit pattern; the kernels convert on
+// load and round to nearest even on store).
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct io_traits;
+
+template <>
+struct io_traits<float> {
+  __device__ static inline float load(const float* p) { return *p; }
+  __device__ static inline void store(float* p, float v) { *p = v; }
+};
+
+// fp32 -> bf16 bit pattern, rounded to nearest with ties to even; a NaN stays
+// a quiet NaN.
+__device__ static inline uint16_t bf16_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <>
+struct io_traits<bf16_t> {
+  __device__ static inline float load(const bf16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(p->bits) << 16);
+  }
+  __device__ static inline void store(bf16_t* p, float v) { p->bits = bf16_bits(v); }
+};
+
+// 2^x on the transcendental unit (v_exp_f32).  Arguments far below -126 give
+// 0, which is the correct limit for the decays it is used for.
+__device__ static inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2(x) on the transcendental unit (v_log_f32), for x in [1, 2].
+__device__ static inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|), in fp32.
+// log1p(e) for e = e^-|x| in (0, 1]:
+//   e <  1/8: alternating series to e^7 (truncation below 7e-9 relative);
+//   e >= 1/8: log(w) + (e - (w - 1)) with w = fl(1 + e): the bracket is the
+//             exact rounding error of w (Fast2Sum, valid as e <= 1), and
+//             dividing it by w changes the sum by less than 2^-25.
+__device__ static inline float softplus(float x) {
+  const float ax = fabsf(x);
+  const float e = fast_exp2(-ax * kLog2e);
+  float series = e * (1.0f / 7.0f);
+  series = e * (1.0f / 6.0f - series);
+  series = e * (1.0f / 5.0f - series);
+  series = e * (0.25f - series);
+  series = e * (1.0f / 3.0f - series);
+  series = e * (0.5f - series);
+  series = e * (1.0f - series);
+  const float w = 1.0f + e;
+  const float corr = e - (w - 1.0f);
+  const float logw = fast_log2(w) * kLn2 + corr;
+  const float lp = e < 0.125f ? series : logw;
+  return fmaxf(x, 0.0f) + lp;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z).
+__device__ static inline float silu(float z) {
+  const float den = 1.0f + fast_exp2(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(den);
+}
+
+// Load of a wave-uniform element (B or C) so that it can live in a scalar
+// register.  bf16: the aligned 32-bit word holding the element is read (an
+// aligned word never crosses a page) and the right half selected.
+__device__ inline float load_uniform(const float* p) { return *p; }
+__device__ inline float load_uniform(const bf16_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
+  const uint32_t sh = (a & 2) ? 16u : 0u;
+  return __uint_as_float((word >> sh) << 16);
+}
+
+// Wave-uniform value (lane 0's), kept in a scalar register.
+__device__ static inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace mss

@@ -1,0 +1,86 @@
+// mss_internal.hpp -- parameter blocks and launch entry points shared by the
+// host layer (mss_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mss {
+
+// Scan tiling.  One workgroup is one wave; it owns kCh consecutive channels of
+// one batch row and one time segment.  Lane (g, c) = (lane / kCh, lane % kCh)
+// runs states [g*kStatesPerLane, (g+1)*kStatesPerLane) of channel c, and the
+// segment is walked in chunks of kT time steps.
+constexpr int kCh = 16;
+constexpr int kGroups = 4;
+constexpr int kStatesPerLane = 4;
+constexpr int kMaxState = kGroups * kStatesPerLane;  // 16
+constexpr int kT = 32;
+constexpr int kThreads = 64;                         // one wave
+constexpr int kPerThread = kCh * kT / kThreads;      // 8 tile elements per lane
+
+// Sizes and element strides (logical order) of one scan call.  Pointers are
+// passed as separate kernel arguments so they can carry __restrict__.
+struct ScanShape {
+  int batch, dim, seqlen, dstate;
+  int groups;           // ceil(dim / kCh)
+  int nseg, seg_len;    // time segments (seg_len is a multiple of kT)
+  int64_t nchan_pad;    // batch * groups * kCh: rows of the workspace arrays
+  int64_t su[3], sd[3], sz[3], so[3];  // u, delta_raw, z, out: (b, d, t)
+  int64_t sB[3], sC[3];                // B, C: (b, n, t)
+  int64_t sA[2];                       // A_log: (d, n)
+  int softplus;
+  int vec_ok;           // every 16-byte vector of u/delta_raw/z/out/B/C is 4-byte aligned
+  int use_vec;          // the vector pass runs (else everything is element-wise)
+  int t_first, t_stop;  // this pass covers time steps [t_first, t_stop)
+};
+
+struct StepShape {
+  int batch, dim, dstate;
+  int64_t su[2], sd[2], sz[2], so[2];  // (b, d)
+  int64_t sB[2], sC[2];                // (b, n)
+  int64_t sA[2];
+  int softplus;
+};
+
+struct ScanPtrs {
+  const void* u;
+  const void* delta_raw;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  void* out;
+  float* final_state;
+  float* tail_h0;  // [batch][dim][dstate] state handed from the vector pass to the tail
+  float2* agg;    // [nseg-1][nchan_pad][kMaxState] segment (prod a, h from 0)
+  float* carry;   // [nseg][nchan_pad][kMaxState] state entering each segment
+};
+
+struct StepPtrs {
+  float* state;
+  const void* u;
+  const void* delta_raw;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  void* out;
+};
+
+// Enqueue the scan (segment aggregates, carry propagation when nseg > 1, then
+// the main pass).  io_bf16 selects the bf16 storage type; x_tfast says that
+// u/delta_raw/z/out have unit stride along t (else along d), bc_tfast that B
+// and C have unit stride along t (else along n).
+hipError_t launch_scan(const ScanShape& s, const ScanPtrs& p, bool io_bf16, bool x_tfast,
+                       bool bc_tfast, hipStream_t stream);
+
+hipError_t launch_step(const StepShape& s, const StepPtrs& p, bool io_bf16, hipStream_t stream);
+
+}  // namespace mss

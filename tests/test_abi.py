@@ -1,0 +1,236 @@
+"""The C ABI: every declared symbol is exported, the ctypes structs match the C
+layout, and every argument check fires before any HIP call.
+
+The argument-check tests pass fake device addresses; libmss rejects each call
+on the host before touching them.  They are skipped on machines with a GPU
+device node, so that a broken check could never launch on fake pointers.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mamba_selective_scan_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mss.h")
+HAS_GPU_NODE = os.path.exists("/dev/kfd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mss_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.lib()
+    decl = declared_functions()
+    assert set(decl) == set(_lib.EXPORTS), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mss_\w+)", out))
+    assert set(decl) <= exported
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib.lib()
+    assert lib.mss_abi_version() == _lib.MSS_ABI_VERSION
+    for code in _lib.STATUS:
+        s = lib.mss_status_string(code)
+        assert s and isinstance(s, bytes)
+    assert lib.mss_status_string(999) == b"unknown status"
+
+
+def _c_layout(struct_name, fields, tmp_path):
+    src = tmp_path / "probe.c"
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "mss.h"', "int main(void){",
+             f'printf("%zu\\n", sizeof({struct_name}));']
+    for f in fields:
+        lines.append(f'printf("%zu\\n", offsetof({struct_name}, {f}));')
+    lines.append("return 0;}")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("cls,cname", [(_lib.ScanArgs, "mss_scan_args"),
+                                       (_lib.StepArgs, "mss_step_args")])
+def test_ctypes_struct_matches_c_layout(cls, cname, tmp_path):
+    names = [f[0] for f in cls._fields_]
+    size, offs = _c_layout(cname, names, tmp_path)
+    assert ctypes.sizeof(cls) == size
+    assert [getattr(cls, n).offset for n in names] == offs
+
+
+def test_workspace_size_depends_on_shape_only():
+    lib = _lib.lib()
+    a = _lib.new_scan_args()
+    a.batch, a.dim, a.seqlen, a.dstate = 8, 5120, 4096, 16
+    st = ctypes.c_int(-1)
+    n = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    assert st.value == 0
+    assert n == 0                        # enough channel tiles: no time split, no scratch
+    a.batch, a.dim, a.seqlen = 1, 256, 220500
+    n2 = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    assert st.value == 0 and n2 > 0      # few channels, long sequence: segment carries
+    a.dstate = 17
+    assert lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st)) == 0
+    assert st.value == _lib.STATUS_CODE["MSS_ERR_UNSUPPORTED_DSTATE"]
+    assert lib.mss_selective_scan_workspace_size(None, ctypes.byref(st)) == 0
+    assert st.value == _lib.STATUS_CODE["MSS_ERR_BAD_STRUCT"]
+
+
+# ----------------------------------------------------------- argument checks
+
+BASE = 0x7F0000000000
+GAP = 1 << 32
+
+
+def fake(i):
+    return BASE + i * GAP
+
+
+def scan_args(batch=2, dim=96, seqlen=100, dstate=16, ws=True):
+    # this shape is split in time, so it needs a workspace: a call built with
+    # ws=False stops at the workspace check at the latest
+    a = _lib.new_scan_args()
+    a.io_dtype = _lib.MSS_F32
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, seqlen, dstate
+    x = (dim * seqlen, seqlen, 1)
+    bc = (dstate * seqlen, seqlen, 1)
+    a.u, a.u_stride = fake(0), (ctypes.c_int64 * 3)(*x)
+    a.delta_raw, a.delta_stride = fake(1), (ctypes.c_int64 * 3)(*x)
+    a.A_log, a.A_log_stride = fake(2), (ctypes.c_int64 * 2)(dstate, 1)
+    a.B, a.B_stride = fake(3), (ctypes.c_int64 * 3)(*bc)
+    a.C, a.C_stride = fake(4), (ctypes.c_int64 * 3)(*bc)
+    a.D = fake(5)
+    a.z, a.z_stride = fake(6), (ctypes.c_int64 * 3)(*x)
+    a.dt_bias = fake(7)
+    a.out, a.out_stride = fake(8), (ctypes.c_int64 * 3)(*x)
+    a.final_state = fake(9)
+    a.delta_softplus = 1
+    if ws:
+        st = ctypes.c_int(0)
+        a.workspace = fake(10)
+        a.workspace_bytes = _lib.lib().mss_selective_scan_workspace_size(ctypes.byref(a),
+                                                                         ctypes.byref(st))
+    return a
+
+
+def code(name):
+    return _lib.STATUS_CODE[name]
+
+
+def call_scan(a):
+    return _lib.lib().mss_selective_scan_fwd(ctypes.byref(a) if a is not None else None, None)
+
+
+def _mut_scan(fn, ws=False):
+    a = scan_args(ws=ws)
+    fn(a)
+    return a
+
+
+SCAN_CASES = {
+    "null_struct": (None, "MSS_ERR_BAD_STRUCT"),
+    "struct_size": (lambda a: setattr(a, "struct_size", 8), "MSS_ERR_BAD_STRUCT"),
+    "reserved": (lambda a: setattr(a, "reserved0", 1), "MSS_ERR_BAD_STRUCT"),
+    "dtype": (lambda a: setattr(a, "io_dtype", 7), "MSS_ERR_UNSUPPORTED_DTYPE"),
+    "batch0": (lambda a: setattr(a, "batch", 0), "MSS_ERR_BAD_SHAPE"),
+    "seqlen_neg": (lambda a: setattr(a, "seqlen", -3), "MSS_ERR_BAD_SHAPE"),
+    "seqlen_huge": (lambda a: setattr(a, "seqlen", 1 << 31), "MSS_ERR_BAD_SHAPE"),
+    "dstate0": (lambda a: setattr(a, "dstate", 0), "MSS_ERR_UNSUPPORTED_DSTATE"),
+    "dstate17": (lambda a: setattr(a, "dstate", 17), "MSS_ERR_UNSUPPORTED_DSTATE"),
+    "u_null": (lambda a: setattr(a, "u", None), "MSS_ERR_NULL_POINTER"),
+    "C_null": (lambda a: setattr(a, "C", None), "MSS_ERR_NULL_POINTER"),
+    "out_null": (lambda a: setattr(a, "out", None), "MSS_ERR_NULL_POINTER"),
+    "neg_stride": (lambda a: a.u_stride.__setitem__(1, -1), "MSS_ERR_BAD_STRIDE"),
+    "out_overlap": (lambda a: a.out_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
+    "tile_2gib": (lambda a: a.u_stride.__setitem__(1, 1 << 27), "MSS_ERR_BAD_STRIDE"),
+    "misaligned_u": (lambda a: setattr(a, "u", fake(0) + 2), "MSS_ERR_MISALIGNED"),
+    "misaligned_final": (lambda a: setattr(a, "final_state", fake(9) + 1), "MSS_ERR_MISALIGNED"),
+    "out_is_u": (lambda a: setattr(a, "out", fake(0)), "MSS_ERR_ALIASING"),
+    "final_in_z": (lambda a: setattr(a, "final_state", fake(6) + 64), "MSS_ERR_ALIASING"),
+    "out_on_A_log": (lambda a: setattr(a, "out", fake(2) - 8), "MSS_ERR_ALIASING"),
+    "no_workspace": (lambda a: None, "MSS_ERR_WORKSPACE_TOO_SMALL"),
+}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(SCAN_CASES))
+def test_scan_argument_checks(case):
+    assert scan_args(ws=True).workspace_bytes > 0
+    fn, expect = SCAN_CASES[case]
+    a = None if fn is None else _mut_scan(fn)
+    assert call_scan(a) == code(expect)
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+def test_scan_workspace_checks():
+    a = scan_args(ws=True)
+    a.workspace_bytes -= 1
+    assert call_scan(a) == code("MSS_ERR_WORKSPACE_TOO_SMALL")
+    a = scan_args(ws=True)
+    a.workspace = fake(10) + 128
+    assert call_scan(a) == code("MSS_ERR_MISALIGNED")
+    a = scan_args(ws=True)
+    a.workspace = fake(0)
+    assert call_scan(a) == code("MSS_ERR_ALIASING")
+
+
+def step_args():
+    a = _lib.new_step_args()
+    a.io_dtype = _lib.MSS_F32
+    a.batch, a.dim, a.dstate = 2, 96, 16
+    x = (96, 1)
+    a.state = fake(0)
+    a.u, a.u_stride = fake(1), (ctypes.c_int64 * 2)(*x)
+    a.delta_raw, a.delta_stride = fake(2), (ctypes.c_int64 * 2)(*x)
+    a.A_log, a.A_log_stride = fake(3), (ctypes.c_int64 * 2)(16, 1)
+    a.B, a.B_stride = fake(4), (ctypes.c_int64 * 2)(16, 1)
+    a.C, a.C_stride = fake(5), (ctypes.c_int64 * 2)(16, 1)
+    a.D = fake(6)
+    a.z, a.z_stride = fake(7), (ctypes.c_int64 * 2)(*x)
+    a.dt_bias = fake(8)
+    a.out, a.out_stride = fake(9), (ctypes.c_int64 * 2)(*x)
+    a.delta_softplus = 1
+    return a
+
+
+STEP_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), "MSS_ERR_BAD_STRUCT"),
+    "dtype": (lambda a: setattr(a, "io_dtype", 2), "MSS_ERR_UNSUPPORTED_DTYPE"),
+    "dim0": (lambda a: setattr(a, "dim", 0), "MSS_ERR_BAD_SHAPE"),
+    "dstate20": (lambda a: setattr(a, "dstate", 20), "MSS_ERR_UNSUPPORTED_DSTATE"),
+    "state_null": (lambda a: setattr(a, "state", None), "MSS_ERR_NULL_POINTER"),
+    "neg_stride": (lambda a: a.B_stride.__setitem__(1, -1), "MSS_ERR_BAD_STRIDE"),
+    "out_overlap": (lambda a: a.out_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
+    "misaligned": (lambda a: setattr(a, "state", fake(0) + 2), "MSS_ERR_MISALIGNED"),
+    "out_is_u": (lambda a: setattr(a, "out", fake(1)), "MSS_ERR_ALIASING"),
+    "state_on_B": (lambda a: setattr(a, "state", fake(4)), "MSS_ERR_ALIASING"),
+}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(STEP_CASES))
+def test_step_argument_checks(case):
+    fn, expect = STEP_CASES[case]
+    a = step_args()
+    fn(a)
+    assert _lib.lib().mss_selective_state_update(ctypes.byref(a), None) == code(expect)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib(str(tmp_path / "missing.so"))

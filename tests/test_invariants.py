@@ -1,0 +1,110 @@
+"""Bitwise invariants of the HIP path: determinism, linearity in u, causality,
+layout equivalence and channel permutation."""
+
+import numpy as np
+import pytest
+
+from gpu_util import device, note
+from mamba_selective_scan_amd.inputs import generate, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mss():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import mamba_selective_scan_amd as m
+    return m
+
+
+def _run(mss, dx):
+    return mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                  D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                  return_final_state=True)
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 300), (1, 64, 9000)])
+def test_run_twice_identical(mss, shape):
+    import torch
+    note(f"determinism {shape}")
+    dx = to_torch(generate(*shape, 16, seed=1), device(), "f32")
+    a, fa = _run(mss, dx)
+    b, fb = _run(mss, dx)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(fa, fb)
+
+
+def test_linear_in_u(mss):
+    import torch
+    note("linearity")
+    dx = to_torch(generate(2, 100, 500, 16, seed=2), device(), "f32")
+    a, fa = _run(mss, dx)
+    dx2 = dict(dx)
+    dx2["u"] = dx["u"] * 2
+    b, fb = _run(mss, dx2)
+    torch.cuda.synchronize()
+    assert torch.equal(b, 2 * a) and torch.equal(fb, 2 * fa)
+
+
+def test_causal(mss):
+    import torch
+    note("causality")
+    dx = to_torch(generate(1, 130, 700, 16, seed=3), device(), "f32")
+    a, _ = _run(mss, dx)
+    t0 = 333
+    dx2 = dict(dx)
+    for k in ("u", "delta_raw", "z", "B", "C"):
+        v = dx[k].clone()
+        v[:, :, t0:] += 0.25
+        dx2[k] = v
+    b, _ = _run(mss, dx2)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :, :t0], b[:, :, :t0])
+    assert not torch.equal(a[:, :, t0], b[:, :, t0])
+
+
+def test_layout_equivalence(mss):
+    """[B,D,L] and [B,L,D] storage of the same values give the same bits."""
+    import torch
+    note("layout equivalence")
+    x = generate(2, 96, 400, 16, seed=4)
+    dx = to_torch(x, device(), "f32")
+    a, fa = _run(mss, dx)
+    dl = dict(dx)
+    for k in ("u", "delta_raw", "z", "B", "C"):
+        dl[k] = dx[k].transpose(1, 2).contiguous().transpose(1, 2)
+    b, fb = _run(mss, dl)
+    torch.cuda.synchronize()
+    assert b.stride()[1] == 1
+    assert torch.equal(a, b) and torch.equal(fa, fb)
+
+
+def test_channel_permutation(mss):
+    import torch
+    note("channel permutation")
+    dx = to_torch(generate(1, 128, 300, 16, seed=5, a_log="normal", d_skip="normal"), device(), "f32")
+    perm = torch.randperm(128, generator=torch.Generator().manual_seed(0)).to(device())
+    a, fa = _run(mss, dx)
+    dp = dict(dx)
+    for k in ("u", "delta_raw", "z"):
+        dp[k] = dx[k][:, perm].contiguous()
+    for k in ("A_log", "D", "dt_bias"):
+        dp[k] = dx[k][perm].contiguous()
+    b, fb = _run(mss, dp)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, perm], b) and torch.equal(fa[:, perm], fb)
+
+
+def test_argument_errors_with_real_tensors(mss):
+    """Argument checks on real device tensors: rejected before any launch."""
+    import torch
+    from mamba_selective_scan_amd import MssError
+    note("argument errors")
+    dx = to_torch(generate(1, 64, 50, 16, seed=6), device(), "f32")
+    with pytest.raises(MssError) as e:
+        mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                               out=dx["u"])
+    assert e.value.name == "MSS_ERR_ALIASING"
+    with pytest.raises(ValueError):
+        mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"][:, :8], dx["B"], dx["C"])

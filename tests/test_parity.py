@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path against the fp64 oracle on seeded synthetic inputs.
+
+Tolerances (error metric: max |o - r| / (|r| + rms(r))): 1e-4 for fp32 I/O,
+2e-2 for bf16 I/O with fp32 state.  Small problems are compared element by
+element everywhere; full-size workloads are compared on sampled channels, each
+over its whole sequence (the oracle computes one channel at a time), plus the
+exported final state of those channels.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (check, device, note, oracle_full, run_gpu, sample_channels, to_np,
+                      tol_for)
+from mamba_selective_scan_amd.inputs import WORKLOADS, generate, generate_workload, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mss():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import mamba_selective_scan_amd as m
+    return m
+
+
+def _full_case(mss, name, batch, dim, seqlen, dstate, layout="bdl", io="f32", seed=0,
+               a_log="ladder", d_skip="ones", **flags):
+    note(f"{name}: B={batch} D={dim} L={seqlen} N={dstate} {layout} {io} seed={seed} {flags}")
+    x = generate(batch, dim, seqlen, dstate, layout, seed=seed, a_log=a_log, d_skip=d_skip)
+    if not flags.get("softplus", True):
+        # Without softplus delta = delta_raw + dt_bias is used as is; keep it
+        # positive (dt_bias = the time step itself, |delta_raw| scaled down) so
+        # the recurrence stays bounded (a negative delta makes |a| > 1).
+        x["dt_bias"] = np.log1p(np.exp(x["dt_bias"].astype(np.float64))).astype(np.float32)
+        x["delta_raw"] = np.abs(x["delta_raw"]) * np.float32(0.1)
+    dx = to_torch(x, device(), io)
+    h0 = flags.pop("h0", False)
+    init = None
+    if h0:
+        import torch
+        g = torch.Generator().manual_seed(seed + 100)
+        init = torch.randn(batch, dim, dstate, generator=g).to(device())
+    out, fin = run_gpu(mss, dx, initial_state=init, **flags)
+    import torch
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle_full(dx, initial_state=init, **flags)
+    tol = tol_for(io)
+    check(f"{name} out", to_np(out), ref_out, tol)
+    check(f"{name} final_state", to_np(fin), ref_fin, tol)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_workload(mss, seed):
+    w = WORKLOADS["tiny"]
+    _full_case(mss, "tiny", w.batch, w.dim, w.seqlen, w.dstate, seed=seed)
+
+
+def test_mamba130m_layer_full(mss):
+    w = WORKLOADS["mamba130m_layer"]
+    _full_case(mss, "mamba130m_layer", w.batch, w.dim, w.seqlen, w.dstate)
+
+
+@pytest.mark.parametrize("seqlen", [1, 7, 31, 33, 63, 2049, 4097])
+def test_ragged_lengths(mss, seqlen):
+    _full_case(mss, f"ragged L={seqlen}", 2, 72, seqlen, 16)
+
+
+@pytest.mark.parametrize("dstate", [1, 3, 4, 5, 13])
+def test_small_dstate(mss, dstate):
+    _full_case(mss, f"dstate={dstate}", 1, 130, 300, dstate)
+
+
+@pytest.mark.parametrize("flags", [
+    dict(with_z=False), dict(with_D=False), dict(with_bias=False), dict(softplus=False),
+    dict(with_z=False, with_D=False), dict(h0=True), dict(with_z=False, with_D=False, h0=True),
+])
+def test_optional_inputs(mss, flags):
+    _full_case(mss, f"flags {sorted(flags)}", 2, 100, 777, 16, **dict(flags))
+
+
+def test_random_A_log_and_D(mss):
+    _full_case(mss, "random A_log, D", 2, 128, 1000, 16, a_log="normal", d_skip="normal")
+
+
+def test_ssm_only_term(mss):
+    """D = 0 and no gate: the output is the scan term alone."""
+    _full_case(mss, "ssm only", 1, 192, 2048, 16, d_skip="zeros", with_z=False, with_D=False)
+
+
+@pytest.mark.parametrize("seqlen", [100, 5000])
+def test_channel_last_layout_small(mss, seqlen):
+    _full_case(mss, f"bld L={seqlen}", 1, 100, seqlen, 16, layout="bld")
+
+
+@pytest.mark.parametrize("seqlen", [70, 3000])
+def test_bf16_small(mss, seqlen):
+    _full_case(mss, f"bf16 L={seqlen}", 2, 96, seqlen, 16, io="bf16")
+
+
+def test_time_split_with_initial_state(mss):
+    """Few channels and a long sequence: the segmented path, started from h0."""
+    _full_case(mss, "split+h0", 1, 64, 20000, 16, h0=True)
+
+
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+def test_views_into_padded_buffers(mss, layout):
+    """Views with offsets and padded row strides (the unit-stride axis kept)."""
+    import torch
+    note(f"padded views {layout}")
+    bsz, dim, L, N = 2, 80, 301, 16
+    x = generate(bsz, dim, L, N, seed=5)
+    dx = to_torch(x, device(), "f32")
+    big = {}
+    for k in ("u", "delta_raw", "z"):
+        if layout == "bdl":
+            buf = torch.zeros(bsz, dim + 9, L + 11, device=device())
+            buf[:, 1:1 + dim, 5:5 + L] = dx[k]
+            big[k] = buf[:, 1:1 + dim, 5:5 + L]
+        else:
+            buf = torch.zeros(bsz, L + 11, dim + 9, device=device())
+            buf[:, 5:5 + L, 1:1 + dim] = dx[k].transpose(1, 2)
+            big[k] = buf[:, 5:5 + L, 1:1 + dim].transpose(1, 2)
+    for k in ("B", "C"):
+        if layout == "bdl":
+            buf = torch.zeros(bsz, N + 3, L + 7, device=device())
+            buf[:, 2:2 + N, 3:3 + L] = dx[k]
+            big[k] = buf[:, 2:2 + N, 3:3 + L]
+        else:
+            buf = torch.zeros(bsz, L + 7, N + 3, device=device())
+            buf[:, 3:3 + L, 2:2 + N] = dx[k].transpose(1, 2)
+            big[k] = buf[:, 3:3 + L, 2:2 + N].transpose(1, 2)
+    for k in ("A_log", "D", "dt_bias"):
+        big[k] = dx[k]
+    out, fin = run_gpu(mss, big)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle_full(dx)
+    check(f"padded views {layout} out", to_np(out), ref_out, 1e-4)
+    check(f"padded views {layout} final", to_np(fin), ref_fin, 1e-4)
+
+
+def test_no_unit_stride_axis_is_rejected(mss):
+    import torch
+    from mamba_selective_scan_amd import MssError
+    note("no unit-stride axis")
+    dx = to_torch(generate(1, 16, 64, 16, seed=6), device(), "f32")
+    buf = torch.zeros(1, 16, 128, device=device())
+    strided = buf[:, :, ::2]
+    with pytest.raises(MssError) as e:
+        mss.selective_scan_fwd(strided, dx["delta_raw"], dx["A_log"], dx["B"], dx["C"])
+    assert e.value.name == "MSS_ERR_BAD_STRIDE"
+
+
+# ------------------------------------------------------------ full workloads
+
+def _sampled_workload(mss, wname, io, k, seed=0):
+    import torch
+    w = WORKLOADS[wname]
+    note(f"{wname} {io}: generating inputs")
+    x = generate_workload(w, seed=seed)
+    dx = to_torch(x, device(), io)
+    note(f"{wname} {io}: GPU scan")
+    out, fin = run_gpu(mss, dx)
+    torch.cuda.synchronize()
+    chans = sample_channels(w.batch, w.dim, k, seed)
+    note(f"{wname} {io}: oracle on {len(chans)} channels")
+    ref_out, ref_fin = oracle.scan_channels(dx, chans)
+    got_out = np.stack([to_np(out[b, d]) for b, d in chans])
+    got_fin = np.stack([to_np(fin[b, d]) for b, d in chans])
+    tol = tol_for(io)
+    check(f"{wname} {io} out (sampled)", got_out, ref_out, tol)
+    check(f"{wname} {io} final (sampled)", got_fin, ref_fin, tol)
+
+
+def test_mamba2p8b_layer_fp32_sampled(mss):
+    _sampled_workload(mss, "mamba2p8b_layer", "f32", 96)
+
+
+def test_mamba2p8b_layer_bf16_sampled(mss):
+    _sampled_workload(mss, "mamba2p8b_layer", "bf16", 96)
+
+
+def test_audio_channel_last_sampled(mss):
+    _sampled_workload(mss, "audio_channel_last", "f32", 48)
+
+
+def test_golden_fixtures_on_gpu(mss):
+    import golden_cases
+    import torch
+    for name in golden_cases.ALL:
+        c = golden_cases.load(name)
+        note(f"golden {name}")
+        f32 = lambda a: torch.tensor(a, dtype=torch.float32, device=device())
+        if c["kind"] == "scan":
+            out, fin = mss.selective_scan_fwd(f32(c["u"]), f32(c["delta_raw"]), f32(c["A_log"]),
+                                              f32(c["B"]), f32(c["C"]), D=f32(c["D"]),
+                                              delta_softplus=False, return_final_state=True)
+        else:
+            st = f32(c["state"])
+            out = mss.selective_state_update(st, f32(c["u"]), f32(c["delta_raw"]), f32(c["A_log"]),
+                                             f32(c["B"]), f32(c["C"]), D=f32(c["D"]),
+                                             delta_softplus=False)
+            fin = st
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(to_np(out), c["y"], rtol=2e-6, atol=2e-6)
+        np.testing.assert_allclose(to_np(fin), c["final"], rtol=2e-6, atol=2e-6)
