@@ -52,26 +52,16 @@ __device__ static inline float fast_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ static inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|), in fp32.
-// log1p(e) for e = e^-|x| in (0, 1]:
-//   e <  1/8: alternating series to e^7 (truncation below 7e-9 relative);
-//   e >= 1/8: log(w) + (e - (w - 1)) with w = fl(1 + e): the bracket is the
-//             exact rounding error of w (Fast2Sum, valid as e <= 1), and
-//             dividing it by w changes the sum by less than 2^-25.
+// With e = e^-|x| in (0, 1] and w = fl(1 + e), log1p(e) = log(w) + (e - (w - 1))
+// up to a relative 2^-24: the bracket is the exact rounding error of w
+// (Fast2Sum, valid as e <= 1) and dividing it by w would change the sum by less
+// than 2^-25.  The hardware log2 is accurate to a few ulp of its result for w
+// near 1, so the sum keeps full relative precision even when e is tiny.
 __device__ static inline float softplus(float x) {
-  const float ax = fabsf(x);
-  const float e = fast_exp2(-ax * kLog2e);
-  float series = e * (1.0f / 7.0f);
-  series = e * (1.0f / 6.0f - series);
-  series = e * (1.0f / 5.0f - series);
-  series = e * (0.25f - series);
-  series = e * (1.0f / 3.0f - series);
-  series = e * (0.5f - series);
-  series = e * (1.0f - series);
+  const float e = fast_exp2(-fabsf(x) * kLog2e);
   const float w = 1.0f + e;
   const float corr = e - (w - 1.0f);
-  const float logw = fast_log2(w) * kLn2 + corr;
-  const float lp = e < 0.125f ? series : logw;
-  return fmaxf(x, 0.0f) + lp;
+  return fmaxf(x, 0.0f) + fmaf(fast_log2(w), kLn2, corr);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).
