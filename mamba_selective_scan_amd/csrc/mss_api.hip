@@ -74,7 +74,7 @@ bool non_overlapping(const int64_t* sizes, const int64_t* strides, int rank) {
   return true;
 }
 
-// Each 16-channel x 32-step tile (16-state x 32-step for B and C) is
+// Each kCh-channel x kT-step tile (16-state x kT-step for B and C) is
 // addressed with 32-bit byte offsets from a per-tile base.
 bool tile_offsets_fit(const int64_t* st, int64_t elem, int64_t rows = kCh) {
   const int64_t span = ((rows - 1) * st[1] + (kT - 1) * st[2] + 1) * elem;
@@ -88,8 +88,8 @@ struct ScanPlan {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// elements per 16-byte vector of the io type
-int vec_elems(int32_t io_dtype) { return io_dtype == MSS_BF16 ? 8 : 4; }
+// elements per load/store vector (16 bytes of fp32, 8 bytes of bf16)
+int vec_elems(int32_t) { return mss::kVec; }
 
 mss_status check_shape(const mss_scan_args* a) {
   if (a == nullptr || a->struct_size != sizeof(mss_scan_args) || a->reserved0 != 0)
@@ -98,7 +98,7 @@ mss_status check_shape(const mss_scan_args* a) {
   if (a->batch < 1 || a->dim < 1 || a->seqlen < 1) return MSS_ERR_BAD_SHAPE;
   if (a->batch > kMaxDim || a->dim > kMaxDim || a->seqlen > kMaxSeqlen) return MSS_ERR_BAD_SHAPE;
   if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
-  // batch * ceil(dim/64) workgroups in grid x; batch * dim * dstate states
+  // batch * ceil(dim/kCh) workgroups in grid x; batch * dim * dstate states
   const int64_t groups = (a->dim + kCh - 1) / kCh;
   if (a->batch * groups > kMaxDim) return MSS_ERR_BAD_SHAPE;
   if (a->batch * a->dim > kMaxDim) return MSS_ERR_BAD_SHAPE;
@@ -129,7 +129,7 @@ ScanPlan make_plan(const mss_scan_args* a) {
     p.agg_bytes = round_up(static_cast<size_t>(s.nseg - 1) * s.nchan_pad * kMaxState * sizeof(float2), 256);
     p.carry_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float), 256);
   }
-  // a sequence that does not end on a 16-byte vector boundary ends with an
+  // a sequence that does not end on a vector boundary ends with an
   // element-wise pass that starts from a state handed over in the workspace
   if (a->seqlen % vec_elems(a->io_dtype) != 0)
     p.tail_bytes = round_up(static_cast<size_t>(a->batch * a->dim * a->dstate) * sizeof(float), 256);
@@ -246,7 +246,7 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   if (a->z != nullptr) norm_strides(s.sz, a->z_stride, xs);
   else std::memcpy(s.sz, s.su, sizeof(s.sz));
   // Layouts: u/delta_raw/z/out share a unit-stride axis (t or d), and so do
-  // B and C (t or n); loads move 16-byte vectors along that axis.
+  // B and C (t or n); loads move kVec-element vectors along that axis.
   const bool x_tfast = s.su[2] == 1 && s.sd[2] == 1 && s.sz[2] == 1 && s.so[2] == 1;
   const bool x_dfast = s.su[1] == 1 && s.sd[1] == 1 && s.sz[1] == 1 && s.so[1] == 1;
   const bool bc_tfast = s.sB[2] == 1 && s.sC[2] == 1;
@@ -255,8 +255,9 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   const bool xt = x_tfast;
   const bool bt = bc_tfast;
   const int V = vec_elems(a->io_dtype);
-  // bf16 vectors start at 4-byte aligned addresses only if every base pointer
-  // is 4-byte aligned and every stride other than the unit one is even.
+  // bf16 vectors (8 bytes) start at 4-byte aligned addresses only if every
+  // base pointer is 4-byte aligned and every stride other than the unit one is
+  // even.
   s.vec_ok = 1;
   if (es == 2) {
     auto even = [](int64_t v) { return (v % 2) == 0; };
@@ -280,7 +281,7 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   p.h0 = a->initial_state;
   p.out = a->out;
   p.final_state = a->final_state;
-  // 16-byte vectors along the unit-stride axes need the channel count (for
+  // Vectors along the unit-stride axes need the channel count (for
   // d-fast data) and dstate (for n-fast B/C) to be whole vectors; a time axis
   // that is not a whole number of vectors gets an element-wise tail pass.
   s.use_vec = s.vec_ok && (xt || a->dim % V == 0) && (bt || a->dstate % V == 0);

@@ -9,16 +9,18 @@
 namespace mss {
 
 // Scan tiling.  One workgroup is one wave; it owns kCh consecutive channels of
-// one batch row and one time segment.  Lane (g, c) = (lane / kCh, lane % kCh)
-// runs states [g*kStatesPerLane, (g+1)*kStatesPerLane) of channel c, and the
-// segment is walked in chunks of kT time steps.
-constexpr int kCh = 16;
-constexpr int kGroups = 4;
-constexpr int kStatesPerLane = 4;
+// one batch row and one time segment.  In the scan, lane (g, c) =
+// (lane / kCh, lane % kCh) runs states [g*kStatesPerLane, (g+1)*kStatesPerLane)
+// of channel c, and the segment is walked in chunks of kT time steps.  Loads
+// and stores move kVec-element vectors along the unit-stride axis.
+constexpr int kCh = 8;
+constexpr int kGroups = 8;
+constexpr int kStatesPerLane = 2;
 constexpr int kMaxState = kGroups * kStatesPerLane;  // 16
 constexpr int kT = 32;
 constexpr int kThreads = 64;                         // one wave
-constexpr int kPerThread = kCh * kT / kThreads;      // 8 tile elements per lane
+constexpr int kVec = 4;
+constexpr int kPerThread = kCh * kT / kThreads;      // 4 tile elements per lane
 
 // Sizes and element strides (logical order) of one scan call.  Pointers are
 // passed as separate kernel arguments so they can carry __restrict__.
@@ -31,7 +33,7 @@ struct ScanShape {
   int64_t sB[3], sC[3];                // B, C: (b, n, t)
   int64_t sA[2];                       // A_log: (d, n)
   int softplus;
-  int vec_ok;           // every 16-byte vector of u/delta_raw/z/out/B/C is 4-byte aligned
+  int vec_ok;           // every kVec-element vector of u/delta_raw/z/out/B/C is 4-byte aligned
   int use_vec;          // the vector pass runs (else everything is element-wise)
   int t_first, t_stop;  // this pass covers time steps [t_first, t_stop)
 };

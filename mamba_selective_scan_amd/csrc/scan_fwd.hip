@@ -10,21 +10,22 @@
 // "なぜ「scan」か" and "1チャンク内の処理フロー").
 //
 // Mapping.  A is diagonal, so the dstate entries are independent recurrences
-// that only meet in the sum over C.  One wave (the whole workgroup) owns 16
-// channels of one batch row for one time segment.  Lane (g, c) = (lane / 16,
-// lane % 16) runs states 4g..4g+3 of channel c sequentially in time, in
-// registers; A_log becomes exp2 multipliers with log2(e) folded in, once per
-// lane.  The segment is walked in chunks of kT steps, each in three phases:
-//   E  loads of u, delta_raw, B, C (issued one chunk ahead) with time across
-//      lanes for [B,D,L] data (channels across lanes for [B,L,D]); softplus,
-//      delta*u and D*u per element; (delta, delta*u) and B/C go to LDS;
-//   S  per step and state one exp2, two multiplies and two FMAs.  B and C are
-//      the same for all channels: one LDS load gives each 16-lane row the 16
-//      coefficients its state group needs for two steps, and the multiplies
-//      read them through a DPP row broadcast (row_newbcast).  The partial sums
-//      C.h of the four state groups meet through v_permlane32_swap and
-//      v_permlane16_swap: two swap-and-add levels reduce four steps at once
-//      and leave the totals of those steps in the four rows;
+// that only meet in the sum over C.  One wave (the whole workgroup) owns 8
+// channels of one batch row for one time segment.  In the scan, lane
+// (g, c) = (lane / 8, lane % 8) runs states 2g and 2g+1 of channel c
+// sequentially in time, in registers; A_log becomes exp2 multipliers with
+// log2(e) folded in, once per lane.  Small waves keep several per SIMD: the
+// SIMD's VALU switches to another wave while one waits for memory, and the
+// work spreads evenly over the SIMDs.  The segment is walked in chunks of kT
+// steps, each in three phases:
+//   E  loads of u, delta_raw, B and C (issued ahead of use) with 4-element
+//      vectors along the unit-stride axis; softplus, delta*u and D*u per
+//      element; (delta, delta*u) and B/C go to LDS;
+//   S  per step and state one exp2, two multiplies and two FMAs, all on plain
+//      VGPR operands: each lane reads the B and C of its two states from LDS
+//      four steps at a time.  The partial sums C.h of the eight state groups
+//      of a channel meet through v_permlane32_swap, v_permlane16_swap and one
+//      DPP row rotation; two swap-and-add levels reduce four steps at once;
 //   O  the totals go through LDS back to the load layout, where the skip term
 //      and the gate are applied and the output is stored.
 // Every phase is wave-local: there is no workgroup barrier, so waves drift
@@ -54,23 +55,27 @@ constexpr int kRsrcRange = 0x7FFFFFF0;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOffNone = 0x80000000u;
 
+using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
-// 16-byte vector <-> elements, and single-element buffer access, per type.
+// 4-element vectors (16 bytes of fp32, 8 bytes of bf16) and single-element
+// buffer access, per storage type.
 template <typename IO>
 struct vec_io;
 template <>
 struct vec_io<float> {
-  static constexpr int V = 4;
-  __device__ static inline void unpack(u32x4 w, float* o) {
+  __device__ static inline void load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
+                                     float* o) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = __uint_as_float(w[j]);
   }
-  __device__ static inline u32x4 pack(const float* y) {
+  __device__ static inline void store(const float* y, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                      uint32_t soff) {
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(y[j]);
-    return w;
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, soff, 0);
   }
   __device__ static inline float load_one(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
@@ -82,21 +87,23 @@ struct vec_io<float> {
 };
 template <>
 struct vec_io<bf16_t> {
-  static constexpr int V = 8;
-  __device__ static inline void unpack(u32x4 w, float* o) {
+  __device__ static inline void load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff,
+                                     float* o) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       o[2 * j] = __uint_as_float(w[j] << 16);
       o[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
     }
   }
-  __device__ static inline u32x4 pack(const float* y) {
-    u32x4 w;
+  __device__ static inline void store(const float* y, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                      uint32_t soff) {
+    u32x2 w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       w[j] = static_cast<uint32_t>(bf16_bits(y[2 * j])) |
              (static_cast<uint32_t>(bf16_bits(y[2 * j + 1])) << 16);
-    return w;
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, 0);
   }
   __device__ static inline float load_one(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
     return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0))
@@ -108,80 +115,63 @@ struct vec_io<bf16_t> {
   }
 };
 
-constexpr int kXcds = 8;                          // MI355X: 8 accelerator dies, 32 CUs each
-constexpr int kDdPitch = kCh + 1;                 // float2 per step row of (delta, delta*u)
-constexpr int kYPitch = kCh + 1;                  // floats per step row of the totals
-constexpr int kBcPitch = kGroups * 8 + 1;         // floats per step row of the B/C tile
-constexpr int kBcPerLane = 2 * kMaxState * kT / kThreads;  // 16 B/C values per lane per chunk
-
-// Value held by lane K of this lane's 16-lane row (DPP row_newbcast).
-template <int K>
-__device__ inline float row_bcast(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+constexpr int kXcds = 8;                // MI355X: 8 accelerator dies, 32 CUs each
+constexpr int kBcRows = 2 * kMaxState;  // B0..B15, C0..C15
+// LDS layouts (floats).  Rows are 16-byte aligned for 128-bit accesses, and
+// the eight distinct rows that one S-phase instruction reads fall in distinct
+// bank groups: s_dd rows are padded; s_bc rows are not (the LDS budget allows
+// five waves per SIMD only without the padding) and instead store the
+// 4-step group q of row r at position q ^ ((r / 2) % 8).
+constexpr int kDdPitch = 2 * kT + 4;  // s_dd[channel][t] as (delta, delta*u) pairs
+__device__ inline int bc_index(int row, int t) {
+  return row * kT + ((((t >> 2) ^ (row >> 1)) & 7) << 2) + (t & 3);
 }
+constexpr int kSkipPitch = kT + 4;    // s_skip[channel][t]
 
-// acc += (lane K of bc's row) * x, in one v_fmac_f32 with a DPP source.  bc is
-// always an LDS load result, never written by a VALU instruction, so the DPP
-// read needs no wait states.
-template <int K>
-__device__ inline void fmac_row_bcast(float& acc, float bc, float x) {
-  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-      : "+v"(acc)
-      : "v"(bc), "v"(x), "n"(K));
-}
+struct f4 {
+  float x, y, z, w;
+};
+__device__ inline f4 lds_f4(const float* p) { return *reinterpret_cast<const f4*>(p); }
 
-// One time step of a lane's 4 states.  bc holds, per 16-lane row, B0..B3 and
-// C0..C3 of the row's state group for step 2p in lanes 0..7 and for step 2p+1
-// in lanes 8..15; S selects the half.  Returns the partial sum of C.h.
-template <int S, bool AGG>
-__device__ inline float scan_step(float dl, float du, float bc, const float (&A2)[kStatesPerLane],
-                                  float (&h)[kStatesPerLane]) {
-  const float a0 = fast_exp2(dl * A2[0]);
-  const float a1 = fast_exp2(dl * A2[1]);
-  const float a2 = fast_exp2(dl * A2[2]);
-  const float a3 = fast_exp2(dl * A2[3]);
-  h[0] = fmaf(a0, h[0], du * row_bcast<8 * S + 0>(bc));
-  h[1] = fmaf(a1, h[1], du * row_bcast<8 * S + 1>(bc));
-  h[2] = fmaf(a2, h[2], du * row_bcast<8 * S + 2>(bc));
-  h[3] = fmaf(a3, h[3], du * row_bcast<8 * S + 3>(bc));
-  if constexpr (AGG) {
-    return 0.0f;
-  } else {
-    float y = row_bcast<8 * S + 4>(bc) * h[0];
-    fmac_row_bcast<8 * S + 5>(y, bc, h[1]);
-    fmac_row_bcast<8 * S + 6>(y, bc, h[2]);
-    fmac_row_bcast<8 * S + 7>(y, bc, h[3]);
-    return y;
-  }
-}
-
-// Sum over the four rows (state groups) of four per-step partial sums.  Row r
-// of the result holds the total of step {0, 2, 1, 3}[r].
+// Sum over the eight state groups of one channel (lanes c + 8g) of four
+// per-step partial sums.  The two swap-and-add levels sum over lane bits 5 and
+// 4 and leave step {0, 2, 1, 3}[row] in 16-lane row `row`; a DPP rotation by 8
+// within the row adds lane bit 3.  Both lanes c and c + 8 of a row end with
+// the same total.
 __device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
   const auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y0), __float_as_uint(y1),
                                                     false, false);
   const auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y2), __float_as_uint(y3),
                                                     false, false);
-  // rows 0,1: y0 (resp. y2) summed over groups {0,2} and {1,3}; rows 2,3: y1 (resp. y3)
   const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
   const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
   const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(p01), __float_as_uint(p23),
                                                   false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  const float w = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  // row_ror:8 -- lane i of a row reads lane (i + 8) mod 16
+  return w + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x128, 0xF, 0xF,
+                                                        false));
 }
 
+// Five waves per SIMD (at most 96 VGPRs) for the vector paths; the
+// element-wise paths (ragged tails, unaligned views) and the fp32 d-fast
+// n-fast path need more registers and run four.
+template <typename IO, bool VEC, bool XT, bool BT>
+constexpr int kWavesPerSimd = (VEC && (XT || BT || sizeof(IO) == 2)) ? 5 : 4;
+
 template <typename IO, bool XT, bool BT, bool AGG, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void scan_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    kWavesPerSimd<IO, VEC, XT, BT>, 8))) void scan_kernel(
     ScanShape s, const IO* __restrict__ u, const IO* __restrict__ delta_raw,
     const float* __restrict__ A_log, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
     const float* __restrict__ Dskip, const IO* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ h0, IO* __restrict__ out,
     float* __restrict__ final_state, float2* __restrict__ agg,
     const float* __restrict__ carry) {
-  __shared__ float2 s_dd[kT * kDdPitch];            // (delta, delta*u) by [t][channel]
-  __shared__ float s_bc[kT * kBcPitch];             // B/C by [t][group][B0..3, C0..3]
-  __shared__ float s_y[AGG ? 1 : kT * kYPitch];     // step totals by [t][channel]
+  __shared__ __attribute__((aligned(16))) float s_bc[(AGG ? kMaxState : kBcRows) * kT];
+  __shared__ __attribute__((aligned(16))) float s_dd[kCh * kDdPitch];
+  __shared__ __attribute__((aligned(16))) float s_skip[AGG ? 4 : kCh * kSkipPitch];
+  __shared__ __attribute__((aligned(16))) float s_chan[2 * kCh];  // dt_bias, D of the tile (d-fast)
 
   const int lane = threadIdx.x;
   // Workgroups are dispatched round-robin over the XCDs (linear id mod 8).
@@ -201,8 +191,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   constexpr int64_t es = sizeof(IO);
 
   // ---- S-phase constants: lane = (state group sg, channel sc) ----
-  const int sg = lane >> 4;
-  const int sc = lane & 15;
+  const int sg = lane >> 3;
+  const int sc = lane & 7;
   const int d = d0 + sc;
   const bool dvalid = d < s.dim;
   const int64_t chan_row = static_cast<int64_t>(b) * s.groups * kCh + sc + d0;  // workspace row
@@ -230,132 +220,126 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   // an offset beyond the descriptor's range, so the hardware returns 0 (or
   // drops the store) without a branch: every chunk issues the same
   // instruction stream and the compiler counts outstanding loads exactly.
-  // Loads and stores move 16-byte vectors (4 fp32 or 8 bf16) along the
-  // unit-stride axis; a chunk whose vectors would straddle a tensor edge (a
-  // ragged tail) takes an element-wise path instead.
+  // Each lane moves one 4-element vector per x-tensor and chunk along the
+  // unit-stride axis: for t-fast data lane (xa, xb) = (lane / 8, lane % 8)
+  // covers channel xa, steps 4xb..4xb+3 (8 rows of 128 fp32 bytes); for
+  // d-fast data lane (lane / 2, lane % 2) covers step lane / 2, channels
+  // 4(lane % 2)..+3.  A chunk whose vectors would straddle a tensor edge (a
+  // ragged tail) takes the element-wise instantiation instead.
   using VIO = vec_io<IO>;
-  constexpr int V = VIO::V;                 // elements per 16-byte vector
-  constexpr int NV = kPerThread / V;        // vectors per lane per x-tensor
-  constexpr int XL = XT ? kT / V : kCh / V; // lanes per row of vectors
-  constexpr int XR = kThreads / XL;         // rows per load instruction
-  constexpr int NBV = kBcPerLane / V;       // B/C vectors per lane
-  constexpr int BL = BT ? kT / V : kMaxState / V;
-  constexpr int BR = kThreads / BL;
-  const int xr = lane / XL, xv = lane % XL;
-  const int br = lane / BL, bv = lane % BL;
-  // x-tensors: vector v of this lane covers elements e = v*V + j
-  auto x_c = [&](int v, int j) __attribute__((always_inline)) { return XT ? xr + XR * v : xv * V + j; };
-  auto x_t = [&](int v, int j) __attribute__((always_inline)) { return XT ? xv * V + j : xr + XR * v; };
+  const int xa = XT ? lane >> 3 : lane >> 1;
+  const int xb = XT ? lane & 7 : lane & 1;
+  auto x_c = [&](int j) __attribute__((always_inline)) { return XT ? xa : 4 * xb + j; };
+  auto x_t = [&](int j) __attribute__((always_inline)) { return XT ? 4 * xb + j : xa; };
   auto x_voff = [&](const int64_t* st) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>(((XT ? xr : xv * V) * st[1] + (XT ? xv * V : xr) * st[2]) * es);
+    return static_cast<uint32_t>((x_c(0) * st[1] + x_t(0) * st[2]) * es);
   };
-  auto x_soff = [&](const int64_t* st, int v) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>(XR * v * (XT ? st[1] : st[2]) * es);
+  // B/C: instruction i (0, 1: B; 2, 3: C) of a lane covers, for t-fast B/C,
+  // state (lane / 8) + 8(i % 2) at steps 4(lane % 8)..+3, and for n-fast B/C
+  // step (lane / 4) + 16(i % 2) at states 4(lane % 4)..+3.
+  const int ba = BT ? lane >> 3 : lane >> 2;
+  const int bb = BT ? lane & 7 : lane & 3;
+  auto bc_n = [&](int i, int j) __attribute__((always_inline)) {
+    return BT ? ba + 8 * (i & 1) : 4 * bb + j;
   };
-  const uint32_t vo_u = x_voff(s.su), vo_d = x_voff(s.sd), vo_z = x_voff(s.sz), vo_o = x_voff(s.so);
-  // B/C: vector i covers (matrix, state, step) with steps (BT) or states along the vector
-  auto bc_sel = [&](int i) __attribute__((always_inline)) { return (BR * i) / (BT ? kMaxState : kT); };
-  auto bc_n = [&](int i, int j) __attribute__((always_inline)) { return BT ? br + (BR * i) % kMaxState : bv * V + j; };
-  auto bc_tt = [&](int i, int j) __attribute__((always_inline)) { return BT ? bv * V + j : br + (BR * i) % kT; };
+  auto bc_tt = [&](int i, int j) __attribute__((always_inline)) {
+    return BT ? 4 * bb + j : ba + 16 * (i & 1);
+  };
   auto bc_voff = [&](const int64_t* st) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>(((BT ? br : bv * V) * st[1] + (BT ? bv * V : br) * st[2]) * es);
+    return static_cast<uint32_t>(((BT ? ba : 4 * bb) * st[1] + (BT ? 4 * bb : ba) * st[2]) * es);
   };
-  const uint32_t vo_b = bc_voff(s.sB), vo_c = bc_voff(s.sC);
   auto bc_soff = [&](const int64_t* st, int i) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>(((BR * i) % (BT ? kMaxState : kT)) * (BT ? st[1] : st[2]) * es);
+    return static_cast<uint32_t>((i & 1) * (BT ? 8 * st[1] : 16 * st[2]) * es);
   };
 
-  // per-element channel constants
-  float bias[kPerThread], skip[kPerThread];
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int dc = d0 + x_c(e / V, e % V);
-    const bool ok = dc < s.dim;
-    bias[e] = (ok && dt_bias != nullptr) ? dt_bias[dc] : 0.0f;
-    skip[e] = (ok && Dskip != nullptr) ? Dskip[dc] : 0.0f;
+  // Channel constants (dt_bias, D).  With t-fast data each lane's elements
+  // share one channel and the pair stays in registers; with d-fast data a
+  // lane's four elements are four channels, and the pairs of the tile's 8
+  // channels sit in LDS (s_chan) to keep registers for the loads in flight.
+  float bias_t = 0.0f, skip_t = 0.0f;
+  if constexpr (XT) {
+    const int dc = d0 + xa;
+    bias_t = (dc < s.dim && dt_bias != nullptr) ? dt_bias[dc] : 0.0f;
+    skip_t = (dc < s.dim && Dskip != nullptr) ? Dskip[dc] : 0.0f;
+  } else if (lane < 2 * kCh) {
+    const int dc = d0 + (lane & (kCh - 1));
+    const float* src = lane < kCh ? dt_bias : Dskip;
+    s_chan[lane] = (dc < s.dim && src != nullptr) ? src[dc] : 0.0f;
   }
   const bool has_z = z != nullptr;
 
-  auto rsrc = [&](const void* ptr, const int64_t* st, int dd0, int t0) __attribute__((always_inline)) {
+  auto rsrc = [&](const void* ptr, const int64_t* st, int dd0, int t0,
+                  int range = kRsrcRange) __attribute__((always_inline)) {
     const char* base = reinterpret_cast<const char*>(ptr) +
                        (static_cast<int64_t>(b) * st[0] + static_cast<int64_t>(dd0) * st[1] +
                         static_cast<int64_t>(t0) * st[2]) * es;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, kRsrcRange, kRsrcFlags);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, range, kRsrcFlags);
   };
-  // x_ok / b_ok: element (v, j) / B-C value (i, j) lies inside the tensors
-  // and the chunk is one this loop loads (lim: first chunk start not loaded).
-  auto x_ok = [&](int v, int j, int t0, int lim) __attribute__((always_inline)) {
-    return (t0 < lim) && (d0 + x_c(v, j) < s.dim) && (t0 + x_t(v, j) < t_end);
+  // x_ok / b_ok: element j / B-C value (i, j) lies inside the tensors and the
+  // chunk is one this loop loads (lim: first chunk start not loaded).
+  auto x_ok = [&](int j, int t0, int lim) __attribute__((always_inline)) {
+    return (t0 < lim) && (d0 + x_c(j) < s.dim) && (t0 + x_t(j) < t_end);
   };
   auto b_ok = [&](int i, int j, int t0, int lim) __attribute__((always_inline)) {
     return (t0 < lim) && (bc_n(i, j) < s.dstate) && (t0 + bc_tt(i, j) < t_end);
   };
 
-  // Chunk inputs live in registers from issue to use: u, delta_raw, B and C
-  // two chunks ahead of the chunk being scanned, z one chunk ahead.
+  // Chunk inputs live in registers from issue to use: u, delta_raw and B/C
+  // one chunk ahead of the chunk being scanned, z from the end of the
+  // previous chunk's output phase.
   struct InBuf {
-    float u[kPerThread], d[kPerThread], bc[kBcPerLane];
+    float u[kPerThread], d[kPerThread];
   };
   struct ZBuf {
     float z[kPerThread];
   };
-  InBuf in0, in1;
-  ZBuf zb0, zb1;
+  float bcb[4 * kVec];  // B/C of the next chunk
 
-  // Loads of one x-tensor.  VEC: 16-byte vectors (each wholly in or out of
-  // the valid region); else element by element.
-  auto load_x = [&](auto vec, float (&dst)[kPerThread], const IO* ptr, const int64_t* st,
-                    uint32_t vo, int t0, int lim) {
-    const auto rs = rsrc(ptr, st, d0, t0);
+  // Loads of one x-tensor.  VEC: one vector (wholly in or out of the valid
+  // region); else element by element.
+  auto load_x = [&](float (&dst)[kPerThread], const IO* ptr, const int64_t* st, int t0, int lim,
+                    int range = kRsrcRange) __attribute__((always_inline)) {
+    const auto rs = rsrc(ptr, st, d0, t0, range);
+    const uint32_t vo = x_voff(st);
     if constexpr (VEC) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const uint32_t off = x_ok(v, 0, t0, lim) ? vo : kOffNone;
-        VIO::unpack(__builtin_amdgcn_raw_buffer_load_b128(rs, off, x_soff(st, v), 0), dst + v * V);
-      }
+      VIO::load(rs, x_ok(0, t0, lim) ? vo : kOffNone, 0, dst);
     } else {
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e) {
-        const int v = e / V, j = e % V;
-        const uint32_t off = x_ok(v, j, t0, lim)
+      for (int j = 0; j < kPerThread; ++j) {
+        const uint32_t off = x_ok(j, t0, lim)
             ? vo + static_cast<uint32_t>(j * (XT ? st[2] : st[1]) * es) : kOffNone;
-        dst[e] = VIO::load_one(rs, off, x_soff(st, v));
+        dst[j] = VIO::load_one(rs, off, 0);
       }
     }
   };
-  auto issue_z_loads = [&](auto vec, ZBuf& zb, int t0, int lim) __attribute__((always_inline)) {
-    if constexpr (!AGG) {
-      if (has_z) {
-        load_x(vec, zb.z, z, s.sz, vo_z, t0, lim);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kPerThread; ++e) zb.z[e] = 0.0f;
-      }
-    }
+  // Without z the descriptor has an empty range and the loads return 0: the
+  // instruction stream stays the same, so no branch splits the loop body
+  // (a load under a branch makes the compiler drain every outstanding load).
+  const IO* z_ptr = has_z ? z : u;
+  const int z_range = has_z ? kRsrcRange : 0;
+  auto issue_z_loads = [&](ZBuf& zb, int t0, int lim) __attribute__((always_inline)) {
+    if constexpr (!AGG) load_x(zb.z, z_ptr, s.sz, t0, lim, z_range);
   };
-  auto issue_loads = [&](auto vec, InBuf& ib, int t0, int lim) __attribute__((always_inline)) {
-    load_x(vec, ib.u, u, s.su, vo_u, t0, lim);
-    load_x(vec, ib.d, delta_raw, s.sd, vo_d, t0, lim);
+  auto issue_x_loads = [&](InBuf& ib, int t0, int lim) __attribute__((always_inline)) {
+    load_x(ib.u, u, s.su, t0, lim);
+    load_x(ib.d, delta_raw, s.sd, t0, lim);
+  };
+  constexpr int kBcLoads = AGG ? 2 : 4;  // the AGG pass needs no C
+  auto issue_bc_loads = [&](int t0, int lim) __attribute__((always_inline)) {
     const auto rb = rsrc(Bm, s.sB, 0, t0);
     const auto rcm = rsrc(Cm, s.sC, 0, t0);
 #pragma unroll
-    for (int i = 0; i < NBV; ++i) {
-      const bool is_c = bc_sel(i) == 1;
-      float* dst = ib.bc + i * V;
-      if (AGG && is_c) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) dst[j] = 0.0f;
-        continue;
-      }
+    for (int i = 0; i < kBcLoads; ++i) {
+      const bool is_c = i >= 2;
       const auto& rs = is_c ? rcm : rb;
       const int64_t* st = is_c ? s.sC : s.sB;
-      const uint32_t vo = is_c ? vo_c : vo_b;
+      const uint32_t vo = bc_voff(st);
+      float* dst = bcb + i * kVec;
       if constexpr (VEC) {
-        const uint32_t off = b_ok(i, 0, t0, lim) ? vo : kOffNone;
-        VIO::unpack(__builtin_amdgcn_raw_buffer_load_b128(rs, off, bc_soff(st, i), 0), dst);
+        VIO::load(rs, b_ok(i, 0, t0, lim) ? vo : kOffNone, bc_soff(st, i), dst);
       } else {
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
+        for (int j = 0; j < kVec; ++j) {
           const uint32_t off = b_ok(i, j, t0, lim)
               ? vo + static_cast<uint32_t>(j * (BT ? st[2] : st[1]) * es) : kOffNone;
           dst[j] = VIO::load_one(rs, off, bc_soff(st, i));
@@ -364,82 +348,142 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     }
   };
 
-  float cur_du_skip[kPerThread];
+  // E: (delta, delta*u) and D*u of the chunk go to LDS (s_dd, s_skip), B/C
+  // from registers to s_bc.
   auto phase_e = [&](const InBuf& ib, int t0) __attribute__((always_inline)) {
+    float dl[kPerThread], du[kPerThread], sk[kPerThread], bias[kPerThread], skip[kPerThread];
+    if constexpr (XT) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int v = e / V, j = e % V;
-      const bool ok = x_ok(v, j, t0, t_end);
-      const float x = ib.d[e] + bias[e];
-      float dl = s.softplus ? softplus(x) : x;
-      float du = dl * ib.u[e];
-      if (!ok) {
-        dl = 0.0f;
-        du = 0.0f;
+      for (int j = 0; j < kPerThread; ++j) {
+        bias[j] = bias_t;
+        skip[j] = skip_t;
       }
-      s_dd[x_t(v, j) * kDdPitch + x_c(v, j)] = make_float2(dl, du);
-      if constexpr (!AGG) cur_du_skip[e] = skip[e] * ib.u[e];
+    } else {
+      const f4 bv = lds_f4(s_chan + 4 * xb), sv = lds_f4(s_chan + kCh + 4 * xb);
+      bias[0] = bv.x; bias[1] = bv.y; bias[2] = bv.z; bias[3] = bv.w;
+      skip[0] = sv.x; skip[1] = sv.y; skip[2] = sv.z; skip[3] = sv.w;
     }
 #pragma unroll
-    for (int i = 0; i < NBV; ++i) {
+    for (int j = 0; j < kPerThread; ++j) {
+      const bool ok = x_ok(j, t0, t_end);
+      const float x = ib.d[j] + bias[j];
+      dl[j] = s.softplus ? softplus(x) : x;
+      du[j] = dl[j] * ib.u[j];
+      if (!ok) {
+        dl[j] = 0.0f;
+        du[j] = 0.0f;
+      }
+      sk[j] = skip[j] * ib.u[j];
+    }
+    if constexpr (XT) {
+      // 4 consecutive steps of one channel: two 16-byte (delta, delta*u) pairs
+      float* p = s_dd + xa * kDdPitch + 8 * xb;
+      *reinterpret_cast<f4*>(p) = f4{dl[0], du[0], dl[1], du[1]};
+      *reinterpret_cast<f4*>(p + 4) = f4{dl[2], du[2], dl[3], du[3]};
+      if constexpr (!AGG)
+        *reinterpret_cast<f4*>(s_skip + xa * kSkipPitch + 4 * xb) = f4{sk[0], sk[1], sk[2], sk[3]};
+    } else {
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const int n = bc_n(i, j);
-        s_bc[bc_tt(i, j) * kBcPitch + (n >> 2) * 8 + bc_sel(i) * 4 + (n & 3)] = ib.bc[i * V + j];
+      for (int j = 0; j < kPerThread; ++j) {
+        *reinterpret_cast<float2*>(s_dd + (4 * xb + j) * kDdPitch + 2 * xa) =
+            make_float2(dl[j], du[j]);
+        if constexpr (!AGG) s_skip[(4 * xb + j) * kSkipPitch + xa] = sk[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBcLoads; ++i) {
+      const int row0 = (i >= 2 ? kMaxState : 0);
+      if constexpr (BT) {
+        *reinterpret_cast<f4*>(s_bc + bc_index(row0 + bc_n(i, 0), bc_tt(i, 0))) =
+            f4{bcb[i * kVec], bcb[i * kVec + 1], bcb[i * kVec + 2], bcb[i * kVec + 3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j)
+          s_bc[bc_index(row0 + bc_n(i, j), bc_tt(i, j))] = bcb[i * kVec + j];
       }
     }
   };
 
-  const int bc_read = ((sc >> 3) * kBcPitch) + sg * 8 + (sc & 7);
+  // S-phase LDS addresses of this lane: B and C rows of states 2sg, 2sg+1 and
+  // the (delta, delta*u) row of channel sc.
+  // (all four rows share the swizzle key sg)
+  const float* p_b0 = s_bc + (2 * sg) * kT;
+  const float* p_c0 = s_bc + (AGG ? 0 : (kMaxState + 2 * sg) * kT);
+  const float* p_dd = s_dd + sc * kDdPitch;
+  // The group reduction leaves step {0, 2, 1, 3}[row] of each block in row
+  // `row` = lane / 16.  The total of step t replaces delta_t in s_dd: the
+  // block has read it, and later blocks read other steps.
+  const int row = lane >> 4;
+  const int y_step = row == 1 ? 2 : (row == 2 ? 1 : row);
+  float* p_y = s_dd + sc * kDdPitch + 2 * y_step;
 
-  // The group reduction leaves step {0, 2, 1, 3}[sg] of each block in row sg.
-  const int y_row_step = sg == 1 ? 2 : (sg == 2 ? 1 : sg);
   auto phase_s = [&]() __attribute__((always_inline)) {
     // blocks of 4 steps, one state-group reduction each
 #pragma unroll 1
-    for (int q = 0; q < kT / 4; ++q) {
-      const int t4 = 4 * q;
-      const float bcA = s_bc[t4 * kBcPitch + bc_read];
-      const float bcB = s_bc[(t4 + 2) * kBcPitch + bc_read];
-      const float2 dd0 = s_dd[(t4 + 0) * kDdPitch + sc];
-      const float2 dd1 = s_dd[(t4 + 1) * kDdPitch + sc];
-      const float2 dd2 = s_dd[(t4 + 2) * kDdPitch + sc];
-      const float2 dd3 = s_dd[(t4 + 3) * kDdPitch + sc];
-      const float y0 = scan_step<0, AGG>(dd0.x, dd0.y, bcA, A2, h);
-      const float y1 = scan_step<1, AGG>(dd1.x, dd1.y, bcA, A2, h);
-      const float y2 = scan_step<0, AGG>(dd2.x, dd2.y, bcB, A2, h);
-      const float y3 = scan_step<1, AGG>(dd3.x, dd3.y, bcB, A2, h);
-      if constexpr (!AGG) {
-        s_y[(t4 + y_row_step) * kYPitch + sc] = reduce_groups(y0, y1, y2, y3);
+    for (int t4 = 0; t4 < kT; t4 += 4) {
+      const int col = (((t4 >> 2) ^ sg) & 7) << 2;
+      const f4 b0 = lds_f4(p_b0 + col);
+      const f4 b1 = lds_f4(p_b0 + kT + col);
+      const f4 dd01 = lds_f4(p_dd + 2 * t4);
+      const f4 dd23 = lds_f4(p_dd + 2 * t4 + 4);
+      const float dls[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
+      const float dus[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
+      const float bs0[4] = {b0.x, b0.y, b0.z, b0.w};
+      const float bs1[4] = {b1.x, b1.y, b1.z, b1.w};
+      if constexpr (AGG) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
+          h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
+        }
+        sum_delta += (dls[0] + dls[1]) + (dls[2] + dls[3]);
       } else {
-        sum_delta += (dd0.x + dd1.x) + (dd2.x + dd3.x);
+        const f4 c0 = lds_f4(p_c0 + col);
+        const f4 c1 = lds_f4(p_c0 + kT + col);
+        const float cs0[4] = {c0.x, c0.y, c0.z, c0.w};
+        const float cs1[4] = {c1.x, c1.y, c1.z, c1.w};
+        float y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
+          h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
+          y[k] = fmaf(cs1[k], h[1], cs0[k] * h[0]);
+        }
+        p_y[2 * t4] = reduce_groups(y[0], y[1], y[2], y[3]);
       }
     }
   };
 
-  auto phase_o = [&](auto vec, const ZBuf& zb, int t0) __attribute__((always_inline)) {
+  auto phase_o = [&](const ZBuf& zb, int t0) __attribute__((always_inline)) {
     if constexpr (!AGG) {
       float y[kPerThread];
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) {
-        const int v = e / V, j = e % V;
-        y[e] = cur_du_skip[e] + s_y[x_t(v, j) * kYPitch + x_c(v, j)];
-        if (has_z) y[e] *= silu(zb.z[e]);
-      }
-      const auto rs = rsrc(out, s.so, d0, t0);
-      if constexpr (VEC) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const uint32_t off = x_ok(v, 0, t0, t_end) ? vo_o : kOffNone;
-          __builtin_amdgcn_raw_buffer_store_b128(VIO::pack(y + v * V), rs, off, x_soff(s.so, v), 0);
-        }
+      if constexpr (XT) {
+        const float* p = s_dd + xa * kDdPitch + 8 * xb;
+        const f4 v0 = lds_f4(p), v1 = lds_f4(p + 4);
+        const f4 sk = lds_f4(s_skip + xa * kSkipPitch + 4 * xb);
+        y[0] = v0.x + sk.x;
+        y[1] = v0.z + sk.y;
+        y[2] = v1.x + sk.z;
+        y[3] = v1.z + sk.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e) {
-          const int v = e / V, j = e % V;
-          const uint32_t off = x_ok(v, j, t0, t_end)
+        for (int j = 0; j < kPerThread; ++j)
+          y[j] = s_dd[(4 * xb + j) * kDdPitch + 2 * xa] + s_skip[(4 * xb + j) * kSkipPitch + xa];
+      }
+      if (has_z) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) y[j] *= silu(zb.z[j]);
+      }
+      const auto rs = rsrc(out, s.so, d0, t0);
+      const uint32_t vo_o = x_voff(s.so);
+      if constexpr (VEC) {
+        VIO::store(y, rs, x_ok(0, t0, t_end) ? vo_o : kOffNone, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+          const uint32_t off = x_ok(j, t0, t_end)
               ? vo_o + static_cast<uint32_t>(j * (XT ? s.so[2] : s.so[1]) * es) : kOffNone;
-          VIO::store_one(y[e], rs, off, x_soff(s.so, v));
+          VIO::store_one(y[j], rs, off, 0);
         }
       }
     }
@@ -448,32 +492,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   // ---- chunk loop (wave-local: LDS traffic is ordered within the wave) ----
   // One iteration scans chunk c.  Loads are issued in every iteration (past
   // the end they are out-of-range no-ops), so the loop body is branch-free and
-  // the compiler counts outstanding loads exactly.  Issue order keeps every
-  // wait on the oldest loads: z(c+1), then u/delta_raw/B/C(c+2); O(c) waits
-  // for z(c) and E(c+1) for the inputs of c+1, both issued an iteration
-  // earlier.  The body is written twice so that the two register buffers swap
-  // roles.  VEC kernels move 16-byte vectors, so the host only gives them time
-  // ranges and channel tiles in which no vector straddles an edge; the rest
-  // (a tail of fewer steps than a vector, or layouts that cannot vectorise)
-  // runs through the element-wise instantiation.
+  // the compiler counts outstanding loads exactly.  B/C and u/delta_raw of
+  // chunk c+1 are issued before the scan of chunk c and z of chunk c+1 once
+  // O(c) has consumed z(c); E(c+1) then waits for the loads issued before the
+  // scan and O(c+1) for z(c+1), the oldest loads in flight at each point.
+  // With several waves per SIMD, the scans of the other waves cover the
+  // latency.
   const int nchunks = (t_end - t_begin + kT - 1) / kT;
-  constexpr std::integral_constant<bool, VEC> vec{};
-  issue_z_loads(vec, zb0, t_begin, t_end);
-  issue_loads(vec, in0, t_begin, t_end);
-  issue_loads(vec, in1, t_begin + kT, t_end);
-  phase_e(in0, t_begin);
-  auto iteration = [&](int c, InBuf& in_c, InBuf& in_next, ZBuf& z_c, ZBuf& z_next)
-      __attribute__((always_inline)) {
+  InBuf in;
+  ZBuf zb;
+  issue_bc_loads(t_begin, t_end);
+  issue_x_loads(in, t_begin, t_end);
+  issue_z_loads(zb, t_begin, t_end);
+  phase_e(in, t_begin);
+  // Priorities: the SIMD issues from the oldest wave among those of the
+  // highest priority.  A wave scans at priority 0 and raises itself to 2 for
+  // the output and input phases, so a wave whose scan is done gets to its
+  // memory waits and load issue at once instead of queueing behind the scans
+  // of older waves: loads leave earlier and have longer to arrive.
+  for (int c = 0; c < nchunks; ++c) {
     const int t0 = t_begin + c * kT;
-    issue_z_loads(vec, z_next, t0 + kT, t_end);
-    issue_loads(vec, in_c, t0 + 2 * kT, t_end);
+    issue_bc_loads(t0 + kT, t_end);
+    issue_x_loads(in, t0 + kT, t_end);
+    __builtin_amdgcn_s_setprio(0);
     phase_s();
-    phase_o(vec, z_c, t0);
-    phase_e(in_next, t0 + kT);
-  };
-  for (int c = 0; c < nchunks; c += 2) {
-    iteration(c, in0, in1, zb0, zb1);
-    if (c + 1 < nchunks) iteration(c + 1, in1, in0, zb1, zb0);
+    __builtin_amdgcn_s_setprio(2);
+    phase_o(zb, t0);
+    issue_z_loads(zb, t0 + kT, t_end);
+    phase_e(in, t0 + kT);
   }
 
   // ---- segment end ----
