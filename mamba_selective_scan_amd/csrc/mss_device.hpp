@@ -57,11 +57,14 @@ __device__ static inline float fast_log2(float x) { return __builtin_amdgcn_logf
 // (Fast2Sum, valid as e <= 1) and dividing it by w would change the sum by less
 // than 2^-25.  The hardware log2 is accurate to a few ulp of its result for w
 // near 1, so the sum keeps full relative precision even when e is tiny.
+// The last step uses max(x, 0) + v = max(x + v, v) for v = log1p(e) >= 0,
+// which holds exactly in floating point as well.
 __device__ static inline float softplus(float x) {
   const float e = fast_exp2(-fabsf(x) * kLog2e);
   const float w = 1.0f + e;
   const float corr = e - (w - 1.0f);
-  return fmaxf(x, 0.0f) + fmaf(fast_log2(w), kLn2, corr);
+  const float v = fmaf(fast_log2(w), kLn2, corr);
+  return fmaxf(x + v, v);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).

@@ -363,16 +363,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       bias[0] = bv.x; bias[1] = bv.y; bias[2] = bv.z; bias[3] = bv.w;
       skip[0] = sv.x; skip[1] = sv.y; skip[2] = sv.z; skip[3] = sv.w;
     }
+    // Outside the tensors u reads 0, so delta*u and D*u are 0 already; delta
+    // itself is zeroed there so that the state passes through unchanged.  A
+    // vector is wholly inside or outside.
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      const bool ok = x_ok(j, t0, t_end);
+      const bool ok = x_ok(VEC ? 0 : j, t0, t_end);
       const float x = ib.d[j] + bias[j];
-      dl[j] = s.softplus ? softplus(x) : x;
+      const float sp = s.softplus ? softplus(x) : x;
+      dl[j] = ok ? sp : 0.0f;
       du[j] = dl[j] * ib.u[j];
-      if (!ok) {
-        dl[j] = 0.0f;
-        du[j] = 0.0f;
-      }
       sk[j] = skip[j] * ib.u[j];
     }
     if constexpr (XT) {
@@ -417,40 +417,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int y_step = row == 1 ? 2 : (row == 2 ? 1 : row);
   float* p_y = s_dd + sc * kDdPitch + 2 * y_step;
 
-  auto phase_s = [&]() __attribute__((always_inline)) {
-    // blocks of 4 steps, one state-group reduction each
-#pragma unroll 1
-    for (int t4 = 0; t4 < kT; t4 += 4) {
-      const int col = (((t4 >> 2) ^ sg) & 7) << 2;
-      const f4 b0 = lds_f4(p_b0 + col);
-      const f4 b1 = lds_f4(p_b0 + kT + col);
-      const f4 dd01 = lds_f4(p_dd + 2 * t4);
-      const f4 dd23 = lds_f4(p_dd + 2 * t4 + 4);
-      const float dls[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
-      const float dus[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
-      const float bs0[4] = {b0.x, b0.y, b0.z, b0.w};
-      const float bs1[4] = {b1.x, b1.y, b1.z, b1.w};
-      if constexpr (AGG) {
+  // One block of 4 steps: the scan of this lane's two states and, outside
+  // the AGG pass, one state-group reduction of C.h.
+  auto scan_block = [&](int t4) __attribute__((always_inline)) {
+    const int col = (((t4 >> 2) ^ sg) & 7) << 2;
+    const f4 b0 = lds_f4(p_b0 + col);
+    const f4 b1 = lds_f4(p_b0 + kT + col);
+    const f4 dd01 = lds_f4(p_dd + 2 * t4);
+    const f4 dd23 = lds_f4(p_dd + 2 * t4 + 4);
+    const float dls[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
+    const float dus[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
+    const float bs0[4] = {b0.x, b0.y, b0.z, b0.w};
+    const float bs1[4] = {b1.x, b1.y, b1.z, b1.w};
+    if constexpr (AGG) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
-          h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
-        }
-        sum_delta += (dls[0] + dls[1]) + (dls[2] + dls[3]);
-      } else {
-        const f4 c0 = lds_f4(p_c0 + col);
-        const f4 c1 = lds_f4(p_c0 + kT + col);
-        const float cs0[4] = {c0.x, c0.y, c0.z, c0.w};
-        const float cs1[4] = {c1.x, c1.y, c1.z, c1.w};
-        float y[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
-          h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
-          y[k] = fmaf(cs1[k], h[1], cs0[k] * h[0]);
-        }
-        p_y[2 * t4] = reduce_groups(y[0], y[1], y[2], y[3]);
+      for (int k = 0; k < 4; ++k) {
+        h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
+        h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
       }
+      sum_delta += (dls[0] + dls[1]) + (dls[2] + dls[3]);
+    } else {
+      const f4 c0 = lds_f4(p_c0 + col);
+      const f4 c1 = lds_f4(p_c0 + kT + col);
+      const float cs0[4] = {c0.x, c0.y, c0.z, c0.w};
+      const float cs1[4] = {c1.x, c1.y, c1.z, c1.w};
+      float y[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
+        h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
+        y[k] = fmaf(cs1[k], h[1], cs0[k] * h[0]);
+      }
+      p_y[2 * t4] = reduce_groups(y[0], y[1], y[2], y[3]);
+    }
+  };
+  // The main pass unrolls the blocks: the swizzled B/C offsets become
+  // loop-invariant registers and the other LDS offsets immediates.  The AGG
+  // pass keeps a loop (unrolled, its LDS reads would all be hoisted).
+  auto phase_s = [&]() __attribute__((always_inline)) {
+    if constexpr (AGG) {
+#pragma unroll 1
+      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4);
+    } else {
+#pragma unroll
+      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4);
     }
   };
 
