@@ -10,8 +10,9 @@ Prints one JSON line:
   value         whole-step throughput in GB/s of algorithmic bytes (each input
                 read once, each output written once);
   roofline      the scan forward call timed with HIP events on its stream
-                against the 8 TB/s HBM peak, with HBM traffic from rocprofv3
-                counters when a matching profile is committed under profiles/;
+                against the VALU issue peak (the binding resource), with the
+                HBM fraction beside it and HBM traffic from rocprofv3 counters
+                when a matching profile is committed under profiles/;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
                 the host's cores.
 
@@ -33,6 +34,24 @@ if ROOT not in sys.path:
 
 METRIC = "selective-scan fwd achieved HBM GB/s (% of 8 TB/s) and Gtok·ch/s"
 HBM_PEAK_GBS = 8000.0
+# VALU issue roofline: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-slots per
+# second without packed fp32 (which the build disables); a transcendental
+# (exp2, log2, rcp) takes 4 slots (quarter rate), every other op one.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def valu_slots_per_element(dstate: int, softplus: bool = True, has_z: bool = True) -> int:
+    """Algorithmic VALU slots per (b, d, t) element of the forward.
+
+    Per state: exp2 (4) + delta*A2 + (delta*u)*B + the h FMA + the C.h FMA.
+    Per element: delta_raw + dt_bias; softplus as exp2 (4) + log2 (4) + 7 ops;
+    delta*u; D*u and its add; silu as exp2 (4) + rcp (4) + 3 ops; the gate.
+    """
+    n = dstate * (4 + 4)
+    n += 1 + (15 if softplus else 0) + 1 + 2
+    if has_z:
+        n += 11 + 1
+    return n
 KERNEL_SOURCES = ["mamba_selective_scan_amd/csrc/scan_fwd.hip",
                   "mamba_selective_scan_amd/csrc/mss_device.hpp",
                   "mamba_selective_scan_amd/csrc/mss_internal.hpp"]
@@ -190,9 +209,11 @@ def main(argv=None):
     scan_ms_sorted = sorted(scan_ms)
 
     fwd_bytes = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, io_bytes, final_state=True)
+    fwd_slots = w.elems * valu_slots_per_element(w.dstate)
     total_bytes = fwd_bytes + (0 if args.no_step else step_bytes(w.batch, w.dim, w.dstate, io_bytes))
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = fwd_bytes / (scan_ms_mean * 1e-3) / 1e9
+    achieved_slots = fwd_slots / (scan_ms_mean * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     traffic = load_traffic(w.name, args.io, src_hash)
     log(f"step {ms_per_step:.4f} ms; scan fwd mean {scan_ms_mean * 1e3:.1f} us "
@@ -220,14 +241,22 @@ def main(argv=None):
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gtok_ch_per_s": round(w.elems / (ms_per_step * 1e-3) / 1e9, 4),
         "roofline": {
-            "bound": "hbm",
+            "bound": "alu",
             "kernel": "scan_kernel (mss_selective_scan_fwd) on the current stream",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "achieved": round(achieved_slots, 3),
+            "peak": round(VALU_PEAK_TSLOTS, 3),
+            "unit": "T VALU lane-slots/s",
+            "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": fwd_bytes,
+            "algorithmic_slots": fwd_slots,
+            "slots_per_element": valu_slots_per_element(w.dstate),
+            "hbm": {
+                "achieved": round(achieved, 2),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": fwd_bytes,
+            },
             "event_us_mean": round(scan_ms_mean * 1e3, 2),
             "event_us_median": round(scan_ms_sorted[len(scan_ms) // 2] * 1e3, 2),
             "kernel_source_hash": src_hash,
