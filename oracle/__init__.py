@@ -1,12 +1,14 @@
-"""fp64 CPU oracle for the Mamba selective-scan forward and state update.
+"""fp64 CPU oracle for the Mamba selective-scan forward and state update, and
+for the causal depthwise conv1d (+ SiLU) that feeds the scan, with its
+sliding-window decode step.
 
 TEST INFRASTRUCTURE ONLY.  The test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only callers.  The product package
 (``mamba_selective_scan_amd``) never imports this module, and this module
 imports nothing from the product package.
 
-The arithmetic lives in ``mss_oracle.c`` (plain C, fp64, sequential in time,
-OpenMP across independent channels).  This wrapper only marshals numpy arrays:
+The arithmetic lives in ``mss_oracle.c`` and ``mss_oracle_conv.c`` (plain C,
+fp64, sequential in time, OpenMP across independent channels).  This wrapper only marshals numpy arrays:
 every input is converted exactly to float64 and laid out contiguously as
 
     u, delta_raw, z, out : [batch, dim, seqlen]
@@ -14,6 +16,8 @@ every input is converted exactly to float64 and laid out contiguously as
     A_log                : [dim, dstate]
     D, dt_bias           : [dim]
     h0, final_state      : [batch, dim, dstate]
+    conv: x, out [batch, dim, seqlen]; w [dim, width]; bias [dim];
+          windows (init, final, state) [batch, dim, width - 1]
 
 Values stored in float32 or bfloat16 upcast to float64 without rounding, so the
 oracle consumes exactly the bytes the GPU consumes.
@@ -29,15 +33,25 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mss_oracle.c")
+SOURCES = {"scan": _SRC, "conv": os.path.join(_HERE, "mss_oracle_conv.c")}
 LIB_PATH = os.path.join(_HERE, "libmss_oracle.so")
 
 _lib = None
 
 
-def build(src: str = _SRC, out: str = LIB_PATH) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+def build(src: str | None = None, out: str = LIB_PATH, replace: dict | None = None) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math).
+
+    ``replace`` maps a key of SOURCES to another file to compile in its place
+    (the mutation tests build a library with one source file altered);
+    ``src`` is shorthand for replacing the scan source.
+    """
+    srcs = dict(SOURCES)
+    if src is not None:
+        srcs["scan"] = src
+    srcs.update(replace or {})
     cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-ffp-contract=off", src, "-o", out, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *srcs.values(), "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -57,6 +71,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_oracle_state_update.argtypes = [i64, i64, i64, dp] + [dp] * 8 + [
         ctypes.c_int, dp]
     lib.mss_oracle_state_update.restype = ctypes.c_int
+    lib.mss_oracle_conv1d_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 4 + [ctypes.c_int, dp, dp]
+    lib.mss_oracle_conv1d_fwd.restype = ctypes.c_int
+    lib.mss_oracle_conv1d_update.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp]
+    lib.mss_oracle_conv1d_update.restype = ctypes.c_int
     return lib
 
 
@@ -195,3 +213,45 @@ def scan_channels(inputs: dict, channels, delta_softplus=True, use_h0=False, thr
             out[i] = o[0, j]
             fin[i] = f[0, j]
     return np.stack(out), np.stack(fin)
+
+
+def conv1d_fwd(x, w, bias=None, init=None, silu=True, lib=None):
+    """Causal depthwise conv1d (+ SiLU) in fp64.
+
+    x [b, d, l]; w [d, width]; bias [d]; init [b, d, width-1] (the carried
+    window, oldest first; None means zeros).  Returns (out [b, d, l],
+    final_window [b, d, width-1])."""
+    x = _f64(x)
+    batch, dim, seqlen = x.shape
+    w = _f64(w)
+    width = w.shape[1]
+    w = _f64(w, (dim, width))
+    bias = _f64(bias, (dim,))
+    init = _f64(init, (batch, dim, width - 1))
+    out = np.empty((batch, dim, seqlen), dtype=np.float64)
+    final = np.empty((batch, dim, width - 1), dtype=np.float64)
+    rc = (lib or load()).mss_oracle_conv1d_fwd(
+        batch, dim, seqlen, width, _ptr(x), _ptr(w), _ptr(bias), _ptr(init), int(bool(silu)),
+        _ptr(out), _ptr(final))
+    if rc != 0:
+        raise ValueError(f"oracle conv1d_fwd rejected its arguments (rc={rc})")
+    return out, final
+
+
+def conv1d_update(state, x, w, bias=None, silu=True, lib=None):
+    """One conv1d decode step in fp64.  Returns (out [b, d], new_state
+    [b, d, width-1]); the input ``state`` is not modified."""
+    w = _f64(w)
+    dim, width = w.shape
+    x = _f64(x)
+    batch = x.shape[0]
+    x = _f64(x, (batch, dim))
+    new_state = _f64(state, (batch, dim, width - 1)).copy()
+    bias = _f64(bias, (dim,))
+    out = np.empty((batch, dim), dtype=np.float64)
+    rc = (lib or load()).mss_oracle_conv1d_update(
+        batch, dim, width, _ptr(new_state), _ptr(x), _ptr(w), _ptr(bias), int(bool(silu)),
+        _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle conv1d_update rejected its arguments (rc={rc})")
+    return out, new_state

@@ -1,7 +1,7 @@
 """Loader for the hand-derived worked examples in tests/golden/.
 
-Each fixture lists its inputs and its expected outputs as exact rationals
-c0 + c1 * ln(2).  See the header of each file for the derivation.
+Each scan fixture lists its inputs and its expected outputs as exact rationals
+c0 + c1 * ln(2); each conv fixture lists exact rationals.  See the header of each file for the derivation.
 """
 
 from __future__ import annotations
@@ -32,8 +32,22 @@ def load(name: str) -> dict:
             k, v = (s.strip() for s in line.split("=", 1))
             fields[k] = v
     kind = fields["kind"]
-    N = int(fields["dstate"])
     vec = lambda k: np.array([_num(t) for t in fields[k].split(",")])
+    if kind in ("conv", "conv_step"):
+        w = vec("w")
+        width = w.size
+        case = {"kind": kind, "name": name, "w": w.reshape(1, width), "bias": vec("bias"),
+                "final": vec("final").reshape(1, 1, width - 1)}
+        if kind == "conv":
+            x = vec("x")
+            case["x"] = x.reshape(1, 1, x.size)
+            case["y"] = vec("y").reshape(1, 1, x.size)
+        else:
+            case["state"] = vec("state").reshape(1, 1, width - 1)
+            case["x"] = vec("x").reshape(1, 1)
+            case["y"] = vec("y").reshape(1, 1)
+        return case
+    N = int(fields["dstate"])
     ln2 = math.log(2.0)
     case = {"kind": kind, "dstate": N, "name": name}
     if kind == "scan":

@@ -10,7 +10,11 @@ import oracle
 @pytest.mark.parametrize("name", golden_cases.ALL)
 def test_oracle_matches_golden(name, oracle_lib):
     c = golden_cases.load(name)
-    if c["kind"] == "scan":
+    if c["kind"] == "conv":
+        out, fin = oracle.conv1d_fwd(c["x"], c["w"], c["bias"], silu=False)
+    elif c["kind"] == "conv_step":
+        out, fin = oracle.conv1d_update(c["state"], c["x"], c["w"], c["bias"], silu=False)
+    elif c["kind"] == "scan":
         out, fin = oracle.scan_fwd(c["u"], c["delta_raw"], c["A_log"], c["B"], c["C"], D=c["D"],
                                    delta_softplus=False)
     else:

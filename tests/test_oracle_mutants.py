@@ -1,10 +1,12 @@
 """The pins have teeth: each plausible mistake planted in a copy of the oracle
 makes at least one pin fail.
 
-Every mutant below is a one-line edit of oracle/mss_oracle.c (a dropped term,
-a wrong sign or index, a transposed or swapped operand, exp2 for exp, ...).
-The copy is compiled into a temporary library and the pins are run against
-it; the real oracle source is never modified.
+Every mutant below is a one-line edit of one oracle source file
+(oracle/mss_oracle.c for the scan, oracle/mss_oracle_conv.c for the conv1d): a
+dropped term, a wrong sign or index, a transposed or swapped operand, exp2 for
+exp, and so on.  The altered copy is compiled, with the other sources as they
+are, into a temporary library and every pin is run against it; the real
+oracle sources are never modified.
 """
 
 import os
@@ -12,6 +14,7 @@ import os
 import pytest
 
 import oracle
+import conv_oracle_pins as CP
 import oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "mss_oracle.c")
@@ -61,10 +64,33 @@ MUTANTS = {
     "step_no_bias": ("dt_bias ? dt_bias[d] : 0.0, delta_softplus);", "0.0, delta_softplus);"),
 }
 
+# conv1d mutants (oracle/mss_oracle_conv.c)
+CONV_MUTANTS = {
+    "conv_no_bias": ("double pre = bias ? bias[d] : 0.0;\n                for",
+                     "double pre = 0.0;\n                for"),
+    "conv_taps_reversed": ("pre += w_row[k] * extended_sample",
+                           "pre += w_row[width - 1 - k] * extended_sample"),
+    "conv_drop_current": ("for (int64_t k = 0; k < width; ++k)\n                    pre +=",
+                          "for (int64_t k = 0; k + 1 < width; ++k)\n                    pre +="),
+    "conv_window_shift": ("t - (width - 1) + k)", "t - (width - 1) + k - (t > 0))"),
+    "conv_init_ignored": ("return init_row ? init_row[width - 1 + tau] : 0.0;", "return 0.0;"),
+    "conv_init_reversed": ("return init_row ? init_row[width - 1 + tau] : 0.0;",
+                           "return init_row ? init_row[-1 - tau] : 0.0;"),
+    "conv_silu_ignored": ("out_row[t] = silu ? mss_oracle_silu(pre) : pre;", "out_row[t] = pre;"),
+    "conv_final_shift": ("seqlen - (width - 1) + j);", "seqlen - width + j);"),
+    "conv_step_no_shift": ("s[k] = window[k + 1];", "s[k] = window[k];"),
+    "conv_step_taps_reversed": ("pre += w[d * width + k] * window[k];",
+                                "pre += w[d * width + width - 1 - k] * window[k];"),
+    "conv_step_x_dropped": ("window[width - 1] = x[b * dim + d];", "window[width - 1] = 0.0;"),
+    "conv_step_no_bias": ("double pre = bias ? bias[d] : 0.0;\n            for",
+                          "double pre = 0.0;\n            for"),
+}
+CONV_SRC = oracle.SOURCES["conv"]
+
 
 def _run_pins(lib):
     failures = []
-    for pin in P.ALL_PINS:
+    for pin in P.ALL_PINS + CP.ALL_CONV_PINS:
         try:
             pin(lib)
         except AssertionError as e:
@@ -83,6 +109,19 @@ def test_mutant_is_caught(name, tmp_path):
     oracle.build(str(mutated), str(so))
     # The library stays loaded: unloading a library whose OpenMP worker
     # threads are still parked is unsafe, and each mutant is small.
+    failures = _run_pins(oracle.load(str(so)))
+    assert failures, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_is_caught(name, tmp_path):
+    old, new = CONV_MUTANTS[name]
+    src = open(CONV_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutated = tmp_path / "mutant_conv.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    oracle.build(out=str(so), replace={"conv": str(mutated)})
     failures = _run_pins(oracle.load(str(so)))
     assert failures, f"mutant {name} passed every pin"
 
