@@ -16,7 +16,12 @@ Prints one JSON line:
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
                 the host's cores.
 
+With --op conv1d the step is instead the causal depthwise conv1d + SiLU
+(width 4) with window export followed by one conv decode step, on the same
+workload shapes, reported against the HBM roofline.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--io f32|bf16]
+                       [--op scan|conv1d]
 """
 
 from __future__ import annotations
@@ -135,6 +140,136 @@ def cpu_baseline(x, w, io_bytes, target_s: float):
     }
 
 
+def conv_cpu_baseline(x, io_bytes, target_s: float):
+    """Time the conv oracle (as is) on a bounded channel sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from mamba_selective_scan_amd.inputs import conv_algorithmic_bytes
+
+    batch, dim, seqlen = x["x"].shape
+    width = x["weight"].shape[1]
+    rng = np.random.default_rng(123)
+    total = batch * dim
+
+    def run(k):
+        bs = rng.integers(batch, size=k)
+        ds = rng.integers(dim, size=k)
+        t = time.perf_counter()
+        for b, d in zip(bs, ds):
+            oracle.conv1d_fwd(x["x"][b:b + 1, d:d + 1], x["weight"][d:d + 1], x["bias"][d:d + 1])
+        return time.perf_counter() - t
+
+    k0 = 4
+    while True:
+        dt0 = run(k0)
+        if dt0 >= 0.5 or k0 >= total:
+            break
+        k0 = min(total, k0 * 4)
+    k = int(max(k0, min(total, k0 * target_s / dt0)))
+    dt = run(k)
+    per_elem = conv_algorithmic_bytes(batch, dim, seqlen, width, io_bytes) / (batch * dim * seqlen)
+    return {
+        "value": round(k * seqlen * per_elem / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{k} of {total} channels (random, with repeats) x full seqlen {seqlen}, "
+                  f"fp64 conv1d + SiLU, one channel per call, {dt:.1f} s",
+    }
+
+
+def main_conv(args):
+    import torch
+
+    import mamba_selective_scan_amd as mss
+    from mamba_selective_scan_amd.inputs import (WORKLOADS, conv_algorithmic_bytes,
+                                                 conv_to_torch, generate_conv)
+
+    w = WORKLOADS[args.workload]
+    width = 4
+    io_bytes = 2 if args.io == "bf16" else 4
+    dev = torch.device("cuda:0")
+    log(f"conv1d workload {w.name}: B={w.batch} D={w.dim} L={w.seqlen} W={width} {w.layout} {args.io}")
+    x = generate_conv(w.batch, w.dim, w.seqlen, width, w.layout, seed=args.seed)
+    dx = conv_to_torch(x, dev, args.io)
+    out = torch.empty_like(dx["x"])
+    win = torch.empty(w.batch, w.dim, width - 1, dtype=dx["x"].dtype, device=dev)
+    x_last = dx["x"][:, :, -1].contiguous()
+    y_last = torch.empty_like(x_last)
+
+    def conv():
+        mss.causal_conv1d_fwd(dx["x"], dx["weight"], dx["bias"], out=out, final_state=win)
+
+    def decode():
+        mss.causal_conv1d_update(win, x_last, dx["weight"], dx["bias"], out=y_last)
+
+    for _ in range(args.warmup):
+        conv()
+        if not args.no_step:
+            decode()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        conv()
+        ev[i][1].record(stream)
+        if not args.no_step:
+            decode()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / len(ms)
+    fwd_bytes = conv_algorithmic_bytes(w.batch, w.dim, w.seqlen, width, io_bytes)
+    fwd_bytes += w.batch * w.dim * (width - 1) * io_bytes          # exported window
+    step_b = 0 if args.no_step else (2 * w.batch * w.dim * (width - 1) * io_bytes
+                                     + 2 * w.batch * w.dim * io_bytes + w.dim * (width + 1) * 4)
+    achieved = fwd_bytes / (mean_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step:.4f} ms; conv fwd mean {mean_ms * 1e3:.1f} us (min {ms[0] * 1e3:.1f}); "
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s")
+    rec = {
+        "metric": "causal conv1d + SiLU fwd achieved HBM GB/s (% of 8 TB/s)",
+        "value": round((fwd_bytes + step_b) / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.io,
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "conv1d", "batch": w.batch, "dim": w.dim,
+                   "seqlen": w.seqlen, "width": width, "layout": w.layout, "io_dtype": args.io,
+                   "step": "conv1d+SiLU fwd + window export" +
+                           ("" if args.no_step else " + 1 conv decode step")},
+        "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "causal conv1d (mss_causal_conv1d_fwd) on the current stream",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": fwd_bytes,
+            "event_us_mean": round(mean_ms * 1e3, 2),
+            "event_us_median": round(ms[len(ms) // 2] * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: conv oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
+        rec["cpu_baseline"] = conv_cpu_baseline(x, io_bytes, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,7 +280,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-step", action="store_true", help="time the scan forward alone")
+    ap.add_argument("--no-step", action="store_true", help="time the forward alone")
+    ap.add_argument("--op", default="scan", choices=["scan", "conv1d"])
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -153,6 +289,8 @@ def main(argv=None):
               f"(asked for --gpus {args.gpus}); channel sharding across GPUs is described "
               f"in DESIGN.md but not built.", file=sys.stderr)
         return 2
+    if args.op == "conv1d":
+        return main_conv(args)
 
     import torch
 

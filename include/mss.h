@@ -27,6 +27,25 @@
  *     ("mamba-metal", section "O(L) インクリメンタルデコード", per-step
  *     equation, closed by the z gate).
  *
+ *  3. mss_causal_conv1d_fwd: the causal depthwise conv1d, with an optional
+ *     SiLU, that produces the scan's input u in a Mamba block
+ *     ("mamba-metal", section "カーネルから推論まで": in_proj -> conv1d ->
+ *     SiLU -> ... -> SSM).  Per channel (b, d) and step t, with `width` taps
+ *     (4 in the pages' models):
+ *        pre[b,d,t] = bias[d] + sum_k weight[d,k] * x~[b,d,t-(width-1)+k]
+ *        out[b,d,t] = silu(pre) (or pre without the activation)
+ *     where x~ is x extended to the left by the carried window
+ *     initial_state[b,d,0..width-2] (oldest first), or by zeros when it is
+ *     NULL: three zero samples on the causal left edge for width 4
+ *     (SpeechLens kernel-optimization notes, causal depthwise convolution
+ *     section and its contract table).  The window after the last step (the
+ *     last width-1 samples of x~) can be exported for decoding.
+ *
+ *  4. mss_causal_conv1d_update: one decode step of that conv: the carried
+ *     window followed by the new sample is filtered, and the window slides
+ *     by one in place ("mamba-metal", section "O(L) インクリメンタルデコード":
+ *     the conv1d sliding window is carried between calls).
+ *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    never allocates, frees or retains caller memory and keeps no per-call
@@ -65,11 +84,13 @@ extern "C" {
 
 #define MSS_ABI_VERSION 1
 #define MSS_MAX_DSTATE 16
+#define MSS_MAX_CONV_WIDTH 4
 
 typedef enum mss_status {
     MSS_OK = 0,
     MSS_ERR_NULL_POINTER = 1,       /* a required pointer is NULL                      */
-    MSS_ERR_BAD_SHAPE = 2,          /* batch, dim or seqlen < 1, or sizes overflow     */
+    MSS_ERR_BAD_SHAPE = 2,          /* batch, dim, seqlen < 1, sizes overflow, or a    */
+                                    /* conv width outside [1, MSS_MAX_CONV_WIDTH]      */
     MSS_ERR_BAD_STRIDE = 3,         /* negative, overlapping or no unit-stride axis    */
     MSS_ERR_UNSUPPORTED_DTYPE = 4,  /* io_dtype is not MSS_F32 or MSS_BF16             */
     MSS_ERR_UNSUPPORTED_DSTATE = 5, /* dstate outside [1, MSS_MAX_DSTATE]              */
@@ -84,6 +105,12 @@ typedef enum mss_dtype {
     MSS_F32 = 0,
     MSS_BF16 = 1
 } mss_dtype;
+
+/* Activation applied after the conv1d. */
+typedef enum mss_activation {
+    MSS_ACT_NONE = 0,
+    MSS_ACT_SILU = 1             /* silu(v) = v * sigmoid(v)                             */
+} mss_activation;
 
 /* Arguments of mss_selective_scan_fwd.  Set struct_size = sizeof(mss_scan_args). */
 typedef struct mss_scan_args {
@@ -150,6 +177,51 @@ typedef struct mss_step_args {
     int32_t reserved0;           /* must be 0                                            */
 } mss_step_args;
 
+/* Arguments of mss_causal_conv1d_fwd.  Set struct_size = sizeof(mss_conv_args). */
+typedef struct mss_conv_args {
+    uint32_t struct_size;
+    int32_t io_dtype;            /* mss_dtype of x, out and both windows                 */
+    int64_t batch;               /* B >= 1                                               */
+    int64_t dim;                 /* D >= 1 channels                                      */
+    int64_t seqlen;              /* 1 <= L <= 2^30                                       */
+    int64_t width;               /* taps, 1..MSS_MAX_CONV_WIDTH                          */
+
+    const void *x;               /* [b,d,t] input                                        */
+    int64_t x_stride[3];
+    const float *weight;         /* [d,k] fp32 taps, oldest sample first (a framework    */
+    int64_t weight_stride[2];    /* Conv1d weight [D,1,W] or [D,W,1] viewed as [D,W])    */
+    const float *bias;           /* [d] fp32 contiguous; NULL means 0                    */
+    const void *initial_state;   /* [b,d,width-1] io_dtype contiguous: the window before */
+                                 /* t = 0, oldest first; NULL means zeros                */
+    void *out;                   /* [b,d,t] result, io_dtype                             */
+    int64_t out_stride[3];
+    void *final_state;           /* [b,d,width-1] io_dtype contiguous: the window after  */
+                                 /* the last step; NULL: not written                     */
+    int32_t activation;          /* mss_activation                                       */
+    int32_t reserved0;           /* must be 0                                            */
+} mss_conv_args;
+
+/* Arguments of mss_causal_conv1d_update.  Set struct_size = sizeof(mss_conv_step_args). */
+typedef struct mss_conv_step_args {
+    uint32_t struct_size;
+    int32_t io_dtype;            /* mss_dtype of state, x and out                        */
+    int64_t batch;
+    int64_t dim;
+    int64_t width;               /* 1..MSS_MAX_CONV_WIDTH                                */
+
+    void *state;                 /* [b,d,width-1] io_dtype contiguous window, oldest     */
+                                 /* first, read and slid in place (NULL iff width == 1)  */
+    const void *x;               /* [b,d] new sample                                     */
+    int64_t x_stride[2];
+    const float *weight;         /* [d,k] fp32                                           */
+    int64_t weight_stride[2];
+    const float *bias;           /* [d] fp32 contiguous; NULL means 0                    */
+    void *out;                   /* [b,d] result, io_dtype                               */
+    int64_t out_stride[2];
+    int32_t activation;          /* mss_activation                                       */
+    int32_t reserved0;           /* must be 0                                            */
+} mss_conv_step_args;
+
 /* ABI version of the loaded library (MSS_ABI_VERSION of its build). */
 int mss_abi_version(void);
 
@@ -172,6 +244,20 @@ mss_status mss_selective_scan_fwd(const mss_scan_args *args, void *stream);
 
 /* One-token state update (see the top of this file). */
 mss_status mss_selective_state_update(const mss_step_args *args, void *stream);
+
+/* Causal depthwise conv1d with optional SiLU (see the top of this file).
+ * Any non-negative strides are accepted.  When x and out share a unit-stride
+ * axis, t or d ([B,D,L] or channel-last [B,L,D] buffers), and 4-element
+ * vectors along it are aligned (base pointers aligned to 4 elements, the other
+ * strides multiples of 4, and for the d axis dim a multiple of 4), the kernel
+ * moves whole vectors; otherwise it reads element by element.  The result is
+ * the same either way.  out and final_state must not overlap any input.  No
+ * workspace. */
+mss_status mss_causal_conv1d_fwd(const mss_conv_args *args, void *stream);
+
+/* One decode step of the conv1d (see the top of this file).  The window
+ * `state` is the only in/out buffer; out must not overlap it or any input. */
+mss_status mss_causal_conv1d_update(const mss_conv_step_args *args, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
-"""mamba_selective_scan_amd -- Mamba selective-scan forward and state update on
-MI355X (gfx950), through the C ABI of libmss (include/mss.h).
+"""mamba_selective_scan_amd -- Mamba selective-scan forward and state update, and
+the causal depthwise conv1d (+ SiLU) that feeds the scan with its decode step,
+on MI355X (gfx950), through the C ABI of libmss (include/mss.h).
 
 This module marshals arguments only: it reads tensor pointers, logical strides
 and torch's current HIP stream and calls libmss, whose HIP kernels do every
@@ -9,12 +10,17 @@ is no CPU or PyTorch fallback; without the built library every call raises.
     out = selective_scan_fwd(u, delta_raw, A_log, B, C, D, z, dt_bias)
     out, h = selective_scan_fwd(..., return_final_state=True)
     y = selective_state_update(state, u_t, delta_raw_t, A_log, B_t, C_t, D, z_t, dt_bias)
+    u = causal_conv1d_fwd(x, weight, bias)                  # silu(causal conv)
+    u, window = causal_conv1d_fwd(x, weight, bias, return_final_state=True)
+    u_t = causal_conv1d_update(window, x_t, weight, bias)   # window slides in place
 
 Shapes (logical index order, any strides): u, delta_raw, z, out [B, D, L];
 B, C [B, N, L]; A_log [D, N]; D, dt_bias [D]; states [B, D, N] (fp32,
 contiguous).  A channel-last [B, L, D] buffer is passed as its transpose(1, 2)
 view.  u, delta_raw, z, B, C share one dtype (float32 or bfloat16); A_log, D,
-dt_bias and the states are float32.
+dt_bias and the states are float32.  The conv takes x, out [B, D, L] (any
+strides), weight [D, W] fp32 (W <= 4; a [D, 1, W] or [D, W, 1] weight is
+viewed as [D, W]), bias [D] fp32, and windows [B, D, W-1] of x's dtype.
 """
 
 from __future__ import annotations
@@ -25,7 +31,8 @@ from . import _lib
 from ._lib import MSS_MAX_DSTATE, MssError
 
 __all__ = ["selective_scan_fwd", "selective_state_update", "scan_workspace_size",
-           "MssError", "MSS_MAX_DSTATE", "library_path"]
+           "causal_conv1d_fwd", "causal_conv1d_update", "MssError", "MSS_MAX_DSTATE",
+           "library_path"]
 
 
 def library_path() -> str:
@@ -223,4 +230,109 @@ def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_
     a.out, a.out_stride = _ptr(out), _strides(out, 2)
     a.delta_softplus = 1 if delta_softplus else 0
     _lib.check(lib.mss_selective_state_update(ctypes.byref(a), _stream_handle(dev)))
+    return out
+
+
+_ACTIVATIONS = {None: _lib.MSS_ACT_NONE, "none": _lib.MSS_ACT_NONE, "silu": _lib.MSS_ACT_SILU}
+
+
+def _conv_weight(weight, dim, device):
+    torch = _torch()
+    _need(weight, "weight", weight.dim(), torch.float32, device)
+    if weight.dim() == 3:
+        if weight.shape[1] == 1:
+            weight = weight[:, 0, :]
+        elif weight.shape[2] == 1:
+            weight = weight[:, :, 0]
+        else:
+            raise ValueError(f"a 3-d conv weight must be [D, 1, W] or [D, W, 1], got "
+                             f"{tuple(weight.shape)}")
+    if weight.dim() != 2 or weight.shape[0] != dim:
+        raise ValueError(f"weight must be [{dim}, W], got {tuple(weight.shape)}")
+    return weight
+
+
+def _window(t, name, shape, dtype, device):
+    if t is None:
+        return None
+    _need(t, name, 3, dtype, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def causal_conv1d_fwd(x, weight, bias=None, *, activation="silu", initial_state=None,
+                      return_final_state=False, out=None, final_state=None):
+    """Causal depthwise conv1d with optional SiLU, ordered on torch's current stream.
+
+    x [B, D, L] (float32 or bfloat16, any strides); weight [D, W] fp32;
+    bias [D] fp32 or None; activation "silu" or None; initial_state
+    [B, D, W-1] (x's dtype, contiguous) is the window before the first step
+    (None means zeros).  Returns out (x's shape and dtype), or
+    (out, final_state) with the window after the last step when
+    ``return_final_state``.
+    """
+    torch = _torch()
+    lib = _lib.lib()
+    dev = x.device
+    _need(x, "x", 3)
+    bsz, dim, seqlen = x.shape
+    weight = _conv_weight(weight, dim, dev)
+    width = weight.shape[1]
+    _contig_f32(bias, "bias", (dim,), dev)
+    if activation not in _ACTIVATIONS:
+        raise ValueError(f"activation must be 'silu' or None, got {activation!r}")
+    win_shape = (bsz, dim, width - 1)
+    _window(initial_state, "initial_state", win_shape, x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    if tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype or out.device != dev:
+        raise ValueError("out must match x in shape, dtype and device")
+    if return_final_state and final_state is None:
+        final_state = torch.empty(win_shape, dtype=x.dtype, device=dev)
+    _window(final_state, "final_state", win_shape, x.dtype, dev)
+    a = _lib.new_conv_args()
+    a.io_dtype = _io_dtype(x)
+    a.batch, a.dim, a.seqlen, a.width = bsz, dim, seqlen, width
+    a.x, a.x_stride = _ptr(x), _strides(x, 3)
+    a.weight, a.weight_stride = _ptr(weight), _strides(weight, 2)
+    a.bias = _ptr(bias)
+    a.initial_state = _ptr(initial_state)
+    a.out, a.out_stride = _ptr(out), _strides(out, 3)
+    a.final_state = _ptr(final_state)
+    a.activation = _ACTIVATIONS[activation]
+    _lib.check(lib.mss_causal_conv1d_fwd(ctypes.byref(a), _stream_handle(dev)))
+    if return_final_state:
+        return out, final_state
+    return out
+
+
+def causal_conv1d_update(state, x, weight, bias=None, *, activation="silu", out=None):
+    """One conv1d decode step: returns out [B, D] for the new sample x [B, D] and
+    slides ``state`` [B, D, W-1] (x's dtype, contiguous) in place."""
+    torch = _torch()
+    lib = _lib.lib()
+    dev = x.device
+    _need(x, "x", 2)
+    bsz, dim = x.shape
+    weight = _conv_weight(weight, dim, dev)
+    width = weight.shape[1]
+    _contig_f32(bias, "bias", (dim,), dev)
+    if activation not in _ACTIVATIONS:
+        raise ValueError(f"activation must be 'silu' or None, got {activation!r}")
+    _window(state, "state", (bsz, dim, width - 1), x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    a = _lib.new_conv_step_args()
+    a.io_dtype = _io_dtype(x)
+    a.batch, a.dim, a.width = bsz, dim, width
+    a.state = _ptr(state) if width > 1 else None
+    a.x, a.x_stride = _ptr(x), _strides(x, 2)
+    a.weight, a.weight_stride = _ptr(weight), _strides(weight, 2)
+    a.bias = _ptr(bias)
+    a.out, a.out_stride = _ptr(out), _strides(out, 2)
+    a.activation = _ACTIVATIONS[activation]
+    _lib.check(lib.mss_causal_conv1d_update(ctypes.byref(a), _stream_handle(dev)))
     return out

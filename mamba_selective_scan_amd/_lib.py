@@ -15,8 +15,11 @@ LIB_PATH = os.path.join(PKG_DIR, "libmss.so")
 
 MSS_ABI_VERSION = 1
 MSS_MAX_DSTATE = 16
+MSS_MAX_CONV_WIDTH = 4
 MSS_F32 = 0
 MSS_BF16 = 1
+MSS_ACT_NONE = 0
+MSS_ACT_SILU = 1
 
 STATUS = {
     0: "MSS_OK",
@@ -34,7 +37,8 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ("mss_abi_version", "mss_status_string", "mss_selective_scan_workspace_size",
-           "mss_selective_scan_fwd", "mss_selective_state_update")
+           "mss_selective_scan_fwd", "mss_selective_state_update", "mss_causal_conv1d_fwd",
+           "mss_causal_conv1d_update")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -79,6 +83,45 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("io_dtype", _i32),
+        ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("width", _i64),
+        ("x", _vp), ("x_stride", _i64 * 3),
+        ("weight", _vp), ("weight_stride", _i64 * 2),
+        ("bias", _vp),
+        ("initial_state", _vp),
+        ("out", _vp), ("out_stride", _i64 * 3),
+        ("final_state", _vp),
+        ("activation", _i32), ("reserved0", _i32),
+    ]
+
+
+class ConvStepArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("io_dtype", _i32),
+        ("batch", _i64), ("dim", _i64), ("width", _i64),
+        ("state", _vp),
+        ("x", _vp), ("x_stride", _i64 * 2),
+        ("weight", _vp), ("weight_stride", _i64 * 2),
+        ("bias", _vp),
+        ("out", _vp), ("out_stride", _i64 * 2),
+        ("activation", _i32), ("reserved0", _i32),
+    ]
+
+
+def new_conv_args() -> ConvArgs:
+    a = ConvArgs()
+    a.struct_size = ctypes.sizeof(ConvArgs)
+    return a
+
+
+def new_conv_step_args() -> ConvStepArgs:
+    a = ConvStepArgs()
+    a.struct_size = ctypes.sizeof(ConvStepArgs)
+    return a
+
+
 def new_scan_args() -> ScanArgs:
     a = ScanArgs()
     a.struct_size = ctypes.sizeof(ScanArgs)
@@ -115,6 +158,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_selective_scan_fwd.restype = ctypes.c_int
     lib.mss_selective_state_update.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.mss_selective_state_update.restype = ctypes.c_int
+    lib.mss_causal_conv1d_fwd.argtypes = [ctypes.POINTER(ConvArgs), _vp]
+    lib.mss_causal_conv1d_fwd.restype = ctypes.c_int
+    lib.mss_causal_conv1d_update.argtypes = [ctypes.POINTER(ConvStepArgs), _vp]
+    lib.mss_causal_conv1d_update.restype = ctypes.c_int
     return lib
 
 

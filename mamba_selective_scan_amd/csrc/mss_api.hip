@@ -137,6 +137,23 @@ ScanPlan make_plan(const mss_scan_args* a) {
   return p;
 }
 
+// Conv strides with every size-1 dimension's stride set to 0: such a dimension
+// is never stepped, so its stride must not decide the path.
+void conv_strides(int64_t* out, const int64_t* st, const int64_t* sizes, int rank) {
+  for (int i = 0; i < rank; ++i) out[i] = sizes[i] == 1 ? 0 : st[i];
+}
+
+bool all_mult(const int64_t* st, int rank, int64_t m, int skip) {
+  for (int i = 0; i < rank; ++i)
+    if (i != skip && st[i] % m != 0) return false;
+  return true;
+}
+
+// Channel-fast conv: time segments per 256-channel group so that the grid
+// holds about this many waves.
+constexpr int64_t kConvTargetWaves = 4096;
+constexpr int64_t kConvMinSeg = 64;
+
 }  // namespace
 
 extern "C" {
@@ -147,7 +164,7 @@ const char* mss_status_string(mss_status status) {
   switch (status) {
     case MSS_OK: return "ok";
     case MSS_ERR_NULL_POINTER: return "a required pointer is NULL";
-    case MSS_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 1 and fit the grid)";
+    case MSS_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 1 and fit the grid; conv width 1..4)";
     case MSS_ERR_BAD_STRIDE: return "invalid stride (negative, overlapping output, or a tile spans >= 2 GiB)";
     case MSS_ERR_UNSUPPORTED_DTYPE: return "unsupported io dtype (expected MSS_F32 or MSS_BF16)";
     case MSS_ERR_UNSUPPORTED_DSTATE: return "dstate must be between 1 and 16";
@@ -351,6 +368,139 @@ mss_status mss_selective_state_update(const mss_step_args* a, void* stream) {
   s.softplus = a->delta_softplus ? 1 : 0;
   mss::StepPtrs p{a->state, a->u, a->delta_raw, a->A_log, a->B, a->C, a->D, a->z, a->dt_bias, a->out};
   const hipError_t e = mss::launch_step(s, p, a->io_dtype == MSS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
+mss_status mss_causal_conv1d_fwd(const mss_conv_args* a, void* stream) {
+  if (a == nullptr || a->struct_size != sizeof(mss_conv_args) || a->reserved0 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
+  if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->width < 1 ||
+      a->width > MSS_MAX_CONV_WIDTH || a->batch > kMaxDim || a->dim > kMaxDim ||
+      a->seqlen > kMaxSeqlen || a->batch * a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->activation != MSS_ACT_NONE && a->activation != MSS_ACT_SILU) return MSS_ERR_BAD_STRUCT;
+  if (a->x == nullptr || a->weight == nullptr || a->out == nullptr) return MSS_ERR_NULL_POINTER;
+  const int64_t es = a->io_dtype == MSS_BF16 ? 2 : 4;
+  const int64_t W = a->width;
+  const int64_t xs[3] = {a->batch, a->dim, a->seqlen};
+  const int64_t ws[2] = {a->dim, W};
+  const int64_t vs[1] = {a->dim};
+  const int64_t win[3] = {a->batch, a->dim, W - 1};
+  const int64_t unit[3] = {a->dim * (W - 1), W - 1, 1};
+  const int64_t one[1] = {1};
+  if (!strides_nonneg(a->x_stride, 3) || !strides_nonneg(a->out_stride, 3) ||
+      !strides_nonneg(a->weight_stride, 2))
+    return MSS_ERR_BAD_STRIDE;
+  if (!non_overlapping(xs, a->out_stride, 3)) return MSS_ERR_BAD_STRIDE;
+  if (!aligned(a->x, es) || !aligned(a->out, es) || !aligned(a->initial_state, es) ||
+      !aligned(a->final_state, es) || !aligned(a->weight, 4) || !aligned(a->bias, 4))
+    return MSS_ERR_MISALIGNED;
+  // The windows are empty for width 1: nothing to read or write.
+  const void* init = W > 1 ? a->initial_state : nullptr;
+  void* fin = W > 1 ? a->final_state : nullptr;
+  const Extent ins[] = {
+      extent_of(a->x, xs, a->x_stride, 3, es),
+      extent_of(a->weight, ws, a->weight_stride, 2, 4),
+      extent_of(a->bias, vs, one, 1, 4),
+      extent_of(init, win, unit, 3, es),
+  };
+  const Extent eo = extent_of(a->out, xs, a->out_stride, 3, es);
+  const Extent ef = extent_of(fin, win, unit, 3, es);
+  for (const Extent& e : ins)
+    if (overlaps(eo, e) || overlaps(ef, e)) return MSS_ERR_ALIASING;
+  if (overlaps(eo, ef)) return MSS_ERR_ALIASING;
+
+  mss::ConvShape s{};
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.seqlen = static_cast<int>(a->seqlen);
+  s.width = static_cast<int>(W);
+  conv_strides(s.sx, a->x_stride, xs, 3);
+  conv_strides(s.so, a->out_stride, xs, 3);
+  std::memcpy(s.sw, a->weight_stride, sizeof(s.sw));
+  s.silu = a->activation == MSS_ACT_SILU ? 1 : 0;
+  s.path = mss::kConvElementwise;
+  s.nseg = 1;
+  s.seg_len = s.seqlen;
+  // 4-element vectors along the unit-stride axis need every vector start
+  // aligned: the base pointers to a whole vector and every other stride a
+  // multiple of 4 elements.
+  const int64_t V = mss::kConvVec;
+  const bool vec_aligned = aligned(a->x, V * es) && aligned(a->out, V * es);
+  if (vec_aligned && a->seqlen > 1 && s.sx[2] == 1 && s.so[2] == 1 && all_mult(s.sx, 3, V, 2) &&
+      all_mult(s.so, 3, V, 2)) {
+    s.path = mss::kConvTimeFast;
+    const int64_t nwg = a->batch * a->dim * ((a->seqlen + 1023) / 1024);
+    if (nwg > 0xFFFFFFFFll) s.path = mss::kConvElementwise;
+  } else if (vec_aligned && a->dim % V == 0 && a->dim > 1 && s.sx[1] == 1 && s.so[1] == 1 &&
+             all_mult(s.sx, 3, V, 1) && all_mult(s.so, 3, V, 1)) {
+    s.path = mss::kConvChanFast;
+    const int64_t groups = (a->dim + 255) / 256;
+    const int64_t base = a->batch * groups;
+    int64_t nseg = std::max<int64_t>(1, (kConvTargetWaves + base - 1) / base);
+    nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, a->seqlen / kConvMinSeg));
+    int64_t seg = (a->seqlen + nseg - 1) / nseg;
+    seg = (seg + 7) / 8 * 8;
+    s.seg_len = static_cast<int>(seg);
+    s.nseg = static_cast<int>((a->seqlen + seg - 1) / seg);
+    if (base * s.nseg > 0xFFFFFFFFll) s.path = mss::kConvElementwise;
+  }
+  if (s.path == mss::kConvElementwise && (a->batch * a->dim * a->seqlen + 255) / 256 > 0xFFFFFFFFll)
+    return MSS_ERR_BAD_SHAPE;
+  const mss::ConvPtrs p{a->x, a->weight, a->bias, init, a->out, fin};
+  const hipError_t e = mss::launch_conv(s, p, a->io_dtype == MSS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
+mss_status mss_causal_conv1d_update(const mss_conv_step_args* a, void* stream) {
+  if (a == nullptr || a->struct_size != sizeof(mss_conv_step_args) || a->reserved0 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
+  if (a->batch < 1 || a->dim < 1 || a->width < 1 || a->width > MSS_MAX_CONV_WIDTH ||
+      a->batch > kMaxDim || a->dim > kMaxDim || a->batch * a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->activation != MSS_ACT_NONE && a->activation != MSS_ACT_SILU) return MSS_ERR_BAD_STRUCT;
+  const int64_t W = a->width;
+  if (a->x == nullptr || a->weight == nullptr || a->out == nullptr ||
+      (W > 1 && a->state == nullptr))
+    return MSS_ERR_NULL_POINTER;
+  const int64_t es = a->io_dtype == MSS_BF16 ? 2 : 4;
+  if (!strides_nonneg(a->x_stride, 2) || !strides_nonneg(a->out_stride, 2) ||
+      !strides_nonneg(a->weight_stride, 2))
+    return MSS_ERR_BAD_STRIDE;
+  const int64_t xs[2] = {a->batch, a->dim};
+  if (!non_overlapping(xs, a->out_stride, 2)) return MSS_ERR_BAD_STRIDE;
+  if (!aligned(a->x, es) || !aligned(a->out, es) || !aligned(a->state, es) ||
+      !aligned(a->weight, 4) || !aligned(a->bias, 4))
+    return MSS_ERR_MISALIGNED;
+  const int64_t ws[2] = {a->dim, W};
+  const int64_t vs[1] = {a->dim};
+  const int64_t one[1] = {1};
+  const int64_t win[3] = {a->batch, a->dim, W - 1};
+  const int64_t unit[3] = {a->dim * (W - 1), W - 1, 1};
+  void* state = W > 1 ? a->state : nullptr;
+  const Extent ins[] = {
+      extent_of(a->x, xs, a->x_stride, 2, es),
+      extent_of(a->weight, ws, a->weight_stride, 2, 4),
+      extent_of(a->bias, vs, one, 1, 4),
+  };
+  const Extent eo = extent_of(a->out, xs, a->out_stride, 2, es);
+  const Extent est = extent_of(state, win, unit, 3, es);
+  for (const Extent& e : ins)
+    if (overlaps(eo, e) || overlaps(est, e)) return MSS_ERR_ALIASING;
+  if (overlaps(eo, est)) return MSS_ERR_ALIASING;
+  mss::ConvStepShape s{};
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.width = static_cast<int>(W);
+  std::memcpy(s.sx, a->x_stride, sizeof(s.sx));
+  std::memcpy(s.so, a->out_stride, sizeof(s.so));
+  std::memcpy(s.sw, a->weight_stride, sizeof(s.sw));
+  s.silu = a->activation == MSS_ACT_SILU ? 1 : 0;
+  const mss::ConvStepPtrs p{state, a->x, a->weight, a->bias, a->out};
+  const hipError_t e = mss::launch_conv_step(s, p, a->io_dtype == MSS_BF16,
+                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
 }
 

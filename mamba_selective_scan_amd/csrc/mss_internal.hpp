@@ -76,6 +76,51 @@ struct StepPtrs {
   void* out;
 };
 
+// Causal depthwise conv1d.  Loads and stores move kConvVec-element vectors
+// along the unit-stride axis when the layout allows it.
+constexpr int kConvVec = 4;
+constexpr int kConvMaxWidth = 4;
+
+enum ConvPath : int { kConvElementwise = 0, kConvTimeFast = 1, kConvChanFast = 2 };
+
+struct ConvShape {
+  int batch, dim, seqlen, width;
+  int64_t sx[3], so[3];  // x, out: (b, d, t) element strides
+  int64_t sw[2];         // weight: (d, k)
+  int silu;
+  int path;              // ConvPath
+  int seg_len;           // channel-fast path: steps per thread
+  int nseg;
+};
+
+struct ConvPtrs {
+  const void* x;
+  const float* weight;
+  const float* bias;
+  const void* init;  // [batch][dim][width-1] or null
+  void* out;
+  void* fin;         // [batch][dim][width-1] or null
+};
+
+struct ConvStepShape {
+  int batch, dim, width;
+  int64_t sx[2], so[2];  // (b, d)
+  int64_t sw[2];
+  int silu;
+};
+
+struct ConvStepPtrs {
+  void* state;
+  const void* x;
+  const float* weight;
+  const float* bias;
+  void* out;
+};
+
+hipError_t launch_conv(const ConvShape& s, const ConvPtrs& p, bool io_bf16, hipStream_t stream);
+hipError_t launch_conv_step(const ConvStepShape& s, const ConvStepPtrs& p, bool io_bf16,
+                            hipStream_t stream);
+
 // Enqueue the scan (segment aggregates, carry propagation when nseg > 1, then
 // the main pass).  io_bf16 selects the bf16 storage type; x_tfast says that
 // u/delta_raw/z/out have unit stride along t (else along d), bc_tfast that B

@@ -155,3 +155,55 @@ def algorithmic_bytes(batch: int, dim: int, seqlen: int, dstate: int, io_bytes: 
     if final_state:
         n += batch * dim * dstate * 4
     return n
+
+
+def generate_conv(batch: int, dim: int, seqlen: int, width: int = 4, layout: str = "bld",
+                  seed: int = 0) -> dict:
+    """Draw one conv1d problem.  Returns numpy float32 arrays in logical order.
+
+    One ``numpy.random.default_rng(seed)`` stream, in this order: x ~ N(0, 1) in
+    its storage shape ([B, L, D] for "bld", [B, D, L] for "bdl"); weight [D, W]
+    and bias [D] ~ U(-1/sqrt(W), 1/sqrt(W)) (the default initialisation of a
+    framework Conv1d with W inputs per output); a carried window [B, D, W-1]
+    ~ N(0, 1).  x is returned as a [b, d, t] view over its storage.
+    """
+    if layout not in ("bdl", "bld"):
+        raise ValueError("layout must be 'bdl' or 'bld'")
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    shape = (batch, dim, seqlen) if layout == "bdl" else (batch, seqlen, dim)
+    x = rng.standard_normal(shape, dtype=f32)
+    bound = 1.0 / np.sqrt(width)
+    weight = rng.uniform(-bound, bound, size=(dim, width)).astype(f32)
+    bias = rng.uniform(-bound, bound, size=dim).astype(f32)
+    window = rng.standard_normal((batch, dim, width - 1), dtype=f32)
+    if layout == "bld":
+        x = x.transpose(0, 2, 1)
+    return {"x": x, "weight": weight, "bias": bias, "window": window, "layout": layout}
+
+
+def conv_to_torch(inputs: dict, device, io_dtype: str = "f32") -> dict:
+    """Move a conv problem to ``device``: x and the window in ``io_dtype`` (round to
+    nearest even for bf16), weight and bias float32; x keeps its storage layout."""
+    import torch
+
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[io_dtype]
+    x = inputs["x"]
+    if inputs["layout"] == "bld":
+        t = torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1)))
+        t = t.to(device=device, dtype=dt).transpose(1, 2)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dt)
+    return {
+        "x": t,
+        "weight": torch.from_numpy(inputs["weight"]).to(device),
+        "bias": torch.from_numpy(inputs["bias"]).to(device),
+        "window": torch.from_numpy(inputs["window"]).to(device=device, dtype=dt),
+        "layout": inputs["layout"],
+    }
+
+
+def conv_algorithmic_bytes(batch: int, dim: int, seqlen: int, width: int, io_bytes: int,
+                           has_bias: bool = True) -> int:
+    """Bytes the conv1d must move: x read once, out written once, taps and bias."""
+    return 2 * batch * dim * seqlen * io_bytes + dim * width * 4 + (dim * 4 if has_bias else 0)

@@ -64,7 +64,9 @@ def _c_layout(struct_name, fields, tmp_path):
 
 
 @pytest.mark.parametrize("cls,cname", [(_lib.ScanArgs, "mss_scan_args"),
-                                       (_lib.StepArgs, "mss_step_args")])
+                                       (_lib.StepArgs, "mss_step_args"),
+                                       (_lib.ConvArgs, "mss_conv_args"),
+                                       (_lib.ConvStepArgs, "mss_conv_step_args")])
 def test_ctypes_struct_matches_c_layout(cls, cname, tmp_path):
     names = [f[0] for f in cls._fields_]
     size, offs = _c_layout(cname, names, tmp_path)
@@ -228,6 +230,91 @@ def test_step_argument_checks(case):
     a = step_args()
     fn(a)
     assert _lib.lib().mss_selective_state_update(ctypes.byref(a), None) == code(expect)
+
+
+def conv_args(width=4):
+    a = _lib.new_conv_args()
+    a.io_dtype = _lib.MSS_F32
+    a.batch, a.dim, a.seqlen, a.width = 2, 96, 100, width
+    x = (96 * 100, 1, 96)             # channel-last [B, L, D] storage
+    a.x, a.x_stride = fake(0), (ctypes.c_int64 * 3)(*x)
+    a.weight, a.weight_stride = fake(1), (ctypes.c_int64 * 2)(width, 1)
+    a.bias = fake(2)
+    a.initial_state = fake(3)
+    a.out, a.out_stride = fake(4), (ctypes.c_int64 * 3)(*x)
+    a.final_state = fake(5)
+    a.activation = _lib.MSS_ACT_SILU
+    return a
+
+
+CONV_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 12), "MSS_ERR_BAD_STRUCT"),
+    "reserved": (lambda a: setattr(a, "reserved0", 3), "MSS_ERR_BAD_STRUCT"),
+    "activation": (lambda a: setattr(a, "activation", 5), "MSS_ERR_BAD_STRUCT"),
+    "dtype": (lambda a: setattr(a, "io_dtype", 9), "MSS_ERR_UNSUPPORTED_DTYPE"),
+    "width0": (lambda a: setattr(a, "width", 0), "MSS_ERR_BAD_SHAPE"),
+    "width5": (lambda a: setattr(a, "width", 5), "MSS_ERR_BAD_SHAPE"),
+    "seqlen0": (lambda a: setattr(a, "seqlen", 0), "MSS_ERR_BAD_SHAPE"),
+    "dim_huge": (lambda a: setattr(a, "dim", 1 << 31), "MSS_ERR_BAD_SHAPE"),
+    "x_null": (lambda a: setattr(a, "x", None), "MSS_ERR_NULL_POINTER"),
+    "weight_null": (lambda a: setattr(a, "weight", None), "MSS_ERR_NULL_POINTER"),
+    "out_null": (lambda a: setattr(a, "out", None), "MSS_ERR_NULL_POINTER"),
+    "neg_stride": (lambda a: a.x_stride.__setitem__(2, -96), "MSS_ERR_BAD_STRIDE"),
+    "neg_weight_stride": (lambda a: a.weight_stride.__setitem__(0, -4), "MSS_ERR_BAD_STRIDE"),
+    "out_overlap": (lambda a: a.out_stride.__setitem__(2, 0), "MSS_ERR_BAD_STRIDE"),
+    "misaligned_x": (lambda a: setattr(a, "x", fake(0) + 2), "MSS_ERR_MISALIGNED"),
+    "misaligned_bias": (lambda a: setattr(a, "bias", fake(2) + 1), "MSS_ERR_MISALIGNED"),
+    "out_is_x": (lambda a: setattr(a, "out", fake(0)), "MSS_ERR_ALIASING"),
+    "final_on_weight": (lambda a: setattr(a, "final_state", fake(1)), "MSS_ERR_ALIASING"),
+    "final_in_out": (lambda a: setattr(a, "final_state", fake(4) + 400), "MSS_ERR_ALIASING"),
+    "out_on_init": (lambda a: setattr(a, "out", fake(3) - 16), "MSS_ERR_ALIASING"),
+}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(CONV_CASES))
+def test_conv_argument_checks(case):
+    fn, expect = CONV_CASES[case]
+    a = conv_args()
+    fn(a)
+    assert _lib.lib().mss_causal_conv1d_fwd(ctypes.byref(a), None) == code(expect)
+
+
+def conv_step_args(width=4):
+    a = _lib.new_conv_step_args()
+    a.io_dtype = _lib.MSS_BF16
+    a.batch, a.dim, a.width = 2, 96, width
+    a.state = fake(0)
+    a.x, a.x_stride = fake(1), (ctypes.c_int64 * 2)(96, 1)
+    a.weight, a.weight_stride = fake(2), (ctypes.c_int64 * 2)(width, 1)
+    a.bias = fake(3)
+    a.out, a.out_stride = fake(4), (ctypes.c_int64 * 2)(96, 1)
+    a.activation = _lib.MSS_ACT_NONE
+    return a
+
+
+CONV_STEP_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 0), "MSS_ERR_BAD_STRUCT"),
+    "activation": (lambda a: setattr(a, "activation", -1), "MSS_ERR_BAD_STRUCT"),
+    "width5": (lambda a: setattr(a, "width", 5), "MSS_ERR_BAD_SHAPE"),
+    "batch0": (lambda a: setattr(a, "batch", 0), "MSS_ERR_BAD_SHAPE"),
+    "state_null": (lambda a: setattr(a, "state", None), "MSS_ERR_NULL_POINTER"),
+    "x_null": (lambda a: setattr(a, "x", None), "MSS_ERR_NULL_POINTER"),
+    "neg_stride": (lambda a: a.out_stride.__setitem__(0, -1), "MSS_ERR_BAD_STRIDE"),
+    "out_overlap": (lambda a: a.out_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
+    "misaligned_state": (lambda a: setattr(a, "state", fake(0) + 1), "MSS_ERR_MISALIGNED"),
+    "out_is_state": (lambda a: setattr(a, "out", fake(0) + 8), "MSS_ERR_ALIASING"),
+    "state_on_x": (lambda a: setattr(a, "state", fake(1)), "MSS_ERR_ALIASING"),
+}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(CONV_STEP_CASES))
+def test_conv_step_argument_checks(case):
+    fn, expect = CONV_STEP_CASES[case]
+    a = conv_step_args()
+    fn(a)
+    assert _lib.lib().mss_causal_conv1d_update(ctypes.byref(a), None) == code(expect)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -193,7 +193,14 @@ def test_golden_fixtures_on_gpu(mss):
         c = golden_cases.load(name)
         note(f"golden {name}")
         f32 = lambda a: torch.tensor(a, dtype=torch.float32, device=device())
-        if c["kind"] == "scan":
+        if c["kind"] == "conv":
+            out, fin = mss.causal_conv1d_fwd(f32(c["x"]), f32(c["w"]), f32(c["bias"]),
+                                             activation=None, return_final_state=True)
+        elif c["kind"] == "conv_step":
+            fin = f32(c["state"])
+            out = mss.causal_conv1d_update(fin, f32(c["x"]), f32(c["w"]), f32(c["bias"]),
+                                           activation=None)
+        elif c["kind"] == "scan":
             out, fin = mss.selective_scan_fwd(f32(c["u"]), f32(c["delta_raw"]), f32(c["A_log"]),
                                               f32(c["B"]), f32(c["C"]), D=f32(c["D"]),
                                               delta_softplus=False, return_final_state=True)
