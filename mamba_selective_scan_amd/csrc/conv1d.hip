@@ -14,15 +14,16 @@
 //
 // The op is a stream: every input sample is read once and every output
 // written once, with W FMAs and a SiLU per element in between, so it is bound
-// by HBM bandwidth.  The kernels keep the taps in registers, move 4-element
-// vectors along the unit-stride axis, and take the W-1 samples before each
-// thread's first step from a neighbouring lane or from a few extra loads that
-// hit in L2:
-//   * channel-fast data ([B,L,D]): a lane owns 4 adjacent channels and walks a
-//     time segment, sliding the window in registers (the walk the SpeechLens
-//     notes describe, with 4 channels per lane so one wave reads 1 KB rows);
-//   * time-fast data ([B,D,L]): a lane owns 4 consecutive steps of one
-//     channel and gets the 3 samples before them from the lane below;
+// by HBM bandwidth.  The kernels keep the taps in registers, move 16-byte
+// vectors (4 fp32 or 8 bf16 elements) along the unit-stride axis, and take
+// the W-1 samples before each thread's first step from a neighbouring lane or
+// from a few extra loads that hit in L2:
+//   * channel-fast data ([B,L,D]): a lane owns a vector of adjacent channels
+//     and walks a time segment, sliding the window in registers (the walk the
+//     SpeechLens notes describe, with a vector of channels per lane so one
+//     wave reads 1 KB rows);
+//   * time-fast data ([B,D,L]): a lane owns a vector of consecutive steps of
+//     one channel and gets the 3 samples before them from the lane below;
 //   * any other strides, or vectors that would be misaligned: one element per
 //     thread, each tap read directly.
 #include "mss_device.hpp"
@@ -33,10 +34,13 @@ namespace {
 
 constexpr int kXcdsConv = 8;  // MI355X: 8 accelerator dies
 
+// 16-byte vectors: 4 fp32 or 8 bf16 elements, converted to fp32 on load and
+// rounded to nearest even on a bf16 store.
 template <typename IO>
-struct vec4_io;
+struct vec16;
 template <>
-struct vec4_io<float> {
+struct vec16<float> {
+  static constexpr int N = 4;
   __device__ static inline void load(const float* p, float* v) {
     const float4 q = *reinterpret_cast<const float4*>(p);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
@@ -46,19 +50,24 @@ struct vec4_io<float> {
   }
 };
 template <>
-struct vec4_io<bf16_t> {
+struct vec16<bf16_t> {
+  static constexpr int N = 8;
   __device__ static inline void load(const bf16_t* p, float* v) {
-    const uint2 q = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(q.x << 16);
-    v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16);
-    v[3] = __uint_as_float(q.y & 0xffff0000u);
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
   }
   __device__ static inline void store(bf16_t* p, const float* v) {
-    uint2 q;
-    q.x = static_cast<uint32_t>(bf16_bits(v[0])) | (static_cast<uint32_t>(bf16_bits(v[1])) << 16);
-    q.y = static_cast<uint32_t>(bf16_bits(v[2])) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16);
-    *reinterpret_cast<uint2*>(p) = q;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(bf16_bits(v[2 * i])) |
+             (static_cast<uint32_t>(bf16_bits(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
 
@@ -112,155 +121,178 @@ __global__ __launch_bounds__(256) void conv_elem_kernel(ConvShape s, ConvPtrs p)
   }
 }
 
-// Time-fast ([B,D,L]): thread = 4 consecutive steps of one channel, one
-// workgroup = 1024 steps.  The W-1 samples before a lane's first step are the
-// last ones of the lane below; lane 0 of each wave loads its own.
-constexpr int kTfThreads = 256;
-constexpr int kTfSteps = kTfThreads * kConvVec;
+// Time-fast ([B,D,L]): one wave covers kTfSpan consecutive steps of one
+// channel as kTfSpan / (64 VE) blocks; in a block, lane l owns the VE steps
+// starting at VE l (VE = 4 fp32 or 8 bf16 elements: 16 bytes).  All of a
+// lane's loads are issued before any is used.  The 3 samples before a lane's
+// first step are the last ones of the lane below; lane 0 takes them from lane
+// 63 of the previous block, and in the first block from memory or the window.
+constexpr int kTfSpan = 2048;
 
 template <typename IO, int W>
-__global__ __launch_bounds__(kTfThreads) void conv_tfast_kernel(ConvShape s, ConvPtrs p) {
-  const int64_t tblocks = (s.seqlen + kTfSteps - 1) / kTfSteps;
+__global__ __launch_bounds__(64) void conv_tfast_kernel(ConvShape s, ConvPtrs p) {
+  constexpr int VE = vec16<IO>::N;
+  constexpr int NB = kTfSpan / (64 * VE);
+  const int64_t wblocks = (s.seqlen + kTfSpan - 1) / kTfSpan;
   const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int64_t row = logical / tblocks;
-  const int t = static_cast<int>(logical % tblocks) * kTfSteps + threadIdx.x * kConvVec;
+  const int64_t row = logical / wblocks;
+  const int t_base = static_cast<int>(logical % wblocks) * kTfSpan;
   const int d = static_cast<int>(row % s.dim);
   const int b = static_cast<int>(row / s.dim);
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
   const IO* x = static_cast<const IO*>(p.x) + b * s.sx[0] + d * s.sx[1];
   const IO* init = static_cast<const IO*>(p.init);
 
-  // ext[j] = x~[t - 3 + j], j = 0..6: three earlier samples, then this lane's four.
-  float ext[3 + kConvVec];
-  float* v = ext + 3;
-  const bool full = t + kConvVec <= s.seqlen;
-  if (full) {
-    vec4_io<IO>::load(x + t, v);
-  } else {
+  float v[NB][VE];
 #pragma unroll
-    for (int j = 0; j < kConvVec; ++j) v[j] = t + j < s.seqlen ? io_traits<IO>::load(x + t + j) : 0.0f;
-  }
-  // Every lane takes part in the shuffles (lanes past the end included).
+  for (int j = 0; j < NB; ++j) {
+    const int t = t_base + j * 64 * VE + lane * VE;
+    if (t + VE <= s.seqlen) {
+      vec16<IO>::load(x + t, v[j]);
+    } else {
 #pragma unroll
-  for (int j = 0; j < 3; ++j) ext[j] = __shfl_up(v[j + 1], 1, 64);
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int tau = t - 3 + j;
-      ext[j] = tau >= 0 ? io_traits<IO>::load(x + tau) : window_sample<IO, W>(init, row, tau);
+      for (int e = 0; e < VE; ++e) v[j][e] = t + e < s.seqlen ? io_traits<IO>::load(x + t + e) : 0.0f;
     }
   }
-  if (t >= s.seqlen) return;
-
+  float before[3];  // the 3 samples before t_base
+#pragma unroll
+  for (int e = 0; e < 3; ++e) {
+    const int tau = t_base - 3 + e;
+    before[e] = lane != 0 ? 0.0f
+              : tau >= 0 ? io_traits<IO>::load(x + tau) : window_sample<IO, W>(init, row, tau);
+  }
   float wk[W];
 #pragma unroll
   for (int k = 0; k < W; ++k) wk[k] = p.weight[d * s.sw[0] + k * s.sw[1]];
   const float bias = p.bias != nullptr ? p.bias[d] : 0.0f;
-  float y[kConvVec];
-#pragma unroll
-  for (int i = 0; i < kConvVec; ++i) {
-    float acc = bias;
-#pragma unroll
-    for (int k = 0; k < W; ++k) acc = fmaf(wk[k], ext[i + 4 - W + k], acc);
-    y[i] = activate(acc, s.silu);
-  }
   IO* out = static_cast<IO*>(p.out) + b * s.so[0] + d * s.so[1];
-  if (full) {
-    vec4_io<IO>::store(out + t, y);
-  } else {
+
 #pragma unroll
-    for (int j = 0; j < kConvVec; ++j)
-      if (t + j < s.seqlen) io_traits<IO>::store(out + t + j, y[j]);
-  }
-  // The lane holding step L-1 exports the window x~[L-(W-1) .. L-1].
-  if (p.fin != nullptr && s.seqlen - 1 - t < kConvVec) {
-    IO* fin = static_cast<IO*>(p.fin) + row * (W - 1);
-    const int last = s.seqlen - 1 - t + 3;  // ext index of step L-1
+  for (int j = 0; j < NB; ++j) {
+    const int t = t_base + j * 64 * VE + lane * VE;
+    // ext[i] = x~[t - 3 + i]; every lane takes part in the shuffles.
+    float ext[3 + VE];
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) io_traits<IO>::store(fin + j, ext[last - (W - 2) + j]);
+    for (int e = 0; e < VE; ++e) ext[3 + e] = v[j][e];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const float below = __shfl_up(v[j][VE - 3 + e], 1, 64);
+      const float prev = j > 0 ? __shfl(v[j > 0 ? j - 1 : 0][VE - 3 + e], 63, 64) : before[e];
+      ext[e] = lane == 0 ? prev : below;
+    }
+    if (t < s.seqlen) {
+      float y[VE];
+#pragma unroll
+      for (int i = 0; i < VE; ++i) {
+        float acc = bias;
+#pragma unroll
+        for (int k = 0; k < W; ++k) acc = fmaf(wk[k], ext[i + 4 - W + k], acc);
+        y[i] = activate(acc, s.silu);
+      }
+      if (t + VE <= s.seqlen) {
+        vec16<IO>::store(out + t, y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          if (t + e < s.seqlen) io_traits<IO>::store(out + t + e, y[e]);
+      }
+      // The lane holding step L-1 exports the window x~[L-(W-1) .. L-1].
+      if (p.fin != nullptr && s.seqlen - 1 - t < VE) {
+        IO* fin = static_cast<IO*>(p.fin) + row * (W - 1);
+        const int last = s.seqlen - 1 - t + 3;  // ext index of step L-1
+#pragma unroll
+        for (int e = 0; e < W - 1; ++e) io_traits<IO>::store(fin + e, ext[last - (W - 2) + e]);
+      }
+    }
   }
 }
 
-// Channel-fast ([B,L,D]): thread = 4 adjacent channels, one wave = 256
-// channels, walking a time segment of s.seg_len steps with the window in
-// registers.  Loads are issued kCfUnroll steps ahead of use.
-constexpr int kCfThreads = 64;
-constexpr int kCfChannels = kCfThreads * kConvVec;
+// Channel-fast ([B,L,D]): a lane owns VE adjacent channels (16 bytes: 4 fp32
+// or 8 bf16) and walks a time segment of s.seg_len steps with the window in
+// registers.  A wave is 64 / s.cf_lanes lane groups of s.cf_lanes lanes; each
+// group covers s.cf_lanes * VE channels of its own segment, so that rows
+// narrower than 64 vectors still keep every lane busy.  Loads are issued
+// kCfUnroll steps ahead of use.
 constexpr int kCfUnroll = 8;
 
 template <typename IO, int W>
-__global__ __launch_bounds__(kCfThreads) void conv_cfast_kernel(ConvShape s, ConvPtrs p) {
-  const int groups = (s.dim + kCfChannels - 1) / kCfChannels;
+__global__ __launch_bounds__(64) void conv_cfast_kernel(ConvShape s, ConvPtrs p) {
+  constexpr int VE = vec16<IO>::N;
+  const int lanes = s.cf_lanes;
+  const int per_wave = 64 / lanes;  // segments per wave
+  const int chans = lanes * VE;     // channels per lane group
+  const int groups = (s.dim + chans - 1) / chans;
+  const int wsegs = (s.nseg + per_wave - 1) / per_wave;
   const int64_t logical = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int seg = static_cast<int>(logical % s.nseg);
-  const int64_t rest = logical / s.nseg;
+  const int seg = static_cast<int>(logical % wsegs) * per_wave + threadIdx.x / lanes;
+  const int64_t rest = logical / wsegs;
   const int cg = static_cast<int>(rest % groups);
   const int b = static_cast<int>(rest / groups);
-  const int c = cg * kCfChannels + threadIdx.x * kConvVec;
-  if (c >= s.dim) return;
+  const int c = cg * chans + (threadIdx.x % lanes) * VE;
+  if (c >= s.dim || seg >= s.nseg) return;
   const int t0 = seg * s.seg_len;
   const int t1 = min(s.seqlen, t0 + s.seg_len);
   const IO* x = static_cast<const IO*>(p.x) + b * s.sx[0] + c;
   const IO* init = static_cast<const IO*>(p.init);
   const int64_t row0 = static_cast<int64_t>(b) * s.dim + c;
 
-  float wk[W][kConvVec], bias[kConvVec];
+  float wk[W][VE], bias[VE];
 #pragma unroll
-  for (int i = 0; i < kConvVec; ++i) {
+  for (int i = 0; i < VE; ++i) {
 #pragma unroll
     for (int k = 0; k < W; ++k) wk[k][i] = p.weight[(c + i) * s.sw[0] + k * s.sw[1]];
     bias[i] = p.bias != nullptr ? p.bias[c + i] : 0.0f;
   }
   // win[j] = x~[t - (W-1) + j] for the next step t to compute.
-  float win[W > 1 ? W - 1 : 1][kConvVec];
+  float win[W > 1 ? W - 1 : 1][VE];
 #pragma unroll
   for (int j = 0; j < W - 1; ++j) {
     const int tau = t0 - (W - 1) + j;
     if (tau >= 0) {
-      vec4_io<IO>::load(x + tau * s.sx[2], win[j]);
+      vec16<IO>::load(x + tau * s.sx[2], win[j]);
     } else {
 #pragma unroll
-      for (int i = 0; i < kConvVec; ++i) win[j][i] = window_sample<IO, W>(init, row0 + i, tau);
+      for (int i = 0; i < VE; ++i) win[j][i] = window_sample<IO, W>(init, row0 + i, tau);
     }
   }
   IO* out = static_cast<IO*>(p.out) + b * s.so[0] + c;
   auto step = [&](const float* xv, int t) __attribute__((always_inline)) {
-    float y[kConvVec];
+    float y[VE];
 #pragma unroll
-    for (int i = 0; i < kConvVec; ++i) {
+    for (int i = 0; i < VE; ++i) {
       float acc = bias[i];
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) acc = fmaf(wk[k][i], win[k][i], acc);
       acc = fmaf(wk[W - 1][i], xv[i], acc);
       y[i] = activate(acc, s.silu);
     }
-    vec4_io<IO>::store(out + t * s.so[2], y);
+    vec16<IO>::store(out + t * s.so[2], y);
 #pragma unroll
     for (int k = 0; k + 1 < W - 1; ++k)
 #pragma unroll
-      for (int i = 0; i < kConvVec; ++i) win[k][i] = win[k + 1][i];
+      for (int i = 0; i < VE; ++i) win[k][i] = win[k + 1][i];
     if constexpr (W > 1) {
 #pragma unroll
-      for (int i = 0; i < kConvVec; ++i) win[W - 2][i] = xv[i];
+      for (int i = 0; i < VE; ++i) win[W - 2][i] = xv[i];
     }
   };
   int t = t0;
   for (; t + kCfUnroll <= t1; t += kCfUnroll) {
-    float xv[kCfUnroll][kConvVec];
+    float xv[kCfUnroll][VE];
 #pragma unroll
-    for (int u = 0; u < kCfUnroll; ++u) vec4_io<IO>::load(x + (t + u) * s.sx[2], xv[u]);
+    for (int u = 0; u < kCfUnroll; ++u) vec16<IO>::load(x + (t + u) * s.sx[2], xv[u]);
 #pragma unroll
     for (int u = 0; u < kCfUnroll; ++u) step(xv[u], t + u);
   }
   for (; t < t1; ++t) {
-    float xv[kConvVec];
-    vec4_io<IO>::load(x + t * s.sx[2], xv);
+    float xv[VE];
+    vec16<IO>::load(x + t * s.sx[2], xv);
     step(xv, t);
   }
   if (p.fin != nullptr && t1 == s.seqlen) {
     IO* fin = static_cast<IO*>(p.fin) + row0 * (W - 1);
 #pragma unroll
-    for (int i = 0; i < kConvVec; ++i)
+    for (int i = 0; i < VE; ++i)
 #pragma unroll
       for (int j = 0; j < W - 1; ++j) io_traits<IO>::store(fin + i * (W - 1) + j, win[j][i]);
   }
@@ -290,12 +322,13 @@ __global__ __launch_bounds__(256) void conv_step_kernel(ConvStepShape s, ConvSte
 template <typename IO, int W>
 hipError_t launch_conv_w(const ConvShape& s, const ConvPtrs& p, hipStream_t stream) {
   if (s.path == kConvChanFast) {
-    const int64_t groups = (s.dim + kCfChannels - 1) / kCfChannels;
-    const int64_t nwg = s.batch * groups * s.nseg;
-    conv_cfast_kernel<IO, W><<<dim3(static_cast<unsigned>(nwg)), dim3(kCfThreads), 0, stream>>>(s, p);
+    const int64_t per_wave = 64 / s.cf_lanes;
+    const int64_t groups = (s.dim + s.cf_lanes * vec16<IO>::N - 1) / (s.cf_lanes * vec16<IO>::N);
+    const int64_t nwg = s.batch * groups * ((s.nseg + per_wave - 1) / per_wave);
+    conv_cfast_kernel<IO, W><<<dim3(static_cast<unsigned>(nwg)), dim3(64), 0, stream>>>(s, p);
   } else if (s.path == kConvTimeFast) {
-    const int64_t nwg = static_cast<int64_t>(s.batch) * s.dim * ((s.seqlen + kTfSteps - 1) / kTfSteps);
-    conv_tfast_kernel<IO, W><<<dim3(static_cast<unsigned>(nwg)), dim3(kTfThreads), 0, stream>>>(s, p);
+    const int64_t nwg = static_cast<int64_t>(s.batch) * s.dim * ((s.seqlen + kTfSpan - 1) / kTfSpan);
+    conv_tfast_kernel<IO, W><<<dim3(static_cast<unsigned>(nwg)), dim3(64), 0, stream>>>(s, p);
   } else {
     const int64_t n = static_cast<int64_t>(s.batch) * s.dim * s.seqlen;
     conv_elem_kernel<IO, W><<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(s, p);

@@ -423,28 +423,34 @@ mss_status mss_causal_conv1d_fwd(const mss_conv_args* a, void* stream) {
   s.path = mss::kConvElementwise;
   s.nseg = 1;
   s.seg_len = s.seqlen;
-  // 4-element vectors along the unit-stride axis need every vector start
-  // aligned: the base pointers to a whole vector and every other stride a
-  // multiple of 4 elements.
-  const int64_t V = mss::kConvVec;
-  const bool vec_aligned = aligned(a->x, V * es) && aligned(a->out, V * es);
+  s.cf_lanes = 64;
+  // 16-byte vectors along the unit-stride axis (V = 4 fp32 or 8 bf16
+  // elements) need every vector start aligned: the base pointers to 16 bytes
+  // and every other stride a multiple of V elements.
+  const int64_t V = mss::kConvVecBytes / es;
+  const bool vec_aligned = aligned(a->x, mss::kConvVecBytes) && aligned(a->out, mss::kConvVecBytes);
   if (vec_aligned && a->seqlen > 1 && s.sx[2] == 1 && s.so[2] == 1 && all_mult(s.sx, 3, V, 2) &&
       all_mult(s.so, 3, V, 2)) {
     s.path = mss::kConvTimeFast;
-    const int64_t nwg = a->batch * a->dim * ((a->seqlen + 1023) / 1024);
+    const int64_t nwg = a->batch * a->dim * ((a->seqlen + 2047) / 2048);
     if (nwg > 0xFFFFFFFFll) s.path = mss::kConvElementwise;
   } else if (vec_aligned && a->dim % V == 0 && a->dim > 1 && s.sx[1] == 1 && s.so[1] == 1 &&
              all_mult(s.sx, 3, V, 1) && all_mult(s.so, 3, V, 1)) {
     s.path = mss::kConvChanFast;
-    const int64_t groups = (a->dim + 255) / 256;
+    // lanes per row of channels: enough vectors to cover dim, at most a wave
+    int64_t lanes = 1;
+    while (lanes < 64 && lanes * V < a->dim) lanes *= 2;
+    s.cf_lanes = static_cast<int>(lanes);
+    const int64_t per_wave = 64 / lanes;
+    const int64_t groups = (a->dim + lanes * V - 1) / (lanes * V);
     const int64_t base = a->batch * groups;
-    int64_t nseg = std::max<int64_t>(1, (kConvTargetWaves + base - 1) / base);
+    int64_t nseg = std::max<int64_t>(1, (kConvTargetWaves * per_wave + base - 1) / base);
     nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, a->seqlen / kConvMinSeg));
     int64_t seg = (a->seqlen + nseg - 1) / nseg;
     seg = (seg + 7) / 8 * 8;
     s.seg_len = static_cast<int>(seg);
     s.nseg = static_cast<int>((a->seqlen + seg - 1) / seg);
-    if (base * s.nseg > 0xFFFFFFFFll) s.path = mss::kConvElementwise;
+    if (base * ((s.nseg + per_wave - 1) / per_wave) > 0xFFFFFFFFll) s.path = mss::kConvElementwise;
   }
   if (s.path == mss::kConvElementwise && (a->batch * a->dim * a->seqlen + 255) / 256 > 0xFFFFFFFFll)
     return MSS_ERR_BAD_SHAPE;

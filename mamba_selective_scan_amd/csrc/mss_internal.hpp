@@ -76,9 +76,9 @@ struct StepPtrs {
   void* out;
 };
 
-// Causal depthwise conv1d.  Loads and stores move kConvVec-element vectors
-// along the unit-stride axis when the layout allows it.
-constexpr int kConvVec = 4;
+// Causal depthwise conv1d.  Loads and stores move 16-byte vectors (4 fp32 or
+// 8 bf16 elements) along the unit-stride axis when the layout allows it.
+constexpr int kConvVecBytes = 16;
 constexpr int kConvMaxWidth = 4;
 
 enum ConvPath : int { kConvElementwise = 0, kConvTimeFast = 1, kConvChanFast = 2 };
@@ -91,6 +91,7 @@ struct ConvShape {
   int path;              // ConvPath
   int seg_len;           // channel-fast path: steps per thread
   int nseg;
+  int cf_lanes;          // channel-fast path: lanes per row of channels (power of 2, <= 64)
 };
 
 struct ConvPtrs {

@@ -44,6 +44,13 @@ def _case(mss, name, batch, dim, seqlen, width=4, layout="bld", io="f32", seed=0
         big = torch.empty(batch, dim, seqlen + 1, dtype=xt.dtype, device=xt.device)
         big[:, :, 1:] = xt
         xt = big[:, :, 1:]
+    elif view == "padded":
+        # rows padded to a whole number of 16-byte vectors: the vector path
+        # with a partial vector at the end of every row
+        pad = (-seqlen) % 8 + 8
+        big = torch.zeros(batch, dim, seqlen + pad, dtype=xt.dtype, device=xt.device)
+        big[:, :, :seqlen] = xt
+        xt = big[:, :, :seqlen]
     elif view == "strided":
         # every other channel of a wider buffer: no unit-stride axis for d
         big = torch.zeros(batch, seqlen, 2 * dim, dtype=xt.dtype, device=xt.device)
@@ -104,6 +111,13 @@ def test_channel_counts(mss, dim):
 @pytest.mark.parametrize("view", ["offset", "strided"])
 def test_views(mss, view):
     _case(mss, f"view {view}", 2, 96, 500, view=view, window=True)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("seqlen", [1, 5, 2045, 2049, 4103])
+def test_padded_rows(mss, io, seqlen):
+    _case(mss, f"padded L={seqlen}", 2, 40, seqlen, layout="bdl", io=io, view="padded",
+          window=True)
 
 
 def test_mamba2p8b_shape_sampled(mss):
