@@ -7,8 +7,10 @@ CPU-baseline leg of ``bench.py`` are the only callers.  The product package
 (``mamba_selective_scan_amd``) never imports this module, and this module
 imports nothing from the product package.
 
-The arithmetic lives in ``mss_oracle.c`` and ``mss_oracle_conv.c`` (plain C,
-fp64, sequential in time, OpenMP across independent channels).  This wrapper only marshals numpy arrays:
+The arithmetic lives in ``mss_oracle.c`` (scan forward and state update),
+``mss_oracle_bwd.c`` (the scan's backward) and ``mss_oracle_conv.c`` (plain
+C, fp64, sequential in time, OpenMP across independent channels in the
+forward).  This wrapper only marshals numpy arrays:
 every input is converted exactly to float64 and laid out contiguously as
 
     u, delta_raw, z, out : [batch, dim, seqlen]
@@ -33,7 +35,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mss_oracle.c")
-SOURCES = {"scan": _SRC, "conv": os.path.join(_HERE, "mss_oracle_conv.c")}
+SOURCES = {"scan": _SRC, "conv": os.path.join(_HERE, "mss_oracle_conv.c"),
+           "bwd": os.path.join(_HERE, "mss_oracle_bwd.c")}
 LIB_PATH = os.path.join(_HERE, "libmss_oracle.so")
 
 _lib = None
@@ -71,6 +74,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_oracle_state_update.argtypes = [i64, i64, i64, dp] + [dp] * 8 + [
         ctypes.c_int, dp]
     lib.mss_oracle_state_update.restype = ctypes.c_int
+    lib.mss_oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [dp] * 9 + [ctypes.c_int] + \
+        [dp] * 2 + [dp] * 9
+    lib.mss_oracle_scan_bwd.restype = ctypes.c_int
     lib.mss_oracle_conv1d_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 4 + [ctypes.c_int, dp, dp]
     lib.mss_oracle_conv1d_fwd.restype = ctypes.c_int
     lib.mss_oracle_conv1d_update.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp]
@@ -255,3 +261,42 @@ def conv1d_update(state, x, w, bias=None, silu=True, lib=None):
     if rc != 0:
         raise ValueError(f"oracle conv1d_update rejected its arguments (rc={rc})")
     return out, new_state
+
+
+def scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=None, h0=None,
+             dfinal=None, delta_softplus=True, lib=None):
+    """Backward of scan_fwd in fp64.
+
+    Given dout [b,d,l] (and optionally dfinal [b,d,n], the gradient with respect
+    to the exported final state), returns a dict of gradients: du, ddelta_raw
+    [b,d,l]; dA_log [d,n]; dB, dC [b,n,l]; dD, ddt_bias [d] (always computed);
+    dz [b,d,l] when z is given; dh0 [b,d,n]."""
+    u = _f64(u)
+    batch, dim, seqlen = u.shape
+    A_log = _f64(A_log)
+    dstate = A_log.shape[1]
+    delta_raw = _f64(delta_raw, (batch, dim, seqlen))
+    A_log = _f64(A_log, (dim, dstate))
+    B = _f64(B, (batch, dstate, seqlen))
+    C = _f64(C, (batch, dstate, seqlen))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim, seqlen))
+    dt_bias = _f64(dt_bias, (dim,))
+    h0 = _f64(h0, (batch, dim, dstate))
+    dout = _f64(dout, (batch, dim, seqlen))
+    dfinal = _f64(dfinal, (batch, dim, dstate))
+    g = {
+        "du": np.empty((batch, dim, seqlen)), "ddelta_raw": np.empty((batch, dim, seqlen)),
+        "dA_log": np.empty((dim, dstate)), "dB": np.empty((batch, dstate, seqlen)),
+        "dC": np.empty((batch, dstate, seqlen)), "dD": np.empty(dim),
+        "dz": np.empty((batch, dim, seqlen)) if z is not None else None,
+        "ddt_bias": np.empty(dim), "dh0": np.empty((batch, dim, dstate)),
+    }
+    rc = (lib or load()).mss_oracle_scan_bwd(
+        batch, dim, seqlen, dstate, _ptr(u), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), int(bool(delta_softplus)), _ptr(dout),
+        _ptr(dfinal), _ptr(g["du"]), _ptr(g["ddelta_raw"]), _ptr(g["dA_log"]), _ptr(g["dB"]),
+        _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]), _ptr(g["dh0"]))
+    if rc != 0:
+        raise ValueError(f"oracle scan_bwd rejected its arguments (rc={rc})")
+    return g

@@ -2,11 +2,12 @@
 makes at least one pin fail.
 
 Every mutant below is a one-line edit of one oracle source file
-(oracle/mss_oracle.c for the scan, oracle/mss_oracle_conv.c for the conv1d): a
-dropped term, a wrong sign or index, a transposed or swapped operand, exp2 for
-exp, and so on.  The altered copy is compiled, with the other sources as they
-are, into a temporary library and every pin is run against it; the real
-oracle sources are never modified.
+(oracle/mss_oracle.c for the scan, oracle/mss_oracle_conv.c for the conv1d,
+oracle/mss_oracle_bwd.c for the scan's backward): a dropped term, a wrong
+sign or index, a transposed or swapped operand, exp2 for exp, and so on.  The
+altered copy is compiled, with the other sources as they are, into a
+temporary library, and the pins of that source are run against it until one
+fails; the real oracle sources are never modified.
 """
 
 import os
@@ -14,6 +15,7 @@ import os
 import pytest
 
 import oracle
+import bwd_oracle_pins as BP
 import conv_oracle_pins as CP
 import oracle_pins as P
 
@@ -87,14 +89,39 @@ CONV_MUTANTS = {
 }
 CONV_SRC = oracle.SOURCES["conv"]
 
+# backward mutants (oracle/mss_oracle_bwd.c)
+BWD_MUTANTS = {
+    "bwd_no_dyC": ("double G = g[n] + dy * C_b[n * seqlen + t];", "double G = g[n];"),
+    "bwd_dC_uses_prev": ("+= dy * h_t[n];", "+= dy * h_prev[n];"),
+    "bwd_dB_no_delta": ("+= G * delta[t] * ut;", "+= G * ut;"),
+    "bwd_da_uses_h_t": ("double ga = G * h_prev[n] * a;", "double ga = G * h_t[n] * a;"),
+    "bwd_dA_log_sign": ("dA_log[d * dstate + n] += dA[n] * A[n];",
+                        "dA_log[d * dstate + n] += -dA[n] * A[n];"),
+    "bwd_g_no_decay": ("g[n] = G * a;", "g[n] = G;"),
+    "bwd_no_softplus_grad": ("double dx = delta_softplus ? ddelta * sigmoid(x) : ddelta;",
+                             "double dx = ddelta;"),
+    "bwd_dz_no_y": ("dz[row + t] = dout[row + t] * y * silu_grad(z[row + t]);",
+                    "dz[row + t] = dout[row + t] * silu_grad(z[row + t]);"),
+    "bwd_silu_grad": ("return s * (1.0 + z * (1.0 - s));", "return s * (1.0 - s);"),
+    "bwd_du_no_skip": ("double du_t = dy * skip;", "double du_t = 0.0;"),
+    "bwd_dD_uses_dout": ("sum_dy_u += dy * ut;", "sum_dy_u += dout[row + t] * ut;"),
+    "bwd_dfinal_ignored": ("g[n] = dfinal ? dfinal[(b * dim + d) * dstate + n] : 0.0;",
+                           "g[n] = 0.0;"),
+    "bwd_ddt_bias_raw": ("sum_dx += dx;", "sum_dx += ddelta;"),
+    "bwd_ddelta_from_a_sign": ("ddelta += ga * A[n];", "ddelta -= ga * A[n];"),
+}
+BWD_SRC = oracle.SOURCES["bwd"]
 
-def _run_pins(lib):
+
+def _run_pins(lib, pins=None, stop_at_first=False):
     failures = []
-    for pin in P.ALL_PINS + CP.ALL_CONV_PINS:
+    for pin in pins if pins is not None else P.ALL_PINS + CP.ALL_CONV_PINS + BP.ALL_BWD_PINS:
         try:
             pin(lib)
         except AssertionError as e:
             failures.append((pin.__name__, str(e)[:120]))
+            if stop_at_first:
+                break
     return failures
 
 
@@ -109,7 +136,7 @@ def test_mutant_is_caught(name, tmp_path):
     oracle.build(str(mutated), str(so))
     # The library stays loaded: unloading a library whose OpenMP worker
     # threads are still parked is unsafe, and each mutant is small.
-    failures = _run_pins(oracle.load(str(so)))
+    failures = _run_pins(oracle.load(str(so)), P.ALL_PINS, stop_at_first=True)
     assert failures, f"mutant {name} passed every pin"
 
 
@@ -122,7 +149,20 @@ def test_conv_mutant_is_caught(name, tmp_path):
     mutated.write_text(src.replace(old, new))
     so = tmp_path / "libmutant.so"
     oracle.build(out=str(so), replace={"conv": str(mutated)})
-    failures = _run_pins(oracle.load(str(so)))
+    failures = _run_pins(oracle.load(str(so)), CP.ALL_CONV_PINS, stop_at_first=True)
+    assert failures, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = open(BWD_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutated = tmp_path / "mutant_bwd.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    oracle.build(out=str(so), replace={"bwd": str(mutated)})
+    failures = _run_pins(oracle.load(str(so)), BP.ALL_BWD_PINS, stop_at_first=True)
     assert failures, f"mutant {name} passed every pin"
 
 
