@@ -18,10 +18,12 @@ Prints one JSON line:
 
 With --op conv1d the step is instead the causal depthwise conv1d + SiLU
 (width 4) with window export followed by one conv decode step, on the same
-workload shapes, reported against the HBM roofline.
+workload shapes, reported against the HBM roofline.  With --op scan_bwd it is
+the selective-scan backward (all gradients, initial-state and final-state
+gradients included), reported against the VALU issue roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--io f32|bf16]
-                       [--op scan|conv1d]
+                       [--op scan|conv1d|scan_bwd]
 """
 
 from __future__ import annotations
@@ -270,6 +272,146 @@ def main_conv(args):
     return 0
 
 
+def bwd_valu_slots_per_element(dstate: int) -> int:
+    """Algorithmic VALU slots per (b, d, t) element of the backward.
+
+    Per state: the decay exp2 (4) and Delta*A2; the forward state (Delta*u*B,
+    the h FMA) needed by dC and dA; the adjoint G (FMA), its dC and dB terms,
+    the B.G sum, G*h_prev*a (2), the dA and A.(...) sums, g*a: 15 slots.
+    Per element: softplus (15) and its derivative sigmoid (exp2, rcp, 2 ops:
+    10); dy = dout*silu(z) (12); y = C.h + D*u for dz (1) and silu'(z) (4
+    ops) times dout*y (2); du and ddelta_raw (3); the dD and ddt_bias sums (2).
+    """
+    return dstate * 15 + 15 + 10 + 12 + 1 + 4 + 2 + 3 + 2
+
+
+def main_bwd(args):
+    import torch
+
+    import mamba_selective_scan_amd as mss
+    from mamba_selective_scan_amd.inputs import WORKLOADS, generate, to_torch
+
+    w = WORKLOADS[args.workload]
+    io_bytes = 2 if args.io == "bf16" else 4
+    dev = torch.device("cuda:0")
+    log(f"scan_bwd workload {w.name}: B={w.batch} D={w.dim} L={w.seqlen} N={w.dstate} "
+        f"{w.layout} {args.io}")
+    x = generate(w.batch, w.dim, w.seqlen, w.dstate, w.layout, seed=args.seed)
+    dx = to_torch(x, dev, args.io)
+    g = torch.Generator().manual_seed(args.seed + 1)
+    dout = torch.randn(w.batch, w.dim, w.seqlen, generator=g).to(device=dev, dtype=dx["u"].dtype)
+    h0 = torch.randn(w.batch, w.dim, w.dstate, generator=g).to(dev)
+    dfin = torch.randn(w.batch, w.dim, w.dstate, generator=g).to(dev)
+    ws = torch.empty(mss.scan_bwd_workspace_size(dx["u"], dx["A_log"]), dtype=torch.uint8,
+                     device=dev)
+
+    def bwd():
+        return mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                      dout, D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                      initial_state=h0, dfinal_state=dfin, workspace=ws)
+
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        bwd()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / len(ms)
+    ne = w.elems
+    nbc = w.batch * w.seqlen * w.dstate
+    alg_bytes = ne * 7 * io_bytes + 4 * nbc * io_bytes           # u, dr, z, dout; du, ddr, dz; B, C, dB, dC
+    alg_bytes += 2 * w.dim * (w.dstate + 2) * 4                  # A_log, D, dt_bias and their grads
+    alg_bytes += 3 * w.batch * w.dim * w.dstate * 4              # h0, dfinal, dh0
+    slots = ne * bwd_valu_slots_per_element(w.dstate)
+    achieved_gbs = alg_bytes / (mean_ms * 1e-3) / 1e9
+    achieved_slots = slots / (mean_ms * 1e-3) / 1e12
+    log(f"scan bwd mean {mean_ms * 1e3:.1f} us (min {ms[0] * 1e3:.1f}); {achieved_gbs:.0f} GB/s "
+        f"= {achieved_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s; VALU {achieved_slots / VALU_PEAK_TSLOTS:.1%}")
+    rec = {
+        "metric": "selective-scan bwd achieved HBM GB/s (% of 8 TB/s) and Gtok·ch/s",
+        "value": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.io,
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "scan_bwd", "batch": w.batch, "dim": w.dim,
+                   "seqlen": w.seqlen, "dstate": w.dstate, "layout": w.layout,
+                   "io_dtype": args.io,
+                   "step": "scan bwd: all gradients incl. initial/final state"},
+        "pct_of_hbm_peak": round(100.0 * achieved_gbs / HBM_PEAK_GBS, 2),
+        "gtok_ch_per_s": round(ne / (ms_per_step * 1e-3) / 1e9, 4),
+        "roofline": {
+            "bound": "alu",
+            "kernel": "selective-scan bwd (checkpoint, reverse, reduce passes) on the current stream",
+            "achieved": round(achieved_slots, 3),
+            "peak": round(VALU_PEAK_TSLOTS, 3),
+            "unit": "T VALU lane-slots/s",
+            "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
+            "traffic": None,
+            "algorithmic_slots": slots,
+            "slots_per_element": bwd_valu_slots_per_element(w.dstate),
+            "hbm": {"achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_bytes},
+            "event_us_mean": round(mean_ms * 1e3, 2),
+            "event_us_median": round(ms[len(ms) // 2] * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: backward oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
+        rec["cpu_baseline"] = bwd_cpu_baseline(x, w, io_bytes, alg_bytes, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bwd_cpu_baseline(x, w, io_bytes, alg_bytes, target_s):
+    """Time the backward oracle (as is, one thread) on a growing channel sample
+    of batch row 0 (the oracle sums dB and dC over the sampled channels only)."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(5)
+    k = 1
+    while True:
+        ds = np.sort(rng.choice(w.dim, size=min(k, w.dim), replace=False))
+        sub = lambda a: np.ascontiguousarray(a[0:1, ds]) if a is not None else None
+        dout = rng.standard_normal((1, len(ds), w.seqlen))
+        t = time.perf_counter()
+        oracle.scan_bwd(sub(x["u"]), sub(x["delta_raw"]), x["A_log"][ds], x["B"][0:1],
+                        x["C"][0:1], dout, D=x["D"][ds], z=sub(x["z"]),
+                        dt_bias=x["dt_bias"][ds])
+        dt = time.perf_counter() - t
+        if dt >= target_s or len(ds) >= w.dim or k >= 4096:
+            break
+        k = max(k + 1, int(k * min(8.0, 1.5 * target_s / max(dt, 1e-3))))
+    tokch = len(ds) * w.seqlen
+    return {
+        "value": round(tokch * (alg_bytes / w.elems) / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(ds)} channels of batch row 0 x full seqlen {w.seqlen} "
+                  f"({tokch} token-channels), fp64 reverse-time backward, {dt:.1f} s",
+        "gtok_ch_per_s": round(tokch / dt / 1e9, 6),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,7 +423,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="time the forward alone")
-    ap.add_argument("--op", default="scan", choices=["scan", "conv1d"])
+    ap.add_argument("--op", default="scan", choices=["scan", "conv1d", "scan_bwd"])
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -291,6 +433,8 @@ def main(argv=None):
         return 2
     if args.op == "conv1d":
         return main_conv(args)
+    if args.op == "scan_bwd":
+        return main_bwd(args)
 
     import torch
 

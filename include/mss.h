@@ -1,7 +1,7 @@
 /*
  * mss.h -- C ABI of libmss, the MI355X (gfx950) Mamba selective-scan library.
  *
- * Two operations:
+ * Five operations:
  *
  *  1. mss_selective_scan_fwd: the selective-scan forward over whole sequences.
  *     For every channel (b, d) and time step t, with n over the dstate
@@ -46,15 +46,33 @@
  *     by one in place ("mamba-metal", section "O(L) インクリメンタルデコード":
  *     the conv1d sliding window is carried between calls).
  *
+ *  5. mss_selective_scan_bwd: the backward of operation 1 for training, which
+ *     the pages list as not yet written ("mamba-metal", section "残り課題").
+ *     Given dout = dLoss/dout (and optionally dfinal_state = dLoss/d final
+ *     state) it returns dLoss/d(u, delta_raw, A_log, B, C, D, z, dt_bias,
+ *     initial_state), the chain rule through the forward taken in reverse
+ *     time:  with G_t[n] the adjoint of h_t[n], g[n] the part that reaches
+ *     h_t[n] from later steps (dfinal_state at the end), dy_t = dout_t silu(z_t):
+ *        G_t[n] = g[n] + dy_t C_t[n];   g[n] <- G_t[n] exp(delta_t A[n]);
+ *        dC_t[n] = sum_d dy_t h_t[n];   dB_t[n] = sum_d G_t[n] delta_t u_t;
+ *        du_t = dy_t D + delta_t sum_n G_t[n] B_t[n];
+ *        ddelta_t = u_t sum_n G_t[n] B_t[n] + sum_n G_t[n] h_{t-1}[n] exp(delta_t A[n]) A[n];
+ *        ddelta_raw_t = ddelta_t sigmoid(delta_raw_t + dt_bias) (softplus on);
+ *        dz_t = dout_t y_t silu'(z_t);  dD = sum dy u;  ddt_bias = sum ddelta_raw;
+ *        dA_log[d,n] = A[n] sum_(b,t) G_t[n] h_{t-1}[n] exp(delta_t A[n]) delta_t;
+ *        dinitial_state = g after the first step.
+ *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    never allocates, frees or retains caller memory and keeps no per-call
  *    state; it caches nothing but compiled kernels.
  *  - Tensors are described by element strides in LOGICAL index order:
  *    u / delta_raw / z / out as (b, d, t), B / C as (b, n, t), A_log as (d, n).
- *    u, delta_raw, z and out must share a unit-stride axis, t or d (for
- *    example [B,D,L] or channel-last [B,L,D] buffers); B and C must share one,
- *    t or n.  Other strides are free (views into larger buffers are fine).
+ *    For the scan forward, u, delta_raw, z and out must share a unit-stride
+ *    axis, t or d (for example [B,D,L] or channel-last [B,L,D] buffers), and
+ *    B and C must share one, t or n; the conv1d and the backward accept any
+ *    non-negative strides.  Other strides are free (views into larger
+ *    buffers are fine).
  *    A dimension of size 1 may have any stride.  D, dt_bias and the states
  *    are contiguous.
  *  - io_dtype selects the element type of u, delta_raw, z, B, C and out
@@ -222,6 +240,59 @@ typedef struct mss_conv_step_args {
     int32_t reserved0;           /* must be 0                                            */
 } mss_conv_step_args;
 
+/* Arguments of mss_selective_scan_bwd.  Set struct_size = sizeof(mss_scan_bwd_args).
+ * The forward's inputs have the meaning, layout rules and nullability of
+ * mss_scan_args, except that any non-negative strides are accepted. */
+typedef struct mss_scan_bwd_args {
+    uint32_t struct_size;
+    int32_t io_dtype;            /* mss_dtype of u, delta_raw, z, B, C, dout and of the  */
+                                 /* gradients du, ddelta_raw, dz, dB, dC                 */
+    int64_t batch;
+    int64_t dim;
+    int64_t seqlen;
+    int64_t dstate;              /* 1..MSS_MAX_DSTATE                                    */
+
+    const void *u;               /* [b,d,t]                                              */
+    int64_t u_stride[3];
+    const void *delta_raw;       /* [b,d,t]                                              */
+    int64_t delta_stride[3];
+    const float *A_log;          /* [d,n] fp32                                           */
+    int64_t A_log_stride[2];
+    const void *B;               /* [b,n,t]                                              */
+    int64_t B_stride[3];
+    const void *C;               /* [b,n,t]                                              */
+    int64_t C_stride[3];
+    const float *D;              /* [d] fp32 contiguous; NULL means 0                    */
+    const void *z;               /* [b,d,t]; NULL means no gate                          */
+    int64_t z_stride[3];
+    const float *dt_bias;        /* [d] fp32 contiguous; NULL means 0                    */
+    const float *initial_state;  /* [b,d,n] fp32 contiguous; NULL means 0                */
+    int32_t delta_softplus;
+    int32_t reserved0;           /* must be 0                                            */
+
+    const void *dout;            /* [b,d,t] dLoss/dout                                   */
+    int64_t dout_stride[3];
+    const float *dfinal_state;   /* [b,d,n] fp32 contiguous; NULL means 0                */
+
+    void *du;                    /* [b,d,t] required                                     */
+    int64_t du_stride[3];
+    void *ddelta_raw;            /* [b,d,t] required                                     */
+    int64_t ddelta_stride[3];
+    float *dA_log;               /* [d,n] fp32 contiguous, required                      */
+    void *dB;                    /* [b,n,t] required                                     */
+    int64_t dB_stride[3];
+    void *dC;                    /* [b,n,t] required                                     */
+    int64_t dC_stride[3];
+    float *dD;                   /* [d] fp32; NULL: not written                          */
+    void *dz;                    /* [b,d,t]; NULL: not written (must be NULL without z)  */
+    int64_t dz_stride[3];
+    float *ddt_bias;             /* [d] fp32; NULL: not written                          */
+    float *dinitial_state;       /* [b,d,n] fp32 contiguous; NULL: not written           */
+
+    void *workspace;             /* device scratch, 256-byte aligned, of at least        */
+    size_t workspace_bytes;      /* mss_selective_scan_bwd_workspace_size bytes          */
+} mss_scan_bwd_args;
+
 /* ABI version of the loaded library (MSS_ABI_VERSION of its build). */
 int mss_abi_version(void);
 
@@ -244,6 +315,18 @@ mss_status mss_selective_scan_fwd(const mss_scan_args *args, void *stream);
 
 /* One-token state update (see the top of this file). */
 mss_status mss_selective_state_update(const mss_step_args *args, void *stream);
+
+/* Bytes of device workspace mss_selective_scan_bwd needs: the states entering
+ * every 16-step chunk (batch * dim * seqlen * 4 bytes, rounded up) and the
+ * per-64-channel partial sums of dB and dC (batch * ceil(dim/64) * 32 *
+ * seqlen * 4 bytes).  Depends only on the shapes.  Returns 0 and sets
+ * *status on invalid shapes. */
+size_t mss_selective_scan_bwd_workspace_size(const mss_scan_bwd_args *args, mss_status *status);
+
+/* Selective-scan backward (see the top of this file).  Every gradient output
+ * is overwritten (not accumulated into).  Outputs must not overlap any input,
+ * each other or the workspace.  Deterministic: sums run in a fixed order. */
+mss_status mss_selective_scan_bwd(const mss_scan_bwd_args *args, void *stream);
 
 /* Causal depthwise conv1d with optional SiLU (see the top of this file).
  * Any non-negative strides are accepted.  When x and out share a unit-stride

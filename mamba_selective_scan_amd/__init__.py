@@ -13,6 +13,7 @@ is no CPU or PyTorch fallback; without the built library every call raises.
     u = causal_conv1d_fwd(x, weight, bias)                  # silu(causal conv)
     u, window = causal_conv1d_fwd(x, weight, bias, return_final_state=True)
     u_t = causal_conv1d_update(window, x_t, weight, bias)   # window slides in place
+    g = selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D, z, dt_bias)  # dict of grads
 
 Shapes (logical index order, any strides): u, delta_raw, z, out [B, D, L];
 B, C [B, N, L]; A_log [D, N]; D, dt_bias [D]; states [B, D, N] (fp32,
@@ -31,8 +32,8 @@ from . import _lib
 from ._lib import MSS_MAX_DSTATE, MssError
 
 __all__ = ["selective_scan_fwd", "selective_state_update", "scan_workspace_size",
-           "causal_conv1d_fwd", "causal_conv1d_update", "MssError", "MSS_MAX_DSTATE",
-           "library_path"]
+           "causal_conv1d_fwd", "causal_conv1d_update", "selective_scan_bwd",
+           "scan_bwd_workspace_size", "MssError", "MSS_MAX_DSTATE", "library_path"]
 
 
 def library_path() -> str:
@@ -336,3 +337,79 @@ def causal_conv1d_update(state, x, weight, bias=None, *, activation="silu", out=
     a.activation = _ACTIVATIONS[activation]
     _lib.check(lib.mss_causal_conv1d_update(ctypes.byref(a), _stream_handle(dev)))
     return out
+
+
+def _bwd_shape_args(u, A_log):
+    a = _lib.new_scan_bwd_args()
+    a.io_dtype = _io_dtype(u)
+    a.batch, a.dim, a.seqlen = u.shape
+    a.dstate = A_log.shape[1]
+    return a
+
+
+def scan_bwd_workspace_size(u, A_log) -> int:
+    """Workspace bytes selective_scan_bwd needs for u [B, D, L] and A_log [D, N]."""
+    a = _bwd_shape_args(u, A_log)
+    st = ctypes.c_int(0)
+    n = _lib.lib().mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    _lib.check(st.value)
+    return int(n)
+
+
+def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=None, *,
+                       delta_softplus=True, initial_state=None, dfinal_state=None,
+                       workspace=None):
+    """Backward of selective_scan_fwd, ordered on torch's current stream.
+
+    dout has u's shape and dtype; dfinal_state [B, D, N] fp32 (optional) is the
+    gradient reaching the exported final state.  Returns a dict with du,
+    ddelta_raw, dB, dC (dtype of u, shapes of the inputs), dA_log [D, N] fp32,
+    and dD, dz, ddt_bias, dinitial_state for the optional inputs that are given.
+    """
+    torch = _torch()
+    lib = _lib.lib()
+    a = _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, None, None,
+                   delta_softplus)
+    dev = u.device
+    _need(dout, "dout", 3, u.dtype, dev)
+    if tuple(dout.shape) != tuple(u.shape):
+        raise ValueError("dout must have the shape of u")
+    bsz, dim, _ = u.shape
+    dstate = A_log.shape[1]
+    _contig_f32(dfinal_state, "dfinal_state", (bsz, dim, dstate), dev)
+    g = {
+        "du": torch.empty_like(u), "ddelta_raw": torch.empty_like(delta_raw),
+        "dA_log": torch.empty((dim, dstate), dtype=torch.float32, device=dev),
+        "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+        "dD": torch.empty_like(D) if D is not None else None,
+        "dz": torch.empty_like(z) if z is not None else None,
+        "ddt_bias": torch.empty_like(dt_bias) if dt_bias is not None else None,
+        "dinitial_state": (torch.empty_like(initial_state) if initial_state is not None
+                           else None),
+    }
+    b = _lib.new_scan_bwd_args()
+    for name, *_ in _lib.ScanArgs._fields_:
+        if hasattr(b, name) and name not in ("struct_size", "out", "out_stride", "final_state",
+                                            "workspace", "workspace_bytes"):
+            setattr(b, name, getattr(a, name))
+    b.struct_size = ctypes.sizeof(_lib.ScanBwdArgs)
+    b.dout, b.dout_stride = _ptr(dout), _strides(dout, 3)
+    b.dfinal_state = _ptr(dfinal_state)
+    b.du, b.du_stride = _ptr(g["du"]), _strides(g["du"], 3)
+    b.ddelta_raw, b.ddelta_stride = _ptr(g["ddelta_raw"]), _strides(g["ddelta_raw"], 3)
+    b.dA_log = _ptr(g["dA_log"])
+    b.dB, b.dB_stride = _ptr(g["dB"]), _strides(g["dB"], 3)
+    b.dC, b.dC_stride = _ptr(g["dC"]), _strides(g["dC"], 3)
+    b.dD = _ptr(g["dD"])
+    b.dz, b.dz_stride = _ptr(g["dz"]), _strides(g["dz"], 3)
+    b.ddt_bias = _ptr(g["ddt_bias"])
+    b.dinitial_state = _ptr(g["dinitial_state"])
+    st = ctypes.c_int(0)
+    need = lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(b), ctypes.byref(st))
+    _lib.check(st.value)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    b.workspace = _ptr(workspace)
+    b.workspace_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.mss_selective_scan_bwd(ctypes.byref(b), _stream_handle(dev)))
+    return {k: v for k, v in g.items() if v is not None}

@@ -38,7 +38,8 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ("mss_abi_version", "mss_status_string", "mss_selective_scan_workspace_size",
            "mss_selective_scan_fwd", "mss_selective_state_update", "mss_causal_conv1d_fwd",
-           "mss_causal_conv1d_update")
+           "mss_causal_conv1d_update", "mss_selective_scan_bwd_workspace_size",
+           "mss_selective_scan_bwd")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -81,6 +82,41 @@ class StepArgs(ctypes.Structure):
         ("out", _vp), ("out_stride", _i64 * 2),
         ("delta_softplus", _i32), ("reserved0", _i32),
     ]
+
+
+class ScanBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("io_dtype", _i32),
+        ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("dstate", _i64),
+        ("u", _vp), ("u_stride", _i64 * 3),
+        ("delta_raw", _vp), ("delta_stride", _i64 * 3),
+        ("A_log", _vp), ("A_log_stride", _i64 * 2),
+        ("B", _vp), ("B_stride", _i64 * 3),
+        ("C", _vp), ("C_stride", _i64 * 3),
+        ("D", _vp),
+        ("z", _vp), ("z_stride", _i64 * 3),
+        ("dt_bias", _vp),
+        ("initial_state", _vp),
+        ("delta_softplus", _i32), ("reserved0", _i32),
+        ("dout", _vp), ("dout_stride", _i64 * 3),
+        ("dfinal_state", _vp),
+        ("du", _vp), ("du_stride", _i64 * 3),
+        ("ddelta_raw", _vp), ("ddelta_stride", _i64 * 3),
+        ("dA_log", _vp),
+        ("dB", _vp), ("dB_stride", _i64 * 3),
+        ("dC", _vp), ("dC_stride", _i64 * 3),
+        ("dD", _vp),
+        ("dz", _vp), ("dz_stride", _i64 * 3),
+        ("ddt_bias", _vp),
+        ("dinitial_state", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def new_scan_bwd_args() -> ScanBwdArgs:
+    a = ScanBwdArgs()
+    a.struct_size = ctypes.sizeof(ScanBwdArgs)
+    return a
 
 
 class ConvArgs(ctypes.Structure):
@@ -158,6 +194,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_selective_scan_fwd.restype = ctypes.c_int
     lib.mss_selective_state_update.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.mss_selective_state_update.restype = ctypes.c_int
+    lib.mss_selective_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs),
+                                                          ctypes.POINTER(ctypes.c_int)]
+    lib.mss_selective_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mss_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp]
+    lib.mss_selective_scan_bwd.restype = ctypes.c_int
     lib.mss_causal_conv1d_fwd.argtypes = [ctypes.POINTER(ConvArgs), _vp]
     lib.mss_causal_conv1d_fwd.restype = ctypes.c_int
     lib.mss_causal_conv1d_update.argtypes = [ctypes.POINTER(ConvStepArgs), _vp]

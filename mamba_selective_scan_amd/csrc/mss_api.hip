@@ -149,6 +149,44 @@ bool all_mult(const int64_t* st, int rank, int64_t m, int skip) {
   return true;
 }
 
+// Backward plan: workspace = checkpoints, dB/dC partials, per-row sums.
+struct BwdPlan {
+  mss::BwdShape shape;
+  size_t ckpt_bytes = 0, bc_bytes = 0, chan_bytes = 0, workspace = 0;
+};
+
+mss_status check_bwd_shape(const mss_scan_bwd_args* a) {
+  if (a == nullptr || a->struct_size != sizeof(mss_scan_bwd_args) || a->reserved0 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
+  if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->batch > kMaxDim || a->dim > kMaxDim ||
+      a->seqlen > kMaxSeqlen || a->batch * a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
+  const int64_t tiles = (a->dim + mss::kBwdCh - 1) / mss::kBwdCh;
+  if (a->batch * tiles * mss::kBwdWaves > 0xFFFFFFFFll) return MSS_ERR_BAD_SHAPE;
+  if ((a->batch * 2 * a->dstate * a->seqlen + 255) / 256 > 0xFFFFFFFFll) return MSS_ERR_BAD_SHAPE;
+  return MSS_OK;
+}
+
+BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
+  BwdPlan p;
+  mss::BwdShape& s = p.shape;
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.seqlen = static_cast<int>(a->seqlen);
+  s.dstate = static_cast<int>(a->dstate);
+  s.softplus = a->delta_softplus ? 1 : 0;
+  s.nchunk = static_cast<int>((a->seqlen + mss::kBwdT - 1) / mss::kBwdT);
+  s.tiles = static_cast<int>((a->dim + mss::kBwdCh - 1) / mss::kBwdCh);
+  s.nchan_pad = a->batch * s.tiles * mss::kBwdCh;
+  p.ckpt_bytes = round_up(static_cast<size_t>(s.nchunk) * s.nchan_pad * kMaxState * sizeof(float), 256);
+  p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * a->seqlen * sizeof(float), 256);
+  p.chan_bytes = round_up(static_cast<size_t>(a->batch) * a->dim * (kMaxState + 2) * sizeof(float), 256);
+  p.workspace = p.ckpt_bytes + p.bc_bytes + p.chan_bytes;
+  return p;
+}
+
 // Channel-fast conv: time segments per 256-channel group so that the grid
 // holds about this many waves.
 constexpr int64_t kConvTargetWaves = 4096;
@@ -368,6 +406,138 @@ mss_status mss_selective_state_update(const mss_step_args* a, void* stream) {
   s.softplus = a->delta_softplus ? 1 : 0;
   mss::StepPtrs p{a->state, a->u, a->delta_raw, a->A_log, a->B, a->C, a->D, a->z, a->dt_bias, a->out};
   const hipError_t e = mss::launch_step(s, p, a->io_dtype == MSS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
+size_t mss_selective_scan_bwd_workspace_size(const mss_scan_bwd_args* a, mss_status* status) {
+  const mss_status st = check_bwd_shape(a);
+  if (status != nullptr) *status = st;
+  if (st != MSS_OK) return 0;
+  return make_bwd_plan(a).workspace;
+}
+
+mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
+  const mss_status st = check_bwd_shape(a);
+  if (st != MSS_OK) return st;
+  if (a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr || a->B == nullptr ||
+      a->C == nullptr || a->dout == nullptr || a->du == nullptr || a->ddelta_raw == nullptr ||
+      a->dA_log == nullptr || a->dB == nullptr || a->dC == nullptr)
+    return MSS_ERR_NULL_POINTER;
+  if (a->z == nullptr && a->dz != nullptr) return MSS_ERR_NULL_POINTER;
+  const int64_t es = a->io_dtype == MSS_BF16 ? 2 : 4;
+  const int64_t xs[3] = {a->batch, a->dim, a->seqlen};
+  const int64_t bcs[3] = {a->batch, a->dstate, a->seqlen};
+  const int64_t as[2] = {a->dim, a->dstate};
+  const int64_t vs[1] = {a->dim};
+  const int64_t ss[3] = {a->batch, a->dim, a->dstate};
+  const int64_t unit[3] = {a->dim * a->dstate, a->dstate, 1};
+  const int64_t aunit[2] = {a->dstate, 1};
+  const int64_t one[1] = {1};
+  const int64_t* x_strides[] = {a->u_stride, a->delta_stride, a->dout_stride, a->du_stride,
+                                a->ddelta_stride};
+  for (const int64_t* st3 : x_strides)
+    if (!strides_nonneg(st3, 3)) return MSS_ERR_BAD_STRIDE;
+  if (!strides_nonneg(a->B_stride, 3) || !strides_nonneg(a->C_stride, 3) ||
+      !strides_nonneg(a->dB_stride, 3) || !strides_nonneg(a->dC_stride, 3) ||
+      !strides_nonneg(a->A_log_stride, 2) || (a->z != nullptr && !strides_nonneg(a->z_stride, 3)) ||
+      (a->dz != nullptr && !strides_nonneg(a->dz_stride, 3)))
+    return MSS_ERR_BAD_STRIDE;
+  if (!non_overlapping(xs, a->du_stride, 3) || !non_overlapping(xs, a->ddelta_stride, 3) ||
+      (a->dz != nullptr && !non_overlapping(xs, a->dz_stride, 3)) ||
+      !non_overlapping(bcs, a->dB_stride, 3) || !non_overlapping(bcs, a->dC_stride, 3))
+    return MSS_ERR_BAD_STRIDE;
+  const void* io_ptrs[] = {a->u, a->delta_raw, a->B, a->C, a->z, a->dout, a->du, a->ddelta_raw,
+                           a->dB, a->dC, a->dz};
+  for (const void* q : io_ptrs)
+    if (!aligned(q, es)) return MSS_ERR_MISALIGNED;
+  const void* f32_ptrs[] = {a->A_log, a->D, a->dt_bias, a->initial_state, a->dfinal_state,
+                            a->dA_log, a->dD, a->ddt_bias, a->dinitial_state, a->workspace};
+  for (const void* q : f32_ptrs)
+    if (!aligned(q, 4)) return MSS_ERR_MISALIGNED;
+  const Extent ins[] = {
+      extent_of(a->u, xs, a->u_stride, 3, es),
+      extent_of(a->delta_raw, xs, a->delta_stride, 3, es),
+      extent_of(a->z, xs, a->z_stride, 3, es),
+      extent_of(a->B, bcs, a->B_stride, 3, es),
+      extent_of(a->C, bcs, a->C_stride, 3, es),
+      extent_of(a->A_log, as, a->A_log_stride, 2, 4),
+      extent_of(a->D, vs, one, 1, 4),
+      extent_of(a->dt_bias, vs, one, 1, 4),
+      extent_of(a->initial_state, ss, unit, 3, 4),
+      extent_of(a->dout, xs, a->dout_stride, 3, es),
+      extent_of(a->dfinal_state, ss, unit, 3, 4),
+  };
+  const Extent outs[] = {
+      extent_of(a->du, xs, a->du_stride, 3, es),
+      extent_of(a->ddelta_raw, xs, a->ddelta_stride, 3, es),
+      extent_of(a->dA_log, as, aunit, 2, 4),
+      extent_of(a->dB, bcs, a->dB_stride, 3, es),
+      extent_of(a->dC, bcs, a->dC_stride, 3, es),
+      extent_of(a->dD, vs, one, 1, 4),
+      extent_of(a->dz, xs, a->dz_stride, 3, es),
+      extent_of(a->ddt_bias, vs, one, 1, 4),
+      extent_of(a->dinitial_state, ss, unit, 3, 4),
+  };
+  constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < kOuts; ++i) {
+    for (const Extent& e : ins)
+      if (overlaps(outs[i], e)) return MSS_ERR_ALIASING;
+    for (int j = i + 1; j < kOuts; ++j)
+      if (overlaps(outs[i], outs[j])) return MSS_ERR_ALIASING;
+  }
+  const BwdPlan plan = make_bwd_plan(a);
+  if (a->workspace == nullptr || a->workspace_bytes < plan.workspace)
+    return MSS_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(a->workspace, 256)) return MSS_ERR_MISALIGNED;
+  const Extent ew{reinterpret_cast<uintptr_t>(a->workspace),
+                  reinterpret_cast<uintptr_t>(a->workspace) + plan.workspace, true};
+  for (const Extent& e : ins)
+    if (overlaps(ew, e)) return MSS_ERR_ALIASING;
+  for (const Extent& e : outs)
+    if (overlaps(ew, e)) return MSS_ERR_ALIASING;
+
+  mss::BwdShape s = plan.shape;
+  std::memcpy(s.su, a->u_stride, sizeof(s.su));
+  std::memcpy(s.sd, a->delta_stride, sizeof(s.sd));
+  std::memcpy(s.sdo, a->dout_stride, sizeof(s.sdo));
+  std::memcpy(s.sdu, a->du_stride, sizeof(s.sdu));
+  std::memcpy(s.sddr, a->ddelta_stride, sizeof(s.sddr));
+  std::memcpy(s.sB, a->B_stride, sizeof(s.sB));
+  std::memcpy(s.sC, a->C_stride, sizeof(s.sC));
+  std::memcpy(s.sdB, a->dB_stride, sizeof(s.sdB));
+  std::memcpy(s.sdC, a->dC_stride, sizeof(s.sdC));
+  std::memcpy(s.sA, a->A_log_stride, sizeof(s.sA));
+  if (a->z != nullptr) std::memcpy(s.sz, a->z_stride, sizeof(s.sz));
+  else std::memset(s.sz, 0, sizeof(s.sz));
+  if (a->dz != nullptr) std::memcpy(s.sdz, a->dz_stride, sizeof(s.sdz));
+  else std::memset(s.sdz, 0, sizeof(s.sdz));
+  char* ws = static_cast<char*>(a->workspace);
+  mss::BwdPtrs p{};
+  p.u = a->u;
+  p.delta_raw = a->delta_raw;
+  p.A_log = a->A_log;
+  p.B = a->B;
+  p.C = a->C;
+  p.D = a->D;
+  p.z = a->z;
+  p.dt_bias = a->dt_bias;
+  p.h0 = a->initial_state;
+  p.dout = a->dout;
+  p.dfinal = a->dfinal_state;
+  p.du = a->du;
+  p.ddelta_raw = a->ddelta_raw;
+  p.dA_log = a->dA_log;
+  p.dB = a->dB;
+  p.dC = a->dC;
+  p.dD = a->dD;
+  p.dz = a->dz;
+  p.ddt_bias = a->ddt_bias;
+  p.dh0 = a->dinitial_state;
+  p.ckpt = reinterpret_cast<float*>(ws);
+  p.part_bc = reinterpret_cast<float*>(ws + plan.ckpt_bytes);
+  p.part_chan = reinterpret_cast<float*>(ws + plan.ckpt_bytes + plan.bc_bytes);
+  const hipError_t e = mss::launch_scan_bwd(s, p, a->io_dtype == MSS_BF16,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
 }
 

@@ -84,6 +84,36 @@ __device__ inline float load_uniform(const bf16_t* p) {
   return __uint_as_float((word >> sh) << 16);
 }
 
+// Sum over the eight state groups of one channel (lanes c + 8g) of four
+// per-step partial sums.  The two swap-and-add levels sum over lane bits 5 and
+// 4 and leave step {0, 2, 1, 3}[row] in 16-lane row `row`; a DPP rotation by 8
+// within the row adds lane bit 3.  Both lanes c and c + 8 of a row end with
+// the same total.
+__device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
+  const auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y0), __float_as_uint(y1),
+                                                    false, false);
+  const auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y2), __float_as_uint(y3),
+                                                    false, false);
+  const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+  const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(p01), __float_as_uint(p23),
+                                                  false, false);
+  const float w = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  // row_ror:8 -- lane i of a row reads lane (i + 8) mod 16
+  return w + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x128, 0xF, 0xF,
+                                                        false));
+}
+
+// Sum of v over the 8 lanes of each 8-lane group (a half row, lanes 8g..8g+7),
+// left in every lane of the group: the lane pairs (i, 7-i), then (i, i^2),
+// then (i, i^1) are added with DPP row_half_mirror and quad permutations.
+__device__ inline float sum_half_rows(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  return v;
+}
+
 // Wave-uniform value (lane 0's), kept in a scalar register.
 __device__ static inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -122,6 +122,56 @@ hipError_t launch_conv(const ConvShape& s, const ConvPtrs& p, bool io_bf16, hipS
 hipError_t launch_conv_step(const ConvStepShape& s, const ConvStepPtrs& p, bool io_bf16,
                             hipStream_t stream);
 
+// Selective-scan backward.  A workgroup of kBwdWaves waves owns kBwdCh
+// channels of one batch row (kCh per wave, lanes as in the forward scan:
+// lane (g, c) runs states 2g, 2g+1 of channel c) and walks the sequence in
+// chunks of kBwdT steps, the last chunk first.
+constexpr int kBwdT = 16;
+constexpr int kBwdWaves = 8;
+constexpr int kBwdCh = kCh * kBwdWaves;  // 64
+constexpr int kBwdThreads = 64 * kBwdWaves;
+
+struct BwdShape {
+  int batch, dim, seqlen, dstate;
+  int softplus;
+  int nchunk;         // ceil(seqlen / kBwdT)
+  int tiles;          // ceil(dim / kBwdCh) workgroups per batch row
+  int64_t nchan_pad;  // batch * tiles * kBwdCh: rows of the checkpoint array
+  int64_t su[3], sd[3], sz[3], sdo[3];      // u, delta_raw, z, dout: (b, d, t)
+  int64_t sdu[3], sddr[3], sdz[3];          // du, ddelta_raw, dz
+  int64_t sB[3], sC[3], sdB[3], sdC[3];     // (b, n, t)
+  int64_t sA[2];                            // A_log: (d, n)
+};
+
+struct BwdPtrs {
+  const void* u;
+  const void* delta_raw;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  const void* dout;
+  const float* dfinal;
+  void* du;
+  void* ddelta_raw;
+  float* dA_log;
+  void* dB;
+  void* dC;
+  float* dD;
+  void* dz;
+  float* ddt_bias;
+  float* dh0;
+  // workspace
+  float* ckpt;       // [nchunk][nchan_pad][kMaxState] state entering each chunk
+  float* part_bc;    // [batch][tiles][2 * kMaxState][seqlen] per-workgroup dB, dC sums
+  float* part_chan;  // [batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
+};
+
+hipError_t launch_scan_bwd(const BwdShape& s, const BwdPtrs& p, bool io_bf16, hipStream_t stream);
+
 // Enqueue the scan (segment aggregates, carry propagation when nseg > 1, then
 // the main pass).  io_bf16 selects the bf16 storage type; x_tfast says that
 // u/delta_raw/z/out have unit stride along t (else along d), bc_tfast that B

@@ -1,0 +1,436 @@
+// scan_bwd.hip -- backward of the selective-scan forward, for gfx950 (wave64).
+//
+// Given dout (and optionally dfinal, the gradient reaching the exported final
+// state) the chain rule through the forward (see scan_fwd.hip), taken step by
+// step in reverse time, gives with G_tn the total adjoint of h_tn:
+//   dy_t = dout_t silu(z_t)            dz_t = dout_t y_t silu'(z_t)
+//   G_tn = g_n + dy_t C_tn             g_n <- G_tn a_tn   (adjoint reaching h_(t-1))
+//   dC_tn = sum_d dy_t h_tn            dB_tn = sum_d G_tn delta_t u_t
+//   du_t = dy_t D + delta_t sum_n G_tn B_tn
+//   ddelta_t = u_t sum_n G_tn B_tn + sum_n G_tn h_(t-1)n a_tn A_n
+//   ddelta_raw_t = ddelta_t sigmoid(x_t)  (softplus' = sigmoid)
+//   dA_log_n = A_n sum_(b,t) G_tn h_(t-1)n a_tn delta_t
+//   dD = sum dy u,  ddt_bias = sum ddelta_raw,  dh0 = g after the first step.
+// The training backward is what the pages list as not yet written
+// ("mamba-metal: Apple Silicon で Mamba を動かす", section "残り課題").
+//
+// Passes:
+//   1. ckpt_kernel: the forward recurrence (no outputs) recording the state
+//      entering every kBwdT-step chunk.  One wave per 8 channels, lanes as in
+//      the forward: lane (g, c) runs states 2g, 2g+1 of channel c.
+//   2. bwd_kernel: a workgroup of kBwdWaves waves owns 64 channels of one
+//      batch row and walks the chunks from the last to the first.  Per chunk:
+//        E  inputs of the chunk: B and C into LDS (shared by the workgroup),
+//           per element delta, delta*u and dy into LDS (per wave);
+//        F  the chunk's states recomputed forward from its checkpoint, kept
+//           in registers (16 steps x 2 states per lane); C.h summed over the
+//           state groups gives y for dz;
+//        R  the reverse walk above.  Sums over states (for du and ddelta) go
+//           through the same cross-lane tree as the forward's C.h; sums over
+//           the wave's 8 channels (for dB and dC) through a DPP tree inside
+//           each 8-lane group, then over the workgroup's waves through LDS,
+//           into one partial per workgroup and step;
+//        O  du and ddelta_raw per element.
+//   3. reduce_bc_kernel: dB and dC as sums of the workgroup partials, in a
+//      fixed order (deterministic).
+//   4. finalize_kernel: dA_log, dD and ddt_bias summed over the batch rows.
+#include "mss_device.hpp"
+#include "mss_internal.hpp"
+
+namespace mss {
+namespace {
+
+constexpr int kXcdsBwd = 8;
+// LDS row pitches (floats), padded so that the rows one instruction reads
+// fall in distinct bank groups.
+constexpr int kElPitch = kBwdT * 4 + 4;  // s_el[c][t] = (delta, delta*u, dy, y_ssm)
+constexpr int kBcPitch = kBwdT + 4;      // s_bc[r][t]: r < 16 B_r, r >= 16 C_(r-16)
+constexpr int kGrPitch = kBwdT * 2 + 4;  // s_gr[c][t] = (d(delta*u), ddelta via a)
+constexpr int kDdPitch2 = kBwdT * 2 + 4; // ckpt pass: s_dd[c][t] = (delta, delta*u)
+
+struct f4 {
+  float x, y, z, w;
+};
+__device__ inline f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ inline float f4_at(const f4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+template <typename IO>
+__device__ inline float ld(const IO* p) { return io_traits<IO>::load(p); }
+
+__device__ inline float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+}
+
+__device__ inline int64_t xcd_order(int64_t lin, int64_t nwg) {
+  const int64_t xcd = lin % kXcdsBwd;
+  const int64_t per = nwg / kXcdsBwd, extra = nwg % kXcdsBwd;
+  return xcd * per + (xcd < extra ? xcd : extra) + lin / kXcdsBwd;
+}
+
+// The reduce_groups tree leaves step {0, 2, 1, 3}[row] of a 4-step block in
+// 16-lane row `row`.
+__device__ inline int group_step(int lane) {
+  const int row = lane >> 4;
+  return row == 1 ? 2 : (row == 2 ? 1 : row);
+}
+
+// ---------------------------------------------------------------- pass 1 ---
+template <typename IO>
+__global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
+  __shared__ __attribute__((aligned(16))) float s_b[kMaxState * kBcPitch];
+  __shared__ __attribute__((aligned(16))) float s_dd[kCh * kDdPitch2];
+  const int lane = threadIdx.x;
+  const int64_t groups8 = static_cast<int64_t>(s.tiles) * kBwdWaves;  // 8-channel groups per row
+  const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
+  const int b = static_cast<int>(logical / groups8);
+  const int dg = static_cast<int>(logical % groups8) * kCh;  // first channel of the wave
+  const int sg = lane >> 3, sc = lane & 7;
+  const int d = dg + sc;
+  const bool dvalid = d < s.dim;
+  const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
+  float A2[2], h[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int n = 2 * sg + k;
+    const bool active = dvalid && n < s.dstate;
+    A2[k] = active ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e : 0.0f;
+    h[k] = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+  }
+  const IO* Bm = static_cast<const IO*>(p.B);
+  const IO* u = static_cast<const IO*>(p.u);
+  const IO* dr = static_cast<const IO*>(p.delta_raw);
+  const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
+  for (int q = 0; q < s.nchunk; ++q) {
+    const int t0 = q * kBwdT;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      p.ckpt[(static_cast<int64_t>(q) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] = h[k];
+    // B of the chunk: lane covers row lane / 4, steps 4 (lane % 4) .. + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = lane >> 2, tt = (lane & 3) * 4 + i, t = t0 + tt;
+      const bool ok = n < s.dstate && t < s.seqlen;
+      s_b[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + t * s.sB[2]) : 0.0f;
+    }
+    // delta and delta*u: lane (c, j) covers steps 2j, 2j+1 of channel c
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tt = 2 * sg + e, t = t0 + tt;
+      const bool ok = dvalid && t < s.seqlen;
+      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
+      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
+      const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      *reinterpret_cast<float2*>(s_dd + sc * kDdPitch2 + 2 * tt) = make_float2(dl, dl * uu);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
+      const f4 b0 = ld4(s_b + (2 * sg) * kBcPitch + t4);
+      const f4 b1 = ld4(s_b + (2 * sg + 1) * kBcPitch + t4);
+      const f4 dd01 = ld4(s_dd + sc * kDdPitch2 + 2 * t4);
+      const f4 dd23 = ld4(s_dd + sc * kDdPitch2 + 2 * t4 + 4);
+      const float dl[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
+      const float du[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[0] = fmaf(fast_exp2(dl[i] * A2[0]), h[0], du[i] * f4_at(b0, i));
+        h[1] = fmaf(fast_exp2(dl[i] * A2[1]), h[1], du[i] * f4_at(b1, i));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ---------------------------------------------------------------- pass 2 ---
+template <typename IO>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p) {
+  __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
+  __shared__ __attribute__((aligned(16))) float s_el[kBwdWaves][kCh * kElPitch];
+  __shared__ __attribute__((aligned(16))) float s_gr[kBwdWaves][kCh * kGrPitch];
+  __shared__ __attribute__((aligned(16))) float s_red[kBwdWaves][2 * kMaxState * kBwdT];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
+  const int tile = static_cast<int>(logical % s.tiles);
+  const int b = static_cast<int>(logical / s.tiles);
+  const int d0 = tile * kBwdCh + w * kCh;  // this wave's first channel
+  const int sg = lane >> 3, sc = lane & 7;
+  const int d = d0 + sc;
+  const bool dvalid = d < s.dim;
+  const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
+  const bool has_z = p.z != nullptr;
+
+  const IO* u = static_cast<const IO*>(p.u);
+  const IO* dr = static_cast<const IO*>(p.delta_raw);
+  const IO* zz = static_cast<const IO*>(p.z);
+  const IO* dout = static_cast<const IO*>(p.dout);
+  const IO* Bm = static_cast<const IO*>(p.B);
+  const IO* Cm = static_cast<const IO*>(p.C);
+  IO* du_out = static_cast<IO*>(p.du);
+  IO* ddr_out = static_cast<IO*>(p.ddelta_raw);
+  IO* dz_out = static_cast<IO*>(p.dz);
+
+  float A2[2], An[2], g[2], dA[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int n = 2 * sg + k;
+    const bool active = dvalid && n < s.dstate;
+    An[k] = active ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) : 0.0f;
+    A2[k] = An[k] * kLog2e;
+    g[k] = (active && p.dfinal != nullptr)
+               ? p.dfinal[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+    dA[k] = 0.0f;
+  }
+  // element roles: lane (c, j) = (lane % 8, lane / 8) owns steps 2j, 2j+1 of
+  // channel c (the same channel as its scan role)
+  const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
+  const float skip = (dvalid && p.D != nullptr) ? p.D[d] : 0.0f;
+  float acc_dD = 0.0f, acc_db = 0.0f;
+
+  float* el = s_el[w];
+  float* gr = s_gr[w];
+  for (int q = s.nchunk - 1; q >= 0; --q) {
+    const int t0 = q * kBwdT;
+    // ---- E: B and C of the chunk (one value per thread) ----
+    {
+      const int r = tid >> 4, tt = tid & 15, n = r & 15, t = t0 + tt;
+      const bool ok = n < s.dstate && t < s.seqlen;
+      float v = 0.0f;
+      if (ok) v = r < kMaxState ? ld(Bm + b * s.sB[0] + n * s.sB[1] + t * s.sB[2])
+                                : ld(Cm + b * s.sC[0] + n * s.sC[1] + t * s.sC[2]);
+      s_bc[r * kBcPitch + tt] = v;
+    }
+    // ---- E: per element ----
+    float eu[2], edl[2], edy[2], esig[2], edo[2], ez[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tt = 2 * sg + e, t = t0 + tt;
+      const bool ok = dvalid && t < s.seqlen;
+      eu[e] = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
+      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
+      edo[e] = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + t * s.sdo[2]) : 0.0f;
+      ez[e] = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + t * s.sz[2]) : 0.0f;
+      edl[e] = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      esig[e] = s.softplus ? sigmoid(x) : 1.0f;
+      edy[e] = has_z ? edo[e] * silu(ez[e]) : edo[e];
+      *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{edl[e], edl[e] * eu[e], edy[e], 0.0f};
+    }
+    __syncthreads();
+
+    // ---- F: the chunk's states from its checkpoint ----
+    float hs[2], h[2], hh[kBwdT][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      hs[k] = p.ckpt[(static_cast<int64_t>(q) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k];
+      h[k] = hs[k];
+    }
+    const float* rb0 = s_bc + (2 * sg) * kBcPitch;
+    const float* rb1 = rb0 + kBcPitch;
+    const float* rc0 = s_bc + (kMaxState + 2 * sg) * kBcPitch;
+    const float* rc1 = rc0 + kBcPitch;
+    const float* rdd = el + sc * kElPitch;
+    const int ystep = group_step(lane);
+#pragma unroll
+    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
+      const f4 b0 = ld4(rb0 + t4), b1 = ld4(rb1 + t4), c0 = ld4(rc0 + t4), c1 = ld4(rc1 + t4);
+      float yp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f4 dd = ld4(rdd + 4 * (t4 + i));
+        h[0] = fmaf(fast_exp2(dd.x * A2[0]), h[0], dd.y * f4_at(b0, i));
+        h[1] = fmaf(fast_exp2(dd.x * A2[1]), h[1], dd.y * f4_at(b1, i));
+        hh[t4 + i][0] = h[0];
+        hh[t4 + i][1] = h[1];
+        yp[i] = fmaf(f4_at(c1, i), h[1], f4_at(c0, i) * h[0]);
+      }
+      el[sc * kElPitch + 4 * (t4 + ystep) + 3] = reduce_groups(yp[0], yp[1], yp[2], yp[3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // dz = dout * (C.h + D u) * silu'(z)
+    if (has_z && dz_out != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int tt = 2 * sg + e, t = t0 + tt;
+        if (dvalid && t < s.seqlen) {
+          const float y = el[sc * kElPitch + 4 * tt + 3] + skip * eu[e];
+          const float sz = sigmoid(ez[e]);
+          const float dsilu = sz * fmaf(ez[e], 1.0f - sz, 1.0f);
+          io_traits<IO>::store(dz_out + b * s.sdz[0] + d * s.sdz[1] + t * s.sdz[2],
+                               edo[e] * y * dsilu);
+        }
+      }
+    }
+
+    // ---- R: reverse walk ----
+#pragma unroll
+    for (int t4 = kBwdT - 4; t4 >= 0; t4 -= 4) {
+      const f4 b0 = ld4(rb0 + t4), b1 = ld4(rb1 + t4), c0 = ld4(rc0 + t4), c1 = ld4(rc1 + t4);
+      float qb[4], qa[4], pb0[4], pb1[4], pc0[4], pc1[4];
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const int t = t4 + i;
+        const f4 dd = ld4(rdd + 4 * t);
+        const float bk[2] = {f4_at(b0, i), f4_at(b1, i)};
+        const float ck[2] = {f4_at(c0, i), f4_at(c1, i)};
+        float sb = 0.0f, sa = 0.0f;
+        float pb[2], pc[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float G = fmaf(dd.z, ck[k], g[k]);
+          pc[k] = dd.z * hh[t][k];
+          pb[k] = G * dd.y;
+          sb = fmaf(G, bk[k], sb);
+          const float a = fast_exp2(dd.x * A2[k]);
+          const float hp = t > 0 ? hh[t > 0 ? t - 1 : 0][k] : hs[k];
+          const float r = G * hp * a;
+          dA[k] = fmaf(r, dd.x, dA[k]);
+          sa = fmaf(r, An[k], sa);
+          g[k] = G * a;
+        }
+        qb[i] = sb;
+        qa[i] = sa;
+        pb0[i] = pb[0];
+        pb1[i] = pb[1];
+        pc0[i] = pc[0];
+        pc1[i] = pc[1];
+      }
+      const float gb = reduce_groups(qb[0], qb[1], qb[2], qb[3]);
+      const float ga = reduce_groups(qa[0], qa[1], qa[2], qa[3]);
+      *reinterpret_cast<float2*>(gr + sc * kGrPitch + 2 * (t4 + ystep)) = make_float2(gb, ga);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb0[i] = sum_half_rows(pb0[i]);
+        pb1[i] = sum_half_rows(pb1[i]);
+        pc0[i] = sum_half_rows(pc0[i]);
+        pc1[i] = sum_half_rows(pc1[i]);
+      }
+      if (sc == 0) {
+        float* red = s_red[w];
+        *reinterpret_cast<f4*>(red + (2 * sg) * kBwdT + t4) = f4{pb0[0], pb0[1], pb0[2], pb0[3]};
+        *reinterpret_cast<f4*>(red + (2 * sg + 1) * kBwdT + t4) = f4{pb1[0], pb1[1], pb1[2], pb1[3]};
+        *reinterpret_cast<f4*>(red + (kMaxState + 2 * sg) * kBwdT + t4) =
+            f4{pc0[0], pc0[1], pc0[2], pc0[3]};
+        *reinterpret_cast<f4*>(red + (kMaxState + 2 * sg + 1) * kBwdT + t4) =
+            f4{pc1[0], pc1[1], pc1[2], pc1[3]};
+      }
+    }
+    __syncthreads();
+
+    // ---- the workgroup's dB / dC partial of the chunk (one value per thread) ----
+    {
+      const int r = tid >> 4, tt = tid & 15, t = t0 + tt;
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kBwdWaves; ++ww) sum += s_red[ww][r * kBwdT + tt];
+      if ((r & 15) < s.dstate && t < s.seqlen)
+        p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t] = sum;
+    }
+
+    // ---- O: du and ddelta_raw per element ----
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tt = 2 * sg + e, t = t0 + tt;
+      const float2 v = *reinterpret_cast<const float2*>(gr + sc * kGrPitch + 2 * tt);
+      const float du = fmaf(edy[e], skip, edl[e] * v.x);
+      const float ddr = fmaf(eu[e], v.x, v.y) * esig[e];
+      if (dvalid && t < s.seqlen) {
+        io_traits<IO>::store(du_out + b * s.sdu[0] + d * s.sdu[1] + t * s.sdu[2], du);
+        io_traits<IO>::store(ddr_out + b * s.sddr[0] + d * s.sddr[1] + t * s.sddr[2], ddr);
+        acc_db += ddr;
+        acc_dD = fmaf(edy[e], eu[e], acc_dD);
+      }
+    }
+  }
+
+  // ---- per (row, channel) results ----
+  const int64_t prow = (static_cast<int64_t>(b) * s.dim + d) * (kMaxState + 2);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int n = 2 * sg + k;
+    if (dvalid && n < s.dstate) {
+      p.part_chan[prow + n] = dA[k] * An[k];
+      if (p.dh0 != nullptr) p.dh0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] = g[k];
+    }
+  }
+  // dD and ddt_bias: the 8 lanes of a channel (lanes c + 8j) meet in LDS
+  __syncthreads();
+  float* tmp = s_red[w];
+  tmp[lane] = acc_dD;
+  tmp[64 + lane] = acc_db;
+  __builtin_amdgcn_wave_barrier();
+  if (sg == 0 && dvalid) {
+    float sD = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sD += tmp[sc + 8 * j];
+      sb += tmp[64 + sc + 8 * j];
+    }
+    p.part_chan[prow + kMaxState] = sD;
+    p.part_chan[prow + kMaxState + 1] = sb;
+  }
+}
+
+// ---------------------------------------------------------------- pass 3 ---
+// dB / dC[b, n, t] = sum over the row's workgroups of their partials.
+template <typename IO>
+__global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
+  const int64_t n_items = static_cast<int64_t>(s.batch) * 2 * s.dstate * s.seqlen;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_items) return;
+  const int t = static_cast<int>(i % s.seqlen);
+  const int64_t rest = i / s.seqlen;
+  const int j = static_cast<int>(rest % (2 * s.dstate));
+  const int b = static_cast<int>(rest / (2 * s.dstate));
+  const bool is_c = j >= s.dstate;
+  const int n = is_c ? j - s.dstate : j;
+  const int r = is_c ? kMaxState + n : n;
+  float sum = 0.0f;
+  for (int tile = 0; tile < s.tiles; ++tile)
+    sum += p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t];
+  if (is_c)
+    io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + t * s.sdC[2], sum);
+  else
+    io_traits<IO>::store(static_cast<IO*>(p.dB) + b * s.sdB[0] + n * s.sdB[1] + t * s.sdB[2], sum);
+}
+
+// ---------------------------------------------------------------- pass 4 ---
+__global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(s.dim) * (kMaxState + 2)) return;
+  const int d = static_cast<int>(i / (kMaxState + 2));
+  const int j = static_cast<int>(i % (kMaxState + 2));
+  if (j < kMaxState && j >= s.dstate) return;
+  float sum = 0.0f;
+  for (int b = 0; b < s.batch; ++b) sum += p.part_chan[(static_cast<int64_t>(b) * s.dim + d) * (kMaxState + 2) + j];
+  if (j < kMaxState)
+    p.dA_log[static_cast<int64_t>(d) * s.dstate + j] = sum;
+  else if (j == kMaxState) {
+    if (p.dD != nullptr) p.dD[d] = sum;
+  } else if (p.ddt_bias != nullptr) {
+    p.ddt_bias[d] = sum;
+  }
+}
+
+template <typename IO>
+hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream) {
+  const int64_t waves = static_cast<int64_t>(s.batch) * s.tiles * kBwdWaves;
+  ckpt_kernel<IO><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+  const int64_t wgs = static_cast<int64_t>(s.batch) * s.tiles;
+  bwd_kernel<IO><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
+  const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * s.dstate * s.seqlen;
+  reduce_bc_kernel<IO><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
+  const int64_t nch = static_cast<int64_t>(s.dim) * (kMaxState + 2);
+  finalize_kernel<<<dim3(static_cast<unsigned>((nch + 255) / 256)), dim3(256), 0, stream>>>(s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdShape& s, const BwdPtrs& p, bool io_bf16, hipStream_t stream) {
+  return io_bf16 ? launch_bwd_t<bf16_t>(s, p, stream) : launch_bwd_t<float>(s, p, stream);
+}
+
+}  // namespace mss

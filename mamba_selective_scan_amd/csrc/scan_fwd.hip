@@ -133,26 +133,6 @@ struct f4 {
 };
 __device__ inline f4 lds_f4(const float* p) { return *reinterpret_cast<const f4*>(p); }
 
-// Sum over the eight state groups of one channel (lanes c + 8g) of four
-// per-step partial sums.  The two swap-and-add levels sum over lane bits 5 and
-// 4 and leave step {0, 2, 1, 3}[row] in 16-lane row `row`; a DPP rotation by 8
-// within the row adds lane bit 3.  Both lanes c and c + 8 of a row end with
-// the same total.
-__device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
-  const auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y0), __float_as_uint(y1),
-                                                    false, false);
-  const auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y2), __float_as_uint(y3),
-                                                    false, false);
-  const float p01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
-  const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
-  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(p01), __float_as_uint(p23),
-                                                  false, false);
-  const float w = __uint_as_float(q[0]) + __uint_as_float(q[1]);
-  // row_ror:8 -- lane i of a row reads lane (i + 8) mod 16
-  return w + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x128, 0xF, 0xF,
-                                                        false));
-}
-
 // Five waves per SIMD (at most 96 VGPRs) for the vector paths; the
 // element-wise paths (ragged tails, unaligned views) and the fp32 d-fast
 // n-fast path need more registers and run four.

@@ -66,7 +66,8 @@ def _c_layout(struct_name, fields, tmp_path):
 @pytest.mark.parametrize("cls,cname", [(_lib.ScanArgs, "mss_scan_args"),
                                        (_lib.StepArgs, "mss_step_args"),
                                        (_lib.ConvArgs, "mss_conv_args"),
-                                       (_lib.ConvStepArgs, "mss_conv_step_args")])
+                                       (_lib.ConvStepArgs, "mss_conv_step_args"),
+                                       (_lib.ScanBwdArgs, "mss_scan_bwd_args")])
 def test_ctypes_struct_matches_c_layout(cls, cname, tmp_path):
     names = [f[0] for f in cls._fields_]
     size, offs = _c_layout(cname, names, tmp_path)
@@ -315,6 +316,89 @@ def test_conv_step_argument_checks(case):
     a = conv_step_args()
     fn(a)
     assert _lib.lib().mss_causal_conv1d_update(ctypes.byref(a), None) == code(expect)
+
+
+def bwd_args(ws=True):
+    a = _lib.new_scan_bwd_args()
+    a.io_dtype = _lib.MSS_F32
+    a.batch, a.dim, a.seqlen, a.dstate = 2, 96, 100, 16
+    x = (96 * 100, 100, 1)
+    bc = (16 * 100, 100, 1)
+    a.u, a.u_stride = fake(0), (ctypes.c_int64 * 3)(*x)
+    a.delta_raw, a.delta_stride = fake(1), (ctypes.c_int64 * 3)(*x)
+    a.A_log, a.A_log_stride = fake(2), (ctypes.c_int64 * 2)(16, 1)
+    a.B, a.B_stride = fake(3), (ctypes.c_int64 * 3)(*bc)
+    a.C, a.C_stride = fake(4), (ctypes.c_int64 * 3)(*bc)
+    a.D = fake(5)
+    a.z, a.z_stride = fake(6), (ctypes.c_int64 * 3)(*x)
+    a.dt_bias = fake(7)
+    a.delta_softplus = 1
+    a.dout, a.dout_stride = fake(8), (ctypes.c_int64 * 3)(*x)
+    a.du, a.du_stride = fake(9), (ctypes.c_int64 * 3)(*x)
+    a.ddelta_raw, a.ddelta_stride = fake(10), (ctypes.c_int64 * 3)(*x)
+    a.dA_log = fake(11)
+    a.dB, a.dB_stride = fake(12), (ctypes.c_int64 * 3)(*bc)
+    a.dC, a.dC_stride = fake(13), (ctypes.c_int64 * 3)(*bc)
+    a.dD = fake(14)
+    a.dz, a.dz_stride = fake(15), (ctypes.c_int64 * 3)(*x)
+    a.ddt_bias = fake(16)
+    if ws:
+        st = ctypes.c_int(0)
+        a.workspace = fake(17)
+        a.workspace_bytes = _lib.lib().mss_selective_scan_bwd_workspace_size(ctypes.byref(a),
+                                                                             ctypes.byref(st))
+    return a
+
+
+def test_bwd_workspace_size():
+    lib = _lib.lib()
+    a = bwd_args(ws=False)
+    st = ctypes.c_int(-1)
+    n = lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    assert st.value == 0
+    # checkpoints: 7 chunks x 2*64*2 padded channels x 16 states; partials: 2 rows x 2
+    # tiles x 32 x 100 steps; per-row sums 2 x 96 x 18 (each rounded up to 256 B)
+    r = lambda v: (v + 255) // 256 * 256
+    assert n == r(7 * 2 * 128 * 16 * 4) + r(2 * 2 * 32 * 100 * 4) + r(2 * 96 * 18 * 4)
+    a.dstate = 0
+    assert lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st)) == 0
+    assert st.value == code("MSS_ERR_UNSUPPORTED_DSTATE")
+
+
+BWD_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), "MSS_ERR_BAD_STRUCT"),
+    "reserved": (lambda a: setattr(a, "reserved0", 2), "MSS_ERR_BAD_STRUCT"),
+    "dtype": (lambda a: setattr(a, "io_dtype", 3), "MSS_ERR_UNSUPPORTED_DTYPE"),
+    "seqlen0": (lambda a: setattr(a, "seqlen", 0), "MSS_ERR_BAD_SHAPE"),
+    "dstate17": (lambda a: setattr(a, "dstate", 17), "MSS_ERR_UNSUPPORTED_DSTATE"),
+    "dout_null": (lambda a: setattr(a, "dout", None), "MSS_ERR_NULL_POINTER"),
+    "dB_null": (lambda a: setattr(a, "dB", None), "MSS_ERR_NULL_POINTER"),
+    "dA_log_null": (lambda a: setattr(a, "dA_log", None), "MSS_ERR_NULL_POINTER"),
+    "dz_without_z": (lambda a: setattr(a, "z", None), "MSS_ERR_NULL_POINTER"),
+    "neg_stride": (lambda a: a.dout_stride.__setitem__(2, -1), "MSS_ERR_BAD_STRIDE"),
+    "du_overlap": (lambda a: a.du_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
+    "dC_overlap": (lambda a: a.dC_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
+    "misaligned_dz": (lambda a: setattr(a, "dz", fake(15) + 2), "MSS_ERR_MISALIGNED"),
+    "misaligned_dD": (lambda a: setattr(a, "dD", fake(14) + 1), "MSS_ERR_MISALIGNED"),
+    "du_is_u": (lambda a: setattr(a, "du", fake(0)), "MSS_ERR_ALIASING"),
+    "dB_is_B": (lambda a: setattr(a, "dB", fake(3)), "MSS_ERR_ALIASING"),
+    "dz_on_dout": (lambda a: setattr(a, "dz", fake(8) + 400), "MSS_ERR_ALIASING"),
+    "dD_in_dA_log": (lambda a: setattr(a, "dD", fake(11) + 8), "MSS_ERR_ALIASING"),
+    "no_workspace": (lambda a: setattr(a, "workspace", None), "MSS_ERR_WORKSPACE_TOO_SMALL"),
+    "short_workspace": (lambda a: setattr(a, "workspace_bytes", a.workspace_bytes - 1),
+                        "MSS_ERR_WORKSPACE_TOO_SMALL"),
+    "misaligned_workspace": (lambda a: setattr(a, "workspace", fake(17) + 64), "MSS_ERR_MISALIGNED"),
+    "workspace_on_du": (lambda a: setattr(a, "workspace", fake(9)), "MSS_ERR_ALIASING"),
+}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(BWD_CASES))
+def test_bwd_argument_checks(case):
+    fn, expect = BWD_CASES[case]
+    a = bwd_args()
+    fn(a)
+    assert _lib.lib().mss_selective_scan_bwd(ctypes.byref(a), None) == code(expect)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,144 @@
+"""GPU parity of the selective-scan backward against the fp64 backward oracle.
+
+Tolerances (error metric: max |o - r| / (|r| + rms(r)), per gradient tensor):
+  fp32 I/O 1e-4, as for the forward: every gradient is a short fp32 sum
+      (over the 16 states, the 8 channels of a wave and then the 64 of a
+      workgroup, or the steps of one channel) of products of quantities that
+      the forward's own 1e-4 already bounds, and the reverse adjoint g obeys
+      the same contracting recurrence as the forward state;
+  bf16 I/O 2e-2: the oracle reads the same rounded inputs; the gradients that
+      are stored in bf16 carry a rounding of at most 2^-9 on top of the fp32
+      error, and the fp32 ones (dA_log, dD, ddt_bias, dinitial_state) inherit
+      the bf16 rounding of nothing but their inputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check, device, note, to_np
+from mamba_selective_scan_amd.inputs import WORKLOADS, generate
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+ORACLE_NAME = {"du": "du", "ddelta_raw": "ddelta_raw", "dA_log": "dA_log", "dB": "dB",
+               "dC": "dC", "dD": "dD", "dz": "dz", "ddt_bias": "ddt_bias",
+               "dinitial_state": "dh0"}
+
+
+@pytest.fixture(scope="module")
+def mss():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import mamba_selective_scan_amd as m
+    return m
+
+
+def _problem(batch, dim, seqlen, dstate, layout="bdl", io="f32", seed=0, softplus=True,
+             with_z=True, with_D=True, with_bias=True, h0=False, dfinal=False,
+             a_log="ladder"):
+    import torch
+    from mamba_selective_scan_amd.inputs import to_torch
+    x = generate(batch, dim, seqlen, dstate, layout, seed=seed, a_log=a_log)
+    if not softplus:
+        x["dt_bias"] = np.log1p(np.exp(x["dt_bias"].astype(np.float64))).astype(np.float32)
+        x["delta_raw"] = np.abs(x["delta_raw"]) * np.float32(0.1)
+    dx = to_torch(x, device(), io)
+    g = torch.Generator().manual_seed(seed + 7)
+    dt = dx["u"].dtype
+    dout = torch.randn(batch, dim, seqlen, generator=g)
+    if layout == "bld":
+        dout = dout.transpose(1, 2).contiguous().transpose(1, 2)
+    dx["dout"] = dout.to(device=device(), dtype=dt)
+    dx["h0"] = torch.randn(batch, dim, dstate, generator=g).to(device()) if h0 else None
+    dx["dfinal"] = torch.randn(batch, dim, dstate, generator=g).to(device()) if dfinal else None
+    if not with_z:
+        dx["z"] = None
+    if not with_D:
+        dx["D"] = None
+    if not with_bias:
+        dx["dt_bias"] = None
+    return dx
+
+
+def _run_and_check(mss, name, dx, io="f32", softplus=True):
+    import torch
+    note(f"bwd {name}: shape={tuple(dx['u'].shape)} N={dx['A_log'].shape[1]} {io} "
+         f"softplus={softplus} z={dx['z'] is not None} D={dx['D'] is not None} "
+         f"bias={dx['dt_bias'] is not None} h0={dx['h0'] is not None} "
+         f"dfinal={dx['dfinal'] is not None}")
+    got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                 dx["dout"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                 delta_softplus=softplus, initial_state=dx["h0"],
+                                 dfinal_state=dx["dfinal"])
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dx["dout"],
+                          D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], h0=dx["h0"],
+                          dfinal=dx["dfinal"], delta_softplus=softplus)
+    for k, v in got.items():
+        check(f"bwd {name} {k}", to_np(v), ref[ORACLE_NAME[k]], TOL[io])
+    expect = {"du", "ddelta_raw", "dA_log", "dB", "dC"}
+    expect |= {"dD"} if dx["D"] is not None else set()
+    expect |= {"dz"} if dx["z"] is not None else set()
+    expect |= {"ddt_bias"} if dx["dt_bias"] is not None else set()
+    expect |= {"dinitial_state"} if dx["h0"] is not None else set()
+    assert set(got) == expect
+    return got
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_workload(mss, seed):
+    w = WORKLOADS["tiny"]
+    _run_and_check(mss, "tiny", _problem(w.batch, w.dim, w.seqlen, w.dstate, seed=seed,
+                                         h0=True, dfinal=True))
+
+
+def test_mamba130m_layer(mss):
+    w = WORKLOADS["mamba130m_layer"]
+    _run_and_check(mss, "130m", _problem(w.batch, w.dim, w.seqlen, w.dstate))
+
+
+@pytest.mark.parametrize("seqlen", [1, 7, 16, 17, 33, 100])
+def test_ragged_lengths(mss, seqlen):
+    _run_and_check(mss, f"L={seqlen}", _problem(2, 72, seqlen, 16, h0=True, dfinal=True))
+
+
+@pytest.mark.parametrize("dstate", [1, 5, 13])
+def test_small_dstate(mss, dstate):
+    _run_and_check(mss, f"N={dstate}", _problem(2, 130, 90, dstate))
+
+
+@pytest.mark.parametrize("flags", [dict(with_z=False), dict(with_D=False), dict(with_bias=False),
+                                   dict(softplus=False), dict(h0=True),
+                                   dict(with_z=False, with_D=False, h0=True, dfinal=True)])
+def test_optional_inputs(mss, flags):
+    softplus = flags.get("softplus", True)
+    _run_and_check(mss, f"{flags}", _problem(2, 96, 150, 16, **flags), softplus=softplus)
+
+
+def test_random_a_log(mss):
+    _run_and_check(mss, "A_log~N(0,1)", _problem(1, 128, 300, 16, a_log="normal", h0=True))
+
+
+def test_channel_last_layout(mss):
+    _run_and_check(mss, "bld", _problem(2, 64, 200, 16, layout="bld", h0=True, dfinal=True))
+
+
+def test_bf16(mss):
+    _run_and_check(mss, "bf16", _problem(2, 128, 200, 16, io="bf16", h0=True, dfinal=True),
+                   io="bf16")
+
+
+def test_run_twice_bitwise(mss):
+    import torch
+    dx = _problem(2, 130, 77, 16, h0=True, dfinal=True)
+    note("bwd run-twice determinism")
+    args = (dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dx["dout"])
+    kw = dict(D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], initial_state=dx["h0"],
+              dfinal_state=dx["dfinal"])
+    a = mss.selective_scan_bwd(*args, **kw)
+    b = mss.selective_scan_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
