@@ -152,8 +152,15 @@ bool all_mult(const int64_t* st, int rank, int64_t m, int skip) {
 // Backward plan: workspace = checkpoints, dB/dC partials, per-row sums.
 struct BwdPlan {
   mss::BwdShape shape;
-  size_t ckpt_bytes = 0, bc_bytes = 0, chan_bytes = 0, workspace = 0;
+  size_t ckpt_bytes = 0, bc_bytes = 0, chan_bytes = 0, agg_bytes = 0, carry_bytes = 0;
+  size_t workspace = 0;
 };
+
+// Backward time segments: a shape with fewer (row, 64-channel tile) pairs
+// than this is split along time until it reaches it, with segments of at
+// least kBwdMinSegChunks chunks.
+constexpr int64_t kBwdSplitBelow = 512;
+constexpr int64_t kBwdMinSegChunks = 8;
 
 mss_status check_bwd_shape(const mss_scan_bwd_args* a) {
   if (a == nullptr || a->struct_size != sizeof(mss_scan_bwd_args) || a->reserved0 != 0)
@@ -180,10 +187,21 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
   s.nchunk = static_cast<int>((a->seqlen + mss::kBwdT - 1) / mss::kBwdT);
   s.tiles = static_cast<int>((a->dim + mss::kBwdCh - 1) / mss::kBwdCh);
   s.nchan_pad = a->batch * s.tiles * mss::kBwdCh;
+  const int64_t pairs = a->batch * s.tiles;
+  int64_t nseg = 1;
+  if (pairs < kBwdSplitBelow)
+    nseg = std::min<int64_t>((kBwdSplitBelow + pairs - 1) / pairs,
+                             std::max<int64_t>(1, s.nchunk / kBwdMinSegChunks));
+  s.seg_chunks = static_cast<int>((s.nchunk + nseg - 1) / nseg);
+  s.nseg = (s.nchunk + s.seg_chunks - 1) / s.seg_chunks;
   p.ckpt_bytes = round_up(static_cast<size_t>(s.nchunk) * s.nchan_pad * kMaxState * sizeof(float), 256);
   p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * a->seqlen * sizeof(float), 256);
-  p.chan_bytes = round_up(static_cast<size_t>(a->batch) * a->dim * (kMaxState + 2) * sizeof(float), 256);
-  p.workspace = p.ckpt_bytes + p.bc_bytes + p.chan_bytes;
+  p.chan_bytes = round_up(static_cast<size_t>(s.nseg) * a->batch * a->dim * (kMaxState + 2) * sizeof(float), 256);
+  if (s.nseg > 1) {
+    p.agg_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float4), 256);
+    p.carry_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float), 256);
+  }
+  p.workspace = p.ckpt_bytes + p.bc_bytes + p.chan_bytes + p.agg_bytes + 2 * p.carry_bytes;
   return p;
 }
 
@@ -536,6 +554,12 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
   p.ckpt = reinterpret_cast<float*>(ws);
   p.part_bc = reinterpret_cast<float*>(ws + plan.ckpt_bytes);
   p.part_chan = reinterpret_cast<float*>(ws + plan.ckpt_bytes + plan.bc_bytes);
+  if (plan.agg_bytes > 0) {
+    char* q = ws + plan.ckpt_bytes + plan.bc_bytes + plan.chan_bytes;
+    p.agg = reinterpret_cast<float4*>(q);
+    p.carry_h = reinterpret_cast<float*>(q + plan.agg_bytes);
+    p.carry_g = reinterpret_cast<float*>(q + plan.agg_bytes + plan.carry_bytes);
+  }
   const hipError_t e = mss::launch_scan_bwd(s, p, a->io_dtype == MSS_BF16,
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;

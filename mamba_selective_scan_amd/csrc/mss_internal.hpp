@@ -136,6 +136,8 @@ struct BwdShape {
   int softplus;
   int nchunk;         // ceil(seqlen / kBwdT)
   int tiles;          // ceil(dim / kBwdCh) workgroups per batch row
+  int nseg;           // time segments (each seg_chunks chunks; the last may be shorter)
+  int seg_chunks;
   int64_t nchan_pad;  // batch * tiles * kBwdCh: rows of the checkpoint array
   int64_t su[3], sd[3], sz[3], sdo[3];      // u, delta_raw, z, dout: (b, d, t)
   int64_t sdu[3], sddr[3], sdz[3];          // du, ddelta_raw, dz
@@ -167,7 +169,10 @@ struct BwdPtrs {
   // workspace
   float* ckpt;       // [nchunk][nchan_pad][kMaxState] state entering each chunk
   float* part_bc;    // [batch][tiles][2 * kMaxState][seqlen] per-workgroup dB, dC sums
-  float* part_chan;  // [batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
+  float* part_chan;  // [nseg][batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
+  float4* agg;       // [nseg][nchan_pad][kMaxState] per segment (prod a, h from 0, g from 0, -)
+  float* carry_h;    // [nseg][nchan_pad][kMaxState] state entering each segment
+  float* carry_g;    // [nseg][nchan_pad][kMaxState] adjoint reaching each segment's last state
 };
 
 hipError_t launch_scan_bwd(const BwdShape& s, const BwdPtrs& p, bool io_bf16, hipStream_t stream);

@@ -15,6 +15,16 @@
 // ("mamba-metal: Apple Silicon で Mamba を動かす", section "残り課題").
 //
 // Passes:
+//   0. (few channels, long sequences) the sequence is cut into time segments
+//      so that the grid fills the GPU.  agg_kernel walks every segment forward
+//      from zero and records per (channel, state) the product P of its decays,
+//      the state H it reaches and the adjoint Z it sends back to its first
+//      step's predecessor, Z = sum_t (prod_(r<=t) a_r) dy_t C_t; carry_kernel
+//      composes them, forward for the state entering each segment
+//      (h_in[s+1] = P_s h_in[s] + H_s) and backward for the adjoint reaching
+//      each segment's end (g_in[s-1] = P_s g_in[s] + Z_s): the pair operator
+//      of "mamba-metal", sections "Selective scan の本質" and "チャンク間
+//      running prefix", applied in both directions.
 //   1. ckpt_kernel: the forward recurrence (no outputs) recording the state
 //      entering every kBwdT-step chunk.  One wave per 8 channels, lanes as in
 //      the forward: lane (g, c) runs states 2g, 2g+1 of channel c.
@@ -76,6 +86,120 @@ __device__ inline int group_step(int lane) {
   return row == 1 ? 2 : (row == 2 ? 1 : row);
 }
 
+// ---------------------------------------------------------------- pass 0 ---
+// Segment aggregates, walking each segment forward from zero: per state
+// P = prod a_t, H = the state reached, Z = sum_t (prod_(r<=t) a_r) dy_t C_t.
+template <typename IO>
+__global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
+  __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
+  __shared__ __attribute__((aligned(16))) float s_el[kCh * kElPitch];
+  const int lane = threadIdx.x;
+  const int64_t groups8 = static_cast<int64_t>(s.tiles) * kBwdWaves;
+  const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
+  const int64_t row_seg = logical / groups8;
+  const int b = static_cast<int>(row_seg / s.nseg);
+  const int seg = static_cast<int>(row_seg % s.nseg);
+  const int dg = static_cast<int>(logical % groups8) * kCh;
+  const int sg = lane >> 3, sc = lane & 7;
+  const int d = dg + sc;
+  const bool dvalid = d < s.dim;
+  const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
+  const bool has_z = p.z != nullptr;
+  float A2[2], H[2] = {0.0f, 0.0f}, P[2] = {1.0f, 1.0f}, Z[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int n = 2 * sg + k;
+    A2[k] = (dvalid && n < s.dstate) ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e : 0.0f;
+  }
+  const IO* Bm = static_cast<const IO*>(p.B);
+  const IO* Cm = static_cast<const IO*>(p.C);
+  const IO* u = static_cast<const IO*>(p.u);
+  const IO* dr = static_cast<const IO*>(p.delta_raw);
+  const IO* zz = static_cast<const IO*>(p.z);
+  const IO* dout = static_cast<const IO*>(p.dout);
+  const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
+  const int q_begin = seg * s.seg_chunks;
+  const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
+  for (int q = q_begin; q < q_end; ++q) {
+    const int t0 = q * kBwdT;
+    // B and C: lane covers rows lane / 4 and 16 + lane / 4, steps 4 (lane % 4) .. + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = lane >> 2, tt = (lane & 3) * 4 + i, t = t0 + tt;
+      const bool ok = n < s.dstate && t < s.seqlen;
+      s_bc[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + t * s.sB[2]) : 0.0f;
+      s_bc[(kMaxState + n) * kBcPitch + tt] =
+          ok ? ld(Cm + b * s.sC[0] + n * s.sC[1] + t * s.sC[2]) : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tt = 2 * sg + e, t = t0 + tt;
+      const bool ok = dvalid && t < s.seqlen;
+      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
+      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
+      const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + t * s.sdo[2]) : 0.0f;
+      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + t * s.sz[2]) : 0.0f;
+      const float dy = has_z ? go * silu(zv) : go;
+      *reinterpret_cast<f4*>(s_el + sc * kElPitch + 4 * tt) = f4{dl, dl * uu, dy, 0.0f};
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
+      const f4 b0 = ld4(s_bc + (2 * sg) * kBcPitch + t4);
+      const f4 b1 = ld4(s_bc + (2 * sg + 1) * kBcPitch + t4);
+      const f4 c0 = ld4(s_bc + (kMaxState + 2 * sg) * kBcPitch + t4);
+      const f4 c1 = ld4(s_bc + (kMaxState + 2 * sg + 1) * kBcPitch + t4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f4 dd = ld4(s_el + sc * kElPitch + 4 * (t4 + i));
+        const float bk[2] = {f4_at(b0, i), f4_at(b1, i)};
+        const float ck[2] = {f4_at(c0, i), f4_at(c1, i)};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float a = fast_exp2(dd.x * A2[k]);
+          H[k] = fmaf(a, H[k], dd.y * bk[k]);
+          P[k] *= a;
+          Z[k] = fmaf(P[k], dd.z * ck[k], Z[k]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    p.agg[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] =
+        make_float4(P[k], H[k], Z[k], 0.0f);
+}
+
+// State entering each segment (forward) and adjoint reaching each segment's
+// last state (backward), one lane per (padded channel row, state).
+__global__ __launch_bounds__(256) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= s.nchan_pad * kMaxState) return;
+  const int n = static_cast<int>(idx % kMaxState);
+  const int64_t row = idx / kMaxState;
+  const int64_t per_b = static_cast<int64_t>(s.tiles) * kBwdCh;
+  const int b = static_cast<int>(row / per_b);
+  const int d = static_cast<int>(row % per_b);
+  const bool active = d < s.dim && n < s.dstate;
+  const int64_t sstride = s.nchan_pad * kMaxState;
+  float h = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+  p.carry_h[idx] = h;
+  for (int sgm = 0; sgm + 1 < s.nseg; ++sgm) {
+    const float4 a = p.agg[sgm * sstride + idx];
+    h = fmaf(a.x, h, a.y);
+    p.carry_h[(sgm + 1) * sstride + idx] = h;
+  }
+  float g = (active && p.dfinal != nullptr) ? p.dfinal[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+  p.carry_g[(s.nseg - 1) * sstride + idx] = g;
+  for (int sgm = s.nseg - 1; sgm > 0; --sgm) {
+    const float4 a = p.agg[sgm * sstride + idx];
+    g = fmaf(a.x, g, a.z);
+    p.carry_g[(sgm - 1) * sstride + idx] = g;
+  }
+}
+
 // ---------------------------------------------------------------- pass 1 ---
 template <typename IO>
 __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
@@ -84,7 +208,9 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   const int lane = threadIdx.x;
   const int64_t groups8 = static_cast<int64_t>(s.tiles) * kBwdWaves;  // 8-channel groups per row
   const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
-  const int b = static_cast<int>(logical / groups8);
+  const int64_t row_seg = logical / groups8;
+  const int b = static_cast<int>(row_seg / s.nseg);
+  const int seg = static_cast<int>(row_seg % s.nseg);
   const int dg = static_cast<int>(logical % groups8) * kCh;  // first channel of the wave
   const int sg = lane >> 3, sc = lane & 7;
   const int d = dg + sc;
@@ -96,13 +222,18 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
     const int n = 2 * sg + k;
     const bool active = dvalid && n < s.dstate;
     A2[k] = active ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e : 0.0f;
-    h[k] = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+    if (s.nseg > 1)
+      h[k] = p.carry_h[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + n];
+    else
+      h[k] = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
   }
+  const int q_begin = seg * s.seg_chunks;
+  const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
   const IO* Bm = static_cast<const IO*>(p.B);
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dr = static_cast<const IO*>(p.delta_raw);
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
-  for (int q = 0; q < s.nchunk; ++q) {
+  for (int q = q_begin; q < q_end; ++q) {
     const int t0 = q * kBwdT;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
@@ -155,7 +286,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   const int w = tid >> 6, lane = tid & 63;
   const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
   const int tile = static_cast<int>(logical % s.tiles);
-  const int b = static_cast<int>(logical / s.tiles);
+  const int64_t row_seg = logical / s.tiles;
+  const int b = static_cast<int>(row_seg / s.nseg);
+  const int seg = static_cast<int>(row_seg % s.nseg);
   const int d0 = tile * kBwdCh + w * kCh;  // this wave's first channel
   const int sg = lane >> 3, sc = lane & 7;
   const int d = d0 + sc;
@@ -180,10 +313,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     const bool active = dvalid && n < s.dstate;
     An[k] = active ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) : 0.0f;
     A2[k] = An[k] * kLog2e;
-    g[k] = (active && p.dfinal != nullptr)
-               ? p.dfinal[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+    if (s.nseg > 1)
+      g[k] = p.carry_g[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + n];
+    else
+      g[k] = (active && p.dfinal != nullptr)
+                 ? p.dfinal[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
     dA[k] = 0.0f;
   }
+  const int q_begin = seg * s.seg_chunks;
+  const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
   // element roles: lane (c, j) = (lane % 8, lane / 8) owns steps 2j, 2j+1 of
   // channel c (the same channel as its scan role)
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
@@ -192,7 +330,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
 
   float* el = s_el[w];
   float* gr = s_gr[w];
-  for (int q = s.nchunk - 1; q >= 0; --q) {
+  for (int q = q_end - 1; q >= q_begin; --q) {
     const int t0 = q * kBwdT;
     // ---- E: B and C of the chunk (one value per thread) ----
     {
@@ -346,13 +484,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   }
 
   // ---- per (row, channel) results ----
-  const int64_t prow = (static_cast<int64_t>(b) * s.dim + d) * (kMaxState + 2);
+  const int64_t prow = ((static_cast<int64_t>(seg) * s.batch + b) * s.dim + d) * (kMaxState + 2);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int n = 2 * sg + k;
     if (dvalid && n < s.dstate) {
       p.part_chan[prow + n] = dA[k] * An[k];
-      if (p.dh0 != nullptr) p.dh0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] = g[k];
+      if (p.dh0 != nullptr && seg == 0)
+        p.dh0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] = g[k];
     }
   }
   // dD and ddt_bias: the 8 lanes of a channel (lanes c + 8j) meet in LDS
@@ -404,7 +543,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
   const int j = static_cast<int>(i % (kMaxState + 2));
   if (j < kMaxState && j >= s.dstate) return;
   float sum = 0.0f;
-  for (int b = 0; b < s.batch; ++b) sum += p.part_chan[(static_cast<int64_t>(b) * s.dim + d) * (kMaxState + 2) + j];
+  for (int r = 0; r < s.nseg * s.batch; ++r)
+    sum += p.part_chan[(static_cast<int64_t>(r) * s.dim + d) * (kMaxState + 2) + j];
   if (j < kMaxState)
     p.dA_log[static_cast<int64_t>(d) * s.dstate + j] = sum;
   else if (j == kMaxState) {
@@ -416,9 +556,14 @@ __global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
 
 template <typename IO>
 hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream) {
-  const int64_t waves = static_cast<int64_t>(s.batch) * s.tiles * kBwdWaves;
+  const int64_t waves = static_cast<int64_t>(s.batch) * s.nseg * s.tiles * kBwdWaves;
+  if (s.nseg > 1) {
+    agg_kernel<IO><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+    const int64_t nc = s.nchan_pad * kMaxState;
+    carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
+  }
   ckpt_kernel<IO><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
-  const int64_t wgs = static_cast<int64_t>(s.batch) * s.tiles;
+  const int64_t wgs = static_cast<int64_t>(s.batch) * s.nseg * s.tiles;
   bwd_kernel<IO><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
   const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * s.dstate * s.seqlen;
   reduce_bc_kernel<IO><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream>>>(s, p);

@@ -117,6 +117,32 @@ def test_optional_inputs(mss, flags):
     _run_and_check(mss, f"{flags}", _problem(2, 96, 150, 16, **flags), softplus=softplus)
 
 
+@pytest.mark.parametrize("shape", [(1, 64, 2000), (1, 200, 1500), (3, 40, 999)])
+def test_time_segments(mss, shape):
+    # few channels and long sequences: the backward splits time into segments
+    # joined by forward state carries and backward adjoint carries
+    batch, dim, seqlen = shape
+    _run_and_check(mss, f"segments {shape}", _problem(batch, dim, seqlen, 16, h0=True,
+                                                      dfinal=True, a_log="normal"))
+
+
+def test_long_sequence(mss):
+    """The 32k-token sequence length at 384 channels (a time-split backward with
+    many segments): every gradient against the oracle, element by element."""
+    import torch
+    w = WORKLOADS["long_handoff"]
+    dx = _problem(w.batch, 384, w.seqlen, w.dstate, dfinal=True)
+    note(f"bwd long shape: B={w.batch} D=384 L={w.seqlen}")
+    got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                 dx["dout"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                 dfinal_state=dx["dfinal"])
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dx["dout"],
+                          D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], dfinal=dx["dfinal"])
+    for k, v in got.items():
+        check(f"bwd long {k}", to_np(v), ref[ORACLE_NAME[k]], TOL["f32"])
+
+
 def test_random_a_log(mss):
     _run_and_check(mss, "A_log~N(0,1)", _problem(1, 128, 300, 16, a_log="normal", h0=True))
 
