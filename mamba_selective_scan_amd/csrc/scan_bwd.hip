@@ -55,7 +55,7 @@ constexpr int kXcdsBwd = 8;
 // fall in distinct bank groups.
 constexpr int kElPitch = kBwdT * 4 + 4;  // s_el[c][t] = (delta, delta*u, dy, y_ssm)
 constexpr int kBcPitch = kBwdT + 4;      // s_bc[r][t]: r < 16 B_r, r >= 16 C_(r-16)
-constexpr int kGrPitch = kBwdT * 2 + 4;  // s_gr[c][t] = (d(delta*u), ddelta via a)
+constexpr int kGrPitch = kBwdT * 8 + 4;  // s_gr[c][t] = (u, sigmoid(x), dout, z, d(delta*u), ddelta via a, -, -)
 constexpr int kDdPitch2 = kBwdT * 2 + 4; // ckpt pass: s_dd[c][t] = (delta, delta*u)
 
 struct f4 {
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
 
 // ---------------------------------------------------------------- pass 2 ---
 template <typename IO>
-__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
   __shared__ __attribute__((aligned(16))) float s_el[kBwdWaves][kCh * kElPitch];
   __shared__ __attribute__((aligned(16))) float s_gr[kBwdWaves][kCh * kGrPitch];
@@ -341,20 +341,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
                                 : ld(Cm + b * s.sC[0] + n * s.sC[1] + t * s.sC[2]);
       s_bc[r * kBcPitch + tt] = v;
     }
-    // ---- E: per element ----
-    float eu[2], edl[2], edy[2], esig[2], edo[2], ez[2];
+    // ---- E: per element (lane (c, j) = (lane % 8, lane / 8) owns steps 2j,
+    // 2j+1 of channel c): the scan's inputs go to s_el, the values the output
+    // phase needs to s_gr ----
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
-      eu[e] = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
+      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
       const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
-      edo[e] = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + t * s.sdo[2]) : 0.0f;
-      ez[e] = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + t * s.sz[2]) : 0.0f;
-      edl[e] = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
-      esig[e] = s.softplus ? sigmoid(x) : 1.0f;
-      edy[e] = has_z ? edo[e] * silu(ez[e]) : edo[e];
-      *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{edl[e], edl[e] * eu[e], edy[e], 0.0f};
+      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + t * s.sdo[2]) : 0.0f;
+      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + t * s.sz[2]) : 0.0f;
+      const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      const float sig = s.softplus ? sigmoid(x) : 1.0f;
+      const float dy = has_z ? go * silu(zv) : go;
+      *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{dl, dl * uu, dy, 0.0f};
+      *reinterpret_cast<f4*>(gr + sc * kGrPitch + 8 * tt) = f4{uu, sig, go, zv};
     }
     __syncthreads();
 
@@ -373,53 +375,41 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     const int ystep = group_step(lane);
 #pragma unroll
     for (int t4 = 0; t4 < kBwdT; t4 += 4) {
-      const f4 b0 = ld4(rb0 + t4), b1 = ld4(rb1 + t4), c0 = ld4(rc0 + t4), c1 = ld4(rc1 + t4);
       float yp[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f4 dd = ld4(rdd + 4 * (t4 + i));
-        h[0] = fmaf(fast_exp2(dd.x * A2[0]), h[0], dd.y * f4_at(b0, i));
-        h[1] = fmaf(fast_exp2(dd.x * A2[1]), h[1], dd.y * f4_at(b1, i));
-        hh[t4 + i][0] = h[0];
-        hh[t4 + i][1] = h[1];
-        yp[i] = fmaf(f4_at(c1, i), h[1], f4_at(c0, i) * h[0]);
+        const int t = t4 + i;
+        const f4 dd = ld4(rdd + 4 * t);
+        h[0] = fmaf(fast_exp2(dd.x * A2[0]), h[0], dd.y * rb0[t]);
+        h[1] = fmaf(fast_exp2(dd.x * A2[1]), h[1], dd.y * rb1[t]);
+        hh[t][0] = h[0];
+        hh[t][1] = h[1];
+        yp[i] = fmaf(rc1[t], h[1], rc0[t] * h[0]);
       }
       el[sc * kElPitch + 4 * (t4 + ystep) + 3] = reduce_groups(yp[0], yp[1], yp[2], yp[3]);
     }
     __builtin_amdgcn_wave_barrier();
-    // dz = dout * (C.h + D u) * silu'(z)
-    if (has_z && dz_out != nullptr) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int tt = 2 * sg + e, t = t0 + tt;
-        if (dvalid && t < s.seqlen) {
-          const float y = el[sc * kElPitch + 4 * tt + 3] + skip * eu[e];
-          const float sz = sigmoid(ez[e]);
-          const float dsilu = sz * fmaf(ez[e], 1.0f - sz, 1.0f);
-          io_traits<IO>::store(dz_out + b * s.sdz[0] + d * s.sdz[1] + t * s.sdz[2],
-                               edo[e] * y * dsilu);
-        }
-      }
-    }
-
     // ---- R: reverse walk ----
+    // Per step the sums over the wave's 8 channels of the dB and dC terms are
+    // finished at once (one DPP tree each) and written by lane c = 0 of each
+    // state group; the sums over states collect 4 steps for one cross-lane tree.
+    float* red = s_red[w];
 #pragma unroll
     for (int t4 = kBwdT - 4; t4 >= 0; t4 -= 4) {
-      const f4 b0 = ld4(rb0 + t4), b1 = ld4(rb1 + t4), c0 = ld4(rc0 + t4), c1 = ld4(rc1 + t4);
-      float qb[4], qa[4], pb0[4], pb1[4], pc0[4], pc1[4];
+      float qb[4], qa[4];
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         const int t = t4 + i;
         const f4 dd = ld4(rdd + 4 * t);
-        const float bk[2] = {f4_at(b0, i), f4_at(b1, i)};
-        const float ck[2] = {f4_at(c0, i), f4_at(c1, i)};
+        const float bk[2] = {rb0[t], rb1[t]};
+        const float ck[2] = {rc0[t], rc1[t]};
         float sb = 0.0f, sa = 0.0f;
         float pb[2], pc[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const float G = fmaf(dd.z, ck[k], g[k]);
-          pc[k] = dd.z * hh[t][k];
-          pb[k] = G * dd.y;
+          pc[k] = sum_half_rows(dd.z * hh[t][k]);
+          pb[k] = sum_half_rows(G * dd.y);
           sb = fmaf(G, bk[k], sb);
           const float a = fast_exp2(dd.x * A2[k]);
           const float hp = t > 0 ? hh[t > 0 ? t - 1 : 0][k] : hs[k];
@@ -430,30 +420,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
         }
         qb[i] = sb;
         qa[i] = sa;
-        pb0[i] = pb[0];
-        pb1[i] = pb[1];
-        pc0[i] = pc[0];
-        pc1[i] = pc[1];
+        if (sc == 0) {
+          red[(2 * sg) * kBwdT + t] = pb[0];
+          red[(2 * sg + 1) * kBwdT + t] = pb[1];
+          red[(kMaxState + 2 * sg) * kBwdT + t] = pc[0];
+          red[(kMaxState + 2 * sg + 1) * kBwdT + t] = pc[1];
+        }
       }
       const float gb = reduce_groups(qb[0], qb[1], qb[2], qb[3]);
       const float ga = reduce_groups(qa[0], qa[1], qa[2], qa[3]);
-      *reinterpret_cast<float2*>(gr + sc * kGrPitch + 2 * (t4 + ystep)) = make_float2(gb, ga);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb0[i] = sum_half_rows(pb0[i]);
-        pb1[i] = sum_half_rows(pb1[i]);
-        pc0[i] = sum_half_rows(pc0[i]);
-        pc1[i] = sum_half_rows(pc1[i]);
-      }
-      if (sc == 0) {
-        float* red = s_red[w];
-        *reinterpret_cast<f4*>(red + (2 * sg) * kBwdT + t4) = f4{pb0[0], pb0[1], pb0[2], pb0[3]};
-        *reinterpret_cast<f4*>(red + (2 * sg + 1) * kBwdT + t4) = f4{pb1[0], pb1[1], pb1[2], pb1[3]};
-        *reinterpret_cast<f4*>(red + (kMaxState + 2 * sg) * kBwdT + t4) =
-            f4{pc0[0], pc0[1], pc0[2], pc0[3]};
-        *reinterpret_cast<f4*>(red + (kMaxState + 2 * sg + 1) * kBwdT + t4) =
-            f4{pc1[0], pc1[1], pc1[2], pc1[3]};
-      }
+      *reinterpret_cast<float2*>(gr + sc * kGrPitch + 8 * (t4 + ystep) + 4) = make_float2(gb, ga);
     }
     __syncthreads();
 
@@ -467,18 +443,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
         p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t] = sum;
     }
 
-    // ---- O: du and ddelta_raw per element ----
+    // ---- O: du, ddelta_raw and dz per element ----
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
-      const float2 v = *reinterpret_cast<const float2*>(gr + sc * kGrPitch + 2 * tt);
-      const float du = fmaf(edy[e], skip, edl[e] * v.x);
-      const float ddr = fmaf(eu[e], v.x, v.y) * esig[e];
+      const f4 sv = ld4(el + sc * kElPitch + 4 * tt);      // delta, delta*u, dy, C.h
+      const f4 ev = ld4(gr + sc * kGrPitch + 8 * tt);      // u, sigmoid(x), dout, z
+      const float2 gv = *reinterpret_cast<const float2*>(gr + sc * kGrPitch + 8 * tt + 4);
+      const float du = fmaf(sv.z, skip, sv.x * gv.x);
+      const float ddr = fmaf(ev.x, gv.x, gv.y) * ev.y;
       if (dvalid && t < s.seqlen) {
         io_traits<IO>::store(du_out + b * s.sdu[0] + d * s.sdu[1] + t * s.sdu[2], du);
         io_traits<IO>::store(ddr_out + b * s.sddr[0] + d * s.sddr[1] + t * s.sddr[2], ddr);
+        if (has_z && dz_out != nullptr) {
+          // dz = dout * (C.h + D u) * silu'(z), silu'(z) = sig(z) (1 + z (1 - sig(z)))
+          const float y = fmaf(skip, ev.x, sv.w);
+          const float sz = sigmoid(ev.w);
+          io_traits<IO>::store(dz_out + b * s.sdz[0] + d * s.sdz[1] + t * s.sdz[2],
+                               ev.z * y * (sz * fmaf(ev.w, 1.0f - sz, 1.0f)));
+        }
         acc_db += ddr;
-        acc_dD = fmaf(edy[e], eu[e], acc_dD);
+        acc_dD = fmaf(sv.z, ev.x, acc_dD);
       }
     }
   }
