@@ -59,18 +59,23 @@ def valu_slots_per_element(dstate: int, softplus: bool = True, has_z: bool = Tru
     if has_z:
         n += 11 + 1
     return n
-KERNEL_SOURCES = ["mamba_selective_scan_amd/csrc/scan_fwd.hip",
-                  "mamba_selective_scan_amd/csrc/mss_device.hpp",
-                  "mamba_selective_scan_amd/csrc/mss_internal.hpp"]
+KERNEL_SOURCES = {
+    "scan": ["mamba_selective_scan_amd/csrc/scan_fwd.hip",
+             "mamba_selective_scan_amd/csrc/mss_device.hpp",
+             "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
+    "conv1d": ["mamba_selective_scan_amd/csrc/conv1d.hip",
+               "mamba_selective_scan_amd/csrc/mss_device.hpp",
+               "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(op: str = "scan") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[op]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -85,8 +90,8 @@ def step_bytes(batch, dim, dstate, io_bytes) -> int:
     return n
 
 
-def load_traffic(workload: str, io: str, src_hash: str):
-    path = os.path.join(ROOT, "profiles", f"traffic_scan_{workload}_{io}.json")
+def load_traffic(workload: str, io: str, src_hash: str, op: str = "scan"):
+    path = os.path.join(ROOT, "profiles", f"traffic_{op}_{workload}_{io}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -231,6 +236,8 @@ def main_conv(args):
     step_b = 0 if args.no_step else (2 * w.batch * w.dim * (width - 1) * io_bytes
                                      + 2 * w.batch * w.dim * io_bytes + w.dim * (width + 1) * 4)
     achieved = fwd_bytes / (mean_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash("conv1d")
+    traffic = load_traffic(w.name, args.io, src_hash, op="conv1d")
     log(f"step {ms_per_step:.4f} ms; conv fwd mean {mean_ms * 1e3:.1f} us (min {ms[0] * 1e3:.1f}); "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s")
     rec = {
@@ -258,10 +265,11 @@ def main_conv(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_bytes": fwd_bytes,
             "event_us_mean": round(mean_ms * 1e3, 2),
             "event_us_median": round(ms[len(ms) // 2] * 1e3, 2),
+            "kernel_source_hash": src_hash,
         },
         "cpu_baseline": None,
     }
@@ -532,6 +540,10 @@ def main(argv=None):
             "traffic": traffic,
             "algorithmic_slots": fwd_slots,
             "slots_per_element": valu_slots_per_element(w.dstate),
+            # every VALU instruction one slot (a transcendental mixed with FMAs
+            # measures at about one FMA issue slot): 5 per state-step + 19
+            "frac_one_slot_per_instruction": round(
+                w.elems * (5 * w.dstate + 19) / (scan_ms_mean * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
             "hbm": {
                 "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS,
