@@ -1,7 +1,10 @@
 /*
  * mss.h -- C ABI of libmss, the MI355X (gfx950) Mamba selective-scan library.
  *
- * Five operations:
+ * Five operations.  The scan forward and backward can also run in reverse
+ * time (mss_scan_args.reverse), the second direction of a bidirectional
+ * layer (SpeechLens kernel-optimization notes, the bidirectional variant in
+ * its rejected-fusion list):
  *
  *  1. mss_selective_scan_fwd: the selective-scan forward over whole sequences.
  *     For every channel (b, d) and time step t, with n over the dstate
@@ -100,7 +103,7 @@
 extern "C" {
 #endif
 
-#define MSS_ABI_VERSION 1
+#define MSS_ABI_VERSION 2
 #define MSS_MAX_DSTATE 16
 #define MSS_MAX_CONV_WIDTH 4
 
@@ -160,7 +163,10 @@ typedef struct mss_scan_args {
     float *final_state;          /* [b,d,n] fp32 contiguous h_{L-1}; NULL: not written   */
 
     int32_t delta_softplus;      /* nonzero: delta = softplus(delta_raw + dt_bias)       */
-    int32_t reserved0;           /* must be 0                                            */
+    int32_t reverse;             /* 0: forward in time.  1: reverse time, logical step   */
+                                 /* tau reads and writes storage step seqlen-1-tau (the  */
+                                 /* backward half of a bidirectional layer, no copies);  */
+                                 /* final_state is then the state after storage step 0   */
 
     void *workspace;             /* device scratch, 256-byte aligned, of at least        */
     size_t workspace_bytes;      /* mss_selective_scan_workspace_size bytes (may be 0)   */
@@ -268,7 +274,8 @@ typedef struct mss_scan_bwd_args {
     const float *dt_bias;        /* [d] fp32 contiguous; NULL means 0                    */
     const float *initial_state;  /* [b,d,n] fp32 contiguous; NULL means 0                */
     int32_t delta_softplus;
-    int32_t reserved0;           /* must be 0                                            */
+    int32_t reverse;             /* 0 or 1, as in mss_scan_args: the backward of the     */
+                                 /* reverse-time forward                                 */
 
     const void *dout;            /* [b,d,t] dLoss/dout                                   */
     int64_t dout_stride[3];

@@ -97,7 +97,7 @@ def _stream_handle(device):
 
 
 def _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
-               delta_softplus):
+               delta_softplus, reverse=False):
     torch = _torch()
     dev = u.device
     _need(u, "u", 3)
@@ -136,6 +136,7 @@ def _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, fin
     a.out, a.out_stride = _ptr(out), _strides(out, 3)
     a.final_state = _ptr(final_state)
     a.delta_softplus = 1 if delta_softplus else 0
+    a.reverse = 1 if reverse else 0
     return a
 
 
@@ -153,8 +154,11 @@ def scan_workspace_size(u, A_log) -> int:
 
 def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
                        delta_softplus=True, initial_state=None, return_final_state=False,
-                       out=None, final_state=None, workspace=None):
+                       out=None, final_state=None, workspace=None, reverse=False):
     """Selective-scan forward on u's device, ordered on torch's current stream.
+
+    ``reverse=True`` runs the recurrence from the last step to the first (the
+    second direction of a bidirectional layer) on the same buffers.
 
     Returns ``out`` (shape and layout of u), or ``(out, final_state)`` with the
     fp32 state [B, D, N] after the last step when ``return_final_state``.
@@ -171,7 +175,7 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
     if final_state is not None:
         _contig_f32(final_state, "final_state", (u.shape[0], u.shape[1], A_log.shape[1]), u.device)
     a = _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
-                   delta_softplus)
+                   delta_softplus, reverse)
     if tuple(out.shape) != tuple(u.shape) or out.dtype != u.dtype or out.device != u.device:
         raise ValueError("out must match u in shape, dtype and device")
     st = ctypes.c_int(0)
@@ -358,18 +362,19 @@ def scan_bwd_workspace_size(u, A_log) -> int:
 
 def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=None, *,
                        delta_softplus=True, initial_state=None, dfinal_state=None,
-                       workspace=None):
+                       workspace=None, reverse=False):
     """Backward of selective_scan_fwd, ordered on torch's current stream.
 
     dout has u's shape and dtype; dfinal_state [B, D, N] fp32 (optional) is the
     gradient reaching the exported final state.  Returns a dict with du,
     ddelta_raw, dB, dC (dtype of u, shapes of the inputs), dA_log [D, N] fp32,
     and dD, dz, ddt_bias, dinitial_state for the optional inputs that are given.
+    ``reverse`` must match the forward's.
     """
     torch = _torch()
     lib = _lib.lib()
     a = _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, None, None,
-                   delta_softplus)
+                   delta_softplus, reverse)
     dev = u.device
     _need(dout, "dout", 3, u.dtype, dev)
     if tuple(dout.shape) != tuple(u.shape):

@@ -13,7 +13,7 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmss.so")
 
-MSS_ABI_VERSION = 1
+MSS_ABI_VERSION = 2
 MSS_MAX_DSTATE = 16
 MSS_MAX_CONV_WIDTH = 4
 MSS_F32 = 0
@@ -61,7 +61,7 @@ class ScanArgs(ctypes.Structure):
         ("initial_state", _vp),
         ("out", _vp), ("out_stride", _i64 * 3),
         ("final_state", _vp),
-        ("delta_softplus", _i32), ("reserved0", _i32),
+        ("delta_softplus", _i32), ("reverse", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -97,7 +97,7 @@ class ScanBwdArgs(ctypes.Structure):
         ("z", _vp), ("z_stride", _i64 * 3),
         ("dt_bias", _vp),
         ("initial_state", _vp),
-        ("delta_softplus", _i32), ("reserved0", _i32),
+        ("delta_softplus", _i32), ("reverse", _i32),
         ("dout", _vp), ("dout_stride", _i64 * 3),
         ("dfinal_state", _vp),
         ("du", _vp), ("du_stride", _i64 * 3),

@@ -92,7 +92,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int vec_elems(int32_t) { return mss::kVec; }
 
 mss_status check_shape(const mss_scan_args* a) {
-  if (a == nullptr || a->struct_size != sizeof(mss_scan_args) || a->reserved0 != 0)
+  if (a == nullptr || a->struct_size != sizeof(mss_scan_args) || (a->reverse & ~1) != 0)
     return MSS_ERR_BAD_STRUCT;
   if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
   if (a->batch < 1 || a->dim < 1 || a->seqlen < 1) return MSS_ERR_BAD_SHAPE;
@@ -123,6 +123,7 @@ ScanPlan make_plan(const mss_scan_args* a) {
   s.nseg = static_cast<int>((a->seqlen + s.seg_len - 1) / s.seg_len);
   s.nchan_pad = tiles * kCh;
   s.softplus = a->delta_softplus ? 1 : 0;
+  s.reverse = a->reverse;
   s.t_first = 0;
   s.t_stop = s.seqlen;
   if (s.nseg > 1) {
@@ -163,7 +164,7 @@ constexpr int64_t kBwdSplitBelow = 512;
 constexpr int64_t kBwdMinSegChunks = 8;
 
 mss_status check_bwd_shape(const mss_scan_bwd_args* a) {
-  if (a == nullptr || a->struct_size != sizeof(mss_scan_bwd_args) || a->reserved0 != 0)
+  if (a == nullptr || a->struct_size != sizeof(mss_scan_bwd_args) || (a->reverse & ~1) != 0)
     return MSS_ERR_BAD_STRUCT;
   if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
   if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->batch > kMaxDim || a->dim > kMaxDim ||
@@ -187,6 +188,7 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
   s.nchunk = static_cast<int>((a->seqlen + mss::kBwdT - 1) / mss::kBwdT);
   s.tiles = static_cast<int>((a->dim + mss::kBwdCh - 1) / mss::kBwdCh);
   s.nchan_pad = a->batch * s.tiles * mss::kBwdCh;
+  s.reverse = a->reverse;
   const int64_t pairs = a->batch * s.tiles;
   int64_t nseg = 1;
   if (pairs < kBwdSplitBelow)
@@ -342,6 +344,9 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
     const void* bps[2] = {a->B, a->C};
     for (int i = 0; i < 2; ++i)
       if (!aligned(bps[i], 4) || !even(bsts[i][0]) || !even(bsts[i][bt ? 1 : 2])) s.vec_ok = 0;
+    // in reverse time a t-fast vector starts at storage step seqlen-4-tau:
+    // 4-byte aligned only for an even length
+    if (a->reverse && (xt || bt) && (a->seqlen % 2) != 0) s.vec_ok = 0;
   }
   p.u = a->u;
   p.delta_raw = a->delta_raw;

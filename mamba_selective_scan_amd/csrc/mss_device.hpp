@@ -107,10 +107,12 @@ __device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
 // Sum of v over the 8 lanes of each 8-lane group (a half row, lanes 8g..8g+7),
 // left in every lane of the group: the lane pairs (i, 7-i), then (i, i^2),
 // then (i, i^1) are added with DPP row_half_mirror and quad permutations.
+// Every source lane is valid for these patterns; bound_ctrl lets the compiler
+// fold each move into the add (v_add_f32_dpp).
 __device__ inline float sum_half_rows(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
   return v;
 }
 

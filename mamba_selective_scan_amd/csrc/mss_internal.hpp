@@ -36,6 +36,7 @@ struct ScanShape {
   int vec_ok;           // every kVec-element vector of u/delta_raw/z/out/B/C is 4-byte aligned
   int use_vec;          // the vector pass runs (else everything is element-wise)
   int t_first, t_stop;  // this pass covers time steps [t_first, t_stop)
+  int reverse;          // logical step tau is storage step seqlen-1-tau
 };
 
 struct StepShape {
@@ -143,6 +144,7 @@ struct BwdShape {
   int64_t sdu[3], sddr[3], sdz[3];          // du, ddelta_raw, dz
   int64_t sB[3], sC[3], sdB[3], sdC[3];     // (b, n, t)
   int64_t sA[2];                            // A_log: (d, n)
+  int reverse;                              // logical step tau is storage step seqlen-1-tau
 };
 
 struct BwdPtrs {

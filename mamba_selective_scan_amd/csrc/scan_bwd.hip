@@ -13,6 +13,8 @@
 //   dD = sum dy u,  ddt_bias = sum ddelta_raw,  dh0 = g after the first step.
 // The training backward is what the pages list as not yet written
 // ("mamba-metal: Apple Silicon で Mamba を動かす", section "残り課題").
+// Every kernel works in logical time; in reverse time (s.reverse) logical
+// step t reads and writes storage step L-1-t.
 //
 // Passes:
 //   0. (few channels, long sequences) the sequence is cut into time segments
@@ -73,6 +75,11 @@ __device__ inline float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
 }
 
+// Storage step of logical step t: mirrored when the scan runs in reverse time.
+__device__ inline int64_t tstore(const BwdShape& s, int t) {
+  return s.reverse ? static_cast<int64_t>(s.seqlen) - 1 - t : t;
+}
+
 __device__ inline int64_t xcd_order(int64_t lin, int64_t nwg) {
   const int64_t xcd = lin % kXcdsBwd;
   const int64_t per = nwg / kXcdsBwd, extra = nwg % kXcdsBwd;
@@ -127,19 +134,19 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     for (int i = 0; i < 4; ++i) {
       const int n = lane >> 2, tt = (lane & 3) * 4 + i, t = t0 + tt;
       const bool ok = n < s.dstate && t < s.seqlen;
-      s_bc[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + t * s.sB[2]) : 0.0f;
+      s_bc[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2]) : 0.0f;
       s_bc[(kMaxState + n) * kBcPitch + tt] =
-          ok ? ld(Cm + b * s.sC[0] + n * s.sC[1] + t * s.sC[2]) : 0.0f;
+          ok ? ld(Cm + b * s.sC[0] + n * s.sC[1] + tstore(s, t) * s.sC[2]) : 0.0f;
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
-      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
-      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
+      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2]) : 0.0f;
+      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2]) : 0.0f) + bias;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
-      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + t * s.sdo[2]) : 0.0f;
-      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + t * s.sz[2]) : 0.0f;
+      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + tstore(s, t) * s.sdo[2]) : 0.0f;
+      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + tstore(s, t) * s.sz[2]) : 0.0f;
       const float dy = has_z ? go * silu(zv) : go;
       *reinterpret_cast<f4*>(s_el + sc * kElPitch + 4 * tt) = f4{dl, dl * uu, dy, 0.0f};
     }
@@ -243,15 +250,15 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
     for (int i = 0; i < 4; ++i) {
       const int n = lane >> 2, tt = (lane & 3) * 4 + i, t = t0 + tt;
       const bool ok = n < s.dstate && t < s.seqlen;
-      s_b[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + t * s.sB[2]) : 0.0f;
+      s_b[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2]) : 0.0f;
     }
     // delta and delta*u: lane (c, j) covers steps 2j, 2j+1 of channel c
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
-      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
-      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
+      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2]) : 0.0f;
+      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2]) : 0.0f) + bias;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
       *reinterpret_cast<float2*>(s_dd + sc * kDdPitch2 + 2 * tt) = make_float2(dl, dl * uu);
     }
@@ -337,8 +344,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4, 
       const int r = tid >> 4, tt = tid & 15, n = r & 15, t = t0 + tt;
       const bool ok = n < s.dstate && t < s.seqlen;
       float v = 0.0f;
-      if (ok) v = r < kMaxState ? ld(Bm + b * s.sB[0] + n * s.sB[1] + t * s.sB[2])
-                                : ld(Cm + b * s.sC[0] + n * s.sC[1] + t * s.sC[2]);
+      if (ok) v = r < kMaxState ? ld(Bm + b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2])
+                                : ld(Cm + b * s.sC[0] + n * s.sC[1] + tstore(s, t) * s.sC[2]);
       s_bc[r * kBcPitch + tt] = v;
     }
     // ---- E: per element (lane (c, j) = (lane % 8, lane / 8) owns steps 2j,
@@ -348,10 +355,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4, 
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
-      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + t * s.su[2]) : 0.0f;
-      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + t * s.sd[2]) : 0.0f) + bias;
-      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + t * s.sdo[2]) : 0.0f;
-      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + t * s.sz[2]) : 0.0f;
+      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2]) : 0.0f;
+      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2]) : 0.0f) + bias;
+      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + tstore(s, t) * s.sdo[2]) : 0.0f;
+      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + tstore(s, t) * s.sz[2]) : 0.0f;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
       const float sig = s.softplus ? sigmoid(x) : 1.0f;
       const float dy = has_z ? go * silu(zv) : go;
@@ -453,13 +460,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4, 
       const float du = fmaf(sv.z, skip, sv.x * gv.x);
       const float ddr = fmaf(ev.x, gv.x, gv.y) * ev.y;
       if (dvalid && t < s.seqlen) {
-        io_traits<IO>::store(du_out + b * s.sdu[0] + d * s.sdu[1] + t * s.sdu[2], du);
-        io_traits<IO>::store(ddr_out + b * s.sddr[0] + d * s.sddr[1] + t * s.sddr[2], ddr);
+        io_traits<IO>::store(du_out + b * s.sdu[0] + d * s.sdu[1] + tstore(s, t) * s.sdu[2], du);
+        io_traits<IO>::store(ddr_out + b * s.sddr[0] + d * s.sddr[1] + tstore(s, t) * s.sddr[2], ddr);
         if (has_z && dz_out != nullptr) {
           // dz = dout * (C.h + D u) * silu'(z), silu'(z) = sig(z) (1 + z (1 - sig(z)))
           const float y = fmaf(skip, ev.x, sv.w);
           const float sz = sigmoid(ev.w);
-          io_traits<IO>::store(dz_out + b * s.sdz[0] + d * s.sdz[1] + t * s.sdz[2],
+          io_traits<IO>::store(dz_out + b * s.sdz[0] + d * s.sdz[1] + tstore(s, t) * s.sdz[2],
                                ev.z * y * (sz * fmaf(ev.w, 1.0f - sz, 1.0f)));
         }
         acc_db += ddr;
@@ -515,9 +522,9 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
   for (int tile = 0; tile < s.tiles; ++tile)
     sum += p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t];
   if (is_c)
-    io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + t * s.sdC[2], sum);
+    io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + tstore(s, t) * s.sdC[2], sum);
   else
-    io_traits<IO>::store(static_cast<IO*>(p.dB) + b * s.sdB[0] + n * s.sdB[1] + t * s.sdB[2], sum);
+    io_traits<IO>::store(static_cast<IO*>(p.dB) + b * s.sdB[0] + n * s.sdB[1] + tstore(s, t) * s.sdB[2], sum);
 }
 
 // ---------------------------------------------------------------- pass 4 ---

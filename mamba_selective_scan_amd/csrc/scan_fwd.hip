@@ -31,6 +31,13 @@
 // Every phase is wave-local: there is no workgroup barrier, so waves drift
 // apart and memory waits of one wave overlap the recurrence of others.
 //
+// Reverse time (REV): logical step tau reads and writes storage step L-1-tau,
+// so a backward-direction scan (one half of a bidirectional layer) runs on
+// the caller's buffers without a flipped copy.  A chunk's descriptor then
+// sits at storage step L-kT-t0 and every time offset inside the chunk is
+// mirrored; a 4-step vector along t is loaded whole and its elements taken in
+// the opposite order.
+//
 // Long sequences with few channels are split into time segments so that the
 // grid covers the GPU.  Segment s needs the state entering it.  A first pass
 // (AGG) runs every segment but the last from a zero state and records, per
@@ -139,7 +146,7 @@ __device__ inline f4 lds_f4(const float* p) { return *reinterpret_cast<const f4*
 template <typename IO, bool VEC, bool XT, bool BT>
 constexpr int kWavesPerSimd = (VEC && (XT || BT || sizeof(IO) == 2)) ? 5 : 4;
 
-template <typename IO, bool XT, bool BT, bool AGG, bool VEC>
+template <typename IO, bool XT, bool BT, bool AGG, bool VEC, bool REV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     kWavesPerSimd<IO, VEC, XT, BT>, 8))) void scan_kernel(
     ScanShape s, const IO* __restrict__ u, const IO* __restrict__ delta_raw,
@@ -211,8 +218,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int xb = XT ? lane & 7 : lane & 1;
   auto x_c = [&](int j) __attribute__((always_inline)) { return XT ? xa : 4 * xb + j; };
   auto x_t = [&](int j) __attribute__((always_inline)) { return XT ? 4 * xb + j : xa; };
+  // Time offset of a lane's first x element inside a chunk (mirrored in
+  // reverse time: for t-fast vectors the storage start of the vector).
+  const int x_toff = REV ? (XT ? kT - kVec - 4 * xb : kT - 1 - xa) : x_t(0);
   auto x_voff = [&](const int64_t* st) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>((x_c(0) * st[1] + x_t(0) * st[2]) * es);
+    return static_cast<uint32_t>((x_c(0) * st[1] + x_toff * st[2]) * es);
+  };
+  // Offset of element j from the lane's first element, for element-wise access.
+  auto x_eoff = [&](const int64_t* st, int j) __attribute__((always_inline)) -> uint32_t {
+    return static_cast<uint32_t>((XT ? (REV ? kVec - 1 - j : j) * st[2] : j * st[1]) * es);
+  };
+  // A t-fast vector read in reverse time holds its steps in the opposite order.
+  auto mirror4 = [&](float* v) __attribute__((always_inline)) {
+    if constexpr (REV) {
+      const float a0 = v[0], a1 = v[1];
+      v[0] = v[3];
+      v[1] = v[2];
+      v[2] = a1;
+      v[3] = a0;
+    }
   };
   // B/C: instruction i (0, 1: B; 2, 3: C) of a lane covers, for t-fast B/C,
   // state (lane / 8) + 8(i % 2) at steps 4(lane % 8)..+3, and for n-fast B/C
@@ -225,11 +249,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   auto bc_tt = [&](int i, int j) __attribute__((always_inline)) {
     return BT ? 4 * bb + j : ba + 16 * (i & 1);
   };
+  // In reverse time the n-fast lanes' steps ba and ba + 16 sit at storage
+  // offsets kT-1-ba and kT-17-ba: the vector offset takes the latter and the
+  // scalar offset adds 16 steps for the even instructions.
+  const int bc_toff = REV ? (BT ? kT - kVec - 4 * bb : kT - 17 - ba) : (BT ? 4 * bb : ba);
   auto bc_voff = [&](const int64_t* st) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>(((BT ? ba : 4 * bb) * st[1] + (BT ? 4 * bb : ba) * st[2]) * es);
+    return static_cast<uint32_t>(((BT ? ba : 4 * bb) * st[1] + bc_toff * st[2]) * es);
   };
   auto bc_soff = [&](const int64_t* st, int i) __attribute__((always_inline)) -> uint32_t {
-    return static_cast<uint32_t>((i & 1) * (BT ? 8 * st[1] : 16 * st[2]) * es);
+    if constexpr (BT) return static_cast<uint32_t>((i & 1) * 8 * st[1] * es);
+    return static_cast<uint32_t>((REV ? 1 - (i & 1) : (i & 1)) * 16 * st[2] * es);
+  };
+  auto bc_eoff = [&](const int64_t* st, int j) __attribute__((always_inline)) -> uint32_t {
+    return static_cast<uint32_t>((BT ? (REV ? kVec - 1 - j : j) * st[2] : j * st[1]) * es);
   };
 
   // Channel constants (dt_bias, D).  With t-fast data each lane's elements
@@ -248,11 +280,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   }
   const bool has_z = z != nullptr;
 
+  // Chunk descriptor base: storage step t0, or L-kT-t0 in reverse time (it may
+  // lie before the tensor; only in-range offsets are ever used).
   auto rsrc = [&](const void* ptr, const int64_t* st, int dd0, int t0,
                   int range = kRsrcRange) __attribute__((always_inline)) {
+    const int64_t ts = REV ? static_cast<int64_t>(s.seqlen) - kT - t0 : t0;
     const char* base = reinterpret_cast<const char*>(ptr) +
                        (static_cast<int64_t>(b) * st[0] + static_cast<int64_t>(dd0) * st[1] +
-                        static_cast<int64_t>(t0) * st[2]) * es;
+                        ts * st[2]) * es;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, range, kRsrcFlags);
   };
   // x_ok / b_ok: element j / B-C value (i, j) lies inside the tensors and the
@@ -283,11 +318,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const uint32_t vo = x_voff(st);
     if constexpr (VEC) {
       VIO::load(rs, x_ok(0, t0, lim) ? vo : kOffNone, 0, dst);
+      if constexpr (XT) mirror4(dst);
     } else {
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
-        const uint32_t off = x_ok(j, t0, lim)
-            ? vo + static_cast<uint32_t>(j * (XT ? st[2] : st[1]) * es) : kOffNone;
+        const uint32_t off = x_ok(j, t0, lim) ? vo + x_eoff(st, j) : kOffNone;
         dst[j] = VIO::load_one(rs, off, 0);
       }
     }
@@ -317,11 +352,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       float* dst = bcb + i * kVec;
       if constexpr (VEC) {
         VIO::load(rs, b_ok(i, 0, t0, lim) ? vo : kOffNone, bc_soff(st, i), dst);
+        if constexpr (BT) mirror4(dst);
       } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
-          const uint32_t off = b_ok(i, j, t0, lim)
-              ? vo + static_cast<uint32_t>(j * (BT ? st[2] : st[1]) * es) : kOffNone;
+          const uint32_t off = b_ok(i, j, t0, lim) ? vo + bc_eoff(st, j) : kOffNone;
           dst[j] = VIO::load_one(rs, off, bc_soff(st, i));
         }
       }
@@ -467,12 +502,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       const auto rs = rsrc(out, s.so, d0, t0);
       const uint32_t vo_o = x_voff(s.so);
       if constexpr (VEC) {
+        if constexpr (XT) mirror4(y);
         VIO::store(y, rs, x_ok(0, t0, t_end) ? vo_o : kOffNone, 0);
       } else {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-          const uint32_t off = x_ok(j, t0, t_end)
-              ? vo_o + static_cast<uint32_t>(j * (XT ? s.so[2] : s.so[1]) * es) : kOffNone;
+          const uint32_t off = x_ok(j, t0, t_end) ? vo_o + x_eoff(s.so, j) : kOffNone;
           VIO::store_one(y[j], rs, off, 0);
         }
       }
@@ -555,7 +590,7 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanShape s, const float2* _
   }
 }
 
-template <typename IO, bool XT, bool BT, bool VEC>
+template <typename IO, bool XT, bool BT, bool VEC, bool REV>
 static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, float* final_state,
                         hipStream_t stream) {
   const dim3 block(kThreads);
@@ -567,36 +602,43 @@ static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, 
   const IO* z = static_cast<const IO*>(p.z);
   IO* out = static_cast<IO*>(p.out);
   if (s.nseg > 1) {
-    scan_kernel<IO, XT, BT, true, VEC><<<dim3(G, s.nseg - 1), block, 0, stream>>>(
+    scan_kernel<IO, XT, BT, true, VEC, REV><<<dim3(G, s.nseg - 1), block, 0, stream>>>(
         s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry);
     const int64_t n = s.nchan_pad * kMaxState;
     carry_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
         s, p.agg, h0, p.carry);
   }
-  scan_kernel<IO, XT, BT, false, VEC><<<dim3(G, s.nseg), block, 0, stream>>>(
+  scan_kernel<IO, XT, BT, false, VEC, REV><<<dim3(G, s.nseg), block, 0, stream>>>(
       s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry);
 }
 
 // The vector pass covers [0, s.t_stop); when s.t_stop < seqlen it exports its
 // state to p.tail_h0 and an element-wise pass covers the remaining steps.
-template <typename IO, bool XT, bool BT>
-static hipError_t launch_scan_t(const ScanShape& s, const ScanPtrs& p, hipStream_t stream) {
+template <typename IO, bool XT, bool BT, bool REV>
+static hipError_t launch_dir(const ScanShape& s, const ScanPtrs& p, hipStream_t stream) {
   if (!s.use_vec) {
-    launch_pass<IO, XT, BT, false>(s, p, p.h0, p.final_state, stream);
+    launch_pass<IO, XT, BT, false, REV>(s, p, p.h0, p.final_state, stream);
     return hipGetLastError();
   }
   const bool tail = s.t_stop < s.seqlen;
   if (s.t_stop > 0)
-    launch_pass<IO, XT, BT, true>(s, p, p.h0, tail ? p.tail_h0 : p.final_state, stream);
+    launch_pass<IO, XT, BT, true, REV>(s, p, p.h0, tail ? p.tail_h0 : p.final_state, stream);
   if (tail) {
     ScanShape t = s;
     t.t_first = s.t_stop;
     t.t_stop = s.seqlen;
     t.nseg = 1;
     t.seg_len = s.seqlen - s.t_stop;
-    launch_pass<IO, XT, BT, false>(t, p, s.t_stop > 0 ? p.tail_h0 : p.h0, p.final_state, stream);
+    launch_pass<IO, XT, BT, false, REV>(t, p, s.t_stop > 0 ? p.tail_h0 : p.h0, p.final_state,
+                                        stream);
   }
   return hipGetLastError();
+}
+
+template <typename IO, bool XT, bool BT>
+static hipError_t launch_scan_t(const ScanShape& s, const ScanPtrs& p, hipStream_t stream) {
+  return s.reverse ? launch_dir<IO, XT, BT, true>(s, p, stream)
+                   : launch_dir<IO, XT, BT, false>(s, p, stream);
 }
 
 hipError_t launch_scan(const ScanShape& s, const ScanPtrs& p, bool io_bf16, bool x_tfast,

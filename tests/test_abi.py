@@ -147,7 +147,7 @@ def _mut_scan(fn, ws=False):
 SCAN_CASES = {
     "null_struct": (None, "MSS_ERR_BAD_STRUCT"),
     "struct_size": (lambda a: setattr(a, "struct_size", 8), "MSS_ERR_BAD_STRUCT"),
-    "reserved": (lambda a: setattr(a, "reserved0", 1), "MSS_ERR_BAD_STRUCT"),
+    "reverse2": (lambda a: setattr(a, "reverse", 2), "MSS_ERR_BAD_STRUCT"),
     "dtype": (lambda a: setattr(a, "io_dtype", 7), "MSS_ERR_UNSUPPORTED_DTYPE"),
     "batch0": (lambda a: setattr(a, "batch", 0), "MSS_ERR_BAD_SHAPE"),
     "seqlen_neg": (lambda a: setattr(a, "seqlen", -3), "MSS_ERR_BAD_SHAPE"),
@@ -367,7 +367,7 @@ def test_bwd_workspace_size():
 
 BWD_CASES = {
     "struct_size": (lambda a: setattr(a, "struct_size", 4), "MSS_ERR_BAD_STRUCT"),
-    "reserved": (lambda a: setattr(a, "reserved0", 2), "MSS_ERR_BAD_STRUCT"),
+    "reverse_neg": (lambda a: setattr(a, "reverse", -1), "MSS_ERR_BAD_STRUCT"),
     "dtype": (lambda a: setattr(a, "io_dtype", 3), "MSS_ERR_UNSUPPORTED_DTYPE"),
     "seqlen0": (lambda a: setattr(a, "seqlen", 0), "MSS_ERR_BAD_SHAPE"),
     "dstate17": (lambda a: setattr(a, "dstate", 17), "MSS_ERR_UNSUPPORTED_DSTATE"),

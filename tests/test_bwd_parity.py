@@ -143,6 +143,23 @@ def test_long_sequence(mss):
         check(f"bwd long {k}", to_np(v), ref[ORACLE_NAME[k]], TOL["f32"])
 
 
+def test_time_invariant_B_C(mss):
+    """B and C constant in time, passed as stride-0 views: the gradient of the
+    [B, N] parameters is the time sum of dB and dC."""
+    import torch
+    dx = _problem(2, 96, 300, 16, h0=True)
+    g = torch.Generator().manual_seed(4)
+    base = {k: torch.randn(2, 16, generator=g).to(device()) for k in ("B", "C")}
+    for k in ("B", "C"):
+        dx[k] = base[k][:, :, None].expand(2, 16, 300)
+    got = _run_and_check(mss, "time-invariant B/C", dx)
+    ref = oracle.scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dx["dout"],
+                          D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], h0=dx["h0"])
+    for k, r in (("dB", "dB"), ("dC", "dC")):
+        check(f"bwd time-invariant sum_t {k}", to_np(got[k]).sum(axis=2), ref[r].sum(axis=2),
+              TOL["f32"])
+
+
 def test_random_a_log(mss):
     _run_and_check(mss, "A_log~N(0,1)", _problem(1, 128, 300, 16, a_log="normal", h0=True))
 

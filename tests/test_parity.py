@@ -105,6 +105,32 @@ def test_time_split_with_initial_state(mss):
     _full_case(mss, "split+h0", 1, 64, 20000, 16, h0=True)
 
 
+@pytest.mark.parametrize("shared_batch", [False, True])
+@pytest.mark.parametrize("seqlen", [77, 4096])
+def test_time_invariant_B_C(mss, shared_batch, seqlen):
+    """Time-invariant B and C (the S4-style variant): [B, N] (or [N]) tensors
+    broadcast along time as stride-0 views, with no copy."""
+    import torch
+    bsz, dim, N = 2, 96, 16
+    note(f"time-invariant B/C L={seqlen} shared_batch={shared_batch}")
+    x = generate(bsz, dim, seqlen, N, seed=11)
+    dx = to_torch(x, device(), "f32")
+    g = torch.Generator().manual_seed(3)
+    for k in ("B", "C"):
+        if shared_batch:
+            base = torch.randn(N, generator=g).to(device())
+            dx[k] = base[None, :, None].expand(bsz, N, seqlen)
+        else:
+            base = torch.randn(bsz, N, generator=g).to(device())
+            dx[k] = base[:, :, None].expand(bsz, N, seqlen)
+        assert dx[k].stride()[2] == 0
+    out, fin = run_gpu(mss, dx)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle_full(dx)
+    check(f"time-invariant B/C L={seqlen} out", to_np(out), ref_out, 1e-4)
+    check(f"time-invariant B/C L={seqlen} final", to_np(fin), ref_fin, 1e-4)
+
+
 @pytest.mark.parametrize("layout", ["bdl", "bld"])
 def test_views_into_padded_buffers(mss, layout):
     """Views with offsets and padded row strides (the unit-stride axis kept)."""
