@@ -14,6 +14,7 @@ is no CPU or PyTorch fallback; without the built library every call raises.
     u, window = causal_conv1d_fwd(x, weight, bias, return_final_state=True)
     u_t = causal_conv1d_update(window, x_t, weight, bias)   # window slides in place
     g = selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D, z, dt_bias)  # dict of grads
+    out = selective_scan(u, delta_raw, A_log, B, C, D, z, dt_bias)  # autograd: fwd + bwd
 
 Shapes (logical index order, any strides): u, delta_raw, z, out [B, D, L];
 B, C [B, N, L]; A_log [D, N]; D, dt_bias [D]; states [B, D, N] (fp32,
@@ -33,7 +34,8 @@ from ._lib import MSS_MAX_DSTATE, MssError
 
 __all__ = ["selective_scan_fwd", "selective_state_update", "scan_workspace_size",
            "causal_conv1d_fwd", "causal_conv1d_update", "selective_scan_bwd",
-           "scan_bwd_workspace_size", "MssError", "MSS_MAX_DSTATE", "library_path"]
+           "scan_bwd_workspace_size", "selective_scan", "MssError", "MSS_MAX_DSTATE",
+           "library_path"]
 
 
 def library_path() -> str:
@@ -418,3 +420,53 @@ def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=
     b.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.mss_selective_scan_bwd(ctypes.byref(b), _stream_handle(dev)))
     return {k: v for k, v in g.items() if v is not None}
+
+
+_SCAN_FN = None
+
+
+def _scan_fn():
+    """torch.autograd.Function over selective_scan_fwd / selective_scan_bwd
+    (built on first use so that importing this module does not import torch)."""
+    global _SCAN_FN
+    if _SCAN_FN is not None:
+        return _SCAN_FN
+    torch = _torch()
+
+    class SelectiveScanFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state,
+                    delta_softplus, reverse):
+            out, final = selective_scan_fwd(u, delta_raw, A_log, B, C, D, z, dt_bias,
+                                            delta_softplus=delta_softplus,
+                                            initial_state=initial_state,
+                                            return_final_state=True, reverse=reverse)
+            ctx.save_for_backward(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state)
+            ctx.flags = (delta_softplus, reverse)
+            return out, final
+
+        @staticmethod
+        def backward(ctx, dout, dfinal):
+            u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state = ctx.saved_tensors
+            delta_softplus, reverse = ctx.flags
+            if dout is None:
+                dout = torch.zeros_like(u)
+            g = selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D, z, dt_bias,
+                                   delta_softplus=delta_softplus, initial_state=initial_state,
+                                   dfinal_state=dfinal, reverse=reverse)
+            return (g["du"], g["ddelta_raw"], g["dA_log"], g["dB"], g["dC"], g.get("dD"),
+                    g.get("dz"), g.get("ddt_bias"), g.get("dinitial_state"), None, None)
+
+    _SCAN_FN = SelectiveScanFn
+    return _SCAN_FN
+
+
+def selective_scan(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
+                   delta_softplus=True, initial_state=None, reverse=False,
+                   return_final_state=False):
+    """Selective scan with autograd: the forward of selective_scan_fwd, and on
+    ``backward()`` the gradients of every tensor input from selective_scan_bwd
+    (including through the final state when it is returned and used)."""
+    out, final = _scan_fn().apply(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state,
+                                  delta_softplus, reverse)
+    return (out, final) if return_final_state else out

@@ -185,3 +185,34 @@ def test_run_twice_bitwise(mss):
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_autograd_function(mss, reverse):
+    """selective_scan under torch.autograd: loss = sum(w * out) + sum(v * final)
+    gives the oracle's gradients for dout = w, dfinal = v."""
+    import torch
+    dx = _problem(2, 64, 120, 16, h0=True)
+    g = torch.Generator().manual_seed(9)
+    w = torch.randn(2, 64, 120, generator=g).to(device())
+    v = torch.randn(2, 64, 16, generator=g).to(device())
+    names = ["u", "delta_raw", "A_log", "B", "C", "D", "z", "dt_bias", "h0"]
+    leaves = {k: dx[k].detach().clone().requires_grad_(True) for k in names}
+    note(f"autograd function reverse={reverse}")
+    out, fin = mss.selective_scan(leaves["u"], leaves["delta_raw"], leaves["A_log"],
+                                  leaves["B"], leaves["C"], leaves["D"], leaves["z"],
+                                  leaves["dt_bias"], initial_state=leaves["h0"],
+                                  reverse=reverse, return_final_state=True)
+    ((out * w).sum() + (fin * v).sum()).backward()
+    torch.cuda.synchronize()
+    flip = (lambda a: np.ascontiguousarray(to_np(a)[:, :, ::-1])) if reverse else to_np
+    ref = oracle.scan_bwd(flip(dx["u"]), flip(dx["delta_raw"]), dx["A_log"], flip(dx["B"]),
+                          flip(dx["C"]), flip(w), D=dx["D"], z=flip(dx["z"]),
+                          dt_bias=dx["dt_bias"], h0=dx["h0"], dfinal=v)
+    oname = {"u": "du", "delta_raw": "ddelta_raw", "A_log": "dA_log", "B": "dB", "C": "dC",
+             "D": "dD", "z": "dz", "dt_bias": "ddt_bias", "h0": "dh0"}
+    for k in names:
+        r = ref[oname[k]]
+        if reverse and k in ("u", "delta_raw", "B", "C", "z"):
+            r = r[:, :, ::-1]
+        check(f"autograd grad {k} reverse={reverse}", to_np(leaves[k].grad), r, TOL["f32"])
