@@ -71,6 +71,16 @@ __device__ inline float f4_at(const f4& v, int i) {
 template <typename IO>
 __device__ inline float ld(const IO* p) { return io_traits<IO>::load(p); }
 
+// Load of base[off] for lanes with ok, 0 for the others, without a branch:
+// masked lanes read base[0] (always inside the tensor) and drop the value.
+// Unconditional loads let the compiler wait for each one exactly when it is
+// used, so a chunk's loads can be issued a chunk ahead.
+template <typename IO>
+__device__ inline float ld_masked(const IO* base, int64_t off, bool ok) {
+  const float v = io_traits<IO>::load(base + (ok ? off : 0));
+  return ok ? v : 0.0f;
+}
+
 __device__ inline float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
 }
@@ -240,28 +250,44 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dr = static_cast<const IO*>(p.delta_raw);
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
+  // Raw inputs of a chunk, issued one chunk ahead of use: B (lane covers row
+  // lane / 4, steps 4 (lane % 4) .. + 3) and u, delta_raw (lane (c, j) covers
+  // steps 2j, 2j+1 of channel c).
+  float rb[4], ru[2], rx[2];
+  auto load_chunk = [&](int q) __attribute__((always_inline)) {
+    const int t0 = q * kBwdT;
+    const bool qok = q < q_end;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = lane >> 2, t = t0 + (lane & 3) * 4 + i;
+      rb[i] = ld_masked(Bm, b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2],
+                        qok && n < s.dstate && t < s.seqlen);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int t = t0 + 2 * sg + e;
+      const bool ok = qok && dvalid && t < s.seqlen;
+      ru[e] = ld_masked(u, b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2], ok);
+      rx[e] = ld_masked(dr, b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2], ok);
+    }
+  };
+  load_chunk(q_begin);
   for (int q = q_begin; q < q_end; ++q) {
     const int t0 = q * kBwdT;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       p.ckpt[(static_cast<int64_t>(q) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] = h[k];
-    // B of the chunk: lane covers row lane / 4, steps 4 (lane % 4) .. + 3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = lane >> 2, tt = (lane & 3) * 4 + i, t = t0 + tt;
-      const bool ok = n < s.dstate && t < s.seqlen;
-      s_b[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2]) : 0.0f;
-    }
-    // delta and delta*u: lane (c, j) covers steps 2j, 2j+1 of channel c
+    for (int i = 0; i < 4; ++i) s_b[(lane >> 2) * kBcPitch + (lane & 3) * 4 + i] = rb[i];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
-      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2]) : 0.0f;
-      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2]) : 0.0f) + bias;
+      const float x = rx[e] + bias;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
-      *reinterpret_cast<float2*>(s_dd + sc * kDdPitch2 + 2 * tt) = make_float2(dl, dl * uu);
+      *reinterpret_cast<float2*>(s_dd + sc * kDdPitch2 + 2 * tt) = make_float2(dl, dl * ru[e]);
     }
+    load_chunk(q + 1);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t4 = 0; t4 < kBwdT; t4 += 4) {
@@ -283,7 +309,7 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
 
 // ---------------------------------------------------------------- pass 2 ---
 template <typename IO>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_kernel(BwdShape s, BwdPtrs p) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
   __shared__ __attribute__((aligned(16))) float s_el[kBwdWaves][kCh * kElPitch];
   __shared__ __attribute__((aligned(16))) float s_gr[kBwdWaves][kCh * kGrPitch];
@@ -337,43 +363,63 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
   float* el = s_el[w];
   float* gr = s_gr[w];
+  // Raw inputs of a chunk, issued one chunk ahead of use: one B or C value
+  // per thread, u, delta_raw, dout and z for the lane's two elements (lane
+  // (c, j) = (lane % 8, lane / 8) owns steps 2j, 2j+1 of channel c), and the
+  // checkpoint of the lane's two states.
+  const IO* z_base = has_z ? zz : u;
+  float rbc, ru[2], rx[2], rgo[2], rz[2], rck[2];
+  auto load_chunk = [&](int q) __attribute__((always_inline)) {
+    const int t0 = q * kBwdT;
+    const bool qok = q >= q_begin;
+    {
+      const int r = tid >> 4, n = r & 15, t = t0 + (tid & 15);
+      const bool ok = qok && n < s.dstate && t < s.seqlen;
+      rbc = r < kMaxState ? ld_masked(Bm, b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2], ok)
+                          : ld_masked(Cm, b * s.sC[0] + n * s.sC[1] + tstore(s, t) * s.sC[2], ok);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int t = t0 + 2 * sg + e;
+      const bool ok = qok && dvalid && t < s.seqlen;
+      const int64_t ts = tstore(s, t);
+      ru[e] = ld_masked(u, b * s.su[0] + d * s.su[1] + ts * s.su[2], ok);
+      rx[e] = ld_masked(dr, b * s.sd[0] + d * s.sd[1] + ts * s.sd[2], ok);
+      rgo[e] = ld_masked(dout, b * s.sdo[0] + d * s.sdo[1] + ts * s.sdo[2], ok);
+      rz[e] = ld_masked(z_base, b * s.sz[0] + d * s.sz[1] + ts * s.sz[2], ok && has_z);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      rck[k] = p.ckpt[(static_cast<int64_t>(qok ? q : q_begin) * s.nchan_pad + chan_row) *
+                          kMaxState + 2 * sg + k];
+  };
+  load_chunk(q_end - 1);
   for (int q = q_end - 1; q >= q_begin; --q) {
     const int t0 = q * kBwdT;
-    // ---- E: B and C of the chunk (one value per thread) ----
-    {
-      const int r = tid >> 4, tt = tid & 15, n = r & 15, t = t0 + tt;
-      const bool ok = n < s.dstate && t < s.seqlen;
-      float v = 0.0f;
-      if (ok) v = r < kMaxState ? ld(Bm + b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2])
-                                : ld(Cm + b * s.sC[0] + n * s.sC[1] + tstore(s, t) * s.sC[2]);
-      s_bc[r * kBcPitch + tt] = v;
-    }
-    // ---- E: per element (lane (c, j) = (lane % 8, lane / 8) owns steps 2j,
-    // 2j+1 of channel c): the scan's inputs go to s_el, the values the output
-    // phase needs to s_gr ----
+    // ---- E: B and C into LDS; per element, the scan's inputs into s_el and
+    // the values the output phase needs into s_gr ----
+    s_bc[(tid >> 4) * kBcPitch + (tid & 15)] = rbc;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
-      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2]) : 0.0f;
-      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2]) : 0.0f) + bias;
-      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + tstore(s, t) * s.sdo[2]) : 0.0f;
-      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + tstore(s, t) * s.sz[2]) : 0.0f;
+      const float x = rx[e] + bias;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
       const float sig = s.softplus ? sigmoid(x) : 1.0f;
-      const float dy = has_z ? go * silu(zv) : go;
-      *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{dl, dl * uu, dy, 0.0f};
-      *reinterpret_cast<f4*>(gr + sc * kGrPitch + 8 * tt) = f4{uu, sig, go, zv};
+      const float dy = has_z ? rgo[e] * silu(rz[e]) : rgo[e];
+      *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
+      *reinterpret_cast<f4*>(gr + sc * kGrPitch + 8 * tt) = f4{ru[e], sig, rgo[e], rz[e]};
     }
-    __syncthreads();
-
-    // ---- F: the chunk's states from its checkpoint ----
     float hs[2], h[2], hh[kBwdT][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      hs[k] = p.ckpt[(static_cast<int64_t>(q) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k];
+      hs[k] = rck[k];
       h[k] = hs[k];
     }
+    load_chunk(q - 1);
+    __syncthreads();
+
+    // ---- F: the chunk's states from its checkpoint ----
     const float* rb0 = s_bc + (2 * sg) * kBcPitch;
     const float* rb1 = rb0 + kBcPitch;
     const float* rc0 = s_bc + (kMaxState + 2 * sg) * kBcPitch;
