@@ -219,6 +219,8 @@ def main_conv(args):
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -226,7 +228,9 @@ def main_conv(args):
         conv()
         ev[i][1].record(stream)
         if not args.no_step:
+            dev_ev[i][0].record(stream)
             decode()
+            dev_ev[i][1].record(stream)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = sorted(a.elapsed_time(b) for a, b in ev)
@@ -273,6 +277,16 @@ def main_conv(args):
         },
         "cpu_baseline": None,
     }
+    if not args.no_step:
+        dec_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)
+        dec_mean = sum(dec_ms) / len(dec_ms)
+        rec["decode_step"] = {
+            "kernel": "conv_step_kernel (mss_causal_conv1d_update)",
+            "event_us_mean": round(dec_mean * 1e3, 2),
+            "event_us_median": round(dec_ms[len(dec_ms) // 2] * 1e3, 2),
+            "algorithmic_bytes": step_b,
+            "achieved_gbs": round(step_b / (dec_mean * 1e-3) / 1e9, 1),
+        }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: conv oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
         rec["cpu_baseline"] = conv_cpu_baseline(x, io_bytes, args.cpu_seconds)
@@ -483,6 +497,8 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -490,7 +506,9 @@ def main(argv=None):
         scan()
         ev[i][1].record(stream)
         if not args.no_step:
+            dev_ev[i][0].record(stream)
             decode()
+            dev_ev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -557,6 +575,19 @@ def main(argv=None):
         },
         "cpu_baseline": None,
     }
+    if not args.no_step:
+        dec_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)
+        dec_mean = sum(dec_ms) / len(dec_ms)
+        dec_bytes = step_bytes(w.batch, w.dim, w.dstate, io_bytes)
+        rec["decode_step"] = {
+            "kernel": "state_update_kernel (mss_selective_state_update)",
+            "event_us_mean": round(dec_mean * 1e3, 2),
+            "event_us_median": round(dec_ms[len(dec_ms) // 2] * 1e3, 2),
+            "algorithmic_bytes": dec_bytes,
+            "achieved_gbs": round(dec_bytes / (dec_mean * 1e-3) / 1e9, 1),
+        }
+        log(f"decode step mean {dec_mean * 1e3:.2f} us, "
+            f"{dec_bytes / (dec_mean * 1e-3) / 1e9:.0f} GB/s")
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
         rec["cpu_baseline"] = cpu_baseline(x, w, io_bytes, args.cpu_seconds)

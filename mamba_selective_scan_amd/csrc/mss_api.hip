@@ -378,7 +378,7 @@ mss_status mss_selective_state_update(const mss_step_args* a, void* stream) {
   if (a->io_dtype != MSS_F32 && a->io_dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED_DTYPE;
   if (a->batch < 1 || a->dim < 1 || a->batch > kMaxDim || a->dim > kMaxDim)
     return MSS_ERR_BAD_SHAPE;
-  if (a->batch * ((a->dim + 63) / 64) > kMaxDim || a->batch * a->dim > kMaxDim)
+  if (a->batch * a->dim > kMaxDim)
     return MSS_ERR_BAD_SHAPE;
   if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
   if (a->state == nullptr || a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr ||

@@ -8,49 +8,71 @@
 // "O(L) インクリメンタルデコード": an elementwise step on the carried state,
 // closed by the z gate).
 //
-// One lane per channel, one wave per 64 channels of one batch row, so B and C
-// are wave-uniform scalar loads; the dstate entries are walked in registers.
-// The step moves a few hundred kilobytes at decode shapes and is bound by
-// launch latency, not bandwidth.
+// One lane per (channel, state): a 16-lane row of a wave holds one channel's
+// 16 states, so the state, A_log, B and C loads are contiguous across the
+// row, and y = sum_n C[n] h[n] is a 4-step DPP rotation sum inside the row.
+// Lanes past dstate carry zeros.  Every row computes its channel's delta (the
+// same value in all 16 lanes); lane 0 of the row adds the skip term, applies
+// the gate and stores.  The step moves a few megabytes at most and is bound
+// by launch latency at decode shapes.
 #include "mss_device.hpp"
 #include "mss_internal.hpp"
 
 namespace mss {
 
+constexpr int kStepThreads = 256;                   // 16 channels per workgroup
+constexpr int kStepChannels = kStepThreads / kMaxState;
+
+// Sum over the 16 lanes of a DPP row, left in every lane of the row.
+__device__ inline float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, true));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, true));  // row_ror:1
+  return v;
+}
+
 template <typename IO>
-__global__ __launch_bounds__(64) void state_update_kernel(
+__global__ __launch_bounds__(kStepThreads) void state_update_kernel(
     StepShape s, float* __restrict__ state, const IO* __restrict__ u,
     const IO* __restrict__ delta_raw, const float* __restrict__ A_log,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dskip,
     const IO* __restrict__ z, const float* __restrict__ dt_bias, IO* __restrict__ out) {
-  const int groups = (s.dim + 63) / 64;
-  const int b = blockIdx.x / groups;
-  const int d = (blockIdx.x - b * groups) * 64 + static_cast<int>(threadIdx.x);
-  if (d >= s.dim) return;
-  const float x = io_traits<IO>::load(delta_raw + b * s.sd[0] + d * s.sd[1]) +
-                  (dt_bias != nullptr ? dt_bias[d] : 0.0f);
-  const float dl = s.softplus ? softplus(x) : x;
-  const float uv = io_traits<IO>::load(u + b * s.su[0] + d * s.su[1]);
-  const float du = dl * uv;
-  float* hp = state + (static_cast<int64_t>(b) * s.dim + d) * s.dstate;
-  float y = 0.0f;
-  for (int n = 0; n < s.dstate; ++n) {
-    const float a2 = -expf(A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e;
-    const float bn = load_uniform(Bm + b * s.sB[0] + n * s.sB[1]);
-    const float cn = load_uniform(Cm + b * s.sC[0] + n * s.sC[1]);
-    const float hn = fmaf(fast_exp2(dl * a2), hp[n], du * bn);
-    hp[n] = hn;
-    y = fmaf(cn, hn, y);
+  const int n = threadIdx.x % kMaxState;
+  const int64_t ch = static_cast<int64_t>(blockIdx.x) * kStepChannels + threadIdx.x / kMaxState;
+  const bool cvalid = ch < static_cast<int64_t>(s.batch) * s.dim;
+  const int b = cvalid ? static_cast<int>(ch / s.dim) : 0;
+  const int d = cvalid ? static_cast<int>(ch % s.dim) : 0;
+  const bool active = cvalid && n < s.dstate;
+  float dl = 0.0f, uv = 0.0f, y = 0.0f;
+  if (cvalid) {
+    const float x = io_traits<IO>::load(delta_raw + b * s.sd[0] + d * s.sd[1]) +
+                    (dt_bias != nullptr ? dt_bias[d] : 0.0f);
+    dl = s.softplus ? softplus(x) : x;
+    uv = io_traits<IO>::load(u + b * s.su[0] + d * s.su[1]);
   }
-  y = fmaf(Dskip != nullptr ? Dskip[d] : 0.0f, uv, y);
-  if (z != nullptr) y *= silu(io_traits<IO>::load(z + b * s.sz[0] + d * s.sz[1]));
-  io_traits<IO>::store(out + b * s.so[0] + d * s.so[1], y);
+  if (active) {
+    const float a2 = -expf(A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e;
+    const float bn = io_traits<IO>::load(Bm + b * s.sB[0] + n * s.sB[1]);
+    const float cn = io_traits<IO>::load(Cm + b * s.sC[0] + n * s.sC[1]);
+    float* hp = state + ch * s.dstate + n;
+    const float hn = fmaf(fast_exp2(dl * a2), *hp, dl * uv * bn);
+    *hp = hn;
+    y = cn * hn;
+  }
+  y = row_sum16(y);  // every lane of the row takes part
+  if (cvalid && n == 0) {
+    y = fmaf(Dskip != nullptr ? Dskip[d] : 0.0f, uv, y);
+    if (z != nullptr) y *= silu(io_traits<IO>::load(z + b * s.sz[0] + d * s.sz[1]));
+    io_traits<IO>::store(out + b * s.so[0] + d * s.so[1], y);
+  }
 }
 
 template <typename IO>
 static hipError_t launch_step_t(const StepShape& s, const StepPtrs& p, hipStream_t stream) {
-  const unsigned groups = static_cast<unsigned>((s.dim + 63) / 64);
-  state_update_kernel<IO><<<dim3(groups * static_cast<unsigned>(s.batch)), dim3(64), 0, stream>>>(
+  const int64_t nch = static_cast<int64_t>(s.batch) * s.dim;
+  const unsigned blocks = static_cast<unsigned>((nch + kStepChannels - 1) / kStepChannels);
+  state_update_kernel<IO><<<dim3(blocks), dim3(kStepThreads), 0, stream>>>(
       s, p.state, static_cast<const IO*>(p.u), static_cast<const IO*>(p.delta_raw), p.A_log,
       static_cast<const IO*>(p.B), static_cast<const IO*>(p.C), p.D, static_cast<const IO*>(p.z),
       p.dt_bias, static_cast<IO*>(p.out));

@@ -64,13 +64,15 @@ def test_long_handoff(mss, io):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dstate", [16, 5])
-def test_state_update_matches_oracle(mss, io, dstate):
+@pytest.mark.parametrize("shape", [(3, 200), (1, 7), (8, 5120)])
+def test_state_update_matches_oracle(mss, io, dstate, shape):
     import torch
-    note(f"state_update {io} N={dstate}")
-    x = generate(3, 200, 1, dstate, seed=11)
+    batch, dim = shape
+    note(f"state_update {io} N={dstate} B={batch} D={dim}")
+    x = generate(batch, dim, 1, dstate, seed=11)
     dx = to_torch(x, device(), io)
     g = torch.Generator().manual_seed(3)
-    state = torch.randn(3, 200, dstate, generator=g).to(device())
+    state = torch.randn(batch, dim, dstate, generator=g).to(device())
     s0 = state.clone()
     y = mss.selective_state_update(state, dx["u"][:, :, 0], dx["delta_raw"][:, :, 0], dx["A_log"],
                                    dx["B"][:, :, 0], dx["C"][:, :, 0], D=dx["D"],
