@@ -96,6 +96,21 @@ __device__ inline int64_t xcd_order(int64_t lin, int64_t nwg) {
   return xcd * per + (xcd < extra ? xcd : extra) + lin / kXcdsBwd;
 }
 
+// Sum over the 8 lanes of a half row (the 8 channels of one state group) of
+// one state's per-lane terms, for a pair of states held in a lane-dependent
+// order: lanes 0-3 of the half hold (keep, give) = (state 2g, state 2g+1),
+// lanes 4-7 hold (state 2g+1, state 2g).  The first level adds each lane's
+// keep term to its mirror partner's give term (row_half_mirror pairs i with
+// 7 - i, which holds the same state in its give slot), so one DPP add
+// reduces both states at once; two quad permutations finish the sum.  Lanes
+// 0-3 end with state 2g's total, lanes 4-7 with state 2g+1's.
+__device__ inline float sum_pair_half_rows(float keep, float give) {
+  float v = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0x141, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  return v;
+}
+
 // The reduce_groups tree leaves step {0, 2, 1, 3}[row] of a 4-step block in
 // 16-lane row `row`.
 __device__ inline int group_step(int lane) {
@@ -310,10 +325,17 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
 // ---------------------------------------------------------------- pass 2 ---
 template <typename IO>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p) {
-  __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
-  __shared__ __attribute__((aligned(16))) float s_el[kBwdWaves][kCh * kElPitch];
-  __shared__ __attribute__((aligned(16))) float s_gr[kBwdWaves][kCh * kGrPitch];
-  __shared__ __attribute__((aligned(16))) float s_red[kBwdWaves][2 * kMaxState * kBwdT];
+  // One LDS block, B/C first and the reduction rows next, so that the rows
+  // addressed with per-lane bases plus a step offset stay within reach of the
+  // 16-bit DS instruction offset.
+  constexpr int kRedSize = 2 * kMaxState * kBwdT;
+  constexpr int kBcSize = 2 * kMaxState * kBcPitch;
+  __shared__ __attribute__((aligned(16)))
+  float smem[kBcSize + kBwdWaves * (kRedSize + kCh * kElPitch + kCh * kGrPitch)];
+  float* const s_bc = smem;
+  float* const s_red = smem + kBcSize;
+  float* const s_el = s_red + kBwdWaves * kRedSize;
+  float* const s_gr = s_el + kBwdWaves * kCh * kElPitch;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -328,6 +350,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   const bool dvalid = d < s.dim;
   const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
   const bool has_z = p.z != nullptr;
+  // lane (c, g) runs states 2g, 2g+1 of channel c, in the order that
+  // sum_pair_half_rows expects: slot k holds state nk[k]
+  const int swap = sc >> 2;
+  const int nk[2] = {2 * sg + swap, 2 * sg + (swap ^ 1)};
 
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dr = static_cast<const IO*>(p.delta_raw);
@@ -342,7 +368,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   float A2[2], An[2], g[2], dA[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int n = 2 * sg + k;
+    const int n = nk[k];
     const bool active = dvalid && n < s.dstate;
     An[k] = active ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) : 0.0f;
     A2[k] = An[k] * kLog2e;
@@ -361,8 +387,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   const float skip = (dvalid && p.D != nullptr) ? p.D[d] : 0.0f;
   float acc_dD = 0.0f, acc_db = 0.0f;
 
-  float* el = s_el[w];
-  float* gr = s_gr[w];
+  float* el = s_el + w * (kCh * kElPitch);
+  float* gr = s_gr + w * (kCh * kGrPitch);
   // Raw inputs of a chunk, issued one chunk ahead of use: one B or C value
   // per thread, u, delta_raw, dout and z for the lane's two elements (lane
   // (c, j) = (lane % 8, lane / 8) owns steps 2j, 2j+1 of channel c), and the
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       rck[k] = p.ckpt[(static_cast<int64_t>(qok ? q : q_begin) * s.nchan_pad + chan_row) *
-                          kMaxState + 2 * sg + k];
+                          kMaxState + nk[k]];
   };
   load_chunk(q_end - 1);
   for (int q = q_end - 1; q >= q_begin; --q) {
@@ -410,7 +436,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
       *reinterpret_cast<f4*>(gr + sc * kGrPitch + 8 * tt) = f4{ru[e], sig, rgo[e], rz[e]};
     }
-    float hs[2], h[2], hh[kBwdT][2];
+    float hs[2], h[2], hh[kBwdT][2], aa[kBwdT][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       hs[k] = rck[k];
@@ -419,11 +445,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     load_chunk(q - 1);
     __syncthreads();
 
-    // ---- F: the chunk's states from its checkpoint ----
-    const float* rb0 = s_bc + (2 * sg) * kBcPitch;
-    const float* rb1 = rb0 + kBcPitch;
-    const float* rc0 = s_bc + (kMaxState + 2 * sg) * kBcPitch;
-    const float* rc1 = rc0 + kBcPitch;
+    // ---- F: the chunk's states and decays from its checkpoint ----
+    const float* rb0 = s_bc + nk[0] * kBcPitch;
+    const float* rb1 = s_bc + nk[1] * kBcPitch;
+    const float* rc0 = s_bc + (kMaxState + nk[0]) * kBcPitch;
+    const float* rc1 = s_bc + (kMaxState + nk[1]) * kBcPitch;
     const float* rdd = el + sc * kElPitch;
     const int ystep = group_step(lane);
 #pragma unroll
@@ -433,8 +459,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       for (int i = 0; i < 4; ++i) {
         const int t = t4 + i;
         const f4 dd = ld4(rdd + 4 * t);
-        h[0] = fmaf(fast_exp2(dd.x * A2[0]), h[0], dd.y * rb0[t]);
-        h[1] = fmaf(fast_exp2(dd.x * A2[1]), h[1], dd.y * rb1[t]);
+        aa[t][0] = fast_exp2(dd.x * A2[0]);
+        aa[t][1] = fast_exp2(dd.x * A2[1]);
+        h[0] = fmaf(aa[t][0], h[0], dd.y * rb0[t]);
+        h[1] = fmaf(aa[t][1], h[1], dd.y * rb1[t]);
         hh[t][0] = h[0];
         hh[t][1] = h[1];
         yp[i] = fmaf(rc1[t], h[1], rc0[t] * h[0]);
@@ -444,9 +472,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     __builtin_amdgcn_wave_barrier();
     // ---- R: reverse walk ----
     // Per step the sums over the wave's 8 channels of the dB and dC terms are
-    // finished at once (one DPP tree each) and written by lane c = 0 of each
-    // state group; the sums over states collect 4 steps for one cross-lane tree.
-    float* red = s_red[w];
+    // finished at once (one DPP tree each for the lane's two states) and
+    // written by lanes c = 0 and c = 4 of each state group; the sums over
+    // states collect 4 steps for one cross-lane tree.
+    float* red = s_red + w * kRedSize;
+    const bool writer = (sc & 3) == 0;
 #pragma unroll
     for (int t4 = kBwdT - 4; t4 >= 0; t4 -= 4) {
       float qb[4], qa[4];
@@ -454,30 +484,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       for (int i = 3; i >= 0; --i) {
         const int t = t4 + i;
         const f4 dd = ld4(rdd + 4 * t);
-        const float bk[2] = {rb0[t], rb1[t]};
-        const float ck[2] = {rc0[t], rc1[t]};
-        float sb = 0.0f, sa = 0.0f;
-        float pb[2], pc[2];
+        float G[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) G[k] = fmaf(dd.z, k == 0 ? rc0[t] : rc1[t], g[k]);
+        float pb = sum_pair_half_rows(G[0] * dd.y, G[1] * dd.y);
+        float pc = sum_pair_half_rows(dd.z * hh[t][0], dd.z * hh[t][1]);
+        // finish both sums in every lane (one DPP add each) rather than let
+        // the compiler move the last add into the writers' branch as a move
+        // plus an add
+        asm volatile("" : "+v"(pb), "+v"(pc));
+        float sb = G[0] * rb0[t];
+        sb = fmaf(G[1], rb1[t], sb);
+        float sa = 0.0f;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-          const float G = fmaf(dd.z, ck[k], g[k]);
-          pc[k] = sum_half_rows(dd.z * hh[t][k]);
-          pb[k] = sum_half_rows(G * dd.y);
-          sb = fmaf(G, bk[k], sb);
-          const float a = fast_exp2(dd.x * A2[k]);
-          const float hp = t > 0 ? hh[t > 0 ? t - 1 : 0][k] : hs[k];
-          const float r = G * hp * a;
+          const float ga = G[k] * aa[t][k];
+          const float r = ga * (t > 0 ? hh[t > 0 ? t - 1 : 0][k] : hs[k]);
           dA[k] = fmaf(r, dd.x, dA[k]);
           sa = fmaf(r, An[k], sa);
-          g[k] = G * a;
+          g[k] = ga;
         }
         qb[i] = sb;
         qa[i] = sa;
-        if (sc == 0) {
-          red[(2 * sg) * kBwdT + t] = pb[0];
-          red[(2 * sg + 1) * kBwdT + t] = pb[1];
-          red[(kMaxState + 2 * sg) * kBwdT + t] = pc[0];
-          red[(kMaxState + 2 * sg + 1) * kBwdT + t] = pc[1];
+        if (writer) {
+          red[nk[0] * kBwdT + t] = pb;
+          red[(kMaxState + nk[0]) * kBwdT + t] = pc;
         }
       }
       const float gb = reduce_groups(qb[0], qb[1], qb[2], qb[3]);
@@ -491,7 +522,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       const int r = tid >> 4, tt = tid & 15, t = t0 + tt;
       float sum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < kBwdWaves; ++ww) sum += s_red[ww][r * kBwdT + tt];
+      for (int ww = 0; ww < kBwdWaves; ++ww) sum += s_red[ww * kRedSize + r * kBwdT + tt];
       if ((r & 15) < s.dstate && t < s.seqlen)
         p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t] = sum;
     }
@@ -525,7 +556,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   const int64_t prow = ((static_cast<int64_t>(seg) * s.batch + b) * s.dim + d) * (kMaxState + 2);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int n = 2 * sg + k;
+    const int n = nk[k];
     if (dvalid && n < s.dstate) {
       p.part_chan[prow + n] = dA[k] * An[k];
       if (p.dh0 != nullptr && seg == 0)
@@ -534,7 +565,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   }
   // dD and ddt_bias: the 8 lanes of a channel (lanes c + 8j) meet in LDS
   __syncthreads();
-  float* tmp = s_red[w];
+  float* tmp = s_red + w * kRedSize;
   tmp[lane] = acc_dD;
   tmp[64 + lane] = acc_db;
   __builtin_amdgcn_wave_barrier();
