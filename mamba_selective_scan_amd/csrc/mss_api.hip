@@ -459,11 +459,16 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
   const int64_t* x_strides[] = {a->u_stride, a->delta_stride, a->dout_stride, a->du_stride,
                                 a->ddelta_stride};
   for (const int64_t* st3 : x_strides)
-    if (!strides_nonneg(st3, 3)) return MSS_ERR_BAD_STRIDE;
+    if (!strides_nonneg(st3, 3) || !tile_offsets_fit(st3, es)) return MSS_ERR_BAD_STRIDE;
   if (!strides_nonneg(a->B_stride, 3) || !strides_nonneg(a->C_stride, 3) ||
       !strides_nonneg(a->dB_stride, 3) || !strides_nonneg(a->dC_stride, 3) ||
       !strides_nonneg(a->A_log_stride, 2) || (a->z != nullptr && !strides_nonneg(a->z_stride, 3)) ||
       (a->dz != nullptr && !strides_nonneg(a->dz_stride, 3)))
+    return MSS_ERR_BAD_STRIDE;
+  // the reverse walk addresses its tiles with 32-bit offsets, as the forward
+  if (!tile_offsets_fit(a->B_stride, es, kMaxState) || !tile_offsets_fit(a->C_stride, es, kMaxState) ||
+      (a->z != nullptr && !tile_offsets_fit(a->z_stride, es)) ||
+      (a->dz != nullptr && !tile_offsets_fit(a->dz_stride, es)))
     return MSS_ERR_BAD_STRIDE;
   if (!non_overlapping(xs, a->du_stride, 3) || !non_overlapping(xs, a->ddelta_stride, 3) ||
       (a->dz != nullptr && !non_overlapping(xs, a->dz_stride, 3)) ||

@@ -116,6 +116,38 @@ __device__ inline float sum_half_rows(float v) {
   return v;
 }
 
+// Raw buffer descriptors: a range that keeps every valid 32-bit tile offset
+// in bounds; kOffNone lies past it, so an access with that offset reads 0 or
+// writes nothing.  Flags: the gfx9 raw-buffer data format word.
+constexpr int kRsrcRange = 0x7FFFFFF0;
+constexpr int kRsrcFlags = 0x00020000;
+constexpr uint32_t kOffNone = 0x80000000u;
+
+// One element through a buffer descriptor, per storage type.
+template <typename IO>
+struct buf_one;
+template <>
+struct buf_one<float> {
+  __device__ static inline float load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+  }
+  __device__ static inline void store(float y, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                      uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), r, off, soff, 0);
+  }
+};
+template <>
+struct buf_one<bf16_t> {
+  __device__ static inline float load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0))
+                           << 16);
+  }
+  __device__ static inline void store(float y, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                      uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(y), r, off, soff, 0);
+  }
+};
+
 // Wave-uniform value (lane 0's), kept in a scalar register.
 __device__ static inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   float* const s_gr = s_el + kBwdWaves * kCh * kElPitch;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
   const int tile = static_cast<int>(logical % s.tiles);
   const int64_t row_seg = logical / s.tiles;
@@ -350,6 +350,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   const bool dvalid = d < s.dim;
   const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
   const bool has_z = p.z != nullptr;
+  const bool has_dz = has_z && p.dz != nullptr;
   // lane (c, g) runs states 2g, 2g+1 of channel c, in the order that
   // sum_pair_half_rows expects: slot k holds state nk[k]
   const int swap = sc >> 2;
@@ -389,35 +390,75 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
 
   float* el = s_el + w * (kCh * kElPitch);
   float* gr = s_gr + w * (kCh * kGrPitch);
+  // Buffer descriptors of one chunk, based at (b, row0) and the chunk's
+  // lowest storage step: t0 in forward time, L - kBwdT - t0 in reverse time
+  // (that base may lie before the tensor; only in-range offsets are used).
+  // Offsets inside a chunk tile are loop-invariant 32-bit byte offsets, and
+  // kOffNone reads 0 or drops the store.  An absent tensor gets an empty range.
+  constexpr int64_t es = sizeof(IO);
+  auto rsrc = [&](const void* ptr, const int64_t* st, int row0, int t0, bool present)
+      __attribute__((always_inline)) {
+    const int64_t ts = s.reverse ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : t0;
+    const char* base = static_cast<const char*>(present ? ptr : p.u) +
+                       (present ? (b * st[0] + static_cast<int64_t>(row0) * st[1] + ts * st[2]) * es : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, present ? kRsrcRange : 0,
+                                             kRsrcFlags);
+  };
+  auto tile_off = [&](const int64_t* st, int row, int tt) __attribute__((always_inline)) {
+    const int tl = s.reverse ? kBwdT - 1 - tt : tt;
+    return static_cast<uint32_t>((row * st[1] + tl * st[2]) * es);
+  };
+  // lane (c, j) owns steps 2j, 2j+1 of channel c; thread (r, i) = (tid / 16,
+  // tid % 16) loads row r of B (r < 16) or C (r >= 16, the upper four waves)
+  // at step i
+  uint32_t o_u[2], o_dr[2], o_do[2], o_z[2], o_du[2], o_ddr[2], o_dz[2], o_ck[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int tt = 2 * sg + e;
+    o_u[e] = dvalid ? tile_off(s.su, sc, tt) : kOffNone;
+    o_dr[e] = dvalid ? tile_off(s.sd, sc, tt) : kOffNone;
+    o_do[e] = dvalid ? tile_off(s.sdo, sc, tt) : kOffNone;
+    o_z[e] = dvalid ? tile_off(s.sz, sc, tt) : kOffNone;
+    o_du[e] = dvalid ? tile_off(s.sdu, sc, tt) : kOffNone;
+    o_ddr[e] = dvalid ? tile_off(s.sddr, sc, tt) : kOffNone;
+    o_dz[e] = dvalid ? tile_off(s.sdz, sc, tt) : kOffNone;
+    o_ck[e] = static_cast<uint32_t>((sc * kMaxState + nk[e]) * sizeof(float));
+  }
+  const bool bc_is_c = w >= kBwdWaves / 2;
+  const IO* bc_ptr = bc_is_c ? Cm : Bm;
+  const int64_t bc_st[3] = {bc_is_c ? s.sC[0] : s.sB[0], bc_is_c ? s.sC[1] : s.sB[1],
+                            bc_is_c ? s.sC[2] : s.sB[2]};
+  const int bc_n = (tid >> 4) & (kMaxState - 1), bc_t = tid & 15;
+  const uint32_t o_bc = bc_n < s.dstate ? tile_off(bc_st, bc_n, bc_t) : kOffNone;
+  const int64_t ck_row0 = static_cast<int64_t>(b) * s.tiles * kBwdCh + d0;
+
   // Raw inputs of a chunk, issued one chunk ahead of use: one B or C value
-  // per thread, u, delta_raw, dout and z for the lane's two elements (lane
-  // (c, j) = (lane % 8, lane / 8) owns steps 2j, 2j+1 of channel c), and the
-  // checkpoint of the lane's two states.
-  const IO* z_base = has_z ? zz : u;
+  // per thread, u, delta_raw, dout and z for the lane's two elements, and the
+  // checkpoint of the lane's two states.  A chunk before the segment loads
+  // nothing.
   float rbc, ru[2], rx[2], rgo[2], rz[2], rck[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
     const bool qok = q >= q_begin;
-    {
-      const int r = tid >> 4, n = r & 15, t = t0 + (tid & 15);
-      const bool ok = qok && n < s.dstate && t < s.seqlen;
-      rbc = r < kMaxState ? ld_masked(Bm, b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2], ok)
-                          : ld_masked(Cm, b * s.sC[0] + n * s.sC[1] + tstore(s, t) * s.sC[2], ok);
-    }
+    const auto r_bc = rsrc(bc_ptr, bc_st, 0, t0, true);
+    rbc = buf_one<IO>::load(r_bc, (qok && t0 + bc_t < s.seqlen) ? o_bc : kOffNone, 0);
+    const auto r_u = rsrc(u, s.su, d0, t0, true);
+    const auto r_dr = rsrc(dr, s.sd, d0, t0, true);
+    const auto r_do = rsrc(dout, s.sdo, d0, t0, true);
+    const auto r_z = rsrc(zz, s.sz, d0, t0, has_z);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int t = t0 + 2 * sg + e;
-      const bool ok = qok && dvalid && t < s.seqlen;
-      const int64_t ts = tstore(s, t);
-      ru[e] = ld_masked(u, b * s.su[0] + d * s.su[1] + ts * s.su[2], ok);
-      rx[e] = ld_masked(dr, b * s.sd[0] + d * s.sd[1] + ts * s.sd[2], ok);
-      rgo[e] = ld_masked(dout, b * s.sdo[0] + d * s.sdo[1] + ts * s.sdo[2], ok);
-      rz[e] = ld_masked(z_base, b * s.sz[0] + d * s.sz[1] + ts * s.sz[2], ok && has_z);
+      const bool ok = qok && t0 + 2 * sg + e < s.seqlen;
+      ru[e] = buf_one<IO>::load(r_u, ok ? o_u[e] : kOffNone, 0);
+      rx[e] = buf_one<IO>::load(r_dr, ok ? o_dr[e] : kOffNone, 0);
+      rgo[e] = buf_one<IO>::load(r_do, ok ? o_do[e] : kOffNone, 0);
+      rz[e] = buf_one<IO>::load(r_z, ok ? o_z[e] : kOffNone, 0);
     }
+    const auto r_ck = __builtin_amdgcn_make_buffer_rsrc(
+        p.ckpt + (static_cast<int64_t>(q) * s.nchan_pad + ck_row0) * kMaxState, 0, kRsrcRange,
+        kRsrcFlags);
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      rck[k] = p.ckpt[(static_cast<int64_t>(qok ? q : q_begin) * s.nchan_pad + chan_row) *
-                          kMaxState + nk[k]];
+    for (int k = 0; k < 2; ++k) rck[k] = buf_one<float>::load(r_ck, qok ? o_ck[k] : kOffNone, 0);
   };
   load_chunk(q_end - 1);
   for (int q = q_end - 1; q >= q_begin; --q) {
@@ -472,14 +513,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     __builtin_amdgcn_wave_barrier();
     // ---- R: reverse walk ----
     // Per step the sums over the wave's 8 channels of the dB and dC terms are
-    // finished at once (one DPP tree each for the lane's two states) and
-    // written by lanes c = 0 and c = 4 of each state group; the sums over
-    // states collect 4 steps for one cross-lane tree.
+    // finished at once (one DPP tree each for the lane's two states); lanes
+    // c = 0 and c = 4 of each state group write them for 4 steps at a time,
+    // so that the 4 steps stay one branch-free block.  The sums over states
+    // collect 4 steps for one cross-lane tree.
     float* red = s_red + w * kRedSize;
     const bool writer = (sc & 3) == 0;
 #pragma unroll
     for (int t4 = kBwdT - 4; t4 >= 0; t4 -= 4) {
-      float qb[4], qa[4];
+      float qb[4], qa[4], vb[4], vc[4];
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         const int t = t4 + i;
@@ -487,12 +529,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
         float G[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) G[k] = fmaf(dd.z, k == 0 ? rc0[t] : rc1[t], g[k]);
-        float pb = sum_pair_half_rows(G[0] * dd.y, G[1] * dd.y);
-        float pc = sum_pair_half_rows(dd.z * hh[t][0], dd.z * hh[t][1]);
-        // finish both sums in every lane (one DPP add each) rather than let
-        // the compiler move the last add into the writers' branch as a move
-        // plus an add
-        asm volatile("" : "+v"(pb), "+v"(pc));
+        vb[i] = sum_pair_half_rows(G[0] * dd.y, G[1] * dd.y);
+        vc[i] = sum_pair_half_rows(dd.z * hh[t][0], dd.z * hh[t][1]);
         float sb = G[0] * rb0[t];
         sb = fmaf(G[1], rb1[t], sb);
         float sa = 0.0f;
@@ -506,10 +544,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
         }
         qb[i] = sb;
         qa[i] = sa;
-        if (writer) {
-          red[nk[0] * kBwdT + t] = pb;
-          red[(kMaxState + nk[0]) * kBwdT + t] = pc;
-        }
+      }
+      // finish the sums in every lane (one DPP add each) rather than let the
+      // compiler move the last add into the writers' branch as a move plus
+      // an add
+      asm volatile("" : "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
+      asm volatile("" : "+v"(vc[0]), "+v"(vc[1]), "+v"(vc[2]), "+v"(vc[3]));
+      if (writer) {
+        *reinterpret_cast<f4*>(red + nk[0] * kBwdT + t4) = f4{vb[0], vb[1], vb[2], vb[3]};
+        *reinterpret_cast<f4*>(red + (kMaxState + nk[0]) * kBwdT + t4) = f4{vc[0], vc[1], vc[2], vc[3]};
       }
       const float gb = reduce_groups(qb[0], qb[1], qb[2], qb[3]);
       const float ga = reduce_groups(qa[0], qa[1], qa[2], qa[3]);
@@ -528,6 +571,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     }
 
     // ---- O: du, ddelta_raw and dz per element ----
+    const auto r_du = rsrc(du_out, s.sdu, d0, t0, true);
+    const auto r_ddr = rsrc(ddr_out, s.sddr, d0, t0, true);
+    const auto r_dz = rsrc(dz_out, s.sdz, d0, t0, has_dz);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
@@ -536,16 +582,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       const float2 gv = *reinterpret_cast<const float2*>(gr + sc * kGrPitch + 8 * tt + 4);
       const float du = fmaf(sv.z, skip, sv.x * gv.x);
       const float ddr = fmaf(ev.x, gv.x, gv.y) * ev.y;
-      if (dvalid && t < s.seqlen) {
-        io_traits<IO>::store(du_out + b * s.sdu[0] + d * s.sdu[1] + tstore(s, t) * s.sdu[2], du);
-        io_traits<IO>::store(ddr_out + b * s.sddr[0] + d * s.sddr[1] + tstore(s, t) * s.sddr[2], ddr);
-        if (has_z && dz_out != nullptr) {
-          // dz = dout * (C.h + D u) * silu'(z), silu'(z) = sig(z) (1 + z (1 - sig(z)))
-          const float y = fmaf(skip, ev.x, sv.w);
-          const float sz = sigmoid(ev.w);
-          io_traits<IO>::store(dz_out + b * s.sdz[0] + d * s.sdz[1] + tstore(s, t) * s.sdz[2],
-                               ev.z * y * (sz * fmaf(ev.w, 1.0f - sz, 1.0f)));
-        }
+      const bool ok = t < s.seqlen;
+      buf_one<IO>::store(du, r_du, ok ? o_du[e] : kOffNone, 0);
+      buf_one<IO>::store(ddr, r_ddr, ok ? o_ddr[e] : kOffNone, 0);
+      if (has_dz) {
+        // dz = dout * (C.h + D u) * silu'(z), silu'(z) = sig(z) (1 + z (1 - sig(z)))
+        const float y = fmaf(skip, ev.x, sv.w);
+        const float sz = sigmoid(ev.w);
+        buf_one<IO>::store(ev.z * y * (sz * fmaf(ev.w, 1.0f - sz, 1.0f)), r_dz,
+                           ok ? o_dz[e] : kOffNone, 0);
+      }
+      if (dvalid && ok) {
         acc_db += ddr;
         acc_dD = fmaf(sv.z, ev.x, acc_dD);
       }

@@ -55,13 +55,6 @@
 
 namespace mss {
 
-// Raw buffer descriptors: the range keeps every valid 32-bit tile offset in
-// bounds; kOffNone is past it, so accesses with that offset read 0 / write
-// nothing.  Flags: the gfx9 raw-buffer data format word.
-constexpr int kRsrcRange = 0x7FFFFFF0;
-constexpr int kRsrcFlags = 0x00020000;
-constexpr uint32_t kOffNone = 0x80000000u;
-
 using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
@@ -85,11 +78,11 @@ struct vec_io<float> {
     __builtin_amdgcn_raw_buffer_store_b128(w, r, off, soff, 0);
   }
   __device__ static inline float load_one(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+    return buf_one<float>::load(r, off, soff);
   }
   __device__ static inline void store_one(float y, __amdgpu_buffer_rsrc_t r, uint32_t off,
                                           uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), r, off, soff, 0);
+    buf_one<float>::store(y, r, off, soff);
   }
 };
 template <>
@@ -113,12 +106,11 @@ struct vec_io<bf16_t> {
     __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, 0);
   }
   __device__ static inline float load_one(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
-    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0))
-                           << 16);
+    return buf_one<bf16_t>::load(r, off, soff);
   }
   __device__ static inline void store_one(float y, __amdgpu_buffer_rsrc_t r, uint32_t off,
                                           uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(y), r, off, soff, 0);
+    buf_one<bf16_t>::store(y, r, off, soff);
   }
 };
 
