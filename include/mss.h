@@ -325,7 +325,7 @@ mss_status mss_selective_state_update(const mss_step_args *args, void *stream);
 
 /* Bytes of device workspace mss_selective_scan_bwd needs: the states entering
  * every 16-step chunk (batch * dim * seqlen * 4 bytes, rounded up) and the
- * per-64-channel partial sums of dB and dC (batch * ceil(dim/64) * 32 *
+ * per-32-channel partial sums of dB and dC (batch * ceil(dim/32) * 32 *
  * seqlen * 4 bytes).  Depends only on the shapes.  Returns 0 and sets
  * *status on invalid shapes. */
 size_t mss_selective_scan_bwd_workspace_size(const mss_scan_bwd_args *args, mss_status *status);

@@ -157,10 +157,11 @@ struct BwdPlan {
   size_t workspace = 0;
 };
 
-// Backward time segments: a shape with fewer (row, 64-channel tile) pairs
-// than this is split along time until it reaches it, with segments of at
-// least kBwdMinSegChunks chunks.
-constexpr int64_t kBwdSplitBelow = 512;
+// Backward time segments: a shape with fewer (row, channel tile) pairs than
+// the reverse walk's resident workgroups (three per CU on 256 CUs) is split
+// along time until it fills them, with segments of at least kBwdMinSegChunks
+// chunks.
+constexpr int64_t kBwdSplitBelow = 768;
 constexpr int64_t kBwdMinSegChunks = 8;
 
 mss_status check_bwd_shape(const mss_scan_bwd_args* a) {

@@ -126,10 +126,11 @@ hipError_t launch_conv_step(const ConvStepShape& s, const ConvStepPtrs& p, bool 
 // Selective-scan backward.  A workgroup of kBwdWaves waves owns kBwdCh
 // channels of one batch row (kCh per wave, lanes as in the forward scan:
 // lane (g, c) runs states 2g, 2g+1 of channel c) and walks the sequence in
-// chunks of kBwdT steps, the last chunk first.
+// chunks of kBwdT steps, the last chunk first.  Four-wave workgroups at up
+// to 168 VGPRs and 46 KB of LDS put three workgroups on a CU.
 constexpr int kBwdT = 16;
-constexpr int kBwdWaves = 8;
-constexpr int kBwdCh = kCh * kBwdWaves;  // 64
+constexpr int kBwdWaves = 4;
+constexpr int kBwdCh = kCh * kBwdWaves;  // 32
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
 struct BwdShape {

@@ -30,8 +30,9 @@
 //   1. ckpt_kernel: the forward recurrence (no outputs) recording the state
 //      entering every kBwdT-step chunk.  One wave per 8 channels, lanes as in
 //      the forward: lane (g, c) runs states 2g, 2g+1 of channel c.
-//   2. bwd_kernel: a workgroup of kBwdWaves waves owns 64 channels of one
-//      batch row and walks the chunks from the last to the first.  Per chunk:
+//   2. bwd_kernel: a workgroup of kBwdWaves waves owns kBwdCh channels of
+//      one batch row and walks the chunks from the last to the first.  Per
+//      chunk:
 //        E  inputs of the chunk: B and C into LDS (shared by the workgroup),
 //           per element delta, delta*u and dy into LDS (per wave);
 //        F  the chunk's states recomputed forward from its checkpoint, kept
@@ -324,17 +325,19 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
 
 // ---------------------------------------------------------------- pass 2 ---
 template <typename IO>
-__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_kernel(BwdShape s, BwdPtrs p) {
   // One LDS block, B/C first and the reduction rows next, so that the rows
   // addressed with per-lane bases plus a step offset stay within reach of the
-  // 16-bit DS instruction offset.
+  // 16-bit DS instruction offset.  B/C and the reduction rows are double
+  // buffered by chunk parity, so that one workgroup barrier per chunk orders
+  // every shared access (see the loop).
   constexpr int kRedSize = 2 * kMaxState * kBwdT;
   constexpr int kBcSize = 2 * kMaxState * kBcPitch;
   __shared__ __attribute__((aligned(16)))
-  float smem[kBcSize + kBwdWaves * (kRedSize + kCh * kElPitch + kCh * kGrPitch)];
-  float* const s_bc = smem;
-  float* const s_red = smem + kBcSize;
-  float* const s_el = s_red + kBwdWaves * kRedSize;
+  float smem[2 * kBcSize + kBwdWaves * (2 * kRedSize + kCh * kElPitch + kCh * kGrPitch)];
+  float* const s_bc2 = smem;
+  float* const s_red2 = smem + 2 * kBcSize;
+  float* const s_el = s_red2 + 2 * kBwdWaves * kRedSize;
   float* const s_gr = s_el + kBwdWaves * kCh * kElPitch;
 
   const int tid = threadIdx.x;
@@ -424,24 +427,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     o_dz[e] = dvalid ? tile_off(s.sdz, sc, tt) : kOffNone;
     o_ck[e] = static_cast<uint32_t>((sc * kMaxState + nk[e]) * sizeof(float));
   }
-  const bool bc_is_c = w >= kBwdWaves / 2;
-  const IO* bc_ptr = bc_is_c ? Cm : Bm;
-  const int64_t bc_st[3] = {bc_is_c ? s.sC[0] : s.sB[0], bc_is_c ? s.sC[1] : s.sB[1],
-                            bc_is_c ? s.sC[2] : s.sB[2]};
-  const int bc_n = (tid >> 4) & (kMaxState - 1), bc_t = tid & 15;
-  const uint32_t o_bc = bc_n < s.dstate ? tile_off(bc_st, bc_n, bc_t) : kOffNone;
+  // B/C rows of a chunk: thread (r, i) = (tid / 16, tid % 16) covers step i of
+  // rows r + j kBcRowStep, j < kBcPerThread; rows r < 16 are B, the others C
+  // (which tensor is wave-uniform)
+  constexpr int kBcPerThread = 2 * kMaxState * kBwdT / kBwdThreads;
+  constexpr int kBcRowStep = kBwdThreads / kBwdT;
+  static_assert(kBcPerThread * kBwdThreads == 2 * kMaxState * kBwdT, "B/C tile split");
+  const int bc_t = tid & 15;
+  uint32_t o_bc[kBcPerThread];
+  auto bc_row = [&](int j) __attribute__((always_inline)) { return (tid >> 4) + j * kBcRowStep; };
+  auto bc_is_c = [&](int j) __attribute__((always_inline)) {
+    return kBcPerThread == 1 ? w >= kBwdWaves / 2 : j >= kBcPerThread / 2;
+  };
+#pragma unroll
+  for (int j = 0; j < kBcPerThread; ++j) {
+    const int n = bc_row(j) & (kMaxState - 1);
+    const int64_t st[3] = {0, bc_is_c(j) ? s.sC[1] : s.sB[1], bc_is_c(j) ? s.sC[2] : s.sB[2]};
+    o_bc[j] = n < s.dstate ? tile_off(st, n, bc_t) : kOffNone;
+  }
   const int64_t ck_row0 = static_cast<int64_t>(b) * s.tiles * kBwdCh + d0;
 
   // Raw inputs of a chunk, issued one chunk ahead of use: one B or C value
   // per thread, u, delta_raw, dout and z for the lane's two elements, and the
   // checkpoint of the lane's two states.  A chunk before the segment loads
   // nothing.
-  float rbc, ru[2], rx[2], rgo[2], rz[2], rck[2];
+  float rbc[kBcPerThread], ru[2], rx[2], rgo[2], rz[2], rck[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
     const bool qok = q >= q_begin;
-    const auto r_bc = rsrc(bc_ptr, bc_st, 0, t0, true);
-    rbc = buf_one<IO>::load(r_bc, (qok && t0 + bc_t < s.seqlen) ? o_bc : kOffNone, 0);
+#pragma unroll
+    for (int j = 0; j < kBcPerThread; ++j) {
+      const auto r_bc = bc_is_c(j) ? rsrc(Cm, s.sC, 0, t0, true) : rsrc(Bm, s.sB, 0, t0, true);
+      rbc[j] = buf_one<IO>::load(r_bc, (qok && t0 + bc_t < s.seqlen) ? o_bc[j] : kOffNone, 0);
+    }
     const auto r_u = rsrc(u, s.su, d0, t0, true);
     const auto r_dr = rsrc(dr, s.sd, d0, t0, true);
     const auto r_do = rsrc(dout, s.sdo, d0, t0, true);
@@ -460,12 +478,36 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
 #pragma unroll
     for (int k = 0; k < 2; ++k) rck[k] = buf_one<float>::load(r_ck, qok ? o_ck[k] : kOffNone, 0);
   };
+  // The workgroup's dB / dC partial of chunk q (the thread's B/C tile
+  // positions): the sum over the waves of their reduction rows.
+  auto chunk_partial = [&](int q) __attribute__((always_inline)) {
+    const float* red = s_red2 + (q & 1) * (kBwdWaves * kRedSize);
+    const int tt = tid & 15, t = q * kBwdT + tt;
+#pragma unroll
+    for (int j = 0; j < kBcPerThread; ++j) {
+      const int r = bc_row(j);
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kBwdWaves; ++ww) sum += red[ww * kRedSize + r * kBwdT + tt];
+      if ((r & 15) < s.dstate && t < s.seqlen)
+        p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t] = sum;
+    }
+  };
+
+  // One barrier per chunk.  Iteration q writes B/C buffer q & 1 before it and
+  // reduction buffer q & 1 after it, and sums reduction buffer (q + 1) & 1
+  // (chunk q + 1) right after it.  Every wave that passes the barrier of
+  // iteration q has seen all waves finish iteration q + 1, the last to read
+  // B/C buffer q & 1 (chunk q + 2) or to sum reduction buffer q & 1 (chunk
+  // q + 2), and to write reduction buffer (q + 1) & 1.
   load_chunk(q_end - 1);
   for (int q = q_end - 1; q >= q_begin; --q) {
     const int t0 = q * kBwdT;
+    float* const s_bc = s_bc2 + (q & 1) * kBcSize;
     // ---- E: B and C into LDS; per element, the scan's inputs into s_el and
     // the values the output phase needs into s_gr ----
-    s_bc[(tid >> 4) * kBcPitch + (tid & 15)] = rbc;
+#pragma unroll
+    for (int j = 0; j < kBcPerThread; ++j) s_bc[bc_row(j) * kBcPitch + bc_t] = rbc[j];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
@@ -477,7 +519,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       *reinterpret_cast<f4*>(el + sc * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
       *reinterpret_cast<f4*>(gr + sc * kGrPitch + 8 * tt) = f4{ru[e], sig, rgo[e], rz[e]};
     }
-    float hs[2], h[2], hh[kBwdT][2], aa[kBwdT][2];
+    float hs[2], h[2], hh[kBwdT][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       hs[k] = rck[k];
@@ -485,8 +527,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     }
     load_chunk(q - 1);
     __syncthreads();
+    if (q + 1 < q_end) chunk_partial(q + 1);
 
-    // ---- F: the chunk's states and decays from its checkpoint ----
+    // ---- F: the chunk's states from its checkpoint ----
     const float* rb0 = s_bc + nk[0] * kBcPitch;
     const float* rb1 = s_bc + nk[1] * kBcPitch;
     const float* rc0 = s_bc + (kMaxState + nk[0]) * kBcPitch;
@@ -500,10 +543,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       for (int i = 0; i < 4; ++i) {
         const int t = t4 + i;
         const f4 dd = ld4(rdd + 4 * t);
-        aa[t][0] = fast_exp2(dd.x * A2[0]);
-        aa[t][1] = fast_exp2(dd.x * A2[1]);
-        h[0] = fmaf(aa[t][0], h[0], dd.y * rb0[t]);
-        h[1] = fmaf(aa[t][1], h[1], dd.y * rb1[t]);
+        h[0] = fmaf(fast_exp2(dd.x * A2[0]), h[0], dd.y * rb0[t]);
+        h[1] = fmaf(fast_exp2(dd.x * A2[1]), h[1], dd.y * rb1[t]);
         hh[t][0] = h[0];
         hh[t][1] = h[1];
         yp[i] = fmaf(rc1[t], h[1], rc0[t] * h[0]);
@@ -517,7 +558,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
     // c = 0 and c = 4 of each state group write them for 4 steps at a time,
     // so that the 4 steps stay one branch-free block.  The sums over states
     // collect 4 steps for one cross-lane tree.
-    float* red = s_red + w * kRedSize;
+    float* red = s_red2 + (q & 1) * (kBwdWaves * kRedSize) + w * kRedSize;
     const bool writer = (sc & 3) == 0;
 #pragma unroll
     for (int t4 = kBwdT - 4; t4 >= 0; t4 -= 4) {
@@ -536,7 +577,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
         float sa = 0.0f;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-          const float ga = G[k] * aa[t][k];
+          const float ga = G[k] * fast_exp2(dd.x * A2[k]);
           const float r = ga * (t > 0 ? hh[t > 0 ? t - 1 : 0][k] : hs[k]);
           dA[k] = fmaf(r, dd.x, dA[k]);
           sa = fmaf(r, An[k], sa);
@@ -558,17 +599,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
       const float ga = reduce_groups(qa[0], qa[1], qa[2], qa[3]);
       *reinterpret_cast<float2*>(gr + sc * kGrPitch + 8 * (t4 + ystep) + 4) = make_float2(gb, ga);
     }
-    __syncthreads();
-
-    // ---- the workgroup's dB / dC partial of the chunk (one value per thread) ----
-    {
-      const int r = tid >> 4, tt = tid & 15, t = t0 + tt;
-      float sum = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < kBwdWaves; ++ww) sum += s_red[ww * kRedSize + r * kBwdT + tt];
-      if ((r & 15) < s.dstate && t < s.seqlen)
-        p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t] = sum;
-    }
+    __builtin_amdgcn_wave_barrier();  // R's per-element sums, written by other lanes
 
     // ---- O: du, ddelta_raw and dz per element ----
     const auto r_du = rsrc(du_out, s.sdu, d0, t0, true);
@@ -612,7 +643,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(BwdShape s, BwdPtrs p)
   }
   // dD and ddt_bias: the 8 lanes of a channel (lanes c + 8j) meet in LDS
   __syncthreads();
-  float* tmp = s_red + w * kRedSize;
+  chunk_partial(q_begin);
+  // the other reduction buffer is free: its last reader (chunk q_begin + 1's
+  // sum) ran before the barrier
+  float* tmp = s_red2 + ((q_begin & 1) ^ 1) * (kBwdWaves * kRedSize) + w * kRedSize;
   tmp[lane] = acc_dD;
   tmp[64 + lane] = acc_db;
   __builtin_amdgcn_wave_barrier();

@@ -356,10 +356,11 @@ def test_bwd_workspace_size():
     st = ctypes.c_int(-1)
     n = lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st))
     assert st.value == 0
-    # checkpoints: 7 chunks x 2*64*2 padded channels x 16 states; partials: 2 rows x 2
-    # tiles x 32 x 100 steps; per-row sums 2 x 96 x 18 (each rounded up to 256 B)
+    # the reverse walk takes 32-channel tiles: checkpoints 7 chunks x 2*3*32 padded
+    # channels x 16 states; partials 2 rows x 3 tiles x 32 x 100 steps; per-row sums
+    # 2 x 96 x 18 (each rounded up to 256 B)
     r = lambda v: (v + 255) // 256 * 256
-    assert n == r(7 * 2 * 128 * 16 * 4) + r(2 * 2 * 32 * 100 * 4) + r(2 * 96 * 18 * 4)
+    assert n == r(7 * 2 * 96 * 16 * 4) + r(2 * 3 * 32 * 100 * 4) + r(2 * 96 * 18 * 4)
     a.dstate = 0
     assert lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st)) == 0
     assert st.value == code("MSS_ERR_UNSUPPORTED_DSTATE")
