@@ -91,6 +91,37 @@ __device__ inline int64_t tstore(const BwdShape& s, int t) {
   return s.reverse ? static_cast<int64_t>(s.seqlen) - 1 - t : t;
 }
 
+// Buffer descriptor of one chunk tile of a [b][row][t] tensor: based at
+// (b, row0) and the chunk's lowest storage step, t0 in forward time and
+// L - kBwdT - t0 in reverse time (that base may lie before the tensor; only
+// in-range offsets are used).  An absent tensor gets an empty range based at
+// `fallback`, so that its loads read 0 and its stores are dropped.
+__device__ inline __amdgpu_buffer_rsrc_t chunk_rsrc(const BwdShape& s, const void* ptr,
+                                                    const int64_t* st, int64_t es, int b, int row0,
+                                                    int t0, bool present, const void* fallback) {
+  const int64_t ts = s.reverse ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : t0;
+  const char* base = static_cast<const char*>(present ? ptr : fallback) +
+                     (present ? (b * st[0] + static_cast<int64_t>(row0) * st[1] + ts * st[2]) * es : 0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, present ? kRsrcRange : 0,
+                                           kRsrcFlags);
+}
+
+// Byte offset of (row, logical step tt of the chunk) inside a chunk tile
+// (loop-invariant; the host checks that tiles span less than 2 GiB).
+__device__ inline uint32_t chunk_off(const BwdShape& s, const int64_t* st, int64_t es, int row,
+                                     int tt) {
+  const int tl = s.reverse ? kBwdT - 1 - tt : tt;
+  return static_cast<uint32_t>((row * st[1] + tl * st[2]) * es);
+}
+
+__device__ inline void store2(float a, float b, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  v[0] = __float_as_uint(a);
+  v[1] = __float_as_uint(b);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
 __device__ inline int64_t xcd_order(int64_t lin, int64_t nwg) {
   const int64_t xcd = lin % kXcdsBwd;
   const int64_t per = nwg / kXcdsBwd, extra = nwg % kXcdsBwd;
@@ -262,37 +293,49 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   }
   const int q_begin = seg * s.seg_chunks;
   const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
-  const IO* Bm = static_cast<const IO*>(p.B);
-  const IO* u = static_cast<const IO*>(p.u);
-  const IO* dr = static_cast<const IO*>(p.delta_raw);
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
-  // Raw inputs of a chunk, issued one chunk ahead of use: B (lane covers row
-  // lane / 4, steps 4 (lane % 4) .. + 3) and u, delta_raw (lane (c, j) covers
-  // steps 2j, 2j+1 of channel c).
+  // Raw inputs of a chunk, issued one chunk ahead of use through buffer
+  // descriptors (chunk_rsrc) with loop-invariant lane offsets: B (lane covers
+  // row lane / 4, steps 4 (lane % 4) .. + 3) and u, delta_raw (lane (c, j)
+  // covers steps 2j, 2j+1 of channel c).
+  constexpr int64_t es = sizeof(IO);
+  const int bn = lane >> 2;
+  uint32_t o_b[4], o_u[2], o_dr[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o_b[i] = bn < s.dstate ? chunk_off(s, s.sB, es, bn, (lane & 3) * 4 + i) : kOffNone;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    o_u[e] = dvalid ? chunk_off(s, s.su, es, sc, 2 * sg + e) : kOffNone;
+    o_dr[e] = dvalid ? chunk_off(s, s.sd, es, sc, 2 * sg + e) : kOffNone;
+  }
+  const uint32_t o_ck = static_cast<uint32_t>((sc * kMaxState + 2 * sg) * sizeof(float));
+  const int64_t ck_row0 = static_cast<int64_t>(b) * s.tiles * kBwdCh + dg;  // wave-uniform
   float rb[4], ru[2], rx[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
     const bool qok = q < q_end;
+    const auto r_b = chunk_rsrc(s, p.B, s.sB, es, b, 0, t0, true, p.u);
+    const auto r_u = chunk_rsrc(s, p.u, s.su, es, b, dg, t0, true, p.u);
+    const auto r_dr = chunk_rsrc(s, p.delta_raw, s.sd, es, b, dg, t0, true, p.u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = lane >> 2, t = t0 + (lane & 3) * 4 + i;
-      rb[i] = ld_masked(Bm, b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2],
-                        qok && n < s.dstate && t < s.seqlen);
-    }
+    for (int i = 0; i < 4; ++i)
+      rb[i] = buf_one<IO>::load(r_b, (qok && t0 + (lane & 3) * 4 + i < s.seqlen) ? o_b[i] : kOffNone, 0);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int t = t0 + 2 * sg + e;
-      const bool ok = qok && dvalid && t < s.seqlen;
-      ru[e] = ld_masked(u, b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2], ok);
-      rx[e] = ld_masked(dr, b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2], ok);
+      const bool ok = qok && t0 + 2 * sg + e < s.seqlen;
+      ru[e] = buf_one<IO>::load(r_u, ok ? o_u[e] : kOffNone, 0);
+      rx[e] = buf_one<IO>::load(r_dr, ok ? o_dr[e] : kOffNone, 0);
     }
   };
   load_chunk(q_begin);
   for (int q = q_begin; q < q_end; ++q) {
     const int t0 = q * kBwdT;
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      p.ckpt[(static_cast<int64_t>(q) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] = h[k];
+    store2(h[0], h[1],
+           __builtin_amdgcn_make_buffer_rsrc(
+               p.ckpt + (static_cast<int64_t>(q) * s.nchan_pad + ck_row0) * kMaxState, 0,
+               kRsrcRange, kRsrcFlags),
+           o_ck);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_b[(lane >> 2) * kBcPitch + (lane & 3) * 4 + i] = rb[i];
 #pragma unroll
@@ -300,7 +343,8 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
       const float x = rx[e] + bias;
-      const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      const float sp = s.softplus ? softplus(x) : x;
+      const float dl = ok ? sp : 0.0f;
       *reinterpret_cast<float2*>(s_dd + sc * kDdPitch2 + 2 * tt) = make_float2(dl, dl * ru[e]);
     }
     load_chunk(q + 1);
@@ -393,23 +437,16 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 
   float* el = s_el + w * (kCh * kElPitch);
   float* gr = s_gr + w * (kCh * kGrPitch);
-  // Buffer descriptors of one chunk, based at (b, row0) and the chunk's
-  // lowest storage step: t0 in forward time, L - kBwdT - t0 in reverse time
-  // (that base may lie before the tensor; only in-range offsets are used).
-  // Offsets inside a chunk tile are loop-invariant 32-bit byte offsets, and
-  // kOffNone reads 0 or drops the store.  An absent tensor gets an empty range.
+  // Chunk tiles are read and written through buffer descriptors (chunk_rsrc)
+  // with loop-invariant 32-bit lane offsets; kOffNone reads 0 or drops the
+  // store.
   constexpr int64_t es = sizeof(IO);
   auto rsrc = [&](const void* ptr, const int64_t* st, int row0, int t0, bool present)
       __attribute__((always_inline)) {
-    const int64_t ts = s.reverse ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : t0;
-    const char* base = static_cast<const char*>(present ? ptr : p.u) +
-                       (present ? (b * st[0] + static_cast<int64_t>(row0) * st[1] + ts * st[2]) * es : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, present ? kRsrcRange : 0,
-                                             kRsrcFlags);
+    return chunk_rsrc(s, ptr, st, es, b, row0, t0, present, p.u);
   };
   auto tile_off = [&](const int64_t* st, int row, int tt) __attribute__((always_inline)) {
-    const int tl = s.reverse ? kBwdT - 1 - tt : tt;
-    return static_cast<uint32_t>((row * st[1] + tl * st[2]) * es);
+    return chunk_off(s, st, es, row, tt);
   };
   // lane (c, j) owns steps 2j, 2j+1 of channel c; thread (r, i) = (tid / 16,
   // tid % 16) loads row r of B (r < 16) or C (r >= 16, the upper four waves)
