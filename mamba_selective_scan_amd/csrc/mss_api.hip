@@ -540,6 +540,20 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
   else std::memset(s.sz, 0, sizeof(s.sz));
   if (a->dz != nullptr) std::memcpy(s.sdz, a->dz_stride, sizeof(s.sdz));
   else std::memset(s.sdz, 0, sizeof(s.sdz));
+  // Step pairs: every (b, d) row starts on a pair boundary and holds whole
+  // pairs, so that a 2-element access never straddles a row or the tensor.
+  {
+    const void* xp[] = {a->u, a->delta_raw, a->dout, a->z, a->du, a->ddelta_raw, a->dz};
+    const int64_t* xst[] = {a->u_stride, a->delta_stride, a->dout_stride, a->z_stride,
+                            a->du_stride, a->ddelta_stride, a->dz_stride};
+    bool ok = a->seqlen % 2 == 0;
+    for (int i = 0; i < 7 && ok; ++i) {
+      if (xp[i] == nullptr) continue;
+      ok = xst[i][2] == 1 && aligned(xp[i], 2 * es) && (a->batch == 1 || xst[i][0] % 2 == 0) &&
+           (a->dim == 1 || xst[i][1] % 2 == 0);
+    }
+    s.pairs = ok ? 1 : 0;
+  }
   char* ws = static_cast<char*>(a->workspace);
   mss::BwdPtrs p{};
   p.u = a->u;

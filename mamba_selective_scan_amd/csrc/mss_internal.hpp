@@ -146,6 +146,8 @@ struct BwdShape {
   int64_t sB[3], sC[3], sdB[3], sdC[3];     // (b, n, t)
   int64_t sA[2];                            // A_log: (d, n)
   int reverse;                              // logical step tau is storage step seqlen-1-tau
+  int pairs;  // the reverse walk moves u, delta_raw, dout, z, du, ddelta_raw, dz
+              // as pairs of adjacent steps (unit time stride, even length and strides)
 };
 
 struct BwdPtrs {

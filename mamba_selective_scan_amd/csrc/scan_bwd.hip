@@ -114,6 +114,59 @@ __device__ inline uint32_t chunk_off(const BwdShape& s, const int64_t* st, int64
   return static_cast<uint32_t>((row * st[1] + tl * st[2]) * es);
 }
 
+// Two adjacent elements of one row through a buffer descriptor, the one at
+// the lower address first.
+template <typename IO>
+struct pair_io;
+template <>
+struct pair_io<float> {
+  using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
+  __device__ static inline void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float& lo, float& hi) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    lo = __uint_as_float(v[0]);
+    hi = __uint_as_float(v[1]);
+  }
+  __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float lo, float hi) {
+    u32x2 v;
+    v[0] = __float_as_uint(lo);
+    v[1] = __float_as_uint(hi);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  }
+};
+template <>
+struct pair_io<bf16_t> {
+  __device__ static inline void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float& lo, float& hi) {
+    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    lo = __uint_as_float(v << 16);
+    hi = __uint_as_float(v & 0xffff0000u);
+  }
+  __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float lo, float hi) {
+    __builtin_amdgcn_raw_buffer_store_b32(
+        static_cast<uint32_t>(bf16_bits(lo)) | (static_cast<uint32_t>(bf16_bits(hi)) << 16), r, off,
+        0, 0);
+  }
+};
+
+// A tensor's row (b, row0) as the loop keeps it: its base address and the
+// bytes per time step (32-bit: tiles span less than 2 GiB), three scalar
+// registers; each chunk's descriptor is built from them with one multiply-add.
+struct RowBase {
+  const char* row;
+  int32_t step;
+};
+__device__ inline RowBase row_base(const void* ptr, const int64_t* st, int64_t es, int b, int row0,
+                                   bool present, const void* fallback) {
+  if (!present) return RowBase{static_cast<const char*>(fallback), 0};
+  return RowBase{static_cast<const char*>(ptr) + (b * st[0] + static_cast<int64_t>(row0) * st[1]) * es,
+                 static_cast<int32_t>(st[2] * es)};
+}
+// Descriptor of the chunk whose lowest storage step is ts (an absent tensor:
+// empty range).
+__device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const RowBase& r, int64_t ts, bool present) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(r.row + ts * r.step), 0,
+                                           present ? kRsrcRange : 0, kRsrcFlags);
+}
+
 __device__ inline void store2(float a, float b, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
   u32x2 v;
@@ -368,7 +421,9 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
 }
 
 // ---------------------------------------------------------------- pass 2 ---
-template <typename IO>
+// PAIR: the lane's two elements (steps 2j, 2j+1 of its channel) are one
+// 2-element access per tensor (s.pairs).
+template <typename IO, bool PAIR>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_kernel(BwdShape s, BwdPtrs p) {
   // One LDS block, B/C first and the reduction rows next, so that the rows
   // addressed with per-lane bases plus a step offset stay within reach of the
@@ -441,9 +496,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
   // with loop-invariant 32-bit lane offsets; kOffNone reads 0 or drops the
   // store.
   constexpr int64_t es = sizeof(IO);
-  auto rsrc = [&](const void* ptr, const int64_t* st, int row0, int t0, bool present)
-      __attribute__((always_inline)) {
-    return chunk_rsrc(s, ptr, st, es, b, row0, t0, present, p.u);
+  const RowBase rb_u = row_base(u, s.su, es, b, d0, true, u);
+  const RowBase rb_dr = row_base(dr, s.sd, es, b, d0, true, u);
+  const RowBase rb_do = row_base(dout, s.sdo, es, b, d0, true, u);
+  const RowBase rb_z = row_base(zz, s.sz, es, b, d0, has_z, u);
+  const RowBase rb_du = row_base(du_out, s.sdu, es, b, d0, true, u);
+  const RowBase rb_ddr = row_base(ddr_out, s.sddr, es, b, d0, true, u);
+  const RowBase rb_dz = row_base(dz_out, s.sdz, es, b, d0, has_dz, u);
+  const RowBase rb_B = row_base(Bm, s.sB, es, b, 0, true, u);
+  const RowBase rb_C = row_base(Cm, s.sC, es, b, 0, true, u);
+  // lowest storage step of the chunk starting at logical step t0
+  auto chunk_ts = [&](int t0) __attribute__((always_inline)) {
+    return s.reverse ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : static_cast<int64_t>(t0);
   };
   auto tile_off = [&](const int64_t* st, int row, int tt) __attribute__((always_inline)) {
     return chunk_off(s, st, es, row, tt);
@@ -451,10 +515,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
   // lane (c, j) owns steps 2j, 2j+1 of channel c; thread (r, i) = (tid / 16,
   // tid % 16) loads row r of B (r < 16) or C (r >= 16, the upper four waves)
   // at step i
+  // With PAIR only slot 0 is used: the offset of the pair's lower address,
+  // which holds step 2j in forward time and step 2j+1 in reverse time.
   uint32_t o_u[2], o_dr[2], o_do[2], o_z[2], o_du[2], o_ddr[2], o_dz[2], o_ck[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int tt = 2 * sg + e;
+    const int tt = PAIR ? 2 * sg + (s.reverse ? 1 : 0) : 2 * sg + e;
     o_u[e] = dvalid ? tile_off(s.su, sc, tt) : kOffNone;
     o_dr[e] = dvalid ? tile_off(s.sd, sc, tt) : kOffNone;
     o_do[e] = dvalid ? tile_off(s.sdo, sc, tt) : kOffNone;
@@ -491,23 +557,40 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
   float rbc[kBcPerThread], ru[2], rx[2], rgo[2], rz[2], rck[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
+    const int64_t ts = chunk_ts(t0);
     const bool qok = q >= q_begin;
 #pragma unroll
     for (int j = 0; j < kBcPerThread; ++j) {
-      const auto r_bc = bc_is_c(j) ? rsrc(Cm, s.sC, 0, t0, true) : rsrc(Bm, s.sB, 0, t0, true);
+      const auto r_bc = row_rsrc(bc_is_c(j) ? rb_C : rb_B, ts, true);
       rbc[j] = buf_one<IO>::load(r_bc, (qok && t0 + bc_t < s.seqlen) ? o_bc[j] : kOffNone, 0);
     }
-    const auto r_u = rsrc(u, s.su, d0, t0, true);
-    const auto r_dr = rsrc(dr, s.sd, d0, t0, true);
-    const auto r_do = rsrc(dout, s.sdo, d0, t0, true);
-    const auto r_z = rsrc(zz, s.sz, d0, t0, has_z);
+    const auto r_u = row_rsrc(rb_u, ts, true);
+    const auto r_dr = row_rsrc(rb_dr, ts, true);
+    const auto r_do = row_rsrc(rb_do, ts, true);
+    const auto r_z = row_rsrc(rb_z, ts, has_z);
+    if constexpr (PAIR) {
+      // even length: a pair is wholly inside or wholly past the sequence
+      const bool ok = qok && t0 + 2 * sg < s.seqlen;
+      auto ld2 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[2])
+          __attribute__((always_inline)) {
+        float lo, hi;
+        pair_io<IO>::load(r, ok ? off : kOffNone, lo, hi);
+        x[0] = s.reverse ? hi : lo;
+        x[1] = s.reverse ? lo : hi;
+      };
+      ld2(r_u, o_u[0], ru);
+      ld2(r_dr, o_dr[0], rx);
+      ld2(r_do, o_do[0], rgo);
+      ld2(r_z, o_z[0], rz);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const bool ok = qok && t0 + 2 * sg + e < s.seqlen;
-      ru[e] = buf_one<IO>::load(r_u, ok ? o_u[e] : kOffNone, 0);
-      rx[e] = buf_one<IO>::load(r_dr, ok ? o_dr[e] : kOffNone, 0);
-      rgo[e] = buf_one<IO>::load(r_do, ok ? o_do[e] : kOffNone, 0);
-      rz[e] = buf_one<IO>::load(r_z, ok ? o_z[e] : kOffNone, 0);
+      for (int e = 0; e < 2; ++e) {
+        const bool ok = qok && t0 + 2 * sg + e < s.seqlen;
+        ru[e] = buf_one<IO>::load(r_u, ok ? o_u[e] : kOffNone, 0);
+        rx[e] = buf_one<IO>::load(r_dr, ok ? o_dr[e] : kOffNone, 0);
+        rgo[e] = buf_one<IO>::load(r_do, ok ? o_do[e] : kOffNone, 0);
+        rz[e] = buf_one<IO>::load(r_z, ok ? o_z[e] : kOffNone, 0);
+      }
     }
     const auto r_ck = __builtin_amdgcn_make_buffer_rsrc(
         p.ckpt + (static_cast<int64_t>(q) * s.nchan_pad + ck_row0) * kMaxState, 0, kRsrcRange,
@@ -639,30 +722,43 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     __builtin_amdgcn_wave_barrier();  // R's per-element sums, written by other lanes
 
     // ---- O: du, ddelta_raw and dz per element ----
-    const auto r_du = rsrc(du_out, s.sdu, d0, t0, true);
-    const auto r_ddr = rsrc(ddr_out, s.sddr, d0, t0, true);
-    const auto r_dz = rsrc(dz_out, s.sdz, d0, t0, has_dz);
+    const auto r_du = row_rsrc(rb_du, chunk_ts(t0), true);
+    const auto r_ddr = row_rsrc(rb_ddr, chunk_ts(t0), true);
+    const auto r_dz = row_rsrc(rb_dz, chunk_ts(t0), has_dz);
+    float o_du_v[2], o_ddr_v[2], o_dz_v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tt = 2 * sg + e, t = t0 + tt;
       const f4 sv = ld4(el + sc * kElPitch + 4 * tt);      // delta, delta*u, dy, C.h
       const f4 ev = ld4(gr + sc * kGrPitch + 8 * tt);      // u, sigmoid(x), dout, z
       const float2 gv = *reinterpret_cast<const float2*>(gr + sc * kGrPitch + 8 * tt + 4);
-      const float du = fmaf(sv.z, skip, sv.x * gv.x);
-      const float ddr = fmaf(ev.x, gv.x, gv.y) * ev.y;
-      const bool ok = t < s.seqlen;
-      buf_one<IO>::store(du, r_du, ok ? o_du[e] : kOffNone, 0);
-      buf_one<IO>::store(ddr, r_ddr, ok ? o_ddr[e] : kOffNone, 0);
-      if (has_dz) {
-        // dz = dout * (C.h + D u) * silu'(z), silu'(z) = sig(z) (1 + z (1 - sig(z)))
-        const float y = fmaf(skip, ev.x, sv.w);
-        const float sz = sigmoid(ev.w);
-        buf_one<IO>::store(ev.z * y * (sz * fmaf(ev.w, 1.0f - sz, 1.0f)), r_dz,
-                           ok ? o_dz[e] : kOffNone, 0);
-      }
-      if (dvalid && ok) {
-        acc_db += ddr;
+      o_du_v[e] = fmaf(sv.z, skip, sv.x * gv.x);
+      o_ddr_v[e] = fmaf(ev.x, gv.x, gv.y) * ev.y;
+      // dz = dout * (C.h + D u) * silu'(z), silu'(z) = sig(z) (1 + z (1 - sig(z)))
+      const float y = fmaf(skip, ev.x, sv.w);
+      const float sz = sigmoid(ev.w);
+      o_dz_v[e] = ev.z * y * (sz * fmaf(ev.w, 1.0f - sz, 1.0f));
+      if (dvalid && t < s.seqlen) {
+        acc_db += o_ddr_v[e];
         acc_dD = fmaf(sv.z, ev.x, acc_dD);
+      }
+    }
+    if constexpr (PAIR) {
+      const bool ok = t0 + 2 * sg < s.seqlen;
+      auto st2 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[2])
+          __attribute__((always_inline)) {
+        pair_io<IO>::store(r, ok ? off : kOffNone, s.reverse ? x[1] : x[0], s.reverse ? x[0] : x[1]);
+      };
+      st2(r_du, o_du[0], o_du_v);
+      st2(r_ddr, o_ddr[0], o_ddr_v);
+      if (has_dz) st2(r_dz, o_dz[0], o_dz_v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool ok = t0 + 2 * sg + e < s.seqlen;
+        buf_one<IO>::store(o_du_v[e], r_du, ok ? o_du[e] : kOffNone, 0);
+        buf_one<IO>::store(o_ddr_v[e], r_ddr, ok ? o_ddr[e] : kOffNone, 0);
+        if (has_dz) buf_one<IO>::store(o_dz_v[e], r_dz, ok ? o_dz[e] : kOffNone, 0);
       }
     }
   }
@@ -751,7 +847,10 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
   }
   ckpt_kernel<IO><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
   const int64_t wgs = static_cast<int64_t>(s.batch) * s.nseg * s.tiles;
-  bwd_kernel<IO><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
+  if (s.pairs)
+    bwd_kernel<IO, true><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
+  else
+    bwd_kernel<IO, false><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
   const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * s.dstate * s.seqlen;
   reduce_bc_kernel<IO><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   const int64_t nch = static_cast<int64_t>(s.dim) * (kMaxState + 2);

@@ -168,9 +168,25 @@ def test_channel_last_layout(mss):
     _run_and_check(mss, "bld", _problem(2, 64, 200, 16, layout="bld", h0=True, dfinal=True))
 
 
-def test_bf16(mss):
-    _run_and_check(mss, "bf16", _problem(2, 128, 200, 16, io="bf16", h0=True, dfinal=True),
-                   io="bf16")
+@pytest.mark.parametrize("seqlen", [200, 201])
+def test_bf16(mss, seqlen):
+    # an even length moves the step pairs as one 32-bit access; an odd one
+    # takes the element-wise path
+    _run_and_check(mss, f"bf16 L={seqlen}",
+                   _problem(2, 128, seqlen, 16, io="bf16", h0=True, dfinal=True), io="bf16")
+
+
+def test_odd_row_stride(mss):
+    """Even length but rows of odd pitch (views into a wider buffer): the
+    element-wise path, since a step pair would straddle an 8-byte boundary."""
+    import torch
+    dx = _problem(2, 96, 120, 16, h0=True, dfinal=True)
+    for k in ("u", "delta_raw", "z", "dout"):
+        wide = torch.zeros(2, 96, 121, device=device(), dtype=dx[k].dtype)
+        wide[:, :, :120] = dx[k]
+        dx[k] = wide[:, :, :120]
+    assert dx["u"].stride(1) == 121
+    _run_and_check(mss, "odd row stride", dx)
 
 
 def test_run_twice_bitwise(mss):
