@@ -554,6 +554,15 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
     }
     s.pairs = ok ? 1 : 0;
   }
+  {
+    const void* xp[] = {a->u, a->delta_raw};
+    const int64_t* xst[] = {a->u_stride, a->delta_stride};
+    bool ok = a->seqlen % 4 == 0;
+    for (int i = 0; i < 2 && ok; ++i)
+      ok = xst[i][2] == 1 && aligned(xp[i], 4 * es) && (a->batch == 1 || xst[i][0] % 4 == 0) &&
+           (a->dim == 1 || xst[i][1] % 4 == 0);
+    s.quads = ok ? 1 : 0;
+  }
   char* ws = static_cast<char*>(a->workspace);
   mss::BwdPtrs p{};
   p.u = a->u;

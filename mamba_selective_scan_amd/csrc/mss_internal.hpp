@@ -148,6 +148,8 @@ struct BwdShape {
   int reverse;                              // logical step tau is storage step seqlen-1-tau
   int pairs;  // the reverse walk moves u, delta_raw, dout, z, du, ddelta_raw, dz
               // as pairs of adjacent steps (unit time stride, even length and strides)
+  int quads;  // the checkpoint pass reads u, delta_raw as 4-step vectors
+              // (unit time stride, length and strides multiples of 4)
 };
 
 struct BwdPtrs {

@@ -59,7 +59,10 @@ constexpr int kXcdsBwd = 8;
 constexpr int kElPitch = kBwdT * 4 + 4;  // s_el[c][t] = (delta, delta*u, dy, y_ssm)
 constexpr int kBcPitch = kBwdT + 4;      // s_bc[r][t]: r < 16 B_r, r >= 16 C_(r-16)
 constexpr int kGrPitch = kBwdT * 8 + 4;  // s_gr[c][t] = (u, sigmoid(x), dout, z, d(delta*u), ddelta via a, -, -)
-constexpr int kDdPitch2 = kBwdT * 2 + 4; // ckpt pass: s_dd[c][t] = (delta, delta*u)
+// checkpoint pass, staged in blocks of two chunks
+constexpr int kCkSpan = 2 * kBwdT;
+constexpr int kCkBPitch = kCkSpan + 4;    // s_b[n][t]
+constexpr int kCkDdPitch = kCkSpan * 2 + 4;  // s_dd[c][t] = (delta, delta*u)
 
 struct f4 {
   float x, y, z, w;
@@ -96,21 +99,24 @@ __device__ inline int64_t tstore(const BwdShape& s, int t) {
 // L - kBwdT - t0 in reverse time (that base may lie before the tensor; only
 // in-range offsets are used).  An absent tensor gets an empty range based at
 // `fallback`, so that its loads read 0 and its stores are dropped.
+template <int SPAN = kBwdT>
 __device__ inline __amdgpu_buffer_rsrc_t chunk_rsrc(const BwdShape& s, const void* ptr,
                                                     const int64_t* st, int64_t es, int b, int row0,
                                                     int t0, bool present, const void* fallback) {
-  const int64_t ts = s.reverse ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : t0;
+  const int64_t ts = s.reverse ? static_cast<int64_t>(s.seqlen) - SPAN - t0 : t0;
   const char* base = static_cast<const char*>(present ? ptr : fallback) +
                      (present ? (b * st[0] + static_cast<int64_t>(row0) * st[1] + ts * st[2]) * es : 0);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, present ? kRsrcRange : 0,
                                            kRsrcFlags);
 }
 
-// Byte offset of (row, logical step tt of the chunk) inside a chunk tile
-// (loop-invariant; the host checks that tiles span less than 2 GiB).
+// Byte offset of (row, logical step tt of the chunk) inside a chunk tile of
+// SPAN steps (loop-invariant; the host checks that tiles span less than
+// 2 GiB).
+template <int SPAN = kBwdT>
 __device__ inline uint32_t chunk_off(const BwdShape& s, const int64_t* st, int64_t es, int row,
                                      int tt) {
-  const int tl = s.reverse ? kBwdT - 1 - tt : tt;
+  const int tl = s.reverse ? SPAN - 1 - tt : tt;
   return static_cast<uint32_t>((row * st[1] + tl * st[2]) * es);
 }
 
@@ -166,6 +172,31 @@ __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const RowBase& r, int64_t ts, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(r.row + ts * r.step), 0,
                                            present ? kRsrcRange : 0, kRsrcFlags);
 }
+
+// Four adjacent elements of one row, the one at the lower address first.
+template <typename IO>
+struct quad_io;
+template <>
+struct quad_io<float> {
+  __device__ static inline void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[4]) {
+    using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(v[i]);
+  }
+};
+template <>
+struct quad_io<bf16_t> {
+  __device__ static inline void load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[4]) {
+    using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      x[2 * j] = __uint_as_float(v[j] << 16);
+      x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+  }
+};
 
 __device__ inline void store2(float a, float b, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
@@ -318,10 +349,11 @@ __global__ __launch_bounds__(256) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
 }
 
 // ---------------------------------------------------------------- pass 1 ---
-template <typename IO>
+// QUAD: u and delta_raw are read as 4-step vectors (s.quads).
+template <typename IO, bool QUAD>
 __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
-  __shared__ __attribute__((aligned(16))) float s_b[kMaxState * kBcPitch];
-  __shared__ __attribute__((aligned(16))) float s_dd[kCh * kDdPitch2];
+  __shared__ __attribute__((aligned(16))) float s_b[kMaxState * kCkBPitch];
+  __shared__ __attribute__((aligned(16))) float s_dd[kCh * kCkDdPitch];
   const int lane = threadIdx.x;
   const int64_t groups8 = static_cast<int64_t>(s.tiles) * kBwdWaves;  // 8-channel groups per row
   const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
@@ -347,75 +379,109 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   const int q_begin = seg * s.seg_chunks;
   const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
-  // Raw inputs of a chunk, issued one chunk ahead of use through buffer
-  // descriptors (chunk_rsrc) with loop-invariant lane offsets: B (lane covers
-  // row lane / 4, steps 4 (lane % 4) .. + 3) and u, delta_raw (lane (c, j)
-  // covers steps 2j, 2j+1 of channel c).
+  // The inputs are staged in blocks of two chunks (32 steps), so that a
+  // wave's loads cover whole 128-byte rows of [B, D, L] data: B (lane covers
+  // row lane / 4, steps 8 (lane % 4) .. + 7) and u, delta_raw (lane (c, j)
+  // covers steps 4j .. 4j+3 of channel c, one vector when QUAD).  Loads go
+  // through buffer descriptors (chunk_rsrc) with loop-invariant lane offsets
+  // and are issued one block ahead of use.
   constexpr int64_t es = sizeof(IO);
   const int bn = lane >> 2;
-  uint32_t o_b[4], o_u[2], o_dr[2];
+  uint32_t o_b[8], o_u[4], o_dr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o_b[i] = bn < s.dstate ? chunk_off(s, s.sB, es, bn, (lane & 3) * 4 + i) : kOffNone;
+  for (int i = 0; i < 8; ++i)
+    o_b[i] = bn < s.dstate ? chunk_off<kCkSpan>(s, s.sB, es, bn, (lane & 3) * 8 + i) : kOffNone;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    o_u[e] = dvalid ? chunk_off(s, s.su, es, sc, 2 * sg + e) : kOffNone;
-    o_dr[e] = dvalid ? chunk_off(s, s.sd, es, sc, 2 * sg + e) : kOffNone;
+  for (int e = 0; e < 4; ++e) {
+    // QUAD: slot 0 holds the vector's lower address: step 4j forward, 4j+3 reversed
+    const int tt = QUAD ? 4 * sg + (s.reverse ? 3 : 0) : 4 * sg + e;
+    o_u[e] = dvalid ? chunk_off<kCkSpan>(s, s.su, es, sc, tt) : kOffNone;
+    o_dr[e] = dvalid ? chunk_off<kCkSpan>(s, s.sd, es, sc, tt) : kOffNone;
   }
   const uint32_t o_ck = static_cast<uint32_t>((sc * kMaxState + 2 * sg) * sizeof(float));
   const int64_t ck_row0 = static_cast<int64_t>(b) * s.tiles * kBwdCh + dg;  // wave-uniform
-  float rb[4], ru[2], rx[2];
-  auto load_chunk = [&](int q) __attribute__((always_inline)) {
+  float rb[8], ru[4], rx[4];
+  auto load_block = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
     const bool qok = q < q_end;
-    const auto r_b = chunk_rsrc(s, p.B, s.sB, es, b, 0, t0, true, p.u);
-    const auto r_u = chunk_rsrc(s, p.u, s.su, es, b, dg, t0, true, p.u);
-    const auto r_dr = chunk_rsrc(s, p.delta_raw, s.sd, es, b, dg, t0, true, p.u);
+    const auto r_b = chunk_rsrc<kCkSpan>(s, p.B, s.sB, es, b, 0, t0, true, p.u);
+    const auto r_u = chunk_rsrc<kCkSpan>(s, p.u, s.su, es, b, dg, t0, true, p.u);
+    const auto r_dr = chunk_rsrc<kCkSpan>(s, p.delta_raw, s.sd, es, b, dg, t0, true, p.u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rb[i] = buf_one<IO>::load(r_b, (qok && t0 + (lane & 3) * 4 + i < s.seqlen) ? o_b[i] : kOffNone, 0);
+    for (int i = 0; i < 8; ++i)
+      rb[i] = buf_one<IO>::load(r_b, (qok && t0 + (lane & 3) * 8 + i < s.seqlen) ? o_b[i] : kOffNone, 0);
+    if constexpr (QUAD) {
+      // length a multiple of 4: a vector is wholly inside or past the sequence
+      const bool ok = qok && t0 + 4 * sg < s.seqlen;
+      float vu[4], vx[4];
+      quad_io<IO>::load(r_u, ok ? o_u[0] : kOffNone, vu);
+      quad_io<IO>::load(r_dr, ok ? o_dr[0] : kOffNone, vx);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const bool ok = qok && t0 + 2 * sg + e < s.seqlen;
-      ru[e] = buf_one<IO>::load(r_u, ok ? o_u[e] : kOffNone, 0);
-      rx[e] = buf_one<IO>::load(r_dr, ok ? o_dr[e] : kOffNone, 0);
+      for (int e = 0; e < 4; ++e) {
+        ru[e] = s.reverse ? vu[3 - e] : vu[e];
+        rx[e] = s.reverse ? vx[3 - e] : vx[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = qok && t0 + 4 * sg + e < s.seqlen;
+        ru[e] = buf_one<IO>::load(r_u, ok ? o_u[e] : kOffNone, 0);
+        rx[e] = buf_one<IO>::load(r_dr, ok ? o_dr[e] : kOffNone, 0);
+      }
     }
   };
-  load_chunk(q_begin);
-  for (int q = q_begin; q < q_end; ++q) {
-    const int t0 = q * kBwdT;
+  // Walk the 16 steps of chunk q from LDS step c0 of the block, recording the
+  // state entering it.
+  auto walk_chunk = [&](int q, int c0) __attribute__((always_inline)) {
     store2(h[0], h[1],
            __builtin_amdgcn_make_buffer_rsrc(
                p.ckpt + (static_cast<int64_t>(q) * s.nchan_pad + ck_row0) * kMaxState, 0,
                kRsrcRange, kRsrcFlags),
            o_ck);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_b[(lane >> 2) * kBcPitch + (lane & 3) * 4 + i] = rb[i];
+    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
+      const f4 b0 = ld4(s_b + (2 * sg) * kCkBPitch + c0 + t4);
+      const f4 b1 = ld4(s_b + (2 * sg + 1) * kCkBPitch + c0 + t4);
+      const f4 dd01 = ld4(s_dd + sc * kCkDdPitch + 2 * (c0 + t4));
+      const f4 dd23 = ld4(s_dd + sc * kCkDdPitch + 2 * (c0 + t4) + 4);
+      const float dl[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
+      const float du[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
+      // the block's decays and inputs first, then the two dependent chains
+      float a0[4], a1[4], x0[4], x1[4];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int tt = 2 * sg + e, t = t0 + tt;
+      for (int i = 0; i < 4; ++i) {
+        a0[i] = fast_exp2(dl[i] * A2[0]);
+        a1[i] = fast_exp2(dl[i] * A2[1]);
+        x0[i] = du[i] * f4_at(b0, i);
+        x1[i] = du[i] * f4_at(b1, i);
+      }
+      asm volatile("" : "+v"(a0[0]), "+v"(a0[1]), "+v"(a0[2]), "+v"(a0[3]),
+                        "+v"(a1[0]), "+v"(a1[1]), "+v"(a1[2]), "+v"(a1[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[0] = fmaf(a0[i], h[0], x0[i]);
+        h[1] = fmaf(a1[i], h[1], x1[i]);
+      }
+    }
+  };
+  load_block(q_begin);
+  for (int q = q_begin; q < q_end; q += 2) {
+    const int t0 = q * kBwdT;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_b[bn * kCkBPitch + (lane & 3) * 8 + i] = rb[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tt = 4 * sg + e, t = t0 + tt;
       const bool ok = dvalid && t < s.seqlen;
       const float x = rx[e] + bias;
       const float sp = s.softplus ? softplus(x) : x;
       const float dl = ok ? sp : 0.0f;
-      *reinterpret_cast<float2*>(s_dd + sc * kDdPitch2 + 2 * tt) = make_float2(dl, dl * ru[e]);
+      *reinterpret_cast<float2*>(s_dd + sc * kCkDdPitch + 2 * tt) = make_float2(dl, dl * ru[e]);
     }
-    load_chunk(q + 1);
+    load_block(q + 2);
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
-      const f4 b0 = ld4(s_b + (2 * sg) * kBcPitch + t4);
-      const f4 b1 = ld4(s_b + (2 * sg + 1) * kBcPitch + t4);
-      const f4 dd01 = ld4(s_dd + sc * kDdPitch2 + 2 * t4);
-      const f4 dd23 = ld4(s_dd + sc * kDdPitch2 + 2 * t4 + 4);
-      const float dl[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
-      const float du[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[0] = fmaf(fast_exp2(dl[i] * A2[0]), h[0], du[i] * f4_at(b0, i));
-        h[1] = fmaf(fast_exp2(dl[i] * A2[1]), h[1], du[i] * f4_at(b1, i));
-      }
-    }
+    walk_chunk(q, 0);
+    if (q + 1 < q_end) walk_chunk(q + 1, kBwdT);
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -845,7 +911,10 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
     const int64_t nc = s.nchan_pad * kMaxState;
     carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   }
-  ckpt_kernel<IO><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+  if (s.quads)
+    ckpt_kernel<IO, true><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+  else
+    ckpt_kernel<IO, false><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
   const int64_t wgs = static_cast<int64_t>(s.batch) * s.nseg * s.tiles;
   if (s.pairs)
     bwd_kernel<IO, true><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
