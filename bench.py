@@ -66,6 +66,9 @@ KERNEL_SOURCES = {
     "conv1d": ["mamba_selective_scan_amd/csrc/conv1d.hip",
                "mamba_selective_scan_amd/csrc/mss_device.hpp",
                "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
+    "scan_bwd": ["mamba_selective_scan_amd/csrc/scan_bwd.hip",
+                 "mamba_selective_scan_amd/csrc/mss_device.hpp",
+                 "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
 }
 
 
@@ -356,6 +359,8 @@ def main_bwd(args):
     slots = ne * bwd_valu_slots_per_element(w.dstate)
     achieved_gbs = alg_bytes / (mean_ms * 1e-3) / 1e9
     achieved_slots = slots / (mean_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash("scan_bwd")
+    traffic = load_traffic(w.name, args.io, src_hash, op="scan_bwd")
     log(f"scan bwd mean {mean_ms * 1e3:.1f} us (min {ms[0] * 1e3:.1f}); {achieved_gbs:.0f} GB/s "
         f"= {achieved_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s; VALU {achieved_slots / VALU_PEAK_TSLOTS:.1%}")
     rec = {
@@ -384,13 +389,14 @@ def main_bwd(args):
             "peak": round(VALU_PEAK_TSLOTS, 3),
             "unit": "T VALU lane-slots/s",
             "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_slots": slots,
             "slots_per_element": bwd_valu_slots_per_element(w.dstate),
             "hbm": {"achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_bytes},
             "event_us_mean": round(mean_ms * 1e3, 2),
             "event_us_median": round(ms[len(ms) // 2] * 1e3, 2),
+            "kernel_source_hash": src_hash,
         },
         "cpu_baseline": None,
     }
