@@ -143,6 +143,43 @@ def test_long_sequence(mss):
         check(f"bwd long {k}", to_np(v), ref[ORACLE_NAME[k]], TOL["f32"])
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mamba2p8b_layer_full(mss, io):
+    """The 2.8b layer shape (8 x 5120 x 4096) in the launch configuration
+    bench.py times, with initial state and final-state gradient: one whole
+    batch row against the oracle run on that row (every gradient of the row,
+    dB and dC included, since they sum over the row's channels), and a channel
+    sample across all rows for the gradients that sum over rows (dA_log, dD,
+    ddt_bias)."""
+    import torch
+    w = WORKLOADS["mamba2p8b_layer"]
+    dx = _problem(w.batch, w.dim, w.seqlen, w.dstate, io=io, h0=True, dfinal=True)
+    note(f"bwd full 2.8b layer {io}")
+    got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                 dx["dout"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                 initial_state=dx["h0"], dfinal_state=dx["dfinal"])
+    torch.cuda.synchronize()
+    tol = TOL[io]
+    b = 5
+    rows = {k: dx[k][b:b + 1] for k in ("u", "delta_raw", "B", "C", "dout", "z", "h0", "dfinal")}
+    ref = oracle.scan_bwd(rows["u"], rows["delta_raw"], dx["A_log"], rows["B"], rows["C"],
+                          rows["dout"], D=dx["D"], z=rows["z"], dt_bias=dx["dt_bias"],
+                          h0=rows["h0"], dfinal=rows["dfinal"])
+    for k in ("du", "ddelta_raw", "dz", "dB", "dC", "dinitial_state"):
+        check(f"bwd full {io} row {b} {k}", to_np(got[k][b:b + 1]), ref[ORACLE_NAME[k]], tol)
+    rng = np.random.default_rng(17)
+    chans = np.unique(np.concatenate([[0, 31, 32, w.dim - 1], rng.choice(w.dim, 20, replace=False)]))
+    ci = torch.as_tensor(chans, device=device())
+    sub = {k: dx[k][:, ci] for k in ("u", "delta_raw", "dout", "z", "h0", "dfinal")}
+    ref2 = oracle.scan_bwd(sub["u"], sub["delta_raw"], dx["A_log"][ci], dx["B"], dx["C"],
+                           sub["dout"], D=dx["D"][ci], z=sub["z"], dt_bias=dx["dt_bias"][ci],
+                           h0=sub["h0"], dfinal=sub["dfinal"])
+    for k in ("dA_log", "dD", "ddt_bias"):
+        check(f"bwd full {io} sampled {k}", to_np(got[k][ci]), ref2[ORACLE_NAME[k]], tol)
+    for k in ("du", "ddelta_raw", "dz", "dinitial_state"):
+        check(f"bwd full {io} sampled {k}", to_np(got[k][:, ci]), ref2[ORACLE_NAME[k]], tol)
+
+
 def test_time_invariant_B_C(mss):
     """B and C constant in time, passed as stride-0 views: the gradient of the
     [B, N] parameters is the time sum of dB and dC."""
