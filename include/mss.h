@@ -103,7 +103,15 @@
 extern "C" {
 #endif
 
-#define MSS_ABI_VERSION 2
+#define MSS_ABI_VERSION 3
+
+/* Chunk states: the state entering every MSS_STATE_CHUNK-step chunk of
+ * logical time, fp32, laid out [ceil(L / MSS_STATE_CHUNK)][b][d][MSS_MAX_DSTATE]
+ * contiguous (entries n >= dstate hold 0).  The forward can record them
+ * (mss_scan_args.chunk_states) for the backward to read
+ * (mss_scan_bwd_args.chunk_states), which then skips its own forward pass
+ * over the sequence: the saved-activation scheme of a training step. */
+#define MSS_STATE_CHUNK 16
 #define MSS_MAX_DSTATE 16
 #define MSS_MAX_CONV_WIDTH 4
 
@@ -161,6 +169,8 @@ typedef struct mss_scan_args {
     void *out;                   /* [b,d,t] result, io_dtype                             */
     int64_t out_stride[3];
     float *final_state;          /* [b,d,n] fp32 contiguous h_{L-1}; NULL: not written   */
+    float *chunk_states;         /* see MSS_STATE_CHUNK, 8-byte aligned; NULL: not       */
+                                 /* written                                              */
 
     int32_t delta_softplus;      /* nonzero: delta = softplus(delta_raw + dt_bias)       */
     int32_t reverse;             /* 0: forward in time.  1: reverse time, logical step   */
@@ -280,6 +290,9 @@ typedef struct mss_scan_bwd_args {
     const void *dout;            /* [b,d,t] dLoss/dout                                   */
     int64_t dout_stride[3];
     const float *dfinal_state;   /* [b,d,n] fp32 contiguous; NULL means 0                */
+    const float *chunk_states;   /* chunk states recorded by the forward on the same     */
+                                 /* inputs and flags (see MSS_STATE_CHUNK), 8-byte       */
+                                 /* aligned; NULL: the backward recomputes them          */
 
     void *du;                    /* [b,d,t] required                                     */
     int64_t du_stride[3];

@@ -154,18 +154,30 @@ def scan_workspace_size(u, A_log) -> int:
     return int(n)
 
 
+def chunk_states_shape(u):
+    """Shape of the chunk-state array for u [B, D, L]: (ceil(L / 16), B, D, 16),
+    fp32 -- the state entering every 16-step chunk of logical time, 16 slots
+    per channel (slots n >= dstate hold 0)."""
+    bsz, dim, seqlen = u.shape
+    q = (seqlen + _lib.MSS_STATE_CHUNK - 1) // _lib.MSS_STATE_CHUNK
+    return (q, bsz, dim, _lib.MSS_MAX_DSTATE)
+
+
 def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
                        delta_softplus=True, initial_state=None, return_final_state=False,
-                       out=None, final_state=None, workspace=None, reverse=False):
+                       out=None, final_state=None, workspace=None, reverse=False,
+                       return_chunk_states=False, chunk_states=None):
     """Selective-scan forward on u's device, ordered on torch's current stream.
 
     ``reverse=True`` runs the recurrence from the last step to the first (the
     second direction of a bidirectional layer) on the same buffers.
 
-    Returns ``out`` (shape and layout of u), or ``(out, final_state)`` with the
-    fp32 state [B, D, N] after the last step when ``return_final_state``.
-    ``out``, ``final_state`` and ``workspace`` (uint8, at least
-    scan_workspace_size bytes) may be supplied to avoid allocation.
+    Returns ``out`` (shape and layout of u), followed by the fp32 state
+    [B, D, N] after the last step when ``return_final_state`` and by the chunk
+    states (chunk_states_shape(u), for selective_scan_bwd) when
+    ``return_chunk_states``.  ``out``, ``final_state``, ``chunk_states`` and
+    ``workspace`` (uint8, at least scan_workspace_size bytes) may be supplied
+    to avoid allocation.
     """
     torch = _torch()
     lib = _lib.lib()
@@ -176,8 +188,13 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
                                   device=u.device)
     if final_state is not None:
         _contig_f32(final_state, "final_state", (u.shape[0], u.shape[1], A_log.shape[1]), u.device)
+    if return_chunk_states and chunk_states is None:
+        chunk_states = torch.empty(chunk_states_shape(u), dtype=torch.float32, device=u.device)
+    if chunk_states is not None:
+        _contig_f32(chunk_states, "chunk_states", chunk_states_shape(u), u.device)
     a = _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
                    delta_softplus, reverse)
+    a.chunk_states = _ptr(chunk_states)
     if tuple(out.shape) != tuple(u.shape) or out.dtype != u.dtype or out.device != u.device:
         raise ValueError("out must match u in shape, dtype and device")
     st = ctypes.c_int(0)
@@ -188,9 +205,9 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.mss_selective_scan_fwd(ctypes.byref(a), _stream_handle(u.device)))
-    if return_final_state:
-        return out, final_state
-    return out
+    res = (out,) + ((final_state,) if return_final_state else ()) + \
+        ((chunk_states,) if return_chunk_states else ())
+    return res if len(res) > 1 else out
 
 
 def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
@@ -364,14 +381,16 @@ def scan_bwd_workspace_size(u, A_log) -> int:
 
 def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=None, *,
                        delta_softplus=True, initial_state=None, dfinal_state=None,
-                       workspace=None, reverse=False):
+                       workspace=None, reverse=False, chunk_states=None):
     """Backward of selective_scan_fwd, ordered on torch's current stream.
 
     dout has u's shape and dtype; dfinal_state [B, D, N] fp32 (optional) is the
     gradient reaching the exported final state.  Returns a dict with du,
     ddelta_raw, dB, dC (dtype of u, shapes of the inputs), dA_log [D, N] fp32,
     and dD, dz, ddt_bias, dinitial_state for the optional inputs that are given.
-    ``reverse`` must match the forward's.
+    ``reverse`` must match the forward's.  ``chunk_states``, recorded by
+    selective_scan_fwd on the same inputs and flags, saves the backward its own
+    forward pass over the sequence.
     """
     torch = _torch()
     lib = _lib.lib()
@@ -384,6 +403,8 @@ def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=
     bsz, dim, _ = u.shape
     dstate = A_log.shape[1]
     _contig_f32(dfinal_state, "dfinal_state", (bsz, dim, dstate), dev)
+    if chunk_states is not None:
+        _contig_f32(chunk_states, "chunk_states", chunk_states_shape(u), dev)
     g = {
         "du": torch.empty_like(u), "ddelta_raw": torch.empty_like(delta_raw),
         "dA_log": torch.empty((dim, dstate), dtype=torch.float32, device=dev),
@@ -397,11 +418,12 @@ def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=
     b = _lib.new_scan_bwd_args()
     for name, *_ in _lib.ScanArgs._fields_:
         if hasattr(b, name) and name not in ("struct_size", "out", "out_stride", "final_state",
-                                            "workspace", "workspace_bytes"):
+                                            "chunk_states", "workspace", "workspace_bytes"):
             setattr(b, name, getattr(a, name))
     b.struct_size = ctypes.sizeof(_lib.ScanBwdArgs)
     b.dout, b.dout_stride = _ptr(dout), _strides(dout, 3)
     b.dfinal_state = _ptr(dfinal_state)
+    b.chunk_states = _ptr(chunk_states)
     b.du, b.du_stride = _ptr(g["du"]), _strides(g["du"], 3)
     b.ddelta_raw, b.ddelta_stride = _ptr(g["ddelta_raw"]), _strides(g["ddelta_raw"], 3)
     b.dA_log = _ptr(g["dA_log"])
@@ -437,23 +459,26 @@ def _scan_fn():
         @staticmethod
         def forward(ctx, u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state,
                     delta_softplus, reverse):
-            out, final = selective_scan_fwd(u, delta_raw, A_log, B, C, D, z, dt_bias,
-                                            delta_softplus=delta_softplus,
-                                            initial_state=initial_state,
-                                            return_final_state=True, reverse=reverse)
-            ctx.save_for_backward(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state)
+            # the forward records its chunk states, which the backward reads
+            # instead of recomputing them
+            out, final, states = selective_scan_fwd(u, delta_raw, A_log, B, C, D, z, dt_bias,
+                                                    delta_softplus=delta_softplus,
+                                                    initial_state=initial_state,
+                                                    return_final_state=True,
+                                                    return_chunk_states=True, reverse=reverse)
+            ctx.save_for_backward(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, states)
             ctx.flags = (delta_softplus, reverse)
             return out, final
 
         @staticmethod
         def backward(ctx, dout, dfinal):
-            u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state = ctx.saved_tensors
+            u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, states = ctx.saved_tensors
             delta_softplus, reverse = ctx.flags
             if dout is None:
                 dout = torch.zeros_like(u)
             g = selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D, z, dt_bias,
                                    delta_softplus=delta_softplus, initial_state=initial_state,
-                                   dfinal_state=dfinal, reverse=reverse)
+                                   dfinal_state=dfinal, reverse=reverse, chunk_states=states)
             return (g["du"], g["ddelta_raw"], g["dA_log"], g["dB"], g["dC"], g.get("dD"),
                     g.get("dz"), g.get("ddt_bias"), g.get("dinitial_state"), None, None)
 

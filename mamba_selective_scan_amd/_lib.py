@@ -13,8 +13,9 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmss.so")
 
-MSS_ABI_VERSION = 2
+MSS_ABI_VERSION = 3
 MSS_MAX_DSTATE = 16
+MSS_STATE_CHUNK = 16
 MSS_MAX_CONV_WIDTH = 4
 MSS_F32 = 0
 MSS_BF16 = 1
@@ -61,6 +62,7 @@ class ScanArgs(ctypes.Structure):
         ("initial_state", _vp),
         ("out", _vp), ("out_stride", _i64 * 3),
         ("final_state", _vp),
+        ("chunk_states", _vp),
         ("delta_softplus", _i32), ("reverse", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -100,6 +102,7 @@ class ScanBwdArgs(ctypes.Structure):
         ("delta_softplus", _i32), ("reverse", _i32),
         ("dout", _vp), ("dout_stride", _i64 * 3),
         ("dfinal_state", _vp),
+        ("chunk_states", _vp),
         ("du", _vp), ("du_stride", _i64 * 3),
         ("ddelta_raw", _vp), ("ddelta_stride", _i64 * 3),
         ("dA_log", _vp),

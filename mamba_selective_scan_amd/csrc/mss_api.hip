@@ -42,6 +42,17 @@ Extent extent_of(const void* p, const int64_t* sizes, const int64_t* strides, in
   return e;
 }
 
+// Bytes of the chunk-state array: [ceil(L / 16)][batch][dim][16] fp32.
+Extent chunk_states_extent(const void* p, int64_t batch, int64_t dim, int64_t seqlen) {
+  Extent e;
+  if (p == nullptr) return e;
+  const int64_t nq = (seqlen + mss::kStateChunk - 1) / mss::kStateChunk;
+  e.lo = reinterpret_cast<uintptr_t>(p);
+  e.hi = e.lo + static_cast<uintptr_t>(nq * batch * dim * kMaxState * 4);
+  e.valid = true;
+  return e;
+}
+
 bool overlaps(const Extent& a, const Extent& b) {
   return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi;
 }
@@ -197,7 +208,8 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
                              std::max<int64_t>(1, s.nchunk / kBwdMinSegChunks));
   s.seg_chunks = static_cast<int>((s.nchunk + nseg - 1) / nseg);
   s.nseg = (s.nchunk + s.seg_chunks - 1) / s.seg_chunks;
-  p.ckpt_bytes = round_up(static_cast<size_t>(s.nchunk) * s.nchan_pad * kMaxState * sizeof(float), 256);
+  // checkpoints in the chunk-state layout (unused when the caller passes them)
+  p.ckpt_bytes = round_up(static_cast<size_t>(s.nchunk) * a->batch * a->dim * kMaxState * sizeof(float), 256);
   p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * a->seqlen * sizeof(float), 256);
   p.chan_bytes = round_up(static_cast<size_t>(s.nseg) * a->batch * a->dim * (kMaxState + 2) * sizeof(float), 256);
   if (s.nseg > 1) {
@@ -272,7 +284,7 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   if (!aligned(a->u, es) || !aligned(a->delta_raw, es) || !aligned(a->B, es) ||
       !aligned(a->C, es) || !aligned(a->z, es) || !aligned(a->out, es) || !aligned(a->A_log, 4) ||
       !aligned(a->D, 4) || !aligned(a->dt_bias, 4) || !aligned(a->initial_state, 4) ||
-      !aligned(a->final_state, 4))
+      !aligned(a->final_state, 4) || !aligned(a->chunk_states, 8))
     return MSS_ERR_MISALIGNED;
   // aliasing: outputs against every input and each other
   const Extent ins[] = {
@@ -288,9 +300,10 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   };
   const Extent eo = extent_of(a->out, xs, a->out_stride, 3, es);
   const Extent ef = extent_of(a->final_state, ss, unit, 3, 4);
+  const Extent ecs = chunk_states_extent(a->chunk_states, a->batch, a->dim, a->seqlen);
   for (const Extent& e : ins)
-    if (overlaps(eo, e) || overlaps(ef, e)) return MSS_ERR_ALIASING;
-  if (overlaps(eo, ef)) return MSS_ERR_ALIASING;
+    if (overlaps(eo, e) || overlaps(ef, e) || overlaps(ecs, e)) return MSS_ERR_ALIASING;
+  if (overlaps(eo, ef) || overlaps(ecs, eo) || overlaps(ecs, ef)) return MSS_ERR_ALIASING;
 
   const ScanPlan plan = make_plan(a);
   mss::ScanPtrs p{};
@@ -302,7 +315,7 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
                     reinterpret_cast<uintptr_t>(a->workspace) + plan.workspace, true};
     for (const Extent& e : ins)
       if (overlaps(ew, e)) return MSS_ERR_ALIASING;
-    if (overlaps(ew, eo) || overlaps(ew, ef)) return MSS_ERR_ALIASING;
+    if (overlaps(ew, eo) || overlaps(ew, ef) || overlaps(ew, ecs)) return MSS_ERR_ALIASING;
     char* ws = static_cast<char*>(a->workspace);
     if (plan.agg_bytes > 0) {
       p.agg = reinterpret_cast<float2*>(ws);
@@ -360,6 +373,7 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   p.h0 = a->initial_state;
   p.out = a->out;
   p.final_state = a->final_state;
+  p.chunk_states = a->chunk_states;
   // Vectors along the unit-stride axes need the channel count (for
   // d-fast data) and dstate (for n-fast B/C) to be whole vectors; a time axis
   // that is not a whole number of vectors gets an element-wise tail pass.
@@ -483,7 +497,9 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
                             a->dA_log, a->dD, a->ddt_bias, a->dinitial_state, a->workspace};
   for (const void* q : f32_ptrs)
     if (!aligned(q, 4)) return MSS_ERR_MISALIGNED;
+  if (!aligned(a->chunk_states, 8)) return MSS_ERR_MISALIGNED;
   const Extent ins[] = {
+      chunk_states_extent(a->chunk_states, a->batch, a->dim, a->seqlen),
       extent_of(a->u, xs, a->u_stride, 3, es),
       extent_of(a->delta_raw, xs, a->delta_stride, 3, es),
       extent_of(a->z, xs, a->z_stride, 3, es),
@@ -586,6 +602,12 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
   p.ddt_bias = a->ddt_bias;
   p.dh0 = a->dinitial_state;
   p.ckpt = reinterpret_cast<float*>(ws);
+  s.states_given = 0;
+  if (a->chunk_states != nullptr) {
+    // read only: the checkpoint pass that would write it does not run
+    p.ckpt = const_cast<float*>(a->chunk_states);
+    s.states_given = 1;
+  }
   p.part_bc = reinterpret_cast<float*>(ws + plan.ckpt_bytes);
   p.part_chan = reinterpret_cast<float*>(ws + plan.ckpt_bytes + plan.bc_bytes);
   if (plan.agg_bytes > 0) {

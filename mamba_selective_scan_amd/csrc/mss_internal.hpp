@@ -47,6 +47,11 @@ struct StepShape {
   int softplus;
 };
 
+// Chunk states: the state entering every kStateChunk-step chunk of logical
+// time, [ceil(L / kStateChunk)][batch][dim][kMaxState] fp32.  The forward can
+// record them; the backward reads them as its checkpoints.
+constexpr int kStateChunk = 16;
+
 struct ScanPtrs {
   const void* u;
   const void* delta_raw;
@@ -62,6 +67,7 @@ struct ScanPtrs {
   float* tail_h0;  // [batch][dim][dstate] state handed from the vector pass to the tail
   float2* agg;    // [nseg-1][nchan_pad][kMaxState] segment (prod a, h from 0)
   float* carry;   // [nseg][nchan_pad][kMaxState] state entering each segment
+  float* chunk_states;  // optional output, see kStateChunk
 };
 
 struct StepPtrs {
@@ -128,7 +134,7 @@ hipError_t launch_conv_step(const ConvStepShape& s, const ConvStepPtrs& p, bool 
 // lane (g, c) runs states 2g, 2g+1 of channel c) and walks the sequence in
 // chunks of kBwdT steps, the last chunk first.  Four-wave workgroups at up
 // to 168 VGPRs and 46 KB of LDS put three workgroups on a CU.
-constexpr int kBwdT = 16;
+constexpr int kBwdT = kStateChunk;  // a backward chunk is one chunk-state interval
 constexpr int kBwdWaves = 4;
 constexpr int kBwdCh = kCh * kBwdWaves;  // 32
 constexpr int kBwdThreads = 64 * kBwdWaves;
@@ -150,6 +156,7 @@ struct BwdShape {
               // as pairs of adjacent steps (unit time stride, even length and strides)
   int quads;  // the checkpoint pass reads u, delta_raw as 4-step vectors
               // (unit time stride, length and strides multiples of 4)
+  int states_given;  // ckpt holds chunk states recorded by the forward: no checkpoint pass
 };
 
 struct BwdPtrs {
@@ -174,7 +181,7 @@ struct BwdPtrs {
   float* ddt_bias;
   float* dh0;
   // workspace
-  float* ckpt;       // [nchunk][nchan_pad][kMaxState] state entering each chunk
+  float* ckpt;       // [nchunk][batch][dim][kMaxState] state entering each chunk (chunk states)
   float* part_bc;    // [batch][tiles][2 * kMaxState][seqlen] per-workgroup dB, dC sums
   float* part_chan;  // [nseg][batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
   float4* agg;       // [nseg][nchan_pad][kMaxState] per segment (prod a, h from 0, g from 0, -)

@@ -398,8 +398,11 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
     o_u[e] = dvalid ? chunk_off<kCkSpan>(s, s.su, es, sc, tt) : kOffNone;
     o_dr[e] = dvalid ? chunk_off<kCkSpan>(s, s.sd, es, sc, tt) : kOffNone;
   }
-  const uint32_t o_ck = static_cast<uint32_t>((sc * kMaxState + 2 * sg) * sizeof(float));
-  const int64_t ck_row0 = static_cast<int64_t>(b) * s.tiles * kBwdCh + dg;  // wave-uniform
+  // checkpoints in the chunk-state layout [q][batch][dim][kMaxState]
+  const uint32_t o_ck =
+      dvalid ? static_cast<uint32_t>((sc * kMaxState + 2 * sg) * sizeof(float)) : kOffNone;
+  const int64_t ck_row0 = static_cast<int64_t>(b) * s.dim + dg;  // wave-uniform
+  const int64_t ck_plane = static_cast<int64_t>(s.batch) * s.dim;
   float rb[8], ru[4], rx[4];
   auto load_block = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   auto walk_chunk = [&](int q, int c0) __attribute__((always_inline)) {
     store2(h[0], h[1],
            __builtin_amdgcn_make_buffer_rsrc(
-               p.ckpt + (static_cast<int64_t>(q) * s.nchan_pad + ck_row0) * kMaxState, 0,
+               p.ckpt + (static_cast<int64_t>(q) * ck_plane + ck_row0) * kMaxState, 0,
                kRsrcRange, kRsrcFlags),
            o_ck);
 #pragma unroll
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     o_du[e] = dvalid ? tile_off(s.sdu, sc, tt) : kOffNone;
     o_ddr[e] = dvalid ? tile_off(s.sddr, sc, tt) : kOffNone;
     o_dz[e] = dvalid ? tile_off(s.sdz, sc, tt) : kOffNone;
-    o_ck[e] = static_cast<uint32_t>((sc * kMaxState + nk[e]) * sizeof(float));
+    o_ck[e] = dvalid ? static_cast<uint32_t>((sc * kMaxState + nk[e]) * sizeof(float)) : kOffNone;
   }
   // B/C rows of a chunk: thread (r, i) = (tid / 16, tid % 16) covers step i of
   // rows r + j kBcRowStep, j < kBcPerThread; rows r < 16 are B, the others C
@@ -614,7 +617,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     const int64_t st[3] = {0, bc_is_c(j) ? s.sC[1] : s.sB[1], bc_is_c(j) ? s.sC[2] : s.sB[2]};
     o_bc[j] = n < s.dstate ? tile_off(st, n, bc_t) : kOffNone;
   }
-  const int64_t ck_row0 = static_cast<int64_t>(b) * s.tiles * kBwdCh + d0;
+  const int64_t ck_row0 = static_cast<int64_t>(b) * s.dim + d0;  // chunk-state layout
+  const int64_t ck_plane = static_cast<int64_t>(s.batch) * s.dim;
 
   // Raw inputs of a chunk, issued one chunk ahead of use: one B or C value
   // per thread, u, delta_raw, dout and z for the lane's two elements, and the
@@ -659,7 +663,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
       }
     }
     const auto r_ck = __builtin_amdgcn_make_buffer_rsrc(
-        p.ckpt + (static_cast<int64_t>(q) * s.nchan_pad + ck_row0) * kMaxState, 0, kRsrcRange,
+        p.ckpt + (static_cast<int64_t>(q) * ck_plane + ck_row0) * kMaxState, 0, kRsrcRange,
         kRsrcFlags);
 #pragma unroll
     for (int k = 0; k < 2; ++k) rck[k] = buf_one<float>::load(r_ck, qok ? o_ck[k] : kOffNone, 0);
@@ -911,10 +915,13 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
     const int64_t nc = s.nchan_pad * kMaxState;
     carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   }
-  if (s.quads)
-    ckpt_kernel<IO, true><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
-  else
-    ckpt_kernel<IO, false><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+  // chunk states recorded by the forward replace the checkpoint pass
+  if (s.states_given == 0) {
+    if (s.quads)
+      ckpt_kernel<IO, true><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+    else
+      ckpt_kernel<IO, false><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+  }
   const int64_t wgs = static_cast<int64_t>(s.batch) * s.nseg * s.tiles;
   if (s.pairs)
     bwd_kernel<IO, true><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const float* __restrict__ Dskip, const IO* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ h0, IO* __restrict__ out,
     float* __restrict__ final_state, float2* __restrict__ agg,
-    const float* __restrict__ carry) {
+    const float* __restrict__ carry, float* __restrict__ chunk_states) {
   __shared__ __attribute__((aligned(16))) float s_bc[(AGG ? kMaxState : kBcRows) * kT];
   __shared__ __attribute__((aligned(16))) float s_dd[kCh * kDdPitch];
   __shared__ __attribute__((aligned(16))) float s_skip[AGG ? 4 : kCh * kSkipPitch];
@@ -424,9 +424,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int y_step = row == 1 ? 2 : (row == 2 ? 1 : row);
   float* p_y = s_dd + sc * kDdPitch + 2 * y_step;
 
+  // Chunk states (main pass only): the state entering logical step t when t
+  // is a multiple of kStateChunk, written by the lane for its two states.
+  const int64_t cs_row = static_cast<int64_t>(b) * s.dim + d;
+  const int64_t cs_plane = static_cast<int64_t>(s.batch) * s.dim;
+  auto record_state = [&](int t) __attribute__((always_inline)) {
+    if (!AGG && chunk_states != nullptr && (t & (kStateChunk - 1)) == 0 && t < t_end && dvalid)
+      *reinterpret_cast<float2*>(chunk_states +
+                                 ((t / kStateChunk) * cs_plane + cs_row) * kMaxState +
+                                 sg * kStatesPerLane) = make_float2(h[0], h[1]);
+  };
+
   // One block of 4 steps: the scan of this lane's two states and, outside
   // the AGG pass, one state-group reduction of C.h.
-  auto scan_block = [&](int t4) __attribute__((always_inline)) {
+  auto scan_block = [&](int t4, int t0) __attribute__((always_inline)) {
+    record_state(t0 + t4);
     const int col = (((t4 >> 2) ^ sg) & 7) << 2;
     const f4 b0 = lds_f4(p_b0 + col);
     const f4 b1 = lds_f4(p_b0 + kT + col);
@@ -461,13 +473,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // The main pass unrolls the blocks: the swizzled B/C offsets become
   // loop-invariant registers and the other LDS offsets immediates.  The AGG
   // pass keeps a loop (unrolled, its LDS reads would all be hoisted).
-  auto phase_s = [&]() __attribute__((always_inline)) {
+  auto phase_s = [&](int t0) __attribute__((always_inline)) {
     if constexpr (AGG) {
 #pragma unroll 1
-      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4);
+      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0);
     } else {
 #pragma unroll
-      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4);
+      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0);
     }
   };
 
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     issue_bc_loads(t0 + kT, t_end);
     issue_x_loads(in, t0 + kT, t_end);
     __builtin_amdgcn_s_setprio(0);
-    phase_s();
+    phase_s(t0);
     __builtin_amdgcn_s_setprio(2);
     phase_o(zb, t0);
     issue_z_loads(zb, t0 + kT, t_end);
@@ -595,13 +607,15 @@ static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, 
   IO* out = static_cast<IO*>(p.out);
   if (s.nseg > 1) {
     scan_kernel<IO, XT, BT, true, VEC, REV><<<dim3(G, s.nseg - 1), block, 0, stream>>>(
-        s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry);
+        s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
+        nullptr);
     const int64_t n = s.nchan_pad * kMaxState;
     carry_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
         s, p.agg, h0, p.carry);
   }
   scan_kernel<IO, XT, BT, false, VEC, REV><<<dim3(G, s.nseg), block, 0, stream>>>(
-      s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry);
+      s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
+      p.chunk_states);
 }
 
 // The vector pass covers [0, s.t_stop); when s.t_stop < seqlen it exports its

@@ -165,6 +165,10 @@ SCAN_CASES = {
     "out_is_u": (lambda a: setattr(a, "out", fake(0)), "MSS_ERR_ALIASING"),
     "final_in_z": (lambda a: setattr(a, "final_state", fake(6) + 64), "MSS_ERR_ALIASING"),
     "out_on_A_log": (lambda a: setattr(a, "out", fake(2) - 8), "MSS_ERR_ALIASING"),
+    "misaligned_chunk_states": (lambda a: setattr(a, "chunk_states", fake(11) + 4),
+                                "MSS_ERR_MISALIGNED"),
+    "chunk_states_on_out": (lambda a: setattr(a, "chunk_states", fake(8) + 256), "MSS_ERR_ALIASING"),
+    "chunk_states_on_u": (lambda a: setattr(a, "chunk_states", fake(0) - 8), "MSS_ERR_ALIASING"),
     "no_workspace": (lambda a: None, "MSS_ERR_WORKSPACE_TOO_SMALL"),
 }
 
@@ -390,6 +394,11 @@ BWD_CASES = {
                         "MSS_ERR_WORKSPACE_TOO_SMALL"),
     "misaligned_workspace": (lambda a: setattr(a, "workspace", fake(17) + 64), "MSS_ERR_MISALIGNED"),
     "workspace_on_du": (lambda a: setattr(a, "workspace", fake(9)), "MSS_ERR_ALIASING"),
+    "misaligned_chunk_states": (lambda a: setattr(a, "chunk_states", fake(18) + 4),
+                                "MSS_ERR_MISALIGNED"),
+    "chunk_states_on_du": (lambda a: setattr(a, "chunk_states", fake(9) + 512), "MSS_ERR_ALIASING"),
+    "chunk_states_in_workspace": (lambda a: setattr(a, "chunk_states", fake(17) + 1024),
+                                  "MSS_ERR_ALIASING"),
 }
 
 

@@ -178,6 +178,19 @@ def test_mamba2p8b_layer_full(mss, io):
         check(f"bwd full {io} sampled {k}", to_np(got[k][ci]), ref2[ORACLE_NAME[k]], tol)
     for k in ("du", "ddelta_raw", "dz", "dinitial_state"):
         check(f"bwd full {io} sampled {k}", to_np(got[k][:, ci]), ref2[ORACLE_NAME[k]], tol)
+    # the same backward reading the forward's chunk states
+    _, states = mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                       D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                       initial_state=dx["h0"], return_chunk_states=True)
+    got2 = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                  dx["dout"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                  initial_state=dx["h0"], dfinal_state=dx["dfinal"],
+                                  chunk_states=states)
+    torch.cuda.synchronize()
+    for k in ("du", "dB", "dA_log", "dinitial_state"):
+        check(f"bwd full {io} with chunk states {k}", to_np(got2[k][b:b + 1] if k != "dA_log"
+                                                            else got2[k]),
+              to_np(got[k][b:b + 1] if k != "dA_log" else got[k]), 1e-5 if io == "f32" else 1e-2)
 
 
 def test_time_invariant_B_C(mss):
