@@ -351,6 +351,47 @@ def main_bwd(args):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(ms) / len(ms)
+
+    # The training pair: a forward that records its chunk states and the
+    # backward that reads them (no checkpoint pass), timed both ways.
+    out_buf = torch.empty_like(dx["u"])
+    fin_buf = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+    states = torch.empty(mss.chunk_states_shape(dx["u"]), dtype=torch.float32, device=dev)
+    fws = torch.empty(max(mss.scan_workspace_size(dx["u"], dx["A_log"]), 1), dtype=torch.uint8,
+                      device=dev)
+
+    def fwd_states():
+        mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], D=dx["D"],
+                               z=dx["z"], dt_bias=dx["dt_bias"], initial_state=h0, out=out_buf,
+                               final_state=fin_buf, chunk_states=states, workspace=fws)
+
+    def bwd_states():
+        return mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                      dout, D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                      initial_state=h0, dfinal_state=dfin, workspace=ws,
+                                      chunk_states=states)
+
+    for _ in range(args.warmup):
+        fwd_states()
+        bwd_states()
+    torch.cuda.synchronize()
+    ev_f = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    ev_b = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev_f[i][0].record(stream)
+        fwd_states()
+        ev_f[i][1].record(stream)
+        ev_b[i][0].record(stream)
+        bwd_states()
+        ev_b[i][1].record(stream)
+    torch.cuda.synchronize()
+    f_ms = sum(a.elapsed_time(b) for a, b in ev_f) / args.steps
+    b_ms = sum(a.elapsed_time(b) for a, b in ev_b) / args.steps
+    log(f"training pair: forward recording chunk states {f_ms * 1e3:.1f} us + backward reading "
+        f"them {b_ms * 1e3:.1f} us = {(f_ms + b_ms) * 1e3:.1f} us")
+
     ne = w.elems
     nbc = w.batch * w.seqlen * w.dstate
     alg_bytes = ne * 7 * io_bytes + 4 * nbc * io_bytes           # u, dr, z, dout; du, ddr, dz; B, C, dB, dC
@@ -399,6 +440,13 @@ def main_bwd(args):
             "kernel_source_hash": src_hash,
         },
         "cpu_baseline": None,
+        "training_pair": {
+            "what": "forward recording its chunk states, then the backward reading them "
+                    "(no checkpoint pass); HIP events per call",
+            "fwd_event_us_mean": round(f_ms * 1e3, 2),
+            "bwd_event_us_mean": round(b_ms * 1e3, 2),
+            "total_us": round((f_ms + b_ms) * 1e3, 2),
+        },
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: backward oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
