@@ -8,9 +8,10 @@ CPU-baseline leg of ``bench.py`` are the only callers.  The product package
 imports nothing from the product package.
 
 The arithmetic lives in ``mss_oracle.c`` (scan forward and state update),
-``mss_oracle_bwd.c`` (the scan's backward) and ``mss_oracle_conv.c`` (plain
-C, fp64, sequential in time, OpenMP across independent channels in the
-forward).  This wrapper only marshals numpy arrays:
+``mss_oracle_bwd.c`` (the scan's backward), ``mss_oracle_conv.c`` and
+``mss_oracle_cplx.c`` (the forward with complex A; B, C and the states are
+complex128 there) -- plain C, fp64, sequential in time, OpenMP across
+independent channels in the forward.  This wrapper only marshals numpy arrays:
 every input is converted exactly to float64 and laid out contiguously as
 
     u, delta_raw, z, out : [batch, dim, seqlen]
@@ -36,7 +37,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mss_oracle.c")
 SOURCES = {"scan": _SRC, "conv": os.path.join(_HERE, "mss_oracle_conv.c"),
-           "bwd": os.path.join(_HERE, "mss_oracle_bwd.c")}
+           "bwd": os.path.join(_HERE, "mss_oracle_bwd.c"),
+           "cplx": os.path.join(_HERE, "mss_oracle_cplx.c")}
 LIB_PATH = os.path.join(_HERE, "libmss_oracle.so")
 
 _lib = None
@@ -81,6 +83,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_oracle_conv1d_fwd.restype = ctypes.c_int
     lib.mss_oracle_conv1d_update.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp]
     lib.mss_oracle_conv1d_update.restype = ctypes.c_int
+    lib.mss_oracle_scan_fwd_complex.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [
+        ctypes.c_int, dp, dp, ctypes.c_int]
+    lib.mss_oracle_scan_fwd_complex.restype = ctypes.c_int
     return lib
 
 
@@ -149,6 +154,46 @@ def scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, h0=None,
         _ptr(out), _ptr(final), int(threads))
     if rc != 0:
         raise ValueError(f"oracle scan_fwd rejected its arguments (rc={rc})")
+    return out, final
+
+
+def _c128(x, shape=None):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor: exact upcast on the CPU
+        import torch
+        x = x.detach().to("cpu", torch.complex128).numpy()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.complex128))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None, dt_bias=None, h0=None,
+                     delta_softplus=True, threads=0, lib=None):
+    """Selective-scan forward with complex A = -exp(A_log) + i A_imag, complex
+    B, C and state, in fp64.  Returns (out [b,d,l] real, final_state [b,d,n]
+    complex)."""
+    u = _f64(u)
+    batch, dim, seqlen = u.shape
+    A_log = _f64(A_log)
+    dstate = A_log.shape[1]
+    delta_raw = _f64(delta_raw, (batch, dim, seqlen))
+    A_imag = _f64(A_imag, (dim, dstate))
+    B = _c128(B, (batch, dstate, seqlen))
+    C = _c128(C, (batch, dstate, seqlen))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim, seqlen))
+    dt_bias = _f64(dt_bias, (dim,))
+    h0 = _c128(h0, (batch, dim, dstate))
+    out = np.empty((batch, dim, seqlen), dtype=np.float64)
+    final = np.empty((batch, dim, dstate), dtype=np.complex128)
+    rc = (lib or load()).mss_oracle_scan_fwd_complex(
+        batch, dim, seqlen, dstate, _ptr(u), _ptr(delta_raw), _ptr(A_log), _ptr(A_imag),
+        _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), int(bool(delta_softplus)),
+        _ptr(out), _ptr(final), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle scan_fwd_complex rejected its arguments (rc={rc})")
     return out, final
 
 

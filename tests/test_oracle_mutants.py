@@ -3,7 +3,8 @@ makes at least one pin fail.
 
 Every mutant below is a one-line edit of one oracle source file
 (oracle/mss_oracle.c for the scan, oracle/mss_oracle_conv.c for the conv1d,
-oracle/mss_oracle_bwd.c for the scan's backward): a dropped term, a wrong
+oracle/mss_oracle_bwd.c for the scan's backward, oracle/mss_oracle_cplx.c for
+the complex-A forward): a dropped term, a wrong
 sign or index, a transposed or swapped operand, exp2 for exp, and so on.  The
 altered copy is compiled, with the other sources as they are, into a
 temporary library, and the pins of that source are run against it until one
@@ -17,6 +18,7 @@ import pytest
 import oracle
 import bwd_oracle_pins as BP
 import conv_oracle_pins as CP
+import cplx_oracle_pins as XP
 import oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "mss_oracle.c")
@@ -112,10 +114,37 @@ BWD_MUTANTS = {
 }
 BWD_SRC = oracle.SOURCES["bwd"]
 
+CPLX_MUTANTS = {
+    "cplx_imag_sign": ("-exp(A_log[d * dstate + n]) + I * A_imag[d * dstate + n];",
+                       "-exp(A_log[d * dstate + n]) - I * A_imag[d * dstate + n];"),
+    "cplx_real_no_exp": ("A[n] = -exp(A_log[d * dstate + n]) + I",
+                         "A[n] = -A_log[d * dstate + n] + I"),
+    "cplx_decay_modulus_only": ("double complex a = cexp(delta * A[n]);",
+                                "double complex a = exp(delta * creal(A[n]));"),
+    "cplx_decay_rotation_only": ("double complex a = cexp(delta * A[n]);",
+                                 "double complex a = cexp(I * delta * cimag(A[n]));"),
+    "cplx_decay_no_delta": ("double complex a = cexp(delta * A[n]);",
+                            "double complex a = cexp(A[n]);"),
+    "cplx_b_no_delta": ("double complex bt = delta * B[(b * dstate + n) * seqlen + t] * ut;",
+                        "double complex bt = B[(b * dstate + n) * seqlen + t] * ut;"),
+    "cplx_b_conj": ("double complex bt = delta * B[(b * dstate + n) * seqlen + t] * ut;",
+                    "double complex bt = delta * conj(B[(b * dstate + n) * seqlen + t]) * ut;"),
+    "cplx_h_conj": ("h[n] = a * h[n] + bt;", "h[n] = a * conj(h[n]) + bt;"),
+    "cplx_C_conj": ("y += C[(b * dstate + n) * seqlen + t] * h[n];",
+                    "y += conj(C[(b * dstate + n) * seqlen + t]) * h[n];"),
+    "cplx_y_imag": ("double yr = creal(y) + skip * ut;", "double yr = cimag(y) + skip * ut;"),
+    "cplx_y_modulus": ("double yr = creal(y) + skip * ut;", "double yr = cabs(y) + skip * ut;"),
+    "cplx_no_skip": ("double yr = creal(y) + skip * ut;", "double yr = creal(y);"),
+    "cplx_h0_ignored": ("h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;", "h[n] = 0.0;"),
+    "cplx_no_gate": ("if (z) yr *= mss_oracle_silu(z[(b * dim + d) * seqlen + t]);", ""),
+}
+CPLX_SRC = oracle.SOURCES["cplx"]
+
 
 def _run_pins(lib, pins=None, stop_at_first=False):
     failures = []
-    for pin in pins if pins is not None else P.ALL_PINS + CP.ALL_CONV_PINS + BP.ALL_BWD_PINS:
+    for pin in pins if pins is not None else (P.ALL_PINS + CP.ALL_CONV_PINS + BP.ALL_BWD_PINS +
+                                               XP.ALL_CPLX_PINS):
         try:
             pin(lib)
         except AssertionError as e:
@@ -163,6 +192,19 @@ def test_bwd_mutant_is_caught(name, tmp_path):
     so = tmp_path / "libmutant.so"
     oracle.build(out=str(so), replace={"bwd": str(mutated)})
     failures = _run_pins(oracle.load(str(so)), BP.ALL_BWD_PINS, stop_at_first=True)
+    assert failures, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(CPLX_MUTANTS))
+def test_cplx_mutant_is_caught(name, tmp_path):
+    old, new = CPLX_MUTANTS[name]
+    src = open(CPLX_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutated = tmp_path / "mutant_cplx.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    oracle.build(out=str(so), replace={"cplx": str(mutated)})
+    failures = _run_pins(oracle.load(str(so)), XP.ALL_CPLX_PINS, stop_at_first=True)
     assert failures, f"mutant {name} passed every pin"
 
 
