@@ -1,7 +1,7 @@
 /*
  * mss.h -- C ABI of libmss, the MI355X (gfx950) Mamba selective-scan library.
  *
- * Five operations.  The scan forward and backward can also run in reverse
+ * Six operations.  The scan forward and backward can also run in reverse
  * time (mss_scan_args.reverse), the second direction of a bidirectional
  * layer (SpeechLens kernel-optimization notes, the bidirectional variant in
  * its rejected-fusion list):
@@ -64,6 +64,18 @@
  *        dz_t = dout_t y_t silu'(z_t);  dD = sum dy u;  ddt_bias = sum ddelta_raw;
  *        dA_log[d,n] = A[n] sum_(b,t) G_t[n] h_{t-1}[n] exp(delta_t A[n]) delta_t;
  *        dinitial_state = g after the first step.
+ *
+ *  6. mss_selective_scan_fwd_complex: operation 1 with a complex diagonal A,
+ *     the variant the official CUDA kernel carries with its own complex exp2
+ *     (createcentury's reading of the kernel, section "主要な最適化テクニック"):
+ *        A[n]   = -exp(A_log[d,n]) + i A_imag[d,n]
+ *        h_t[n] = exp(delta_t * A[n]) * h_{t-1}[n] + delta_t * B[b,n,t] * u[b,d,t]
+ *        y_t    = Re(sum_n C[b,n,t] * h_t[n]) + D[d] * u[b,d,t]
+ *     with complex B, C and states, real u, delta_raw, z and out, and delta,
+ *     the skip term and the gate as in operation 1.  The pages do not spell
+ *     out the parameters; this is the plainest reading (the decay from the
+ *     real part as in the real case, the rotation from the imaginary part,
+ *     the real part of the output).  fp32 activations only.
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -335,6 +347,49 @@ mss_status mss_selective_scan_fwd(const mss_scan_args *args, void *stream);
 
 /* One-token state update (see the top of this file). */
 mss_status mss_selective_state_update(const mss_step_args *args, void *stream);
+
+/* Arguments of mss_selective_scan_fwd_complex.  Set struct_size =
+ * sizeof(mss_scan_complex_args).  Complex values are (re, im) fp32 pairs
+ * (8 bytes, 8-byte aligned, the layout of C99 float _Complex); their strides
+ * count complex elements. */
+typedef struct mss_scan_complex_args {
+    uint32_t struct_size;
+    int32_t reserved0;           /* must be 0                                            */
+    int64_t batch;               /* B >= 1                                               */
+    int64_t dim;                 /* D >= 1                                               */
+    int64_t seqlen;              /* 1 <= L <= 2^30                                       */
+    int64_t dstate;              /* N, 1..MSS_MAX_DSTATE                                 */
+
+    const float *u;              /* [b,d,t] fp32                                         */
+    int64_t u_stride[3];
+    const float *delta_raw;      /* [b,d,t] fp32                                         */
+    int64_t delta_stride[3];
+    const float *A_log;          /* [d,n] fp32, Re(A) = -exp(A_log)                      */
+    int64_t A_log_stride[2];
+    const float *A_imag;         /* [d,n] fp32, Im(A)                                    */
+    int64_t A_imag_stride[2];
+    const void *B;               /* [b,n,t] complex                                      */
+    int64_t B_stride[3];
+    const void *C;               /* [b,n,t] complex                                      */
+    int64_t C_stride[3];
+    const float *D;              /* [d] fp32 contiguous; NULL means 0                    */
+    const float *z;              /* [b,d,t] fp32; NULL means no gate                     */
+    int64_t z_stride[3];
+    const float *dt_bias;        /* [d] fp32 contiguous; NULL means 0                    */
+    const void *initial_state;   /* [b,d,n] complex contiguous; NULL means 0             */
+
+    float *out;                  /* [b,d,t] fp32 result                                  */
+    int64_t out_stride[3];
+    void *final_state;           /* [b,d,n] complex contiguous; NULL: not written        */
+
+    int32_t delta_softplus;      /* nonzero: delta = softplus(delta_raw + dt_bias)       */
+    int32_t reserved1;           /* must be 0                                            */
+} mss_scan_complex_args;
+
+/* Selective-scan forward with complex A (operation 6 at the top of this
+ * file).  The same checks and errors as mss_selective_scan_fwd; no workspace.
+ * out and final_state must not overlap any input or each other. */
+mss_status mss_selective_scan_fwd_complex(const mss_scan_complex_args *args, void *stream);
 
 /* Bytes of device workspace mss_selective_scan_bwd needs: the states entering
  * every 16-step chunk (batch * dim * seqlen * 4 bytes, rounded up) and the

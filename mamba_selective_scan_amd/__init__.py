@@ -210,6 +210,70 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
     return res if len(res) > 1 else out
 
 
+def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None, dt_bias=None, *,
+                               delta_softplus=True, initial_state=None,
+                               return_final_state=False, out=None, final_state=None):
+    """Selective-scan forward with complex A = -exp(A_log) + i A_imag, ordered on
+    torch's current stream.
+
+    u, delta_raw, z: fp32 [B, D, L]; A_log, A_imag: fp32 [D, N]; B, C:
+    complex64 [B, N, L] (any strides); initial_state, final_state: complex64
+    [B, D, N] contiguous.  Returns ``out`` (fp32, the real part of C . h plus
+    D u, gated), or ``(out, final_state)`` when ``return_final_state``.
+    """
+    torch = _torch()
+    lib = _lib.lib()
+    dev = u.device
+    _need(u, "u", 3, torch.float32, dev)
+    bsz, dim, seqlen = u.shape
+    _need(delta_raw, "delta_raw", 3, torch.float32, dev)
+    _need(A_log, "A_log", 2, torch.float32, dev)
+    _need(A_imag, "A_imag", 2, torch.float32, dev)
+    dstate = A_log.shape[1]
+    _need(B, "B", 3, torch.complex64, dev)
+    _need(C, "C", 3, torch.complex64, dev)
+    if tuple(delta_raw.shape) != (bsz, dim, seqlen):
+        raise ValueError("delta_raw must have the shape of u")
+    if tuple(A_log.shape) != (dim, dstate) or tuple(A_imag.shape) != (dim, dstate):
+        raise ValueError(f"A_log and A_imag must have shape {(dim, dstate)}")
+    if tuple(B.shape) != (bsz, dstate, seqlen) or tuple(C.shape) != (bsz, dstate, seqlen):
+        raise ValueError(f"B and C must have shape {(bsz, dstate, seqlen)}")
+    if z is not None:
+        _need(z, "z", 3, torch.float32, dev)
+        if tuple(z.shape) != (bsz, dim, seqlen):
+            raise ValueError("z must have the shape of u")
+    _contig_f32(D, "D", (dim,), dev)
+    _contig_f32(dt_bias, "dt_bias", (dim,), dev)
+    for t, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _need(t, name, 3, torch.complex64, dev)
+            if tuple(t.shape) != (bsz, dim, dstate) or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous with shape {(bsz, dim, dstate)}")
+    if out is None:
+        out = torch.empty_like(u)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dim, dstate), dtype=torch.complex64, device=dev)
+    if tuple(out.shape) != tuple(u.shape) or out.dtype != torch.float32 or out.device != dev:
+        raise ValueError("out must be fp32 with the shape of u on its device")
+    a = _lib.new_scan_complex_args()
+    a.batch, a.dim, a.seqlen, a.dstate = bsz, dim, seqlen, dstate
+    a.u, a.u_stride = _ptr(u), _strides(u, 3)
+    a.delta_raw, a.delta_stride = _ptr(delta_raw), _strides(delta_raw, 3)
+    a.A_log, a.A_log_stride = _ptr(A_log), _strides(A_log, 2)
+    a.A_imag, a.A_imag_stride = _ptr(A_imag), _strides(A_imag, 2)
+    a.B, a.B_stride = _ptr(B), _strides(B, 3)
+    a.C, a.C_stride = _ptr(C), _strides(C, 3)
+    a.D = _ptr(D)
+    a.z, a.z_stride = _ptr(z), _strides(z, 3)
+    a.dt_bias = _ptr(dt_bias)
+    a.initial_state = _ptr(initial_state)
+    a.out, a.out_stride = _ptr(out), _strides(out, 3)
+    a.final_state = _ptr(final_state)
+    a.delta_softplus = 1 if delta_softplus else 0
+    _lib.check(lib.mss_selective_scan_fwd_complex(ctypes.byref(a), _stream_handle(dev)))
+    return (out, final_state) if return_final_state else out
+
+
 def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
                            delta_softplus=True, out=None):
     """One decode step: updates ``state`` [B, D, N] (fp32, contiguous) in place and

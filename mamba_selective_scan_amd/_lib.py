@@ -40,7 +40,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("mss_abi_version", "mss_status_string", "mss_selective_scan_workspace_size",
            "mss_selective_scan_fwd", "mss_selective_state_update", "mss_causal_conv1d_fwd",
            "mss_causal_conv1d_update", "mss_selective_scan_bwd_workspace_size",
-           "mss_selective_scan_bwd")
+           "mss_selective_scan_bwd", "mss_selective_scan_fwd_complex")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -167,6 +167,32 @@ def new_scan_args() -> ScanArgs:
     return a
 
 
+class ScanComplexArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("reserved0", _i32),
+        ("batch", _i64), ("dim", _i64), ("seqlen", _i64), ("dstate", _i64),
+        ("u", _vp), ("u_stride", _i64 * 3),
+        ("delta_raw", _vp), ("delta_stride", _i64 * 3),
+        ("A_log", _vp), ("A_log_stride", _i64 * 2),
+        ("A_imag", _vp), ("A_imag_stride", _i64 * 2),
+        ("B", _vp), ("B_stride", _i64 * 3),
+        ("C", _vp), ("C_stride", _i64 * 3),
+        ("D", _vp),
+        ("z", _vp), ("z_stride", _i64 * 3),
+        ("dt_bias", _vp),
+        ("initial_state", _vp),
+        ("out", _vp), ("out_stride", _i64 * 3),
+        ("final_state", _vp),
+        ("delta_softplus", _i32), ("reserved1", _i32),
+    ]
+
+
+def new_scan_complex_args() -> ScanComplexArgs:
+    a = ScanComplexArgs()
+    a.struct_size = ctypes.sizeof(ScanComplexArgs)
+    return a
+
+
 def new_step_args() -> StepArgs:
     a = StepArgs()
     a.struct_size = ctypes.sizeof(StepArgs)
@@ -197,6 +223,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_selective_scan_fwd.restype = ctypes.c_int
     lib.mss_selective_state_update.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.mss_selective_state_update.restype = ctypes.c_int
+    lib.mss_selective_scan_fwd_complex.argtypes = [ctypes.POINTER(ScanComplexArgs), _vp]
+    lib.mss_selective_scan_fwd_complex.restype = ctypes.c_int
     lib.mss_selective_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs),
                                                           ctypes.POINTER(ctypes.c_int)]
     lib.mss_selective_scan_bwd_workspace_size.restype = ctypes.c_size_t

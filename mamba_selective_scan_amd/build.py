@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmss.so")
-SOURCES = ["mss_api.hip", "scan_fwd.hip", "state_update.hip", "conv1d.hip", "scan_bwd.hip"]
+SOURCES = ["mss_api.hip", "scan_fwd.hip", "state_update.hip", "conv1d.hip", "scan_bwd.hip",
+           "scan_cplx.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every kernel: the compiler would

@@ -621,6 +621,87 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
 }
 
+mss_status mss_selective_scan_fwd_complex(const mss_scan_complex_args* a, void* stream) {
+  if (a == nullptr || a->struct_size != sizeof(mss_scan_complex_args) || a->reserved0 != 0 ||
+      a->reserved1 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->batch > kMaxDim || a->dim > kMaxDim ||
+      a->seqlen > kMaxSeqlen || a->batch * a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
+  const int64_t tiles = (a->dim + mss::kCxCh - 1) / mss::kCxCh;
+  if (a->batch * tiles > 0xFFFFFFFFll) return MSS_ERR_BAD_SHAPE;
+  if (a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr || a->A_imag == nullptr ||
+      a->B == nullptr || a->C == nullptr || a->out == nullptr)
+    return MSS_ERR_NULL_POINTER;
+  if (!strides_nonneg(a->u_stride, 3) || !strides_nonneg(a->delta_stride, 3) ||
+      !strides_nonneg(a->B_stride, 3) || !strides_nonneg(a->C_stride, 3) ||
+      !strides_nonneg(a->out_stride, 3) || !strides_nonneg(a->A_log_stride, 2) ||
+      !strides_nonneg(a->A_imag_stride, 2) || (a->z != nullptr && !strides_nonneg(a->z_stride, 3)))
+    return MSS_ERR_BAD_STRIDE;
+  const int64_t xs[3] = {a->batch, a->dim, a->seqlen};
+  const int64_t bcs[3] = {a->batch, a->dstate, a->seqlen};
+  const int64_t as[2] = {a->dim, a->dstate};
+  const int64_t vs[1] = {a->dim};
+  const int64_t ss[3] = {a->batch, a->dim, a->dstate};
+  const int64_t unit[3] = {a->dim * a->dstate, a->dstate, 1};
+  const int64_t one[1] = {1};
+  if (!non_overlapping(xs, a->out_stride, 3)) return MSS_ERR_BAD_STRIDE;
+  if (!aligned(a->u, 4) || !aligned(a->delta_raw, 4) || !aligned(a->A_log, 4) ||
+      !aligned(a->A_imag, 4) || !aligned(a->D, 4) || !aligned(a->z, 4) || !aligned(a->dt_bias, 4) ||
+      !aligned(a->out, 4) || !aligned(a->B, 8) || !aligned(a->C, 8) ||
+      !aligned(a->initial_state, 8) || !aligned(a->final_state, 8))
+    return MSS_ERR_MISALIGNED;
+  const Extent ins[] = {
+      extent_of(a->u, xs, a->u_stride, 3, 4),
+      extent_of(a->delta_raw, xs, a->delta_stride, 3, 4),
+      extent_of(a->z, xs, a->z_stride, 3, 4),
+      extent_of(a->B, bcs, a->B_stride, 3, 8),
+      extent_of(a->C, bcs, a->C_stride, 3, 8),
+      extent_of(a->A_log, as, a->A_log_stride, 2, 4),
+      extent_of(a->A_imag, as, a->A_imag_stride, 2, 4),
+      extent_of(a->D, vs, one, 1, 4),
+      extent_of(a->dt_bias, vs, one, 1, 4),
+      extent_of(a->initial_state, ss, unit, 3, 8),
+  };
+  const Extent eo = extent_of(a->out, xs, a->out_stride, 3, 4);
+  const Extent ef = extent_of(a->final_state, ss, unit, 3, 8);
+  for (const Extent& e : ins)
+    if (overlaps(eo, e) || overlaps(ef, e)) return MSS_ERR_ALIASING;
+  if (overlaps(eo, ef)) return MSS_ERR_ALIASING;
+
+  mss::CplxShape s{};
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.seqlen = static_cast<int>(a->seqlen);
+  s.dstate = static_cast<int>(a->dstate);
+  s.softplus = a->delta_softplus ? 1 : 0;
+  s.tiles = static_cast<int>(tiles);
+  std::memcpy(s.su, a->u_stride, sizeof(s.su));
+  std::memcpy(s.sd, a->delta_stride, sizeof(s.sd));
+  std::memcpy(s.so, a->out_stride, sizeof(s.so));
+  std::memcpy(s.sB, a->B_stride, sizeof(s.sB));
+  std::memcpy(s.sC, a->C_stride, sizeof(s.sC));
+  std::memcpy(s.sA, a->A_log_stride, sizeof(s.sA));
+  std::memcpy(s.sAi, a->A_imag_stride, sizeof(s.sAi));
+  if (a->z != nullptr) std::memcpy(s.sz, a->z_stride, sizeof(s.sz));
+  mss::CplxPtrs p{};
+  p.u = a->u;
+  p.delta_raw = a->delta_raw;
+  p.A_log = a->A_log;
+  p.A_imag = a->A_imag;
+  p.B = static_cast<const float2*>(a->B);
+  p.C = static_cast<const float2*>(a->C);
+  p.D = a->D;
+  p.z = a->z;
+  p.dt_bias = a->dt_bias;
+  p.h0 = static_cast<const float2*>(a->initial_state);
+  p.out = a->out;
+  p.final_state = static_cast<float2*>(a->final_state);
+  const hipError_t e = mss::launch_scan_complex(s, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
 mss_status mss_causal_conv1d_fwd(const mss_conv_args* a, void* stream) {
   if (a == nullptr || a->struct_size != sizeof(mss_conv_args) || a->reserved0 != 0)
     return MSS_ERR_BAD_STRUCT;

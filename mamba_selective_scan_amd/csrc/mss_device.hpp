@@ -116,6 +116,16 @@ __device__ inline float sum_half_rows(float v) {
   return v;
 }
 
+// Sum over the 16 lanes of a DPP row, left in every lane of the row (every
+// source lane of a row rotation is valid, so bound_ctrl changes nothing).
+__device__ inline float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, true));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, true));  // row_ror:1
+  return v;
+}
+
 // Raw buffer descriptors: a range that keeps every valid 32-bit tile offset
 // in bounds; kOffNone lies past it, so an access with that offset reads 0 or
 // writes nothing.  Flags: the gfx9 raw-buffer data format word.

@@ -1,0 +1,143 @@
+// scan_cplx.hip -- selective-scan forward with a complex diagonal A, gfx950.
+//
+// Per channel (b, d), time t and state n, in complex arithmetic:
+//   A[n]  = -exp(A_log[d,n]) + i A_imag[d,n]
+//   a_t   = exp(delta_t A[n])
+//         = 2^(delta_t Re(A) log2 e) (cos(delta_t Im A) + i sin(delta_t Im A))
+//   h_t   = a_t h_(t-1) + delta_t u_t B_t[n]
+//   out_t = (Re(sum_n C_t[n] h_t[n]) + D u_t) silu(z_t)
+// The pages note that the official CUDA kernel carries a complex-A variant
+// with its own complex exp2 ("createcentury" post on the kernel, section
+// "主要な最適化テクニック"); delta, the skip term and the gate are the real
+// forward's (see scan_fwd.hip).
+//
+// Mapping: a workgroup of 256 lanes covers 16 channels of one batch row, one
+// lane per (channel, state): a 16-lane DPP row holds one channel, and
+// Re(C . h) is a 4-step rotation sum inside the row.  Time is walked in
+// chunks of kCxT steps:
+//   E  B and C of the chunk (16 states x kCxT steps, shared by the 16
+//      channels) and, per element, (delta, delta u) into LDS;
+//   S  each lane walks the chunk: the complex decay from exp2, and from the
+//      hardware sin / cos of the fractional turns delta Im(A) / 2 pi (the
+//      fraction keeps v_sin / v_cos inside their input range); one complex
+//      multiply-add; the row sum of Re(C h) lands in LDS;
+//   O  out = (y + D u) silu(z), one store per element.
+// The state never leaves the registers.  Lanes past dstate hold zeros.
+#include "mss_device.hpp"
+#include "mss_internal.hpp"
+
+namespace mss {
+namespace {
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+constexpr int kCxPer = kCxCh * kCxT / kCxThreads;  // elements per lane in E and O (2)
+
+__global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, CplxPtrs p) {
+  __shared__ float2 s_B[kMaxState][kCxT + 1];
+  __shared__ float2 s_C[kMaxState][kCxT + 1];
+  __shared__ float2 s_dd[kCxCh][kCxT + 1];  // (delta, delta * u)
+  __shared__ float s_y[kCxCh][kCxT + 1];
+
+  const int tid = threadIdx.x;
+  const int b = static_cast<int>(blockIdx.x / s.tiles);
+  const int d0 = static_cast<int>(blockIdx.x % s.tiles) * kCxCh;
+
+  // scan role: lane (c, n) = (tid / 16, tid % 16)
+  const int c = tid >> 4, n = tid & (kMaxState - 1);
+  const int d = d0 + c;
+  const bool active = d < s.dim && n < s.dstate;
+  float ar2 = 0.0f, ai = 0.0f, hr = 0.0f, hi = 0.0f;
+  if (active) {
+    ar2 = -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e;  // Re(A) log2 e
+    ai = p.A_imag[d * s.sAi[0] + n * s.sAi[1]] * kInv2Pi;      // Im(A) in turns
+    if (p.h0 != nullptr) {
+      const float2 v = p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
+      hr = v.x;
+      hi = v.y;
+    }
+  }
+
+  // element role: element e = tid + kCxThreads j of the 16 x kCxT tile is
+  // (row e / kCxT, step e % kCxT); rows are channels for u, delta, z, out
+  // and states for B, C
+  int erow[kCxPer], estep[kCxPer];
+  float ebias[kCxPer], eskip[kCxPer];
+#pragma unroll
+  for (int j = 0; j < kCxPer; ++j) {
+    const int e = tid + kCxThreads * j;
+    erow[j] = e / kCxT;
+    estep[j] = e % kCxT;
+    const int dd = d0 + erow[j];
+    const bool ok = dd < s.dim;
+    ebias[j] = (ok && p.dt_bias != nullptr) ? p.dt_bias[dd] : 0.0f;
+    eskip[j] = (ok && p.D != nullptr) ? p.D[dd] : 0.0f;
+  }
+
+  for (int t0 = 0; t0 < s.seqlen; t0 += kCxT) {
+    float eu[kCxPer];
+    // ---- E ----
+#pragma unroll
+    for (int j = 0; j < kCxPer; ++j) {
+      const int t = t0 + estep[j];
+      const bool tin = t < s.seqlen;
+      const int ns = erow[j];
+      const bool bok = tin && ns < s.dstate;
+      s_B[ns][estep[j]] =
+          bok ? p.B[b * s.sB[0] + ns * s.sB[1] + t * s.sB[2]] : make_float2(0.0f, 0.0f);
+      s_C[ns][estep[j]] =
+          bok ? p.C[b * s.sC[0] + ns * s.sC[1] + t * s.sC[2]] : make_float2(0.0f, 0.0f);
+      const int dd = d0 + erow[j];
+      const bool xok = tin && dd < s.dim;
+      float dl = 0.0f, uv = 0.0f;
+      if (xok) {
+        const float x = p.delta_raw[b * s.sd[0] + dd * s.sd[1] + t * s.sd[2]] + ebias[j];
+        dl = s.softplus ? softplus(x) : x;
+        uv = p.u[b * s.su[0] + dd * s.su[1] + t * s.su[2]];
+      }
+      eu[j] = uv;
+      s_dd[erow[j]][estep[j]] = make_float2(dl, dl * uv);
+    }
+    __syncthreads();
+    // ---- S ----
+#pragma unroll 4
+    for (int tt = 0; tt < kCxT; ++tt) {
+      const float2 dd = s_dd[c][tt];
+      const float2 bb = s_B[n][tt];
+      const float2 cc = s_C[n][tt];
+      const float turns = __builtin_amdgcn_fractf(dd.x * ai);
+      const float m = fast_exp2(dd.x * ar2);
+      const float a_r = m * __builtin_amdgcn_cosf(turns);
+      const float a_i = m * __builtin_amdgcn_sinf(turns);
+      const float nr = fmaf(a_r, hr, fmaf(-a_i, hi, dd.y * bb.x));
+      const float ni = fmaf(a_r, hi, fmaf(a_i, hr, dd.y * bb.y));
+      hr = nr;
+      hi = ni;
+      const float y = row_sum16(fmaf(cc.x, hr, -cc.y * hi));
+      if (n == 0) s_y[c][tt] = y;
+    }
+    __syncthreads();
+    // ---- O ----
+#pragma unroll
+    for (int j = 0; j < kCxPer; ++j) {
+      const int t = t0 + estep[j];
+      const int dd = d0 + erow[j];
+      if (t < s.seqlen && dd < s.dim) {
+        float y = fmaf(eskip[j], eu[j], s_y[erow[j]][estep[j]]);
+        if (p.z != nullptr) y *= silu(p.z[b * s.sz[0] + dd * s.sz[1] + t * s.sz[2]]);
+        p.out[b * s.so[0] + dd * s.so[1] + t * s.so[2]] = y;
+      }
+    }
+  }
+  if (active && p.final_state != nullptr)
+    p.final_state[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] = make_float2(hr, hi);
+}
+
+}  // namespace
+
+hipError_t launch_scan_complex(const CplxShape& s, const CplxPtrs& p, hipStream_t stream) {
+  const unsigned wgs = static_cast<unsigned>(static_cast<int64_t>(s.batch) * s.tiles);
+  scan_cplx_kernel<<<dim3(wgs), dim3(kCxThreads), 0, stream>>>(s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mss

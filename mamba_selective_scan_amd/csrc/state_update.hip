@@ -23,15 +23,6 @@ namespace mss {
 constexpr int kStepThreads = 256;                   // 16 channels per workgroup
 constexpr int kStepChannels = kStepThreads / kMaxState;
 
-// Sum over the 16 lanes of a DPP row, left in every lane of the row.
-__device__ inline float row_sum16(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));  // row_ror:8
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));  // row_ror:4
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, true));  // row_ror:2
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, true));  // row_ror:1
-  return v;
-}
-
 template <typename IO>
 __global__ __launch_bounds__(kStepThreads) void state_update_kernel(
     StepShape s, float* __restrict__ state, const IO* __restrict__ u,

@@ -111,6 +111,56 @@ def generate_workload(w: Workload, seed: int = 0, **kw) -> dict:
                     seed=seed, **kw)
 
 
+def generate_complex(batch: int, dim: int, seqlen: int, dstate: int, layout: str = "bdl",
+                     seed: int = 0) -> dict:
+    """A complex-A problem: the real problem of ``generate`` (u, delta_raw, z,
+    A_log = log(n + 1), D = 1, dt_bias) with A_imag[d, n] = pi n (the
+    S4D-Lin rotation ladder) and complex B, C whose real and imaginary parts
+    are independent N(0, 1/2) (unit complex variance), as complex64 in logical
+    index order [batch, dstate, seqlen]."""
+    x = generate(batch, dim, seqlen, dstate, layout, seed=seed)
+    rng = np.random.default_rng(seed + 1_000_003)
+    shape = (batch, dstate, seqlen) if layout == "bdl" else (batch, seqlen, dstate)
+    half = np.float32(np.sqrt(0.5))
+    for k in ("B", "C"):
+        re = rng.standard_normal(shape, dtype=np.float32) * half
+        im = rng.standard_normal(shape, dtype=np.float32) * half
+        c = (re + 1j * im).astype(np.complex64)
+        x[k] = c if layout == "bdl" else c.transpose(0, 2, 1)
+    x["A_imag"] = np.tile(np.float32(np.pi) * np.arange(dstate, dtype=np.float32), (dim, 1))
+    return x
+
+
+def complex_to_torch(inputs: dict, device) -> dict:
+    """Move a complex-A problem to ``device`` (fp32 activations, complex64 B
+    and C), keeping the storage layout as to_torch does."""
+    import torch
+
+    out = {"layout": inputs["layout"]}
+    for k, dt in (("u", torch.float32), ("delta_raw", torch.float32), ("z", torch.float32),
+                  ("B", torch.complex64), ("C", torch.complex64)):
+        a = inputs[k]
+        if inputs["layout"] == "bld":
+            t = torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1)))
+            out[k] = t.to(device=device, dtype=dt).transpose(1, 2)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
+    for k in ("A_log", "A_imag", "D", "dt_bias"):
+        out[k] = torch.from_numpy(np.ascontiguousarray(inputs[k])).to(device)
+    return out
+
+
+def complex_algorithmic_bytes(batch, dim, seqlen, dstate, final_state=True) -> int:
+    """Bytes a complex-A forward must move: u, delta_raw, z read and out
+    written (fp32), B and C read (complex64), the [D, N] parameters and D,
+    dt_bias, and the complex final state."""
+    n = 4 * batch * dim * seqlen * 4 + 2 * batch * dstate * seqlen * 8
+    n += 2 * dim * dstate * 4 + 2 * dim * 4
+    if final_state:
+        n += batch * dim * dstate * 8
+    return n
+
+
 def to_torch(inputs: dict, device, io_dtype: str = "f32") -> dict:
     """Move a generated problem to ``device``.
 

@@ -67,7 +67,8 @@ def _c_layout(struct_name, fields, tmp_path):
                                        (_lib.StepArgs, "mss_step_args"),
                                        (_lib.ConvArgs, "mss_conv_args"),
                                        (_lib.ConvStepArgs, "mss_conv_step_args"),
-                                       (_lib.ScanBwdArgs, "mss_scan_bwd_args")])
+                                       (_lib.ScanBwdArgs, "mss_scan_bwd_args"),
+                                       (_lib.ScanComplexArgs, "mss_scan_complex_args")])
 def test_ctypes_struct_matches_c_layout(cls, cname, tmp_path):
     names = [f[0] for f in cls._fields_]
     size, offs = _c_layout(cname, names, tmp_path)
@@ -415,3 +416,54 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib(str(tmp_path / "missing.so"))
+
+
+def cplx_args():
+    a = _lib.new_scan_complex_args()
+    a.batch, a.dim, a.seqlen, a.dstate = 2, 40, 50, 16
+    x = (40 * 50, 50, 1)
+    bc = (16 * 50, 50, 1)
+    a.u, a.u_stride = fake(0), (ctypes.c_int64 * 3)(*x)
+    a.delta_raw, a.delta_stride = fake(1), (ctypes.c_int64 * 3)(*x)
+    a.A_log, a.A_log_stride = fake(2), (ctypes.c_int64 * 2)(16, 1)
+    a.A_imag, a.A_imag_stride = fake(3), (ctypes.c_int64 * 2)(16, 1)
+    a.B, a.B_stride = fake(4), (ctypes.c_int64 * 3)(*bc)
+    a.C, a.C_stride = fake(5), (ctypes.c_int64 * 3)(*bc)
+    a.D = fake(6)
+    a.z, a.z_stride = fake(7), (ctypes.c_int64 * 3)(*x)
+    a.dt_bias = fake(8)
+    a.initial_state = fake(9)
+    a.out, a.out_stride = fake(10), (ctypes.c_int64 * 3)(*x)
+    a.final_state = fake(11)
+    a.delta_softplus = 1
+    return a
+
+
+CPLX_CASES = {
+    "null_struct": (None, "MSS_ERR_BAD_STRUCT"),
+    "struct_size": (lambda a: setattr(a, "struct_size", 16), "MSS_ERR_BAD_STRUCT"),
+    "reserved0": (lambda a: setattr(a, "reserved0", 1), "MSS_ERR_BAD_STRUCT"),
+    "reserved1": (lambda a: setattr(a, "reserved1", 1), "MSS_ERR_BAD_STRUCT"),
+    "seqlen0": (lambda a: setattr(a, "seqlen", 0), "MSS_ERR_BAD_SHAPE"),
+    "dstate17": (lambda a: setattr(a, "dstate", 17), "MSS_ERR_UNSUPPORTED_DSTATE"),
+    "A_imag_null": (lambda a: setattr(a, "A_imag", None), "MSS_ERR_NULL_POINTER"),
+    "C_null": (lambda a: setattr(a, "C", None), "MSS_ERR_NULL_POINTER"),
+    "neg_stride": (lambda a: a.B_stride.__setitem__(2, -1), "MSS_ERR_BAD_STRIDE"),
+    "out_overlap": (lambda a: a.out_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
+    "misaligned_B": (lambda a: setattr(a, "B", fake(4) + 4), "MSS_ERR_MISALIGNED"),
+    "misaligned_final": (lambda a: setattr(a, "final_state", fake(11) + 4), "MSS_ERR_MISALIGNED"),
+    "out_is_u": (lambda a: setattr(a, "out", fake(0)), "MSS_ERR_ALIASING"),
+    "final_on_C": (lambda a: setattr(a, "final_state", fake(5) + 64), "MSS_ERR_ALIASING"),
+    "final_on_out": (lambda a: setattr(a, "final_state", fake(10) + 64), "MSS_ERR_ALIASING"),
+}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(CPLX_CASES))
+def test_complex_argument_checks(case):
+    fn, expect = CPLX_CASES[case]
+    a = None if fn is None else cplx_args()
+    if fn is not None:
+        fn(a)
+    arg = ctypes.byref(a) if a is not None else None
+    assert _lib.lib().mss_selective_scan_fwd_complex(arg, None) == code(expect)
