@@ -20,10 +20,12 @@ With --op conv1d the step is instead the causal depthwise conv1d + SiLU
 (width 4) with window export followed by one conv decode step, on the same
 workload shapes, reported against the HBM roofline.  With --op scan_bwd it is
 the selective-scan backward (all gradients, initial-state and final-state
-gradients included), reported against the VALU issue roofline.
+gradients included), reported against the VALU issue roofline, and with
+--op scan_complex the complex-A forward (fp32 activations, complex64 B, C
+and states), also against the VALU roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--io f32|bf16]
-                       [--op scan|conv1d|scan_bwd]
+                       [--op scan|conv1d|scan_bwd|scan_complex]
 """
 
 from __future__ import annotations
@@ -66,6 +68,9 @@ KERNEL_SOURCES = {
     "conv1d": ["mamba_selective_scan_amd/csrc/conv1d.hip",
                "mamba_selective_scan_amd/csrc/mss_device.hpp",
                "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
+    "scan_complex": ["mamba_selective_scan_amd/csrc/scan_cplx.hip",
+                     "mamba_selective_scan_amd/csrc/mss_device.hpp",
+                     "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
     "scan_bwd": ["mamba_selective_scan_amd/csrc/scan_bwd.hip",
                  "mamba_selective_scan_amd/csrc/mss_device.hpp",
                  "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
@@ -488,6 +493,155 @@ def bwd_cpu_baseline(x, w, io_bytes, alg_bytes, target_s):
     }
 
 
+def complex_valu_slots_per_element(dstate: int) -> int:
+    """Algorithmic VALU slots per (b, d, t) element of the complex-A forward.
+
+    Per state: exp2, sin and cos (4 each); delta*Re(A) and delta*Im(A); the
+    modulus times cos and sin; the complex multiply-add h = a h + delta u B
+    (delta u times Re and Im of B, then two FMAs per component); Re(C h) (a
+    multiply and an FMA): 24.  Per element as the real forward: 31.
+    """
+    return dstate * 24 + 31
+
+
+def complex_cpu_baseline(x, target_s):
+    """Time the complex oracle (as is) on a growing channel sample."""
+    import numpy as np
+
+    import oracle
+    from mamba_selective_scan_amd.inputs import complex_algorithmic_bytes
+
+    batch, dim, seqlen = x["u"].shape
+    dstate = x["A_log"].shape[1]
+    threads = oracle.max_threads()
+    rng = np.random.default_rng(321)
+
+    def run(k):
+        # k channels: a random subset of batch row 0, or whole leading rows
+        if k < dim:
+            ds = np.sort(rng.choice(dim, size=k, replace=False))
+            sl = (slice(0, 1), ds)
+            args = (x["u"][sl], x["delta_raw"][sl], x["A_log"][ds], x["A_imag"][ds], x["B"][:1],
+                    x["C"][:1])
+            kw = dict(D=x["D"][ds], z=x["z"][sl], dt_bias=x["dt_bias"][ds])
+            used = k
+        else:
+            rows = min(batch, -(-k // dim))
+            args = (x["u"][:rows], x["delta_raw"][:rows], x["A_log"], x["A_imag"], x["B"][:rows],
+                    x["C"][:rows])
+            kw = dict(D=x["D"], z=x["z"][:rows], dt_bias=x["dt_bias"])
+            used = rows * dim
+        t = time.perf_counter()
+        oracle.scan_fwd_complex(*args, **kw)
+        return time.perf_counter() - t, used
+
+    k = 4 * threads
+    while True:
+        dt, k_used = run(k)
+        if dt >= target_s / 8 or k_used >= batch * dim:
+            break
+        k *= 4
+    if dt < target_s and k_used < batch * dim:
+        dt, k_used = run(int(min(batch * dim, k_used * target_s / max(dt, 1e-3))))
+    per_elem = complex_algorithmic_bytes(batch, dim, seqlen, dstate) / (batch * dim * seqlen)
+    return {
+        "value": round(k_used * seqlen * per_elem / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{k_used} of {batch * dim} channels x full seqlen {seqlen}, "
+                  f"fp64 complex recurrence, {dt:.1f} s",
+    }
+
+
+def main_complex(args):
+    import torch
+
+    import mamba_selective_scan_amd as mss
+    from mamba_selective_scan_amd.inputs import (WORKLOADS, complex_algorithmic_bytes,
+                                                 complex_to_torch, generate_complex)
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"complex workload {w.name}: B={w.batch} D={w.dim} L={w.seqlen} N={w.dstate} {w.layout} "
+        "fp32 / complex64")
+    x = generate_complex(w.batch, w.dim, w.seqlen, w.dstate, w.layout, seed=args.seed)
+    dx = complex_to_torch(x, dev)
+    out = torch.empty_like(dx["u"])
+    fin = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.complex64, device=dev)
+
+    def run():
+        mss.selective_scan_fwd_complex(dx["u"], dx["delta_raw"], dx["A_log"], dx["A_imag"],
+                                       dx["B"], dx["C"], D=dx["D"], z=dx["z"],
+                                       dt_bias=dx["dt_bias"], out=out, final_state=fin)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / len(ms)
+    alg = complex_algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate)
+    slots = w.elems * complex_valu_slots_per_element(w.dstate)
+    gbs = alg / (mean_ms * 1e-3) / 1e9
+    tslots = slots / (mean_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash("scan_complex")
+    traffic = load_traffic(w.name, "f32", src_hash, op="scan_complex")
+    log(f"complex scan mean {mean_ms * 1e3:.1f} us (min {ms[0] * 1e3:.1f}); {gbs:.0f} GB/s = "
+        f"{gbs / HBM_PEAK_GBS:.1%} of 8 TB/s; VALU {tslots / VALU_PEAK_TSLOTS:.1%}")
+    rec = {
+        "metric": "complex-A selective-scan fwd achieved HBM GB/s (% of 8 TB/s) and Gtok·ch/s",
+        "value": round(alg / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "scan_complex", "batch": w.batch, "dim": w.dim,
+                   "seqlen": w.seqlen, "dstate": w.dstate, "layout": w.layout,
+                   "io_dtype": "f32 activations, complex64 B/C/states",
+                   "step": "complex-A scan fwd + final-state export"},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "gtok_ch_per_s": round(w.elems / (ms_per_step * 1e-3) / 1e9, 4),
+        "roofline": {
+            "bound": "alu",
+            "kernel": "scan_cplx_kernel (mss_selective_scan_fwd_complex) on the current stream",
+            "achieved": round(tslots, 3),
+            "peak": round(VALU_PEAK_TSLOTS, 3),
+            "unit": "T VALU lane-slots/s",
+            "frac": round(tslots / VALU_PEAK_TSLOTS, 4),
+            "traffic": traffic,
+            "algorithmic_slots": slots,
+            "slots_per_element": complex_valu_slots_per_element(w.dstate),
+            "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg},
+            "event_us_mean": round(mean_ms * 1e3, 2),
+            "event_us_median": round(ms[len(ms) // 2] * 1e3, 2),
+            "kernel_source_hash": src_hash,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: complex oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
+        rec["cpu_baseline"] = complex_cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -499,7 +653,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="time the forward alone")
-    ap.add_argument("--op", default="scan", choices=["scan", "conv1d", "scan_bwd"])
+    ap.add_argument("--op", default="scan", choices=["scan", "conv1d", "scan_bwd", "scan_complex"])
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -511,6 +665,8 @@ def main(argv=None):
         return main_conv(args)
     if args.op == "scan_bwd":
         return main_bwd(args)
+    if args.op == "scan_complex":
+        return main_complex(args)
 
     import torch
 
