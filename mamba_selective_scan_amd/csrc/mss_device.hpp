@@ -73,17 +73,6 @@ __device__ static inline float silu(float z) {
   return z * __builtin_amdgcn_rcpf(den);
 }
 
-// Load of a wave-uniform element (B or C) so that it can live in a scalar
-// register.  bf16: the aligned 32-bit word holding the element is read (an
-// aligned word never crosses a page) and the right half selected.
-__device__ inline float load_uniform(const float* p) { return *p; }
-__device__ inline float load_uniform(const bf16_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t word = *reinterpret_cast<const uint32_t*>(a & ~static_cast<uintptr_t>(3));
-  const uint32_t sh = (a & 2) ? 16u : 0u;
-  return __uint_as_float((word >> sh) << 16);
-}
-
 // Sum over the eight state groups of one channel (lanes c + 8g) of four
 // per-step partial sums.  The two swap-and-add levels sum over lane bits 5 and
 // 4 and leave step {0, 2, 1, 3}[row] in 16-lane row `row`; a DPP rotation by 8
@@ -102,18 +91,6 @@ __device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
   // row_ror:8 -- lane i of a row reads lane (i + 8) mod 16
   return w + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x128, 0xF, 0xF,
                                                         false));
-}
-
-// Sum of v over the 8 lanes of each 8-lane group (a half row, lanes 8g..8g+7),
-// left in every lane of the group: the lane pairs (i, 7-i), then (i, i^2),
-// then (i, i^1) are added with DPP row_half_mirror and quad permutations.
-// Every source lane is valid for these patterns; bound_ctrl lets the compiler
-// fold each move into the add (v_add_f32_dpp).
-__device__ inline float sum_half_rows(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-  return v;
 }
 
 // Sum over the 16 lanes of a DPP row, left in every lane of the row (every

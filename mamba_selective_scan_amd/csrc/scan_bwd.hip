@@ -75,16 +75,6 @@ __device__ inline float f4_at(const f4& v, int i) {
 template <typename IO>
 __device__ inline float ld(const IO* p) { return io_traits<IO>::load(p); }
 
-// Load of base[off] for lanes with ok, 0 for the others, without a branch:
-// masked lanes read base[0] (always inside the tensor) and drop the value.
-// Unconditional loads let the compiler wait for each one exactly when it is
-// used, so a chunk's loads can be issued a chunk ahead.
-template <typename IO>
-__device__ inline float ld_masked(const IO* base, int64_t off, bool ok) {
-  const float v = io_traits<IO>::load(base + (ok ? off : 0));
-  return ok ? v : 0.0f;
-}
-
 __device__ inline float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
 }
