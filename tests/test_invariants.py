@@ -1,7 +1,6 @@
 """Bitwise invariants of the HIP path: determinism, linearity in u, causality,
 layout equivalence and channel permutation."""
 
-import numpy as np
 import pytest
 
 from gpu_util import device, note
