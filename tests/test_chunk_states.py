@@ -89,6 +89,15 @@ def test_chunk_states_time_split(mss):
     _case(mss, "time-split", 1, 64, 2000, h0=True, a_log="normal")
 
 
+def test_chunk_states_reverse_time_split(mss):
+    _case(mss, "reverse time-split", 1, 64, 1500, reverse=True, h0=True, a_log="normal")
+
+
+def test_chunk_states_bf16_reverse(mss):
+    # an odd length: the element-wise pass for bf16 t-fast vectors in reverse
+    _case(mss, "bf16 reverse L=83", 2, 64, 83, io="bf16", reverse=True)
+
+
 def test_chunk_states_channel_last(mss):
     _case(mss, "bld", 2, 64, 77, layout="bld")
 
@@ -104,7 +113,8 @@ def test_chunk_states_small_dstate(mss):
 
 
 @pytest.mark.parametrize("shape,reverse", [((2, 72, 100), False), ((2, 72, 100), True),
-                                           ((1, 64, 1500), False), ((2, 40, 37), False)])
+                                           ((1, 64, 1500), False), ((1, 64, 1500), True),
+                                           ((2, 40, 37), False)])
 def test_bwd_with_chunk_states(mss, shape, reverse):
     """The backward given the forward's chunk states: against the oracle and
     against the backward that recomputes them."""
