@@ -22,6 +22,9 @@ constexpr int kThreads = 64;                         // one wave
 constexpr int kVec = 4;
 constexpr int kPerThread = kCh * kT / kThreads;      // 4 tile elements per lane
 
+// Carry kernels (time segments): aggregates loaded per batch of segments.
+constexpr int kCarryBatch = 16;
+
 // Sizes and element strides (logical order) of one scan call.  Pointers are
 // passed as separate kernel arguments so they can carry __restrict__.
 struct ScanShape {

@@ -324,17 +324,35 @@ __global__ __launch_bounds__(256) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
   const int64_t sstride = s.nchan_pad * kMaxState;
   float h = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
   p.carry_h[idx] = h;
-  for (int sgm = 0; sgm + 1 < s.nseg; ++sgm) {
-    const float4 a = p.agg[sgm * sstride + idx];
-    h = fmaf(a.x, h, a.y);
-    p.carry_h[(sgm + 1) * sstride + idx] = h;
+  // the aggregates do not depend on the chains: load kCarryBatch segments
+  // ahead of the multiply-adds (one memory latency per batch)
+  for (int base = 0; base + 1 < s.nseg; base += kCarryBatch) {
+    float2 a[kCarryBatch];
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      const float4 v = p.agg[min(base + j, s.nseg - 2) * sstride + idx];
+      a[j] = base + j + 1 < s.nseg ? make_float2(v.x, v.y) : make_float2(1.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      h = fmaf(a[j].x, h, a[j].y);
+      if (base + j + 1 < s.nseg) p.carry_h[(base + j + 1) * sstride + idx] = h;
+    }
   }
   float g = (active && p.dfinal != nullptr) ? p.dfinal[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
   p.carry_g[(s.nseg - 1) * sstride + idx] = g;
-  for (int sgm = s.nseg - 1; sgm > 0; --sgm) {
-    const float4 a = p.agg[sgm * sstride + idx];
-    g = fmaf(a.x, g, a.z);
-    p.carry_g[(sgm - 1) * sstride + idx] = g;
+  for (int top = s.nseg - 1; top > 0; top -= kCarryBatch) {
+    float2 a[kCarryBatch];
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      const float4 v = p.agg[max(top - j, 1) * sstride + idx];
+      a[j] = top - j > 0 ? make_float2(v.x, v.z) : make_float2(1.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      g = fmaf(a[j].x, g, a[j].y);
+      if (top - j > 0) p.carry_g[(top - j - 1) * sstride + idx] = g;
+    }
   }
 }
 

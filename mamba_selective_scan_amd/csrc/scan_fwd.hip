@@ -574,6 +574,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
 // carry[s] = state entering segment s, from the segment aggregates:
 //   carry[0] = h0 (or 0),  carry[s+1] = P[s] * carry[s] + H[s].
+// One lane per (channel, state) walks the segments in order.  The aggregates
+// do not depend on the chain, so they are loaded kCarryBatch segments at a
+// time ahead of the multiply-adds: one memory latency per batch instead of
+// one per segment (a 256-channel sequence in 128 segments has only 4096
+// lanes to hide it with).
 __global__ __launch_bounds__(256) void carry_kernel(ScanShape s, const float2* __restrict__ agg,
                                                     const float* __restrict__ h0,
                                                     float* __restrict__ carry) {
@@ -584,13 +589,22 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanShape s, const float2* _
   const int64_t per_b = static_cast<int64_t>(s.groups) * kCh;
   const int b = static_cast<int>(row / per_b);
   const int d = static_cast<int>(row % per_b);
+  const int64_t sstride = s.nchan_pad * kMaxState;  // idx = row * kMaxState + n
   float c = 0.0f;
   if (h0 != nullptr && d < s.dim && n < s.dstate)
     c = h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
-  for (int sgm = 0; sgm + 1 < s.nseg; ++sgm) {
-    const float2 a = agg[(static_cast<int64_t>(sgm) * s.nchan_pad + row) * kMaxState + n];
-    c = fmaf(a.x, c, a.y);
-    carry[(static_cast<int64_t>(sgm + 1) * s.nchan_pad + row) * kMaxState + n] = c;
+  for (int base = 0; base + 1 < s.nseg; base += kCarryBatch) {
+    float2 a[kCarryBatch];
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {  // past the last aggregate: the identity (1, 0)
+      const float2 v = agg[min(base + j, s.nseg - 2) * sstride + idx];
+      a[j] = base + j + 1 < s.nseg ? v : make_float2(1.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      c = fmaf(a[j].x, c, a[j].y);
+      if (base + j + 1 < s.nseg) carry[(base + j + 1) * sstride + idx] = c;
+    }
   }
 }
 
