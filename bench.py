@@ -15,6 +15,10 @@ Prints one JSON line:
                 when a matching profile is committed under profiles/;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
                 the host's cores.
+The roofline and decode objects also give the same calls replayed from a
+recorded HIP graph (graph_us_mean, graph_us_per_step over a recorded 64-step
+decode loop): the GPU time without the host's launch cost, which dominates
+the small shapes and the decode step.
 
 With --op conv1d the step is instead the causal depthwise conv1d + SiLU
 (width 4) with window export followed by one conv decode step, on the same
@@ -108,6 +112,32 @@ def load_traffic(workload: str, io: str, src_hash: str, op: str = "scan"):
         log(f"traffic record {os.path.basename(path)} is for another kernel version; ignored")
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def graph_us(fn, reps: int, inner: int = 1) -> float:
+    """Mean GPU time per call of fn: fn recorded `inner` times in one HIP graph,
+    the graph replayed `reps` times between two events, so no host launch
+    cost enters (what a caller that records its loop sees)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * inner)
 
 
 def cpu_baseline(x, w, io_bytes, target_s: float):
@@ -243,6 +273,8 @@ def main_conv(args):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(ms) / len(ms)
+    conv_graph_us = graph_us(conv, reps=max(5, min(200, int(20e3 / (mean_ms * 1e3)))))
+    dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64)
     fwd_bytes = conv_algorithmic_bytes(w.batch, w.dim, w.seqlen, width, io_bytes)
     fwd_bytes += w.batch * w.dim * (width - 1) * io_bytes          # exported window
     step_b = 0 if args.no_step else (2 * w.batch * w.dim * (width - 1) * io_bytes
@@ -281,6 +313,7 @@ def main_conv(args):
             "algorithmic_bytes": fwd_bytes,
             "event_us_mean": round(mean_ms * 1e3, 2),
             "event_us_median": round(ms[len(ms) // 2] * 1e3, 2),
+            "graph_us_mean": round(conv_graph_us, 2),
             "kernel_source_hash": src_hash,
         },
         "cpu_baseline": None,
@@ -294,6 +327,7 @@ def main_conv(args):
             "event_us_median": round(dec_ms[len(dec_ms) // 2] * 1e3, 2),
             "algorithmic_bytes": step_b,
             "achieved_gbs": round(step_b / (dec_mean * 1e-3) / 1e9, 1),
+            "graph_us_per_step": round(dec_graph_us, 2),
         }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: conv oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
@@ -726,6 +760,9 @@ def main(argv=None):
     scan_ms_mean = sum(scan_ms) / len(scan_ms)
     scan_ms_sorted = sorted(scan_ms)
 
+    scan_graph_us = graph_us(scan, reps=max(5, min(200, int(20e3 / (scan_ms_mean * 1e3)))))
+    dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64)
+
     fwd_bytes = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, io_bytes, final_state=True)
     fwd_slots = w.elems * valu_slots_per_element(w.dstate)
     total_bytes = fwd_bytes + (0 if args.no_step else step_bytes(w.batch, w.dim, w.dstate, io_bytes))
@@ -734,6 +771,7 @@ def main(argv=None):
     achieved_slots = fwd_slots / (scan_ms_mean * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     traffic = load_traffic(w.name, args.io, src_hash)
+    log(f"scan fwd replayed from a graph: {scan_graph_us:.1f} us")
     log(f"step {ms_per_step:.4f} ms; scan fwd mean {scan_ms_mean * 1e3:.1f} us "
         f"(min {scan_ms_sorted[0] * 1e3:.1f}, median {scan_ms_sorted[len(scan_ms) // 2] * 1e3:.1f}); "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s")
@@ -781,6 +819,9 @@ def main(argv=None):
             },
             "event_us_mean": round(scan_ms_mean * 1e3, 2),
             "event_us_median": round(scan_ms_sorted[len(scan_ms) // 2] * 1e3, 2),
+            # the same call replayed from a HIP graph: without the Python
+            # binding's and the launches' host time, which small shapes expose
+            "graph_us_mean": round(scan_graph_us, 2),
             "kernel_source_hash": src_hash,
         },
         "cpu_baseline": None,
@@ -795,9 +836,12 @@ def main(argv=None):
             "event_us_median": round(dec_ms[len(dec_ms) // 2] * 1e3, 2),
             "algorithmic_bytes": dec_bytes,
             "achieved_gbs": round(dec_bytes / (dec_mean * 1e-3) / 1e9, 1),
+            # a 64-step decode loop recorded as one graph, per step
+            "graph_us_per_step": round(dec_graph_us, 2),
         }
         log(f"decode step mean {dec_mean * 1e3:.2f} us, "
-            f"{dec_bytes / (dec_mean * 1e-3) / 1e9:.0f} GB/s")
+            f"{dec_bytes / (dec_mean * 1e-3) / 1e9:.0f} GB/s; {dec_graph_us:.2f} us per step "
+            f"in a recorded 64-step loop")
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a channel sample (~{args.cpu_seconds:.0f} s)")
         rec["cpu_baseline"] = cpu_baseline(x, w, io_bytes, args.cpu_seconds)

@@ -8,8 +8,8 @@
 
 namespace mss {
 
-// Scan tiling.  One workgroup is one wave; it owns kCh consecutive channels of
-// one batch row and one time segment.  In the scan, lane (g, c) =
+// Scan tiling.  One wave owns kCh consecutive channels of one batch row and
+// one time segment (the waves of a workgroup are independent).  In the scan, lane (g, c) =
 // (lane / kCh, lane % kCh) runs states [g*kStatesPerLane, (g+1)*kStatesPerLane)
 // of channel c, and the segment is walked in chunks of kT time steps.  Loads
 // and stores move kVec-element vectors along the unit-stride axis.

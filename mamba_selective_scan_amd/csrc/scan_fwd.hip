@@ -10,8 +10,9 @@
 // "なぜ「scan」か" and "1チャンク内の処理フロー").
 //
 // Mapping.  A is diagonal, so the dstate entries are independent recurrences
-// that only meet in the sum over C.  One wave (the whole workgroup) owns 8
-// channels of one batch row for one time segment.  In the scan, lane
+// that only meet in the sum over C.  One wave owns 8 channels of one batch
+// row for one time segment (a workgroup is that one wave, or four
+// independent ones for d-fast data: kWavesPerWg).  In the scan, lane
 // (g, c) = (lane / 8, lane % 8) runs states 2g and 2g+1 of channel c
 // sequentially in time, in registers; A_log becomes exp2 multipliers with
 // log2(e) folded in, once per lane.  Small waves keep several per SIMD: the
@@ -138,8 +139,17 @@ __device__ inline f4 lds_f4(const float* p) { return *reinterpret_cast<const f4*
 template <typename IO, bool VEC, bool XT, bool BT>
 constexpr int kWavesPerSimd = (VEC && (XT || BT || sizeof(IO) == 2)) ? 5 : 4;
 
+// Waves per workgroup.  The waves of a workgroup stay independent (each owns
+// its own tile and LDS slice; there is no barrier); grouping only places
+// tiles on one CU.  With d-fast data a tile's row of 8 channels is 32 bytes,
+// a quarter of a 128-byte line: the four tiles that share each line then
+// run side by side on one CU and meet in its L1 instead of fetching the line
+// four times from L2.
+template <bool XT>
+constexpr int kWavesPerWg = XT ? 1 : 4;
+
 template <typename IO, bool XT, bool BT, bool AGG, bool VEC, bool REV>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+__global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_waves_per_eu(
     kWavesPerSimd<IO, VEC, XT, BT>, 8))) void scan_kernel(
     ScanShape s, const IO* __restrict__ u, const IO* __restrict__ delta_raw,
     const float* __restrict__ A_log, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
@@ -147,22 +157,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const float* __restrict__ dt_bias, const float* __restrict__ h0, IO* __restrict__ out,
     float* __restrict__ final_state, float2* __restrict__ agg,
     const float* __restrict__ carry, float* __restrict__ chunk_states) {
-  __shared__ __attribute__((aligned(16))) float s_bc[(AGG ? kMaxState : kBcRows) * kT];
-  __shared__ __attribute__((aligned(16))) float s_dd[kCh * kDdPitch];
-  __shared__ __attribute__((aligned(16))) float s_skip[AGG ? 4 : kCh * kSkipPitch];
-  __shared__ __attribute__((aligned(16))) float s_chan[2 * kCh];  // dt_bias, D of the tile (d-fast)
+  constexpr int kWg = kWavesPerWg<XT>;
+  constexpr int kBcSize = (AGG ? kMaxState : kBcRows) * kT;
+  constexpr int kDdSize = kCh * kDdPitch;
+  constexpr int kSkipSize = AGG ? 4 : kCh * kSkipPitch;
+  __shared__ __attribute__((aligned(16))) float s_bc_all[kWg * kBcSize];
+  __shared__ __attribute__((aligned(16))) float s_dd_all[kWg * kDdSize];
+  __shared__ __attribute__((aligned(16))) float s_skip_all[kWg * kSkipSize];
+  __shared__ __attribute__((aligned(16))) float s_chan_all[kWg * 2 * kCh];  // dt_bias, D (d-fast)
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = kWg == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* const s_bc = s_bc_all + wave * kBcSize;
+  float* const s_dd = s_dd_all + wave * kDdSize;
+  float* const s_skip = s_skip_all + wave * kSkipSize;
+  float* const s_chan = s_chan_all + wave * 2 * kCh;
   // Workgroups are dispatched round-robin over the XCDs (linear id mod 8).
   // Renumber them so that each XCD receives a contiguous range of tiles:
   // tiles of one batch row share B and C, which then stay in that XCD's L2.
-  const int nwg = gridDim.x * gridDim.y;
-  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  // Tile i of the pass is channel group i % G, time segment i / G.
+  const int nwg = gridDim.x;
+  const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
   const int per_xcd = nwg / kXcds, extra = nwg % kXcds;
   const int logical = xcd * per_xcd + min(xcd, extra) + lin / kXcds;
-  const int g = logical % gridDim.x;
-  const int seg = logical / gridDim.x;
+  const int G = s.batch * s.groups;
+  const int tile = logical * kWg + wave;
+  if (tile >= G * (AGG ? s.nseg - 1 : s.nseg)) return;  // the last workgroup's spare waves
+  const int g = tile % G;
+  const int seg = tile / G;
   const int b = g / s.groups;
   const int d0 = (g - b * s.groups) * kCh;
   const int t_begin = s.t_first + seg * s.seg_len;
@@ -611,8 +634,10 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanShape s, const float2* _
 template <typename IO, bool XT, bool BT, bool VEC, bool REV>
 static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, float* final_state,
                         hipStream_t stream) {
-  const dim3 block(kThreads);
+  constexpr int kWg = kWavesPerWg<XT>;
+  const dim3 block(kThreads * kWg);
   const unsigned G = static_cast<unsigned>(s.batch) * static_cast<unsigned>(s.groups);
+  auto wgs = [&](int nseg) { return dim3((G * static_cast<unsigned>(nseg) + kWg - 1) / kWg); };
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dr = static_cast<const IO*>(p.delta_raw);
   const IO* Bm = static_cast<const IO*>(p.B);
@@ -620,14 +645,14 @@ static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, 
   const IO* z = static_cast<const IO*>(p.z);
   IO* out = static_cast<IO*>(p.out);
   if (s.nseg > 1) {
-    scan_kernel<IO, XT, BT, true, VEC, REV><<<dim3(G, s.nseg - 1), block, 0, stream>>>(
+    scan_kernel<IO, XT, BT, true, VEC, REV><<<wgs(s.nseg - 1), block, 0, stream>>>(
         s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
         nullptr);
     const int64_t n = s.nchan_pad * kMaxState;
     carry_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
         s, p.agg, h0, p.carry);
   }
-  scan_kernel<IO, XT, BT, false, VEC, REV><<<dim3(G, s.nseg), block, 0, stream>>>(
+  scan_kernel<IO, XT, BT, false, VEC, REV><<<wgs(s.nseg), block, 0, stream>>>(
       s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
       p.chunk_states);
 }
