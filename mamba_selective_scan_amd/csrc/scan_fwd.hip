@@ -420,16 +420,31 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         if constexpr (!AGG) s_skip[(4 * xb + j) * kSkipPitch + xa] = sk[j];
       }
     }
+    if constexpr (BT) {
 #pragma unroll
-    for (int i = 0; i < kBcLoads; ++i) {
-      const int row0 = (i >= 2 ? kMaxState : 0);
-      if constexpr (BT) {
+      for (int i = 0; i < kBcLoads; ++i) {
+        const int row0 = (i >= 2 ? kMaxState : 0);
         *reinterpret_cast<f4*>(s_bc + bc_index(row0 + bc_n(i, 0), bc_tt(i, 0))) =
             f4{bcb[i * kVec], bcb[i * kVec + 1], bcb[i * kVec + 2], bcb[i * kVec + 3]};
-      } else {
+      }
+    } else {
+      // n-fast: value (i, j) is state 4bb+j (+16 rows for C) at step ba+16(i%2).
+      // Its swizzled position follows from two computed ones: rows 4bb+1 and
+      // 4bb+3 share the key of rows 4bb and 4bb+2 (one row further on), step
+      // ba+16 flips bit 2 of the 4-step group (index ^ 16), and C rows keep
+      // the key of the B rows 16 rows before.  Four address registers instead
+      // of one per value.
+      const int e0 = bc_index(bc_n(0, 0), bc_tt(0, 0));
+      const int e2 = bc_index(bc_n(0, 2), bc_tt(0, 0));
 #pragma unroll
-        for (int j = 0; j < kVec; ++j)
-          s_bc[bc_index(row0 + bc_n(i, j), bc_tt(i, j))] = bcb[i * kVec + j];
+      for (int i = 0; i < kBcLoads; ++i) {
+        const int c_rows = i >= 2 ? kMaxState * kT : 0;
+        const int f0 = ((i & 1) ? e0 ^ 16 : e0) + c_rows;
+        const int f2 = ((i & 1) ? e2 ^ 16 : e2) + c_rows;
+        s_bc[f0] = bcb[i * kVec];
+        s_bc[f0 + kT] = bcb[i * kVec + 1];
+        s_bc[f2] = bcb[i * kVec + 2];
+        s_bc[f2 + kT] = bcb[i * kVec + 3];
       }
     }
   };
