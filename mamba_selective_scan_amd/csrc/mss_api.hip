@@ -19,9 +19,11 @@ using mss::kT;
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxSeqlen = int64_t{1} << 30;  // time indices, padded, stay in int32
-// Time segments: a shape whose channel tiles alone give fewer workgroups than
-// this is split along time until it reaches it (the plan depends only on the
-// shape, so results do not depend on the device).
+// Time segments: a shape whose channel tiles alone give fewer than
+// kSplitBelowTiles waves is split along time into as many segments as keep
+// the waves at or below kTargetTiles, four per SIMD: rounding up instead
+// would leave a few SIMDs with a fifth wave and the rest waiting on them.
+// The plan depends only on the shape, so results do not depend on the device.
 constexpr int64_t kSplitBelowTiles = 2048;
 constexpr int64_t kTargetTiles = 4096;
 
@@ -127,7 +129,7 @@ ScanPlan make_plan(const mss_scan_args* a) {
   const int64_t tiles = a->batch * s.groups;
   const int64_t chunks = (a->seqlen + kT - 1) / kT;
   int64_t nseg = 1;
-  if (tiles < kSplitBelowTiles) nseg = std::min<int64_t>((kTargetTiles + tiles - 1) / tiles, chunks);
+  if (tiles < kSplitBelowTiles) nseg = std::max<int64_t>(1, std::min<int64_t>(kTargetTiles / tiles, chunks));
   nseg = std::min<int64_t>(nseg, 65535);
   const int64_t seg_chunks = (chunks + nseg - 1) / nseg;
   s.seg_len = static_cast<int>(seg_chunks * kT);
