@@ -11,8 +11,8 @@
 //
 // Mapping.  A is diagonal, so the dstate entries are independent recurrences
 // that only meet in the sum over C.  One wave owns 8 channels of one batch
-// row for one time segment (a workgroup is that one wave, or four
-// independent ones for d-fast data: kWavesPerWg).  In the scan, lane
+// row for one time segment (a workgroup is that one wave, or the four waves
+// of a 32-channel block for d-fast data: kWavesPerWg).  In the scan, lane
 // (g, c) = (lane / 8, lane % 8) runs states 2g and 2g+1 of channel c
 // sequentially in time, in registers; A_log becomes exp2 multipliers with
 // log2(e) folded in, once per lane.  Small waves keep several per SIMD: the
@@ -29,8 +29,10 @@
 //      DPP row rotation; two swap-and-add levels reduce four steps at once;
 //   O  the totals go through LDS back to the load layout, where the skip term
 //      and the gate are applied and the output is stored.
-// Every phase is wave-local: there is no workgroup barrier, so waves drift
-// apart and memory waits of one wave overlap the recurrence of others.
+// For t-fast data every phase is wave-local: there is no workgroup barrier,
+// so waves drift apart and memory waits of one wave overlap the recurrence
+// of others.  The d-fast vector path exchanges its loads and stores between
+// the four waves of a workgroup through LDS, with two barriers per chunk.
 //
 // Reverse time (REV): logical step tau reads and writes storage step L-1-tau,
 // so a backward-direction scan (one half of a bidirectional layer) runs on
@@ -139,12 +141,11 @@ __device__ inline f4 lds_f4(const float* p) { return *reinterpret_cast<const f4*
 template <typename IO, bool VEC, bool XT, bool BT>
 constexpr int kWavesPerSimd = (VEC && (XT || BT || sizeof(IO) == 2)) ? 5 : 4;
 
-// Waves per workgroup.  The waves of a workgroup stay independent (each owns
-// its own tile and LDS slice; there is no barrier); grouping only places
-// tiles on one CU.  With d-fast data a tile's row of 8 channels is 32 bytes,
-// a quarter of a 128-byte line: the four tiles that share each line then
-// run side by side on one CU and meet in its L1 instead of fetching the line
-// four times from L2.
+// Waves per workgroup.  For t-fast data a workgroup is one wave.  For d-fast
+// data a tile's row of 8 channels is 32 bytes, a quarter of a 128-byte line,
+// so a workgroup holds the four tiles of a 32-channel block: on the vector
+// path they load and store whole rows together (COOP in the kernel); on the
+// element-wise path they stay independent and only share the CU's L1.
 template <bool XT>
 constexpr int kWavesPerWg = XT ? 1 : 4;
 
@@ -158,36 +159,65 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     float* __restrict__ final_state, float2* __restrict__ agg,
     const float* __restrict__ carry, float* __restrict__ chunk_states) {
   constexpr int kWg = kWavesPerWg<XT>;
+  // COOP (the d-fast vector path): the waves of a workgroup own the four
+  // 8-channel tiles of one 32-channel block (same batch row and segment) and
+  // move its data together.  Each wave loads and stores 8 whole 128-byte rows
+  // (8 steps x 32 channels) per tensor and chunk, and every value goes to the
+  // LDS slice of the wave that scans it; B and C are loaded once per
+  // workgroup.  The exchange takes two workgroup barriers per chunk, and the
+  // LDS buffers alternate with the chunk's parity.
+  constexpr bool COOP = !XT && VEC;
+  constexpr int kBufs = COOP ? 2 : 1;
   constexpr int kBcSize = (AGG ? kMaxState : kBcRows) * kT;
   constexpr int kDdSize = kCh * kDdPitch;
-  constexpr int kSkipSize = AGG ? 4 : kCh * kSkipPitch;
-  __shared__ __attribute__((aligned(16))) float s_bc_all[kWg * kBcSize];
-  __shared__ __attribute__((aligned(16))) float s_dd_all[kWg * kDdSize];
-  __shared__ __attribute__((aligned(16))) float s_skip_all[kWg * kSkipSize];
+  constexpr int kSkipSize = (AGG || COOP) ? 4 : kCh * kSkipPitch;  // COOP keeps D*u in registers
+  constexpr int kChanSpan = COOP ? kWg * kCh : kCh;  // channels whose dt_bias, D sit in s_chan
+  __shared__ __attribute__((aligned(16))) float s_bc_all[(COOP ? kBufs : kWg) * kBcSize];
+  __shared__ __attribute__((aligned(16))) float s_dd_all[kBufs * kWg * kDdSize];
+  __shared__ __attribute__((aligned(16))) float s_skip_all[kBufs * kWg * kSkipSize];
   __shared__ __attribute__((aligned(16))) float s_chan_all[kWg * 2 * kCh];  // dt_bias, D (d-fast)
 
   const int lane = threadIdx.x & 63;
   const int wave = kWg == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  float* const s_bc = s_bc_all + wave * kBcSize;
+  // this wave's slices (buffer 0; COOP buffer nb adds nb * kBcSize, nb * kWg * kDdSize, ...)
+  float* const s_bc = s_bc_all + (COOP ? 0 : wave * kBcSize);
   float* const s_dd = s_dd_all + wave * kDdSize;
   float* const s_skip = s_skip_all + wave * kSkipSize;
-  float* const s_chan = s_chan_all + wave * 2 * kCh;
+  float* const s_chan = s_chan_all + (COOP ? 0 : wave * 2 * kCh);
   // Workgroups are dispatched round-robin over the XCDs (linear id mod 8).
   // Renumber them so that each XCD receives a contiguous range of tiles:
   // tiles of one batch row share B and C, which then stay in that XCD's L2.
-  // Tile i of the pass is channel group i % G, time segment i / G.
+  // Tile i of the pass is channel group i % G, time segment i / G (COOP:
+  // workgroup i is 32-channel block i % GQ, segment i / GQ).
   const int nwg = gridDim.x;
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds;
   const int per_xcd = nwg / kXcds, extra = nwg % kXcds;
   const int logical = xcd * per_xcd + min(xcd, extra) + lin / kXcds;
-  const int G = s.batch * s.groups;
-  const int tile = logical * kWg + wave;
-  if (tile >= G * (AGG ? s.nseg - 1 : s.nseg)) return;  // the last workgroup's spare waves
-  const int g = tile % G;
-  const int seg = tile / G;
-  const int b = g / s.groups;
-  const int d0 = (g - b * s.groups) * kCh;
+  const int pass_segs = AGG ? s.nseg - 1 : s.nseg;
+  int b, d0, seg, dx0;  // dx0: first channel of the x data the lane loads and stores
+  bool tile_ok = true;  // COOP: the wave's tile lies inside the channel groups
+  if constexpr (COOP) {
+    const int quads = (s.groups + kWg - 1) / kWg;
+    const int GQ = s.batch * quads;
+    if (logical >= GQ * pass_segs) return;  // uniform over the workgroup
+    const int gq = logical % GQ;
+    seg = logical / GQ;
+    b = gq / quads;
+    const int group = (gq - b * quads) * kWg + wave;
+    tile_ok = group < s.groups;
+    d0 = group * kCh;
+    dx0 = (gq - b * quads) * kWg * kCh;
+  } else {
+    const int G = s.batch * s.groups;
+    const int tile = logical * kWg + wave;
+    if (tile >= G * pass_segs) return;  // the last workgroup's spare waves
+    const int g = tile % G;
+    seg = tile / G;
+    b = g / s.groups;
+    d0 = (g - b * s.groups) * kCh;
+    dx0 = d0;
+  }
   const int t_begin = s.t_first + seg * s.seg_len;
   const int t_end = min(s.t_stop, t_begin + s.seg_len);
   constexpr int64_t es = sizeof(IO);
@@ -229,8 +259,10 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   // 4(lane % 2)..+3.  A chunk whose vectors would straddle a tensor edge (a
   // ragged tail) takes the element-wise instantiation instead.
   using VIO = vec_io<IO>;
-  const int xa = XT ? lane >> 3 : lane >> 1;
-  const int xb = XT ? lane & 7 : lane & 1;
+  // COOP: lane (lane / 8, lane % 8) of wave w covers step 8w + lane / 8,
+  // channels 4(lane % 8)..+3 of the 32-channel block.
+  const int xa = XT ? lane >> 3 : (COOP ? kCh * wave + (lane >> 3) : lane >> 1);
+  const int xb = XT ? lane & 7 : (COOP ? lane & 7 : lane & 1);
   auto x_c = [&](int j) __attribute__((always_inline)) { return XT ? xa : 4 * xb + j; };
   auto x_t = [&](int j) __attribute__((always_inline)) { return XT ? 4 * xb + j : xa; };
   // Time offset of a lane's first x element inside a chunk (mirrored in
@@ -288,6 +320,13 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     const int dc = d0 + xa;
     bias_t = (dc < s.dim && dt_bias != nullptr) ? dt_bias[dc] : 0.0f;
     skip_t = (dc < s.dim && Dskip != nullptr) ? Dskip[dc] : 0.0f;
+  } else if constexpr (COOP) {
+    if (wave == 0) {
+      const int dc = dx0 + (lane & (kChanSpan - 1));
+      const float* src = lane < kChanSpan ? dt_bias : Dskip;
+      s_chan[lane] = (dc < s.dim && src != nullptr) ? src[dc] : 0.0f;
+    }
+    __syncthreads();
   } else if (lane < 2 * kCh) {
     const int dc = d0 + (lane & (kCh - 1));
     const float* src = lane < kCh ? dt_bias : Dskip;
@@ -308,7 +347,7 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   // x_ok / b_ok: element j / B-C value (i, j) lies inside the tensors and the
   // chunk is one this loop loads (lim: first chunk start not loaded).
   auto x_ok = [&](int j, int t0, int lim) __attribute__((always_inline)) {
-    return (t0 < lim) && (d0 + x_c(j) < s.dim) && (t0 + x_t(j) < t_end);
+    return (t0 < lim) && (dx0 + x_c(j) < s.dim) && (t0 + x_t(j) < t_end);
   };
   auto b_ok = [&](int i, int j, int t0, int lim) __attribute__((always_inline)) {
     return (t0 < lim) && (bc_n(i, j) < s.dstate) && (t0 + bc_tt(i, j) < t_end);
@@ -323,13 +362,14 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   struct ZBuf {
     float z[kPerThread];
   };
-  float bcb[4 * kVec];  // B/C of the next chunk
+  constexpr int kBcLoads = COOP ? 1 : (AGG ? 2 : 4);  // the AGG pass needs no C
+  float bcb[kBcLoads * kVec];  // B/C of the next chunk
 
   // Loads of one x-tensor.  VEC: one vector (wholly in or out of the valid
   // region); else element by element.
   auto load_x = [&](float (&dst)[kPerThread], const IO* ptr, const int64_t* st, int t0, int lim,
                     int range = kRsrcRange) __attribute__((always_inline)) {
-    const auto rs = rsrc(ptr, st, d0, t0, range);
+    const auto rs = rsrc(ptr, st, dx0, t0, range);
     const uint32_t vo = x_voff(st);
     if constexpr (VEC) {
       VIO::load(rs, x_ok(0, t0, lim) ? vo : kOffNone, 0, dst);
@@ -354,8 +394,22 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     load_x(ib.u, u, s.su, t0, lim);
     load_x(ib.d, delta_raw, s.sd, t0, lim);
   };
-  constexpr int kBcLoads = AGG ? 2 : 4;  // the AGG pass needs no C
+  // COOP B/C: waves 0, 1 load B and waves 2, 3 load C, one vector per lane:
+  // t-fast, state 8(w % 2) + lane / 8 at steps 4(lane % 8)..+3; n-fast, step
+  // 16(w % 2) + lane / 4 at states 4(lane % 4)..+3.
+  const bool cb_c = COOP && wave >= 2;
+  const int cb_n = BT ? kCh * (wave & 1) + (lane >> 3) : 4 * (lane & 3);
+  const int cb_t = BT ? 4 * (lane & 7) : 16 * (wave & 1) + (lane >> 2);
   auto issue_bc_loads = [&](int t0, int lim) __attribute__((always_inline)) {
+    if constexpr (COOP) {
+      const int64_t* st = cb_c ? s.sC : s.sB;
+      const auto rs = rsrc(cb_c ? Cm : Bm, st, 0, t0);
+      const int ts = REV ? (BT ? kT - kVec - cb_t : kT - 1 - cb_t) : cb_t;
+      const bool ok = (t0 < lim) && !(AGG && cb_c) && cb_n < s.dstate && t0 + cb_t < t_end;
+      VIO::load(rs, ok ? static_cast<uint32_t>((cb_n * st[1] + ts * st[2]) * es) : kOffNone, 0, bcb);
+      if constexpr (BT) mirror4(bcb);
+      return;
+    }
     const auto rb = rsrc(Bm, s.sB, 0, t0);
     const auto rcm = rsrc(Cm, s.sC, 0, t0);
 #pragma unroll
@@ -380,7 +434,21 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
 
   // E: (delta, delta*u) and D*u of the chunk go to LDS (s_dd, s_skip), B/C
   // from registers to s_bc.
-  auto phase_e = [&](const InBuf& ib, int t0) __attribute__((always_inline)) {
+  // d-fast (delta, delta*u) and D*u slots of the lane's element j in LDS
+  // buffer nb: COOP sends channel 4xb+j of the block to wave (4xb+j) / 8.
+  auto e_dd = [&](int nb, int j) __attribute__((always_inline)) -> float* {
+    if constexpr (COOP)
+      return s_dd_all + nb * kWg * kDdSize + (xb >> 1) * kDdSize +
+             (4 * (xb & 1) + j) * kDdPitch + 2 * xa;
+    return s_dd + (4 * xb + j) * kDdPitch + 2 * xa;
+  };
+  auto e_sk = [&](int nb, int j) __attribute__((always_inline)) -> float* {
+    return s_skip + nb * kSkipSize + (4 * xb + j) * kSkipPitch + xa;  // not COOP: nb = 0
+  };
+  // COOP: a lane's E and O phases cover the same elements, so D*u of the
+  // next chunk waits in registers (skr) instead of LDS.
+  float skr[kPerThread];
+  auto phase_e = [&](const InBuf& ib, int t0, int nb) __attribute__((always_inline)) {
     float dl[kPerThread], du[kPerThread], sk[kPerThread], bias[kPerThread], skip[kPerThread];
     if constexpr (XT) {
 #pragma unroll
@@ -389,7 +457,7 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         skip[j] = skip_t;
       }
     } else {
-      const f4 bv = lds_f4(s_chan + 4 * xb), sv = lds_f4(s_chan + kCh + 4 * xb);
+      const f4 bv = lds_f4(s_chan + 4 * xb), sv = lds_f4(s_chan + kChanSpan + 4 * xb);
       bias[0] = bv.x; bias[1] = bv.y; bias[2] = bv.z; bias[3] = bv.w;
       skip[0] = sv.x; skip[1] = sv.y; skip[2] = sv.z; skip[3] = sv.w;
     }
@@ -415,12 +483,32 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     } else {
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
-        *reinterpret_cast<float2*>(s_dd + (4 * xb + j) * kDdPitch + 2 * xa) =
-            make_float2(dl[j], du[j]);
-        if constexpr (!AGG) s_skip[(4 * xb + j) * kSkipPitch + xa] = sk[j];
+        *reinterpret_cast<float2*>(e_dd(nb, j)) = make_float2(dl[j], du[j]);
+        if constexpr (COOP)
+          skr[j] = sk[j];
+        else if constexpr (!AGG)
+          *e_sk(nb, j) = sk[j];
       }
     }
-    if constexpr (BT) {
+    if constexpr (COOP) {
+      // one vector per lane into the workgroup's shared B/C buffer (n-fast:
+      // the two-index form of the non-cooperative path below)
+      float* const sbc = s_bc_all + nb * kBcSize;
+      const int c_rows = cb_c ? kMaxState * kT : 0;
+      if (!(AGG && cb_c)) {
+        if constexpr (BT) {
+          *reinterpret_cast<f4*>(sbc + c_rows + bc_index(cb_n, cb_t)) =
+              f4{bcb[0], bcb[1], bcb[2], bcb[3]};
+        } else {
+          const int f0 = bc_index(cb_n, cb_t) + c_rows;
+          const int f2 = bc_index(cb_n + 2, cb_t) + c_rows;
+          sbc[f0] = bcb[0];
+          sbc[f0 + kT] = bcb[1];
+          sbc[f2] = bcb[2];
+          sbc[f2 + kT] = bcb[3];
+        }
+      }
+    } else if constexpr (BT) {
 #pragma unroll
       for (int i = 0; i < kBcLoads; ++i) {
         const int row0 = (i >= 2 ? kMaxState : 0);
@@ -475,13 +563,15 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
 
   // One block of 4 steps: the scan of this lane's two states and, outside
   // the AGG pass, one state-group reduction of C.h.
-  auto scan_block = [&](int t4, int t0) __attribute__((always_inline)) {
+  auto scan_block = [&](int t4, int t0, int nb) __attribute__((always_inline)) {
     record_state(t0 + t4);
     const int col = (((t4 >> 2) ^ sg) & 7) << 2;
-    const f4 b0 = lds_f4(p_b0 + col);
-    const f4 b1 = lds_f4(p_b0 + kT + col);
-    const f4 dd01 = lds_f4(p_dd + 2 * t4);
-    const f4 dd23 = lds_f4(p_dd + 2 * t4 + 4);
+    const float* pb = p_b0 + nb * kBcSize;
+    const float* pd = p_dd + nb * kWg * kDdSize;
+    const f4 b0 = lds_f4(pb + col);
+    const f4 b1 = lds_f4(pb + kT + col);
+    const f4 dd01 = lds_f4(pd + 2 * t4);
+    const f4 dd23 = lds_f4(pd + 2 * t4 + 4);
     const float dls[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
     const float dus[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
     const float bs0[4] = {b0.x, b0.y, b0.z, b0.w};
@@ -494,8 +584,9 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
       }
       sum_delta += (dls[0] + dls[1]) + (dls[2] + dls[3]);
     } else {
-      const f4 c0 = lds_f4(p_c0 + col);
-      const f4 c1 = lds_f4(p_c0 + kT + col);
+      const float* pc = p_c0 + nb * kBcSize;
+      const f4 c0 = lds_f4(pc + col);
+      const f4 c1 = lds_f4(pc + kT + col);
       const float cs0[4] = {c0.x, c0.y, c0.z, c0.w};
       const float cs1[4] = {c1.x, c1.y, c1.z, c1.w};
       float y[4];
@@ -505,23 +596,23 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
         y[k] = fmaf(cs1[k], h[1], cs0[k] * h[0]);
       }
-      p_y[2 * t4] = reduce_groups(y[0], y[1], y[2], y[3]);
+      p_y[nb * kWg * kDdSize + 2 * t4] = reduce_groups(y[0], y[1], y[2], y[3]);
     }
   };
   // The main pass unrolls the blocks: the swizzled B/C offsets become
   // loop-invariant registers and the other LDS offsets immediates.  The AGG
   // pass keeps a loop (unrolled, its LDS reads would all be hoisted).
-  auto phase_s = [&](int t0) __attribute__((always_inline)) {
+  auto phase_s = [&](int t0, int nb) __attribute__((always_inline)) {
     if constexpr (AGG) {
 #pragma unroll 1
-      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0);
+      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0, nb);
     } else {
 #pragma unroll
-      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0);
+      for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0, nb);
     }
   };
 
-  auto phase_o = [&](const ZBuf& zb, int t0) __attribute__((always_inline)) {
+  auto phase_o = [&](const ZBuf& zb, int t0, int nb) __attribute__((always_inline)) {
     if constexpr (!AGG) {
       float y[kPerThread];
       if constexpr (XT) {
@@ -534,14 +625,13 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         y[3] = v1.z + sk.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j)
-          y[j] = s_dd[(4 * xb + j) * kDdPitch + 2 * xa] + s_skip[(4 * xb + j) * kSkipPitch + xa];
+        for (int j = 0; j < kPerThread; ++j) y[j] = *e_dd(nb, j) + (COOP ? skr[j] : *e_sk(nb, j));
       }
       if (has_z) {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) y[j] *= silu(zb.z[j]);
       }
-      const auto rs = rsrc(out, s.so, d0, t0);
+      const auto rs = rsrc(out, s.so, dx0, t0);
       const uint32_t vo_o = x_voff(s.so);
       if constexpr (VEC) {
         if constexpr (XT) mirror4(y);
@@ -571,22 +661,41 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   issue_bc_loads(t_begin, t_end);
   issue_x_loads(in, t_begin, t_end);
   issue_z_loads(zb, t_begin, t_end);
-  phase_e(in, t_begin);
+  phase_e(in, t_begin, 0);
   // Priorities: the SIMD issues from the oldest wave among those of the
   // highest priority.  A wave scans at priority 0 and raises itself to 2 for
   // the output and input phases, so a wave whose scan is done gets to its
   // memory waits and load issue at once instead of queueing behind the scans
   // of older waves: loads leave earlier and have longer to arrive.
-  for (int c = 0; c < nchunks; ++c) {
+  // COOP: chunk c uses LDS buffer nb = c % 2.  The first barrier publishes
+  // every wave's E(c) before any wave scans c; the second publishes every
+  // wave's totals of c before any wave reads them in O(c).  E(c+1) writes
+  // the other buffer, whose last readers (S(c-1), O(c-1)) all finished
+  // before the first barrier of c.
+  auto chunk = [&](int c, int nb) __attribute__((always_inline)) {
     const int t0 = t_begin + c * kT;
     issue_bc_loads(t0 + kT, t_end);
     issue_x_loads(in, t0 + kT, t_end);
+    if constexpr (COOP) __syncthreads();
     __builtin_amdgcn_s_setprio(0);
-    phase_s(t0);
+    phase_s(t0, nb);
     __builtin_amdgcn_s_setprio(2);
-    phase_o(zb, t0);
+    if constexpr (COOP) __syncthreads();
+    phase_o(zb, t0, nb);
     issue_z_loads(zb, t0 + kT, t_end);
-    phase_e(in, t0 + kT);
+    phase_e(in, t0 + kT, COOP ? nb ^ 1 : 0);
+  };
+  if constexpr (COOP) {
+    // Two chunks per iteration, so that the buffer index is a constant in
+    // the LDS offsets.  An odd count runs one chunk past the segment: its
+    // loads are out of range (zeros), delta is 0 so the state passes through
+    // unchanged, and its stores and chunk states are masked by t_end.
+    for (int c = 0; c < nchunks; c += 2) {
+      chunk(c, 0);
+      chunk(c + 1, 1);
+    }
+  } else {
+    for (int c = 0; c < nchunks; ++c) chunk(c, 0);
   }
 
   // ---- segment end ----
@@ -595,8 +704,9 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     for (int k = 0; k < kStatesPerLane; ++k) {
       const int n = sg * kStatesPerLane + k;
       const float prod_a = fast_exp2(A2[k] * sum_delta);
-      agg[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + n] =
-          make_float2(prod_a, h[k]);
+      if (tile_ok)
+        agg[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + n] =
+            make_float2(prod_a, h[k]);
     }
   } else {
     if (final_state != nullptr && seg == s.nseg - 1) {
@@ -652,7 +762,13 @@ static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, 
   constexpr int kWg = kWavesPerWg<XT>;
   const dim3 block(kThreads * kWg);
   const unsigned G = static_cast<unsigned>(s.batch) * static_cast<unsigned>(s.groups);
-  auto wgs = [&](int nseg) { return dim3((G * static_cast<unsigned>(nseg) + kWg - 1) / kWg); };
+  // COOP (d-fast vector path): one workgroup per 32-channel block and segment
+  auto wgs = [&](int nseg) {
+    if constexpr (!XT && VEC)
+      return dim3(static_cast<unsigned>(s.batch) *
+                  static_cast<unsigned>((s.groups + kWg - 1) / kWg) * static_cast<unsigned>(nseg));
+    return dim3((G * static_cast<unsigned>(nseg) + kWg - 1) / kWg);
+  };
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dr = static_cast<const IO*>(p.delta_raw);
   const IO* Bm = static_cast<const IO*>(p.B);
