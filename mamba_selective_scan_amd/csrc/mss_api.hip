@@ -351,15 +351,20 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   // even.
   s.vec_ok = 1;
   if (es == 2) {
-    auto even = [](int64_t v) { return (v % 2) == 0; };
+    // (a dimension of size 1 is never stepped: its stride does not count)
+    auto even = [](int64_t v, int64_t size) { return size == 1 || (v % 2) == 0; };
     const int64_t* xsts[4] = {s.su, s.sd, s.sz, s.so};
     const void* xps[4] = {a->u, a->delta_raw, a->z != nullptr ? a->z : a->u, a->out};
     for (int i = 0; i < 4; ++i)
-      if (!aligned(xps[i], 4) || !even(xsts[i][0]) || !even(xsts[i][xt ? 1 : 2])) s.vec_ok = 0;
+      if (!aligned(xps[i], 4) || !even(xsts[i][0], a->batch) ||
+          !(xt ? even(xsts[i][1], a->dim) : even(xsts[i][2], a->seqlen)))
+        s.vec_ok = 0;
     const int64_t* bsts[2] = {s.sB, s.sC};
     const void* bps[2] = {a->B, a->C};
     for (int i = 0; i < 2; ++i)
-      if (!aligned(bps[i], 4) || !even(bsts[i][0]) || !even(bsts[i][bt ? 1 : 2])) s.vec_ok = 0;
+      if (!aligned(bps[i], 4) || !even(bsts[i][0], a->batch) ||
+          !(bt ? even(bsts[i][1], a->dstate) : even(bsts[i][2], a->seqlen)))
+        s.vec_ok = 0;
     // in reverse time a t-fast vector starts at storage step seqlen-4-tau:
     // 4-byte aligned only for an even length
     if (a->reverse && (xt || bt) && (a->seqlen % 2) != 0) s.vec_ok = 0;

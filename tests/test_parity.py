@@ -100,6 +100,15 @@ def test_bf16_small(mss, seqlen):
     _full_case(mss, f"bf16 L={seqlen}", 2, 96, seqlen, 16, io="bf16")
 
 
+@pytest.mark.parametrize("layout,dim,seqlen", [("bdl", 1536, 2048), ("bld", 256, 3000),
+                                               ("bld", 200, 1001), ("bdl", 64, 4099)])
+def test_bf16_batch_one(mss, layout, dim, seqlen):
+    """bf16 at batch 1 (the size-1 batch stride is never stepped, so it does
+    not keep the vector paths out), channel-last with time segments and a
+    channel count that is not a whole 32-channel block, and a ragged tail."""
+    _full_case(mss, f"bf16 B=1 {layout}", 1, dim, seqlen, 16, layout=layout, io="bf16", h0=True)
+
+
 def test_time_split_with_initial_state(mss):
     """Few channels and a long sequence: the segmented path, started from h0."""
     _full_case(mss, "split+h0", 1, 64, 20000, 16, h0=True)
