@@ -227,7 +227,9 @@ __device__ inline int group_step(int lane) {
 // ---------------------------------------------------------------- pass 0 ---
 // Segment aggregates, walking each segment forward from zero: per state
 // P = prod a_t, H = the state reached, Z = sum_t (prod_(r<=t) a_r) dy_t C_t.
-template <typename IO>
+// WITH_H: also the forward aggregate H, which only the checkpoint pass
+// needs (forward chunk states given: no checkpoint pass, H is skipped).
+template <typename IO, bool WITH_H>
 __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
   __shared__ __attribute__((aligned(16))) float s_el[kCh * kElPitch];
@@ -258,29 +260,68 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
   const int q_begin = seg * s.seg_chunks;
   const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
-  for (int q = q_begin; q < q_end; ++q) {
+  constexpr int64_t es = sizeof(IO);
+  // Raw inputs go through buffer descriptors with loop-invariant offsets
+  // (out-of-range ones read 0), one chunk ahead of use: B and C, lane covers
+  // rows lane / 4 and 16 + lane / 4 at steps 4 (lane % 4) .. + 3; u,
+  // delta_raw, dout, z, lane (c, j) steps 2j, 2j+1 of channel c.
+  const int bn = lane >> 2, bt0 = (lane & 3) * 4;
+  uint32_t o_b[4], o_c[4], o_u[2], o_dr[2], o_do[2], o_z[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o_b[i] = chunk_off(s, s.sB, es, bn, bt0 + i);
+    o_c[i] = chunk_off(s, s.sC, es, bn, bt0 + i);
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    o_u[e] = chunk_off(s, s.su, es, sc, 2 * sg + e);
+    o_dr[e] = chunk_off(s, s.sd, es, sc, 2 * sg + e);
+    o_do[e] = chunk_off(s, s.sdo, es, sc, 2 * sg + e);
+    o_z[e] = chunk_off(s, s.sz, es, sc, 2 * sg + e);
+  }
+  float rb[4], rc[4], ru[2], rx[2], rgo[2], rz[2];
+  auto load_chunk = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
-    // B and C: lane covers rows lane / 4 and 16 + lane / 4, steps 4 (lane % 4) .. + 3
+    const bool qin = q < q_end;
+    const auto rs_b = chunk_rsrc(s, Bm, s.sB, es, b, 0, t0, true, Bm);
+    const auto rs_c = chunk_rsrc(s, Cm, s.sC, es, b, 0, t0, true, Cm);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int n = lane >> 2, tt = (lane & 3) * 4 + i, t = t0 + tt;
-      const bool ok = n < s.dstate && t < s.seqlen;
-      s_bc[n * kBcPitch + tt] = ok ? ld(Bm + b * s.sB[0] + n * s.sB[1] + tstore(s, t) * s.sB[2]) : 0.0f;
-      s_bc[(kMaxState + n) * kBcPitch + tt] =
-          ok ? ld(Cm + b * s.sC[0] + n * s.sC[1] + tstore(s, t) * s.sC[2]) : 0.0f;
+      const bool ok = qin && bn < s.dstate && t0 + bt0 + i < s.seqlen;
+      rb[i] = WITH_H ? buf_one<IO>::load(rs_b, ok ? o_b[i] : kOffNone, 0) : 0.0f;
+      rc[i] = buf_one<IO>::load(rs_c, ok ? o_c[i] : kOffNone, 0);
+    }
+    const auto rs_u = chunk_rsrc(s, u, s.su, es, b, dg, t0, true, u);
+    const auto rs_dr = chunk_rsrc(s, dr, s.sd, es, b, dg, t0, true, u);
+    const auto rs_do = chunk_rsrc(s, dout, s.sdo, es, b, dg, t0, true, u);
+    const auto rs_z = chunk_rsrc(s, zz, s.sz, es, b, dg, t0, has_z, u);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const bool ok = qin && dvalid && t0 + 2 * sg + e < s.seqlen;
+      ru[e] = buf_one<IO>::load(rs_u, ok ? o_u[e] : kOffNone, 0);
+      rx[e] = buf_one<IO>::load(rs_dr, ok ? o_dr[e] : kOffNone, 0);
+      rgo[e] = buf_one<IO>::load(rs_do, ok ? o_do[e] : kOffNone, 0);
+      rz[e] = buf_one<IO>::load(rs_z, ok ? o_z[e] : kOffNone, 0);
+    }
+  };
+  load_chunk(q_begin);
+  for (int q = q_begin; q < q_end; ++q) {
+    const int t0 = q * kBwdT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_bc[bn * kBcPitch + bt0 + i] = rb[i];
+      s_bc[(kMaxState + bn) * kBcPitch + bt0 + i] = rc[i];
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int tt = 2 * sg + e, t = t0 + tt;
-      const bool ok = dvalid && t < s.seqlen;
-      const float uu = ok ? ld(u + b * s.su[0] + d * s.su[1] + tstore(s, t) * s.su[2]) : 0.0f;
-      const float x = (ok ? ld(dr + b * s.sd[0] + d * s.sd[1] + tstore(s, t) * s.sd[2]) : 0.0f) + bias;
+      const int tt = 2 * sg + e;
+      const bool ok = dvalid && t0 + tt < s.seqlen;
+      const float x = rx[e] + bias;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
-      const float go = ok ? ld(dout + b * s.sdo[0] + d * s.sdo[1] + tstore(s, t) * s.sdo[2]) : 0.0f;
-      const float zv = (ok && has_z) ? ld(zz + b * s.sz[0] + d * s.sz[1] + tstore(s, t) * s.sz[2]) : 0.0f;
-      const float dy = has_z ? go * silu(zv) : go;
-      *reinterpret_cast<f4*>(s_el + sc * kElPitch + 4 * tt) = f4{dl, dl * uu, dy, 0.0f};
+      const float dy = has_z ? rgo[e] * silu(rz[e]) : rgo[e];
+      *reinterpret_cast<f4*>(s_el + sc * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
     }
+    load_chunk(q + 1);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t4 = 0; t4 < kBwdT; t4 += 4) {
@@ -296,7 +337,7 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const float a = fast_exp2(dd.x * A2[k]);
-          H[k] = fmaf(a, H[k], dd.y * bk[k]);
+          if constexpr (WITH_H) H[k] = fmaf(a, H[k], dd.y * bk[k]);
           P[k] *= a;
           Z[k] = fmaf(P[k], dd.z * ck[k], Z[k]);
         }
@@ -919,7 +960,10 @@ template <typename IO>
 hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream) {
   const int64_t waves = static_cast<int64_t>(s.batch) * s.nseg * s.tiles * kBwdWaves;
   if (s.nseg > 1) {
-    agg_kernel<IO><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+    if (s.states_given)
+      agg_kernel<IO, false><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+    else
+      agg_kernel<IO, true><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
     const int64_t nc = s.nchan_pad * kMaxState;
     carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   }
