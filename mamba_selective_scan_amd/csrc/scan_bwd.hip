@@ -915,6 +915,24 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 }
 
 // ---------------------------------------------------------------- pass 3 ---
+// sum_(r < n) f(r) added in order of r (the result is bitwise repeatable);
+// the terms are loaded kSumBatch at a time ahead of the adds, so the chain
+// waits for one memory latency per batch, not per term.
+constexpr int kSumBatch = 8;
+template <typename F>
+__device__ inline float ordered_sum(int n, F f) {
+  float sum = 0.0f;
+  for (int r0 = 0; r0 < n; r0 += kSumBatch) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) v[j] = f(min(r0 + j, n - 1));
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j)
+      if (r0 + j < n) sum += v[j];
+  }
+  return sum;
+}
+
 // dB / dC[b, n, t] = sum over the row's workgroups of their partials.
 template <typename IO>
 __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
@@ -928,9 +946,9 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
   const bool is_c = j >= s.dstate;
   const int n = is_c ? j - s.dstate : j;
   const int r = is_c ? kMaxState + n : n;
-  float sum = 0.0f;
-  for (int tile = 0; tile < s.tiles; ++tile)
-    sum += p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t];
+  const float sum = ordered_sum(s.tiles, [&](int tile) {
+    return p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t];
+  });
   if (is_c)
     io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + tstore(s, t) * s.sdC[2], sum);
   else
@@ -944,9 +962,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
   const int d = static_cast<int>(i / (kMaxState + 2));
   const int j = static_cast<int>(i % (kMaxState + 2));
   if (j < kMaxState && j >= s.dstate) return;
-  float sum = 0.0f;
-  for (int r = 0; r < s.nseg * s.batch; ++r)
-    sum += p.part_chan[(static_cast<int64_t>(r) * s.dim + d) * (kMaxState + 2) + j];
+  const float sum = ordered_sum(s.nseg * s.batch, [&](int r) {
+    return p.part_chan[(static_cast<int64_t>(r) * s.dim + d) * (kMaxState + 2) + j];
+  });
   if (j < kMaxState)
     p.dA_log[static_cast<int64_t>(d) * s.dstate + j] = sum;
   else if (j == kMaxState) {
