@@ -691,9 +691,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}); channel sharding across GPUs is described "
-              f"in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); channels shard across GPUs with no "
+              f"exchange, but that launcher is not built.", file=sys.stderr)
         return 2
     if args.op == "conv1d":
         return main_conv(args)
