@@ -13,14 +13,16 @@
 //
 // Mapping: a workgroup of 256 lanes covers 16 channels of one batch row, one
 // lane per (channel, state): a 16-lane DPP row holds one channel, and
-// Re(C . h) is a 4-step rotation sum inside the row.  Time is walked in
+// Re(C . h) is a DPP reduction inside the row, four time steps at a time
+// (row_sum16_x4).  Time is walked in
 // chunks of kCxT steps:
 //   E  B and C of the chunk (16 states x kCxT steps, shared by the 16
 //      channels) and, per element, (delta, delta u) into LDS;
 //   S  each lane walks the chunk: the complex decay from exp2, and from the
 //      hardware sin / cos of the fractional turns delta Im(A) / 2 pi (the
 //      fraction keeps v_sin / v_cos inside their input range); one complex
-//      multiply-add; the row sum of Re(C h) lands in LDS;
+//      multiply-add; the row sums of Re(C h), four steps per reduction,
+//      land in LDS;
 //   O  out = (y + D u) silu(z), one store per element.
 // The state never leaves the registers.  Lanes past dstate hold zeros.
 #include "mss_device.hpp"
@@ -30,6 +32,29 @@ namespace mss {
 namespace {
 
 constexpr float kInv2Pi = 0.15915494309189535f;
+
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Totals over a 16-lane DPP row of four values per lane, for four steps at
+// once: lanes 4q..4q+3 of the row (rl = lane within the row) receive the
+// total of v_q.  Level 1, row_ror:8 (lane l meets l ^ 8): the lower half
+// keeps (v0, v1) and sends (v2, v3), the upper half the reverse; level 2,
+// row_half_mirror (l meets l ^ 7): lanes with l % 8 < 4 keep the first of
+// their pair; levels 3 and 4: butterflies inside each quad.  Six selects
+// and five adds, against sixteen adds for four separate row sums.
+__device__ inline float row_sum16_x4(float v0, float v1, float v2, float v3, int rl) {
+  const bool up = (rl & 8) != 0;
+  const float w0 = (up ? v2 : v0) + dpp<0x128>(up ? v0 : v2);
+  const float w1 = (up ? v3 : v1) + dpp<0x128>(up ? v1 : v3);
+  const bool second = (rl & 4) != 0;
+  float x = (second ? w1 : w0) + dpp<0x141>(second ? w0 : w1);
+  x += dpp<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+  return x;
+}
 constexpr int kCxPer = kCxCh * kCxT / kCxThreads;  // elements per lane in E and O (2)
 
 __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, CplxPtrs p) {
@@ -99,21 +124,26 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
     }
     __syncthreads();
     // ---- S ----
-#pragma unroll 4
-    for (int tt = 0; tt < kCxT; ++tt) {
-      const float2 dd = s_dd[c][tt];
-      const float2 bb = s_B[n][tt];
-      const float2 cc = s_C[n][tt];
-      const float turns = __builtin_amdgcn_fractf(dd.x * ai);
-      const float m = fast_exp2(dd.x * ar2);
-      const float a_r = m * __builtin_amdgcn_cosf(turns);
-      const float a_i = m * __builtin_amdgcn_sinf(turns);
-      const float nr = fmaf(a_r, hr, fmaf(-a_i, hi, dd.y * bb.x));
-      const float ni = fmaf(a_r, hi, fmaf(a_i, hr, dd.y * bb.y));
-      hr = nr;
-      hi = ni;
-      const float y = row_sum16(fmaf(cc.x, hr, -cc.y * hi));
-      if (n == 0) s_y[c][tt] = y;
+#pragma unroll 2
+    for (int t4 = 0; t4 < kCxT; t4 += 4) {
+      float yv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 dd = s_dd[c][t4 + i];
+        const float2 bb = s_B[n][t4 + i];
+        const float2 cc = s_C[n][t4 + i];
+        const float turns = __builtin_amdgcn_fractf(dd.x * ai);
+        const float m = fast_exp2(dd.x * ar2);
+        const float a_r = m * __builtin_amdgcn_cosf(turns);
+        const float a_i = m * __builtin_amdgcn_sinf(turns);
+        const float nr = fmaf(a_r, hr, fmaf(-a_i, hi, dd.y * bb.x));
+        const float ni = fmaf(a_r, hi, fmaf(a_i, hr, dd.y * bb.y));
+        hr = nr;
+        hi = ni;
+        yv[i] = fmaf(cc.x, hr, -cc.y * hi);
+      }
+      const float y = row_sum16_x4(yv[0], yv[1], yv[2], yv[3], n);
+      if ((n & 3) == 0) s_y[c][t4 + (n >> 2)] = y;
     }
     __syncthreads();
     // ---- O ----
