@@ -29,7 +29,7 @@ gradients included), reported against the VALU issue roofline, and with
 and states), also against the VALU roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--io f32|bf16]
-                       [--op scan|conv1d|scan_bwd|scan_complex]
+                       [--op scan|conv1d|scan_bwd|scan_complex] [--reverse]
 """
 
 from __future__ import annotations
@@ -687,6 +687,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="time the forward alone")
+    ap.add_argument("--reverse", action="store_true",
+                    help="run the scan in reverse time (the second direction of a bidirectional layer)")
     ap.add_argument("--op", default="scan", choices=["scan", "conv1d", "scan_bwd", "scan_complex"])
     args = ap.parse_args(argv)
 
@@ -724,7 +726,7 @@ def main(argv=None):
     def scan():
         mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], D=dx["D"],
                                z=dx["z"], dt_bias=dx["dt_bias"], out=out, final_state=final,
-                               workspace=ws)
+                               workspace=ws, reverse=args.reverse)
 
     def decode():
         mss.selective_state_update(final, step_in["u"], step_in["delta_raw"], dx["A_log"],
@@ -792,7 +794,8 @@ def main(argv=None):
         "config": {
             "workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen,
             "dstate": w.dstate, "layout": w.layout, "io_dtype": args.io,
-            "step": "scan fwd + final-state export" + ("" if args.no_step else " + 1 state update"),
+            "step": ("reverse-time " if args.reverse else "") + "scan fwd + final-state export" +
+                    ("" if args.no_step else " + 1 state update"),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gtok_ch_per_s": round(w.elems / (ms_per_step * 1e-3) / 1e9, 4),
