@@ -585,6 +585,9 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
       ok = xst[i][2] == 1 && aligned(xp[i], 4 * es) && (a->batch == 1 || xst[i][0] % 4 == 0) &&
            (a->dim == 1 || xst[i][1] % 4 == 0);
     s.quads = ok ? 1 : 0;
+    s.bquads = (a->seqlen % 4 == 0 && a->B_stride[2] == 1 && aligned(a->B, 4 * es) &&
+                (a->batch == 1 || a->B_stride[0] % 4 == 0) &&
+                (a->dstate == 1 || a->B_stride[1] % 4 == 0)) ? 1 : 0;
   }
   char* ws = static_cast<char*>(a->workspace);
   mss::BwdPtrs p{};

@@ -159,6 +159,7 @@ struct BwdShape {
               // as pairs of adjacent steps (unit time stride, even length and strides)
   int quads;  // the checkpoint pass reads u, delta_raw as 4-step vectors
               // (unit time stride, length and strides multiples of 4)
+  int bquads;  // ... and B too (the same conditions on B)
   int states_given;  // ckpt holds chunk states recorded by the forward: no checkpoint pass
 };
 

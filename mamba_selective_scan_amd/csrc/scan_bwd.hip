@@ -398,8 +398,9 @@ __global__ __launch_bounds__(256) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
 }
 
 // ---------------------------------------------------------------- pass 1 ---
-// QUAD: u and delta_raw are read as 4-step vectors (s.quads).
-template <typename IO, bool QUAD>
+// QUAD: u and delta_raw are read as 4-step vectors (s.quads); BQUAD: B as
+// well (s.bquads).
+template <typename IO, bool QUAD, bool BQUAD>
 __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_b[kMaxState * kCkBPitch];
   __shared__ __attribute__((aligned(16))) float s_dd[kCh * kCkDdPitch];
@@ -438,8 +439,12 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   const int bn = lane >> 2;
   uint32_t o_b[8], o_u[4], o_dr[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    o_b[i] = bn < s.dstate ? chunk_off<kCkSpan>(s, s.sB, es, bn, (lane & 3) * 8 + i) : kOffNone;
+  for (int i = 0; i < 8; ++i) {
+    // BQUAD: slots 0 and 4 hold the two vectors' lower addresses (steps
+    // 8k and 8k+4 forward, 8k+3 and 8k+7 reversed)
+    const int tt = BQUAD ? (lane & 3) * 8 + (i & 4) + (s.reverse ? 3 : 0) : (lane & 3) * 8 + i;
+    o_b[i] = bn < s.dstate ? chunk_off<kCkSpan>(s, s.sB, es, bn, tt) : kOffNone;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     // QUAD: slot 0 holds the vector's lower address: step 4j forward, 4j+3 reversed
@@ -459,9 +464,21 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
     const auto r_b = chunk_rsrc<kCkSpan>(s, p.B, s.sB, es, b, 0, t0, true, p.u);
     const auto r_u = chunk_rsrc<kCkSpan>(s, p.u, s.su, es, b, dg, t0, true, p.u);
     const auto r_dr = chunk_rsrc<kCkSpan>(s, p.delta_raw, s.sd, es, b, dg, t0, true, p.u);
+    if constexpr (BQUAD) {
+      // length a multiple of 4: a vector is wholly inside or past the sequence
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = buf_one<IO>::load(r_b, (qok && t0 + (lane & 3) * 8 + i < s.seqlen) ? o_b[i] : kOffNone, 0);
+      for (int v = 0; v < 2; ++v) {
+        float vb[4];
+        const bool ok = qok && t0 + (lane & 3) * 8 + 4 * v < s.seqlen;
+        quad_io<IO>::load(r_b, ok ? o_b[4 * v] : kOffNone, vb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rb[4 * v + e] = s.reverse ? vb[3 - e] : vb[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rb[i] = buf_one<IO>::load(r_b, (qok && t0 + (lane & 3) * 8 + i < s.seqlen) ? o_b[i] : kOffNone, 0);
+    }
     if constexpr (QUAD) {
       // length a multiple of 4: a vector is wholly inside or past the sequence
       const bool ok = qok && t0 + 4 * sg < s.seqlen;
@@ -987,10 +1004,15 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
   }
   // chunk states recorded by the forward replace the checkpoint pass
   if (s.states_given == 0) {
-    if (s.quads)
-      ckpt_kernel<IO, true><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+    const dim3 grid(static_cast<unsigned>(waves));
+    if (s.quads && s.bquads)
+      ckpt_kernel<IO, true, true><<<grid, dim3(64), 0, stream>>>(s, p);
+    else if (s.quads)
+      ckpt_kernel<IO, true, false><<<grid, dim3(64), 0, stream>>>(s, p);
+    else if (s.bquads)
+      ckpt_kernel<IO, false, true><<<grid, dim3(64), 0, stream>>>(s, p);
     else
-      ckpt_kernel<IO, false><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+      ckpt_kernel<IO, false, false><<<grid, dim3(64), 0, stream>>>(s, p);
   }
   const int64_t wgs = static_cast<int64_t>(s.batch) * s.nseg * s.tiles;
   if (s.pairs)

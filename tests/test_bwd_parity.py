@@ -226,6 +226,40 @@ def test_bf16(mss, seqlen):
                    _problem(2, 128, seqlen, 16, io="bf16", h0=True, dfinal=True), io="bf16")
 
 
+def _relayout(t, unit_axis):
+    """The same logical [B, X, L] values stored with unit stride on axis 1
+    (channels or states) or axis 2 (time)."""
+    if unit_axis == 2:
+        return t.contiguous()
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+@pytest.mark.parametrize("x_axis,bc_axis", [(2, 1), (1, 2)])
+def test_mixed_layouts(mss, x_axis, bc_axis):
+    """u, delta_raw, z, dout in one layout and B, C in the other: the
+    checkpoint pass reads u, delta_raw as 4-step vectors but B element-wise,
+    or the reverse; dB and dC keep the layout of B and C."""
+    dx = _problem(2, 72, 256, 16, h0=True, dfinal=True)
+    for k in ("u", "delta_raw", "z", "dout"):
+        dx[k] = _relayout(dx[k], x_axis)
+    for k in ("B", "C"):
+        dx[k] = _relayout(dx[k], bc_axis)
+    _run_and_check(mss, f"x axis {x_axis}, B/C axis {bc_axis}", dx)
+
+
+def test_B_odd_row_pitch(mss):
+    """B and C as views with rows of odd pitch: B element-wise in the
+    checkpoint pass while u, delta_raw stay vectors."""
+    import torch
+    dx = _problem(2, 64, 128, 16, h0=True, dfinal=True)
+    for k in ("B", "C"):
+        wide = torch.zeros(2, 16, 129, device=device(), dtype=dx[k].dtype)
+        wide[:, :, :128] = dx[k]
+        dx[k] = wide[:, :, :128]
+    assert dx["B"].stride(1) == 129
+    _run_and_check(mss, "B odd row pitch", dx)
+
+
 def test_odd_row_stride(mss):
     """Even length but rows of odd pitch (views into a wider buffer): the
     element-wise path, since a step pair would straddle an 8-byte boundary."""
