@@ -585,9 +585,12 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
       ok = xst[i][2] == 1 && aligned(xp[i], 4 * es) && (a->batch == 1 || xst[i][0] % 4 == 0) &&
            (a->dim == 1 || xst[i][1] % 4 == 0);
     s.quads = ok ? 1 : 0;
-    s.bquads = (a->seqlen % 4 == 0 && a->B_stride[2] == 1 && aligned(a->B, 4 * es) &&
-                (a->batch == 1 || a->B_stride[0] % 4 == 0) &&
-                (a->dstate == 1 || a->B_stride[1] % 4 == 0)) ? 1 : 0;
+    auto quad_rows = [&](const void* ptr, const int64_t* st) {
+      return a->seqlen % 4 == 0 && st[2] == 1 && aligned(ptr, 4 * es) &&
+             (a->batch == 1 || st[0] % 4 == 0) && (a->dstate == 1 || st[1] % 4 == 0);
+    };
+    s.bquads = quad_rows(a->B, a->B_stride) ? 1 : 0;
+    s.bcquads = (s.bquads && quad_rows(a->C, a->C_stride)) ? 1 : 0;
   }
   char* ws = static_cast<char*>(a->workspace);
   mss::BwdPtrs p{};

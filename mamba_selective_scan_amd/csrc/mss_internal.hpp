@@ -160,6 +160,7 @@ struct BwdShape {
   int quads;  // the checkpoint pass reads u, delta_raw as 4-step vectors
               // (unit time stride, length and strides multiples of 4)
   int bquads;  // ... and B too (the same conditions on B)
+  int bcquads;  // B and C both meet them: the segment aggregates read B, C as 4-step vectors
   int states_given;  // ckpt holds chunk states recorded by the forward: no checkpoint pass
 };
 

@@ -229,7 +229,9 @@ __device__ inline int group_step(int lane) {
 // P = prod a_t, H = the state reached, Z = sum_t (prod_(r<=t) a_r) dy_t C_t.
 // WITH_H: also the forward aggregate H, which only the checkpoint pass
 // needs (forward chunk states given: no checkpoint pass, H is skipped).
-template <typename IO, bool WITH_H>
+// PAIR: u, delta_raw, dout, z as pairs of adjacent steps (s.pairs); BCQ: B
+// and C as 4-step vectors (s.bcquads).
+template <typename IO, bool WITH_H, bool PAIR, bool BCQ>
 __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
   __shared__ __attribute__((aligned(16))) float s_el[kCh * kElPitch];
@@ -267,17 +269,21 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   // delta_raw, dout, z, lane (c, j) steps 2j, 2j+1 of channel c.
   const int bn = lane >> 2, bt0 = (lane & 3) * 4;
   uint32_t o_b[4], o_c[4], o_u[2], o_dr[2], o_do[2], o_z[2];
+  // (BCQ / PAIR use slot 0 only: the vector's or pair's lower address, which
+  // holds its first step in forward time and its last in reverse time)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    o_b[i] = chunk_off(s, s.sB, es, bn, bt0 + i);
-    o_c[i] = chunk_off(s, s.sC, es, bn, bt0 + i);
+    const int tt = BCQ ? bt0 + (s.reverse ? 3 : 0) : bt0 + i;
+    o_b[i] = chunk_off(s, s.sB, es, bn, tt);
+    o_c[i] = chunk_off(s, s.sC, es, bn, tt);
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    o_u[e] = chunk_off(s, s.su, es, sc, 2 * sg + e);
-    o_dr[e] = chunk_off(s, s.sd, es, sc, 2 * sg + e);
-    o_do[e] = chunk_off(s, s.sdo, es, sc, 2 * sg + e);
-    o_z[e] = chunk_off(s, s.sz, es, sc, 2 * sg + e);
+    const int tt = PAIR ? 2 * sg + (s.reverse ? 1 : 0) : 2 * sg + e;
+    o_u[e] = chunk_off(s, s.su, es, sc, tt);
+    o_dr[e] = chunk_off(s, s.sd, es, sc, tt);
+    o_do[e] = chunk_off(s, s.sdo, es, sc, tt);
+    o_z[e] = chunk_off(s, s.sz, es, sc, tt);
   }
   float rb[4], rc[4], ru[2], rx[2], rgo[2], rz[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
@@ -285,23 +291,51 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     const bool qin = q < q_end;
     const auto rs_b = chunk_rsrc(s, Bm, s.sB, es, b, 0, t0, true, Bm);
     const auto rs_c = chunk_rsrc(s, Cm, s.sC, es, b, 0, t0, true, Cm);
+    if constexpr (BCQ) {
+      // length a multiple of 4: a vector is wholly inside or past the sequence
+      const bool ok = qin && bn < s.dstate && t0 + bt0 < s.seqlen;
+      float vb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vc[4];
+      if constexpr (WITH_H) quad_io<IO>::load(rs_b, ok ? o_b[0] : kOffNone, vb);
+      quad_io<IO>::load(rs_c, ok ? o_c[0] : kOffNone, vc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = qin && bn < s.dstate && t0 + bt0 + i < s.seqlen;
-      rb[i] = WITH_H ? buf_one<IO>::load(rs_b, ok ? o_b[i] : kOffNone, 0) : 0.0f;
-      rc[i] = buf_one<IO>::load(rs_c, ok ? o_c[i] : kOffNone, 0);
+      for (int i = 0; i < 4; ++i) {
+        rb[i] = s.reverse ? vb[3 - i] : vb[i];
+        rc[i] = s.reverse ? vc[3 - i] : vc[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = qin && bn < s.dstate && t0 + bt0 + i < s.seqlen;
+        rb[i] = WITH_H ? buf_one<IO>::load(rs_b, ok ? o_b[i] : kOffNone, 0) : 0.0f;
+        rc[i] = buf_one<IO>::load(rs_c, ok ? o_c[i] : kOffNone, 0);
+      }
     }
     const auto rs_u = chunk_rsrc(s, u, s.su, es, b, dg, t0, true, u);
     const auto rs_dr = chunk_rsrc(s, dr, s.sd, es, b, dg, t0, true, u);
     const auto rs_do = chunk_rsrc(s, dout, s.sdo, es, b, dg, t0, true, u);
     const auto rs_z = chunk_rsrc(s, zz, s.sz, es, b, dg, t0, has_z, u);
+    if constexpr (PAIR) {
+      // even length: a pair is wholly inside or past the sequence
+      const bool ok = qin && dvalid && t0 + 2 * sg < s.seqlen;
+      auto pair = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[2]) {
+        float lo, hi;
+        pair_io<IO>::load(r, ok ? off : kOffNone, lo, hi);
+        v[0] = s.reverse ? hi : lo;
+        v[1] = s.reverse ? lo : hi;
+      };
+      pair(rs_u, o_u[0], ru);
+      pair(rs_dr, o_dr[0], rx);
+      pair(rs_do, o_do[0], rgo);
+      pair(rs_z, o_z[0], rz);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const bool ok = qin && dvalid && t0 + 2 * sg + e < s.seqlen;
-      ru[e] = buf_one<IO>::load(rs_u, ok ? o_u[e] : kOffNone, 0);
-      rx[e] = buf_one<IO>::load(rs_dr, ok ? o_dr[e] : kOffNone, 0);
-      rgo[e] = buf_one<IO>::load(rs_do, ok ? o_do[e] : kOffNone, 0);
-      rz[e] = buf_one<IO>::load(rs_z, ok ? o_z[e] : kOffNone, 0);
+      for (int e = 0; e < 2; ++e) {
+        const bool ok = qin && dvalid && t0 + 2 * sg + e < s.seqlen;
+        ru[e] = buf_one<IO>::load(rs_u, ok ? o_u[e] : kOffNone, 0);
+        rx[e] = buf_one<IO>::load(rs_dr, ok ? o_dr[e] : kOffNone, 0);
+        rgo[e] = buf_one<IO>::load(rs_do, ok ? o_do[e] : kOffNone, 0);
+        rz[e] = buf_one<IO>::load(rs_z, ok ? o_z[e] : kOffNone, 0);
+      }
     }
   };
   load_chunk(q_begin);
@@ -991,14 +1025,36 @@ __global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
   }
 }
 
+template <typename IO, bool WITH_H, bool PAIR>
+void launch_agg_q(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
+  if (s.bcquads)
+    agg_kernel<IO, WITH_H, PAIR, true><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+  else
+    agg_kernel<IO, WITH_H, PAIR, false><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+}
+
+template <typename IO, bool WITH_H>
+void launch_agg_p(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
+  if (s.pairs)
+    launch_agg_q<IO, WITH_H, true>(s, p, stream, waves);
+  else
+    launch_agg_q<IO, WITH_H, false>(s, p, stream, waves);
+}
+
+// Forward aggregate H only without the forward's chunk states.
+template <typename IO>
+void launch_agg(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
+  if (s.states_given)
+    launch_agg_p<IO, false>(s, p, stream, waves);
+  else
+    launch_agg_p<IO, true>(s, p, stream, waves);
+}
+
 template <typename IO>
 hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream) {
   const int64_t waves = static_cast<int64_t>(s.batch) * s.nseg * s.tiles * kBwdWaves;
   if (s.nseg > 1) {
-    if (s.states_given)
-      agg_kernel<IO, false><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
-    else
-      agg_kernel<IO, true><<<dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream>>>(s, p);
+    launch_agg<IO>(s, p, stream, static_cast<unsigned>(waves));
     const int64_t nc = s.nchan_pad * kMaxState;
     carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   }
