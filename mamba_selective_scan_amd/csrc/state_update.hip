@@ -30,31 +30,38 @@ __global__ __launch_bounds__(kStepThreads) void state_update_kernel(
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dskip,
     const IO* __restrict__ z, const float* __restrict__ dt_bias, IO* __restrict__ out) {
   const int n = threadIdx.x % kMaxState;
-  const int64_t ch = static_cast<int64_t>(blockIdx.x) * kStepChannels + threadIdx.x / kMaxState;
-  const bool cvalid = ch < static_cast<int64_t>(s.batch) * s.dim;
-  const int b = cvalid ? static_cast<int>(ch / s.dim) : 0;
-  const int d = cvalid ? static_cast<int>(ch % s.dim) : 0;
+  const int64_t nch = static_cast<int64_t>(s.batch) * s.dim;
+  const int64_t ch_lane = static_cast<int64_t>(blockIdx.x) * kStepChannels + threadIdx.x / kMaxState;
+  const bool cvalid = ch_lane < nch;
   const bool active = cvalid && n < s.dstate;
-  float dl = 0.0f, uv = 0.0f, y = 0.0f;
-  if (cvalid) {
-    const float x = io_traits<IO>::load(delta_raw + b * s.sd[0] + d * s.sd[1]) +
-                    (dt_bias != nullptr ? dt_bias[d] : 0.0f);
-    dl = s.softplus ? softplus(x) : x;
-    uv = io_traits<IO>::load(u + b * s.su[0] + d * s.su[1]);
-  }
-  if (active) {
-    const float a2 = -expf(A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e;
-    const float bn = io_traits<IO>::load(Bm + b * s.sB[0] + n * s.sB[1]);
-    const float cn = io_traits<IO>::load(Cm + b * s.sC[0] + n * s.sC[1]);
-    float* hp = state + ch * s.dstate + n;
-    const float hn = fmaf(fast_exp2(dl * a2), *hp, dl * uv * bn);
-    *hp = hn;
-    y = cn * hn;
-  }
+  // Indices clamped into range so that every load below is in bounds and all
+  // of them leave before any arithmetic: one memory round trip, not three
+  // (the inputs, then A_log, B, C and the state, then z).
+  const int64_t ch = cvalid ? ch_lane : 0;
+  const int b = static_cast<int>(ch / s.dim);
+  const int d = static_cast<int>(ch % s.dim);
+  const int nn = n < s.dstate ? n : 0;
+  const float xr = io_traits<IO>::load(delta_raw + b * s.sd[0] + d * s.sd[1]);
+  const float uv = io_traits<IO>::load(u + b * s.su[0] + d * s.su[1]);
+  const float alog = A_log[d * s.sA[0] + nn * s.sA[1]];
+  const float bn = io_traits<IO>::load(Bm + b * s.sB[0] + nn * s.sB[1]);
+  const float cn = io_traits<IO>::load(Cm + b * s.sC[0] + nn * s.sC[1]);
+  float* hp = state + ch * s.dstate + nn;
+  const float h_old = *hp;
+  const float bias = dt_bias != nullptr ? dt_bias[d] : 0.0f;
+  const float skip = Dskip != nullptr ? Dskip[d] : 0.0f;
+  const float zv = z != nullptr ? io_traits<IO>::load(z + b * s.sz[0] + d * s.sz[1]) : 0.0f;
+
+  const float x = xr + bias;
+  const float dl = s.softplus ? softplus(x) : x;
+  const float a2 = -expf(alog) * kLog2e;
+  const float hn = fmaf(fast_exp2(dl * a2), h_old, dl * uv * bn);
+  if (active) *hp = hn;
+  float y = active ? cn * hn : 0.0f;
   y = row_sum16(y);  // every lane of the row takes part
   if (cvalid && n == 0) {
-    y = fmaf(Dskip != nullptr ? Dskip[d] : 0.0f, uv, y);
-    if (z != nullptr) y *= silu(io_traits<IO>::load(z + b * s.sz[0] + d * s.sz[1]));
+    y = fmaf(skip, uv, y);
+    if (z != nullptr) y *= silu(zv);
     io_traits<IO>::store(out + b * s.so[0] + d * s.so[1], y);
   }
 }
