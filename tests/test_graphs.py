@@ -214,3 +214,35 @@ def test_conv_prefill_and_step_replays(mss):
         torch.cuda.synchronize()
         o, w, y = ref[which]
         assert torch.equal(out, o) and torch.equal(win, w) and torch.equal(y1, y), f"replay {rep}"
+
+
+def test_complex_forward_replays(mss):
+    """The complex-A forward recorded once and replayed with new inputs."""
+    import torch
+    from mamba_selective_scan_amd.inputs import complex_to_torch, generate_complex
+    note("graph complex forward")
+    sets = [complex_to_torch(generate_complex(2, 48, 300, 16, seed=s), device()) for s in (9, 10)]
+    static = _clone(sets[0])
+    out = torch.empty_like(static["u"])
+    fin = torch.empty(2, 48, 16, dtype=torch.complex64, device=device())
+    keys = ("u", "delta_raw", "z", "B", "C", "A_log", "A_imag", "D", "dt_bias")
+
+    def call(dx, o, f):
+        mss.selective_scan_fwd_complex(dx["u"], dx["delta_raw"], dx["A_log"], dx["A_imag"], dx["B"],
+                                       dx["C"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                       out=o, final_state=f, return_final_state=True)
+
+    g, _ = _capture(lambda: call(static, out, fin))
+    ref = []
+    for dx in sets:
+        o, f = torch.empty_like(out), torch.empty_like(fin)
+        call(dx, o, f)
+        ref.append((o, f))
+    torch.cuda.synchronize()
+    for rep, which in enumerate((1, 0)):
+        for k in keys:
+            static[k].copy_(sets[which][k])
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[which][0]) and torch.equal(fin, ref[which][1]), f"replay {rep}"
