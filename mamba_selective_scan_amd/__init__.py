@@ -540,6 +540,12 @@ def _scan_fn():
             delta_softplus, reverse = ctx.flags
             if dout is None:
                 dout = torch.zeros_like(u)
+            # The backward reads dout through its strides (a stride-0 gradient
+            # from out.sum() is read as is); the final-state gradient is a
+            # contiguous [B, D, N] array in the ABI, and sum() or mean() of the
+            # final state hands over an expanded stride-0 view.
+            if dfinal is not None:
+                dfinal = dfinal.contiguous()
             g = selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D, z, dt_bias,
                                    delta_softplus=delta_softplus, initial_state=initial_state,
                                    dfinal_state=dfinal, reverse=reverse, chunk_states=states)

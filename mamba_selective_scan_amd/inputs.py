@@ -105,6 +105,31 @@ def generate(batch: int, dim: int, seqlen: int, dstate: int, layout: str = "bdl"
             "A_log": A_log, "D": D, "dt_bias": dt_bias, "layout": layout}
 
 
+def softplus_range_delta(batch: int, dim: int, seqlen: int, seed: int = 0,
+                         big_bias: bool = False) -> tuple:
+    """(delta_raw [batch, dim, seqlen], dt_bias [dim]) float32 whose sum
+    x = delta_raw + dt_bias covers the softplus argument far beyond the usual
+    draw: a uniform grid over [-40, 40] (step 0.5), a dense grid across
+    [19.5, 20.5] (step 0.01, the region of the x > 20 shortcut some kernels
+    take) and U(30, 45) values, repeated along time in a random order per
+    channel.  dt_bias is 0, or with ``big_bias`` 25 on every second channel,
+    whose delta_raw is then the grid minus 25.
+    """
+    rng = np.random.default_rng(seed + 2_000_003)
+    grid = np.concatenate([np.arange(-80, 81) * 0.5, 19.5 + 0.01 * np.arange(101),
+                           rng.uniform(30.0, 45.0, 40)])
+    reps = -(-seqlen // grid.size)
+    xs = np.empty((batch, dim, seqlen), dtype=np.float64)
+    for b in range(batch):
+        for d in range(dim):
+            xs[b, d] = rng.permutation(np.tile(grid, reps))[:seqlen]
+    dt_bias = np.zeros(dim, dtype=np.float32)
+    if big_bias:
+        dt_bias[1::2] = np.float32(25.0)
+    delta_raw = (xs - dt_bias[None, :, None].astype(np.float64)).astype(np.float32)
+    return delta_raw, dt_bias
+
+
 def generate_workload(w: Workload, seed: int = 0, **kw) -> dict:
     """Draw a named workload (with its extra decode timesteps, if any)."""
     return generate(w.batch, w.dim, w.seqlen + w.decode_steps, w.dstate, w.layout,

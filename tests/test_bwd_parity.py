@@ -193,6 +193,21 @@ def test_mamba2p8b_layer_full(mss, io):
               to_np(got[k][b:b + 1] if k != "dA_log" else got[k]), 1e-5 if io == "f32" else 1e-2)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("big_bias", [False, True])
+def test_softplus_upper_range(mss, io, big_bias):
+    """delta_raw + dt_bias over [-40, 40] (a dense grid through 19.5..20.5,
+    values above 30; dt_bias 0 or 25): softplus and its derivative sigmoid in
+    the backward against the oracle, every gradient element by element."""
+    from mamba_selective_scan_amd.inputs import softplus_range_delta
+    dx = _problem(2, 72, 300, 16, io=io, h0=True, dfinal=True)
+    dr, bias = softplus_range_delta(2, 72, 300, seed=3, big_bias=big_bias)
+    import torch
+    dx["delta_raw"] = torch.from_numpy(dr).to(device=device(), dtype=dx["u"].dtype)
+    dx["dt_bias"] = torch.from_numpy(bias).to(device())
+    _run_and_check(mss, f"softplus range {io} big_bias={big_bias}", dx, io=io)
+
+
 def test_time_invariant_B_C(mss):
     """B and C constant in time, passed as stride-0 views: the gradient of the
     [B, N] parameters is the time sum of dB and dC."""
@@ -316,3 +331,39 @@ def test_autograd_function(mss, reverse):
         if reverse and k in ("u", "delta_raw", "B", "C", "z"):
             r = r[:, :, ::-1]
         check(f"autograd grad {k} reverse={reverse}", to_np(leaves[k].grad), r, TOL["f32"])
+
+
+@pytest.mark.parametrize("loss", ["out.sum", "fin.sum", "both.mean", "out.sum bf16"])
+def test_autograd_reduction_losses(mss, loss):
+    """Losses built from sum() and mean(): their gradients reach the backward
+    as expanded stride-0 views (dout from out.sum(), dfinal from fin.sum()),
+    and give the oracle's gradients for a constant dout and dfinal."""
+    import torch
+    io = "bf16" if loss.endswith("bf16") else "f32"
+    dx = _problem(2, 64, 120, 16, io=io, h0=True)
+    names = ["u", "delta_raw", "A_log", "B", "C", "D", "z", "dt_bias", "h0"]
+    leaves = {k: dx[k].detach().clone().requires_grad_(True) for k in names}
+    note(f"autograd {loss}")
+    out, fin = mss.selective_scan(leaves["u"], leaves["delta_raw"], leaves["A_log"],
+                                  leaves["B"], leaves["C"], leaves["D"], leaves["z"],
+                                  leaves["dt_bias"], initial_state=leaves["h0"],
+                                  return_final_state=True)
+    n_out, n_fin = out.numel(), fin.numel()
+    if loss.startswith("out.sum"):
+        out.sum().backward()
+        w, v = 1.0, 0.0
+    elif loss == "fin.sum":
+        fin.sum().backward()
+        w, v = 0.0, 1.0
+    else:
+        (out.mean() + fin.mean()).backward()
+        w, v = 1.0 / n_out, 1.0 / n_fin
+    torch.cuda.synchronize()
+    dout = np.full(tuple(out.shape), w)
+    dfin = np.full(tuple(fin.shape), v)
+    ref = oracle.scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dout,
+                          D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], h0=dx["h0"], dfinal=dfin)
+    oname = {"u": "du", "delta_raw": "ddelta_raw", "A_log": "dA_log", "B": "dB", "C": "dC",
+             "D": "dD", "z": "dz", "dt_bias": "ddt_bias", "h0": "dh0"}
+    for k in names:
+        check(f"autograd {loss} grad {k}", to_np(leaves[k].grad), ref[oname[k]], TOL[io])

@@ -86,6 +86,37 @@ def test_state_update_matches_oracle(mss, io, dstate, shape):
     check("step state", to_np(state), ref_s, 1e-4)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("big_bias", [False, True])
+def test_state_update_softplus_upper_range(mss, io, big_bias):
+    """The decode step with delta_raw + dt_bias over [-40, 40] (a dense grid
+    through 19.5..20.5, values above 30; dt_bias 0 or 25): 342 steps, each on
+    every channel, against the oracle step by step."""
+    import torch
+    from mamba_selective_scan_amd.inputs import softplus_range_delta
+    batch, dim, N, steps = 3, 200, 16, 342
+    note(f"state_update softplus upper range {io} big_bias={big_bias}")
+    x = generate(batch, dim, steps, N, seed=13)
+    x["delta_raw"], x["dt_bias"] = softplus_range_delta(batch, dim, steps, seed=13,
+                                                        big_bias=big_bias)
+    dx = to_torch(x, device(), io)
+    g = torch.Generator().manual_seed(5)
+    state = torch.randn(batch, dim, N, generator=g).to(device())
+    ref_state = to_np(state)
+    outs = _decode_steps(mss, dx, state, 0, steps)
+    torch.cuda.synchronize()
+    ref_outs = []
+    for t in range(steps):
+        y, ref_state = oracle.state_update(ref_state, dx["u"][:, :, t], dx["delta_raw"][:, :, t],
+                                           dx["A_log"], dx["B"][:, :, t], dx["C"][:, :, t],
+                                           D=dx["D"], z=dx["z"][:, :, t], dt_bias=dx["dt_bias"])
+        ref_outs.append(y)
+    tol = 1e-4 if io == "f32" else 2e-2
+    check(f"step softplus range {io} out", to_np(torch.stack(outs, dim=2)),
+          np.stack(ref_outs, axis=2), tol)
+    check(f"step softplus range {io} state", to_np(state), ref_state, tol)
+
+
 def test_step_sequence_equals_scan(mss):
     """Iterating the state update over a sequence reproduces the scan."""
     import torch

@@ -188,6 +188,32 @@ def test_no_unit_stride_axis_is_rejected(mss):
     assert e.value.name == "MSS_ERR_BAD_STRIDE"
 
 
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+@pytest.mark.parametrize("big_bias", [False, True])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_softplus_upper_range(mss, io, big_bias, layout):
+    """delta_raw + dt_bias swept over [-40, 40] (a dense grid through 19.5..20.5
+    and values above 30), with dt_bias = 0 or 25: the kernel's softplus, which
+    takes no threshold shortcut, against the oracle's exact one, element by
+    element, with and without the gate and the skip term."""
+    import torch
+    from mamba_selective_scan_amd.inputs import softplus_range_delta
+    bsz, dim, L, N = 2, 72, 600, 16
+    for with_z, with_D in ((True, True), (False, False)):
+        note(f"softplus upper range {io} big_bias={big_bias} {layout} z={with_z} D={with_D}")
+        x = generate(bsz, dim, L, N, layout, seed=21, d_skip="ones" if with_D else "zeros")
+        x["delta_raw"], x["dt_bias"] = softplus_range_delta(bsz, dim, L, seed=21,
+                                                            big_bias=big_bias)
+        dx = to_torch(x, device(), io)
+        out, fin = run_gpu(mss, dx, with_z=with_z, with_D=with_D)
+        torch.cuda.synchronize()
+        ref_out, ref_fin = oracle_full(dx, with_z=with_z, with_D=with_D)
+        tol = tol_for(io)
+        tag = f"softplus range {io} bias={big_bias} {layout} z={with_z}"
+        check(f"{tag} out", to_np(out), ref_out, tol)
+        check(f"{tag} final_state", to_np(fin), ref_fin, tol)
+
+
 # ------------------------------------------------------------ full workloads
 
 def _sampled_workload(mss, wname, io, k, seed=0):
