@@ -10,11 +10,17 @@ Prints one JSON line:
   value         whole-step throughput in GB/s of algorithmic bytes (each input
                 read once, each output written once);
   roofline      the scan forward call timed with HIP events on its stream
-                against the VALU issue peak (the binding resource), with the
-                HBM fraction beside it and HBM traffic from rocprofv3 counters
-                when a matching profile is committed under profiles/;
+                against the 8 TB/s HBM peak (algorithmic bytes / duration),
+                with HBM traffic from rocprofv3 counters when a matching
+                profile is committed under profiles/, and beside it the same
+                call against the VALU issue rate (one slot per instruction,
+                at 2.4 GHz and at the shader clock sampled while it runs);
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
-                the host's cores.
+                the host's cores and on one core;
+  env           GPU, ROCm/HIP, torch, host CPU and build flags.
+Workloads whose data fit three times in the 256 MB last-level cache rotate
+enough copies of their buffers through the timed loop that every launch
+reads from HBM (the cold figure is the metric; the warm one is context).
 The roofline and decode objects also give the same calls replayed from a
 recorded HIP graph (graph_us_mean, graph_us_per_step over a recorded 64-step
 decode loop): the GPU time without the host's launch cost, which dominates
@@ -47,24 +53,15 @@ if ROOT not in sys.path:
 
 METRIC = "selective-scan fwd achieved HBM GB/s (% of 8 TB/s) and Gtok·ch/s"
 HBM_PEAK_GBS = 8000.0
-# VALU issue roofline: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-slots per
-# second without packed fp32 (which the build disables); a transcendental
-# (exp2, log2, rcp) takes 4 slots (quarter rate), every other op one.
+LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
+PEAK_SCLK_MHZ = 2400.0
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instructions per
+# second without packed fp32 (which the build disables).  The backward and
+# complex lines weight a transcendental (exp2, log2, rcp, sin, cos) as 4 slots
+# (the ISA's quarter rate); the forward line counts one slot per instruction.
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
-def valu_slots_per_element(dstate: int, softplus: bool = True, has_z: bool = True) -> int:
-    """Algorithmic VALU slots per (b, d, t) element of the forward.
-
-    Per state: exp2 (4) + delta*A2 + (delta*u)*B + the h FMA + the C.h FMA.
-    Per element: delta_raw + dt_bias; softplus as exp2 (4) + log2 (4) + 7 ops;
-    delta*u; D*u and its add; silu as exp2 (4) + rcp (4) + 3 ops; the gate.
-    """
-    n = dstate * (4 + 4)
-    n += 1 + (15 if softplus else 0) + 1 + 2
-    if has_z:
-        n += 11 + 1
-    return n
 KERNEL_SOURCES = {
     "scan": ["mamba_selective_scan_amd/csrc/scan_fwd.hip",
              "mamba_selective_scan_amd/csrc/mss_device.hpp",
@@ -81,8 +78,120 @@ KERNEL_SOURCES = {
 }
 
 
+def valu_instr_per_element(dstate: int, softplus: bool = True, has_z: bool = True) -> int:
+    """VALU instructions per (b, d, t) element that the forward's arithmetic
+    needs, every instruction one issue slot (on gfx950 a v_exp_f32 mixed with
+    four FMAs, as in the scan loop, costs about one FMA slot: measured).
+
+    Per state: exp2, delta*A2, (delta*u)*B, the h FMA and the C.h FMA (5).
+    Per element: the bias add; softplus (exp2, log2 and 7 ops); delta*u; D*u
+    and its add to the state sum; silu (exp2, rcp and 3 ops) and the gate
+    multiply: 19.
+    """
+    n = 5 * dstate + 1 + (9 if softplus else 0) + 1 + 2
+    if has_z:
+        n += 5 + 1
+    return n
+
+
+def cache_sets(nbytes: int) -> int:
+    """Buffer sets the timed loop rotates through so that a workload of nbytes
+    per launch moves at least 3x the last-level cache per cycle (at least 8
+    sets, at most 256), or 1 when one launch already moves that much."""
+    if nbytes >= 3 * LLC_BYTES:
+        return 1
+    return int(min(256, max(8, -(-3 * LLC_BYTES // nbytes))))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def env_report() -> dict:
+    """What the run ran on: GPU, runtime versions, host CPU and build flags."""
+    import torch
+
+    from mamba_selective_scan_amd import build as hip_build
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+                break
+        except OSError:
+            pass
+    return {
+        "gpu": props.name,
+        "gcn_arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "hbm_gib": round(props.total_memory / 2**30, 1),
+        "rocm": rocm,
+        "hip_runtime": torch.version.hip,
+        "torch": torch.__version__,
+        "host_cpu": cpu_model(),
+        "host_threads": os.cpu_count(),
+        "build": " ".join(["hipcc"] + [f for f in hip_build.HIP_FLAGS if f != "-shared"]),
+    }
+
+
+def _sclk_now():
+    """Current shader clock in MHz from the driver's sysfs files, or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        v = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                        return float(v.replace("mhz", ""))
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+def sample_sclk(fn, seconds: float = 0.5):
+    """Run fn back to back for about ``seconds`` while a thread samples the
+    shader clock every 2 ms; returns (mean MHz, samples, source) or Nones."""
+    import threading
+
+    import torch
+    if _sclk_now() is None:
+        return None, 0, None
+    vals, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            v = _sclk_now()
+            if v is not None:
+                vals.append(v)
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    torch.cuda.synchronize()
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return None, 0, None
+    return sum(vals) / len(vals), len(vals), "pp_dpm_sclk (current level, sampled every 2 ms)"
 
 
 def kernel_source_hash(op: str = "scan") -> str:
@@ -174,6 +283,13 @@ def cpu_baseline(x, w, io_bytes, target_s: float):
     what = (f"{k} of {total} channels (random, with repeats)" if k < total
             else f"all {total} channels")
     per_elem = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, io_bytes) / w.elems
+    # the same oracle on one thread, on a sample sized to about a third of
+    # the time budget from the all-core rate
+    k1 = int(max(1, min(total, k / max(threads, 1) * (target_s / 3) / max(dt, 1e-6))))
+    chans1 = sample(k1)
+    t = time.perf_counter()
+    oracle.scan_channels(x, chans1, threads=1)
+    dt1 = time.perf_counter() - t
     return {
         "value": round(tokch * per_elem / dt / 1e9, 4),
         "unit": "GB/s",
@@ -182,6 +298,13 @@ def cpu_baseline(x, w, io_bytes, target_s: float):
         "sample": f"{what} x full seqlen {w.seqlen} ({tokch} token-channels), "
                   f"fp64 sequential recurrence, {dt:.1f} s",
         "gtok_ch_per_s": round(tokch / dt / 1e9, 6),
+        "cpu_model": cpu_model(),
+        "one_core": {
+            "value": round(k1 * w.seqlen * per_elem / dt1 / 1e9, 4),
+            "unit": "GB/s",
+            "gtok_ch_per_s": round(k1 * w.seqlen / dt1 / 1e9, 6),
+            "sample": f"{k1} random channels x full seqlen {w.seqlen}, one thread, {dt1:.1f} s",
+        },
     }
 
 
@@ -714,29 +837,48 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     log(f"workload {w.name}: B={w.batch} D={w.dim} L={w.seqlen} N={w.dstate} {w.layout} {args.io}")
     x = generate(w.batch, w.dim, w.seqlen, w.dstate, w.layout, seed=args.seed)
-    dx = to_torch(x, dev, args.io)
-    out = torch.empty_like(dx["u"])
-    final = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
-    ws = torch.empty(max(mss.scan_workspace_size(dx["u"], dx["A_log"]), 1), dtype=torch.uint8,
+    fwd_bytes = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, io_bytes, final_state=True)
+    # Cold-cache protocol: a workload whose bytes fit three times into the
+    # last-level cache gets enough copies of its tensors that one pass over
+    # all of them moves at least 3x the cache; the timed loop rotates through
+    # them, so each launch finds its inputs evicted.
+    nsets = cache_sets(fwd_bytes)
+    base = to_torch(x, dev, args.io)
+    sets = []
+    for i in range(nsets):
+        dx = dict(base) if i == 0 else {k: (v.clone() if k in ("u", "delta_raw", "z", "B", "C")
+                                            else v) for k, v in base.items()}
+        if i > 0 and w.layout == "bld":  # keep the channel-last storage of the copies
+            for k in ("u", "delta_raw", "z", "B", "C"):
+                dx[k] = base[k].transpose(1, 2).clone().transpose(1, 2)
+        dx["out"] = torch.empty_like(dx["u"])
+        dx["final"] = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+        sets.append(dx)
+    if nsets > 1:
+        log(f"cold-cache protocol: {nsets} buffer sets rotated, "
+            f"{nsets * fwd_bytes / 1e6:.0f} MB per cycle")
+    ws = torch.empty(max(mss.scan_workspace_size(base["u"], base["A_log"]), 1), dtype=torch.uint8,
                      device=dev)
     t_last = w.seqlen - 1
-    step_in = {k: dx[k][:, :, t_last].contiguous() for k in ("u", "delta_raw", "z", "B", "C")}
+    step_in = {k: base[k][:, :, t_last].contiguous() for k in ("u", "delta_raw", "z", "B", "C")}
     step_out = torch.empty_like(step_in["u"])
 
-    def scan():
+    def scan(i=0):
+        dx = sets[i % nsets]
         mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], D=dx["D"],
-                               z=dx["z"], dt_bias=dx["dt_bias"], out=out, final_state=final,
-                               workspace=ws, reverse=args.reverse)
+                               z=dx["z"], dt_bias=dx["dt_bias"], out=dx["out"],
+                               final_state=dx["final"], workspace=ws, reverse=args.reverse)
 
-    def decode():
-        mss.selective_state_update(final, step_in["u"], step_in["delta_raw"], dx["A_log"],
+    def decode(i=0):
+        dx = sets[i % nsets]
+        mss.selective_state_update(dx["final"], step_in["u"], step_in["delta_raw"], dx["A_log"],
                                    step_in["B"], step_in["C"], D=dx["D"], z=step_in["z"],
                                    dt_bias=dx["dt_bias"], out=step_out)
 
-    for _ in range(args.warmup):
-        scan()
+    for i in range(max(args.warmup, nsets if nsets > 1 else 0)):
+        scan(i)
         if not args.no_step:
-            decode()
+            decode(i)
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
@@ -749,11 +891,11 @@ def main(argv=None):
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        scan()
+        scan(i)
         ev[i][1].record(stream)
         if not args.no_step:
             dev_ev[i][0].record(stream)
-            decode()
+            decode(i)
             dev_ev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -762,21 +904,36 @@ def main(argv=None):
     scan_ms_mean = sum(scan_ms) / len(scan_ms)
     scan_ms_sorted = sorted(scan_ms)
 
+    warm_us = None
+    if nsets > 1:
+        # context: the same launch with one buffer set, which stays in the cache
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            wev[i][0].record(stream)
+            scan(0)
+            wev[i][1].record(stream)
+        torch.cuda.synchronize()
+        warm_us = sum(a.elapsed_time(b) for a, b in wev) / args.steps * 1e3
     scan_graph_us = graph_us(scan, reps=max(5, min(200, int(20e3 / (scan_ms_mean * 1e3)))))
     dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64)
+    sclk, sclk_n, sclk_src = sample_sclk(scan)
 
-    fwd_bytes = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, io_bytes, final_state=True)
-    fwd_slots = w.elems * valu_slots_per_element(w.dstate)
     total_bytes = fwd_bytes + (0 if args.no_step else step_bytes(w.batch, w.dim, w.dstate, io_bytes))
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = fwd_bytes / (scan_ms_mean * 1e-3) / 1e9
-    achieved_slots = fwd_slots / (scan_ms_mean * 1e-3) / 1e12
+    ipe = valu_instr_per_element(w.dstate)
+    valu_t = w.elems * ipe / (scan_ms_mean * 1e-3) / 1e12
+    valu_peak = VALU_PEAK_TSLOTS
     src_hash = kernel_source_hash()
     traffic = load_traffic(w.name, args.io, src_hash)
     log(f"scan fwd replayed from a graph: {scan_graph_us:.1f} us")
     log(f"step {ms_per_step:.4f} ms; scan fwd mean {scan_ms_mean * 1e3:.1f} us "
         f"(min {scan_ms_sorted[0] * 1e3:.1f}, median {scan_ms_sorted[len(scan_ms) // 2] * 1e3:.1f}); "
-        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s")
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s"
+        + (f"; warm (one buffer set) {warm_us:.1f} us" if warm_us is not None else ""))
+    if sclk is not None:
+        log(f"shader clock while the scan runs: {sclk:.0f} MHz ({sclk_n} samples)")
 
     rec = {
         "metric": METRIC,
@@ -796,38 +953,48 @@ def main(argv=None):
             "dstate": w.dstate, "layout": w.layout, "io_dtype": args.io,
             "step": ("reverse-time " if args.reverse else "") + "scan fwd + final-state export" +
                     ("" if args.no_step else " + 1 state update"),
+            "cache": (f"{nsets} buffer sets rotated ({nsets * fwd_bytes / 1e6:.0f} MB per cycle"
+                      + (", >= 3x the 256 MB last-level cache: cold)" if nsets * fwd_bytes >=
+                         3 * LLC_BYTES else ", fits the last-level cache: warm)")
+                      if nsets > 1 else
+                      "inputs and outputs exceed 3x the 256 MB last-level cache"),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gtok_ch_per_s": round(w.elems / (ms_per_step * 1e-3) / 1e9, 4),
         "roofline": {
-            "bound": "alu",
-            "kernel": "scan_kernel (mss_selective_scan_fwd) on the current stream",
-            "achieved": round(achieved_slots, 3),
-            "peak": round(VALU_PEAK_TSLOTS, 3),
-            "unit": "T VALU lane-slots/s",
-            "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
+            "bound": "hbm",
+            "kernel": "scan_kernel (mss_selective_scan_fwd: every launch of the call) "
+                      "on the current stream",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_slots": fwd_slots,
-            "slots_per_element": valu_slots_per_element(w.dstate),
-            # every VALU instruction one slot (a transcendental mixed with FMAs
-            # measures at about one FMA issue slot): 5 per state-step + 19
-            "frac_one_slot_per_instruction": round(
-                w.elems * (5 * w.dstate + 19) / (scan_ms_mean * 1e-3) / 1e12 / VALU_PEAK_TSLOTS, 4),
-            "hbm": {
-                "achieved": round(achieved, 2),
-                "peak": HBM_PEAK_GBS,
-                "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "algorithmic_bytes": fwd_bytes,
-            },
+            "algorithmic_bytes": fwd_bytes,
             "event_us_mean": round(scan_ms_mean * 1e3, 2),
             "event_us_median": round(scan_ms_sorted[len(scan_ms) // 2] * 1e3, 2),
+            "event_us_min": round(scan_ms_sorted[0] * 1e3, 2),
+            "warm_event_us_mean": None if warm_us is None else round(warm_us, 2),
             # the same call replayed from a HIP graph: without the Python
             # binding's and the launches' host time, which small shapes expose
             "graph_us_mean": round(scan_graph_us, 2),
             "kernel_source_hash": src_hash,
+            "valu": {
+                "what": "the method's VALU instructions per element, one issue slot each, "
+                        "against 256 CU x 4 SIMD x 16 lanes per clock",
+                "instr_per_element": ipe,
+                "achieved": round(valu_t, 3),
+                "unit": "T lane-instructions/s",
+                "peak_at_2400_mhz": round(valu_peak, 3),
+                "frac_at_2400_mhz": round(valu_t / valu_peak, 4),
+                "sclk_mhz": None if sclk is None else round(sclk, 0),
+                "sclk_source": sclk_src,
+                "frac_at_measured_clock": (None if sclk is None else
+                                           round(valu_t / (valu_peak * sclk / PEAK_SCLK_MHZ), 4)),
+            },
         },
         "cpu_baseline": None,
+        "env": env_report(),
     }
     if not args.no_step:
         dec_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)

@@ -33,21 +33,48 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
 
 
-def build(out: str = LIB_PATH, extra_flags=(), verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(proc, what, verbose):
+    text, _ = proc.communicate()
     # hipcc's host pass does not know the packed-fp32 target feature and says
     # so; that message is expected and carries no information.
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    msgs = [ln for ln in text.splitlines() if noise not in ln and ln.strip()]
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({what}):\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def build(out: str = LIB_PATH, extra_flags=(), verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source to an object (in parallel, ``jobs`` at a time;
+    0 = one per source up to the CPU count) and link libmss.so."""
+    import tempfile
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="mss_build_") as tmpdir:
+        objs, pending = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            cmd = [hipcc(), *compile_flags, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            pending.append((src, cmd))
+        running = []
+        while pending or running:
+            while pending and len(running) < jobs:
+                src, cmd = pending.pop(0)
+                running.append((src, _run(cmd, verbose)))
+            src, proc = running.pop(0)
+            _finish(proc, src, verbose)
+        tmp = out + ".tmp"
+        link = [hipcc(), *HIP_FLAGS, *extra_flags, *objs, "-o", tmp]
+        _finish(_run(link, verbose), "link", verbose)
     os.replace(tmp, out)
     return out
 

@@ -39,3 +39,29 @@ def test_step_bytes():
     # state read + write, four activations, B and C, the parameters
     assert bench.step_bytes(1, 2, 3, 4) == 2 * 1 * 2 * 3 * 4 + 4 * 1 * 2 * 4 + 2 * 1 * 3 * 4 + \
         2 * 3 * 4 + 2 * 2 * 4
+
+
+def test_valu_instructions_per_element():
+    # 5 per state-step (exp2, two multiplies, two FMAs) and 19 per element
+    assert bench.valu_instr_per_element(16) == 99
+    assert bench.valu_instr_per_element(16, softplus=False, has_z=False) == 84
+
+
+def test_cold_cache_sets():
+    from mamba_selective_scan_amd.inputs import WORKLOADS, algorithmic_bytes
+    llc = bench.LLC_BYTES
+    for name, w in WORKLOADS.items():
+        nbytes = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, 4, final_state=True)
+        n = bench.cache_sets(nbytes)
+        if nbytes >= 3 * llc:
+            assert n == 1, name
+        else:
+            assert 8 <= n <= 256, name
+    # the 130m-layer shape (50.7 MB) rotates 16 sets, over 3x the cache
+    w = WORKLOADS["mamba130m_layer"]
+    nbytes = algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate, 4, final_state=True)
+    assert bench.cache_sets(nbytes) == 16 and 16 * nbytes >= 3 * llc
+
+
+def test_host_cpu_model():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
