@@ -80,7 +80,8 @@
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    never allocates, frees or retains caller memory and keeps no per-call
- *    state; it caches nothing but compiled kernels.
+ *    state; it caches nothing but compiled kernels and the device address of
+ *    the scratch array of mss_selective_scan_fwd_noalloc.
  *  - Tensors are described by element strides in LOGICAL index order:
  *    u / delta_raw / z / out as (b, d, t), B / C as (b, n, t), A_log as (d, n).
  *    For the scan forward, u, delta_raw, z and out must share a unit-stride
@@ -103,7 +104,9 @@
  *  - out and final_state must not overlap any input (the scan reads its inputs
  *    after it has started writing); the state of a state update is the only
  *    in/out buffer.
- *  - Thread-safe: concurrent calls on different streams are independent.
+ *  - Thread-safe: concurrent calls on different streams are independent,
+ *    except calls of mss_selective_scan_fwd_noalloc on one GPU (they share
+ *    its scratch array).
  */
 #ifndef MSS_H
 #define MSS_H
@@ -115,7 +118,7 @@
 extern "C" {
 #endif
 
-#define MSS_ABI_VERSION 3
+#define MSS_ABI_VERSION 4
 
 /* Chunk states: the state entering every MSS_STATE_CHUNK-step chunk of
  * logical time, fp32, laid out [ceil(L / MSS_STATE_CHUNK)][b][d][MSS_MAX_DSTATE]
@@ -126,6 +129,13 @@ extern "C" {
 #define MSS_STATE_CHUNK 16
 #define MSS_MAX_DSTATE 16
 #define MSS_MAX_CONV_WIDTH 4
+
+/* Device scratch that mss_selective_scan_fwd_noalloc holds per GPU (16 MiB):
+ * enough for the time-segment carries of any shape (at most 6.3 MB, for
+ * fewer than 16384 (batch, channel) pairs) together with its ragged-tail
+ * state hand-off, and for the hand-off alone of up to 262144 pairs (64 bytes
+ * each). */
+#define MSS_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum mss_status {
     MSS_OK = 0,
@@ -139,7 +149,9 @@ typedef enum mss_status {
     MSS_ERR_WORKSPACE_TOO_SMALL = 7,/* workspace_bytes below the required size         */
     MSS_ERR_ALIASING = 8,           /* an output overlaps an input                     */
     MSS_ERR_BAD_STRUCT = 9,         /* args is NULL or struct_size does not match      */
-    MSS_ERR_HIP = 10                /* the HIP runtime reported an error               */
+    MSS_ERR_HIP = 10,               /* the HIP runtime reported an error               */
+    MSS_ERR_SCRATCH_LIMIT = 11      /* mss_selective_scan_fwd_noalloc: the shape needs */
+                                    /* more than MSS_NOALLOC_SCRATCH_BYTES of scratch  */
 } mss_status;
 
 typedef enum mss_dtype {
@@ -344,6 +356,28 @@ size_t mss_selective_scan_workspace_size(const mss_scan_args *args, mss_status *
  * state between calls, and calls that share one workspace on different
  * streams race. */
 mss_status mss_selective_scan_fwd(const mss_scan_args *args, void *stream);
+
+/* Selective-scan forward that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code recorded under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * arguments, checks, kernels and results as mss_selective_scan_fwd, except:
+ *  - args->workspace must be NULL and args->workspace_bytes 0
+ *    (MSS_ERR_BAD_STRUCT otherwise);
+ *  - what the workspace would hold (the time-segment carries and the
+ *    ragged-tail state hand-off) lives in a device array of the library,
+ *    MSS_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held from the first
+ *    call on that GPU until the process ends.  A shape whose
+ *    mss_selective_scan_workspace_size exceeds it returns
+ *    MSS_ERR_SCRATCH_LIMIT, like every argument error before any HIP call;
+ *  - every call on one GPU uses that GPU's one array: calls that overlap in
+ *    time on one GPU (on different streams, or from several host threads)
+ *    race and give wrong results.  Order them on one stream.  Nothing in the
+ *    array has to start at zero: a call reads only what it wrote before;
+ *  - the first call on a GPU looks up the array's device address (a HIP
+ *    runtime query, no allocation), so record that call outside a graph
+ *    capture, or call once before capturing.
+ * No hipMalloc, hipFree or allocating library routine is ever called. */
+mss_status mss_selective_scan_fwd_noalloc(const mss_scan_args *args, void *stream);
 
 /* One-token state update (see the top of this file). */
 mss_status mss_selective_state_update(const mss_step_args *args, void *stream);

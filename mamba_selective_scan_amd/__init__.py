@@ -32,7 +32,7 @@ import ctypes
 from . import _lib
 from ._lib import MSS_MAX_DSTATE, MssError
 
-__all__ = ["selective_scan_fwd", "selective_state_update", "scan_workspace_size",
+__all__ = ["selective_scan_fwd", "selective_scan_fwd_noalloc", "selective_state_update", "scan_workspace_size",
            "causal_conv1d_fwd", "causal_conv1d_update", "selective_scan_bwd",
            "scan_bwd_workspace_size", "selective_scan", "MssError", "MSS_MAX_DSTATE",
            "library_path"]
@@ -166,7 +166,7 @@ def chunk_states_shape(u):
 def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
                        delta_softplus=True, initial_state=None, return_final_state=False,
                        out=None, final_state=None, workspace=None, reverse=False,
-                       return_chunk_states=False, chunk_states=None):
+                       return_chunk_states=False, chunk_states=None, _noalloc=False):
     """Selective-scan forward on u's device, ordered on torch's current stream.
 
     ``reverse=True`` runs the recurrence from the last step to the first (the
@@ -197,17 +197,38 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
     a.chunk_states = _ptr(chunk_states)
     if tuple(out.shape) != tuple(u.shape) or out.dtype != u.dtype or out.device != u.device:
         raise ValueError("out must match u in shape, dtype and device")
-    st = ctypes.c_int(0)
-    need = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
-    _lib.check(st.value)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
-    a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
-    _lib.check(lib.mss_selective_scan_fwd(ctypes.byref(a), _stream_handle(u.device)))
+    if _noalloc:
+        if workspace is not None:
+            raise ValueError("the no-allocation forward takes no workspace")
+        _lib.check(lib.mss_selective_scan_fwd_noalloc(ctypes.byref(a), _stream_handle(u.device)))
+    else:
+        st = ctypes.c_int(0)
+        need = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+        _lib.check(st.value)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+        _lib.check(lib.mss_selective_scan_fwd(ctypes.byref(a), _stream_handle(u.device)))
     res = (out,) + ((final_state,) if return_final_state else ()) + \
         ((chunk_states,) if return_chunk_states else ())
     return res if len(res) > 1 else out
+
+
+def selective_scan_fwd_noalloc(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, *,
+                               delta_softplus=True, initial_state=None, out=None,
+                               final_state=None, reverse=False, chunk_states=None):
+    """selective_scan_fwd through mss_selective_scan_fwd_noalloc: the library
+    allocates nothing and takes no workspace (its scratch is a per-GPU device
+    array of MSS_NOALLOC_SCRATCH_BYTES that all such calls on a GPU share, so
+    calls on one GPU must not overlap in time).  Without ``out`` this binding
+    allocates it from torch; pass ``out`` (and ``final_state`` /
+    ``chunk_states`` when wanted) for a call that allocates nothing at all.
+    Returns ``out``."""
+    return selective_scan_fwd(u, delta_raw, A_log, B, C, D, z, dt_bias,
+                              delta_softplus=delta_softplus, initial_state=initial_state,
+                              out=out, final_state=final_state, reverse=reverse,
+                              chunk_states=chunk_states, _noalloc=True)
 
 
 def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None, dt_bias=None, *,

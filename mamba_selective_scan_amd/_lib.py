@@ -13,10 +13,11 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmss.so")
 
-MSS_ABI_VERSION = 3
+MSS_ABI_VERSION = 4
 MSS_MAX_DSTATE = 16
 MSS_STATE_CHUNK = 16
 MSS_MAX_CONV_WIDTH = 4
+MSS_NOALLOC_SCRATCH_BYTES = 16 << 20
 MSS_F32 = 0
 MSS_BF16 = 1
 MSS_ACT_NONE = 0
@@ -34,13 +35,15 @@ STATUS = {
     8: "MSS_ERR_ALIASING",
     9: "MSS_ERR_BAD_STRUCT",
     10: "MSS_ERR_HIP",
+    11: "MSS_ERR_SCRATCH_LIMIT",
 }
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ("mss_abi_version", "mss_status_string", "mss_selective_scan_workspace_size",
            "mss_selective_scan_fwd", "mss_selective_state_update", "mss_causal_conv1d_fwd",
            "mss_causal_conv1d_update", "mss_selective_scan_bwd_workspace_size",
-           "mss_selective_scan_bwd", "mss_selective_scan_fwd_complex")
+           "mss_selective_scan_bwd", "mss_selective_scan_fwd_complex",
+           "mss_selective_scan_fwd_noalloc")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -221,6 +224,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_selective_scan_workspace_size.restype = ctypes.c_size_t
     lib.mss_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
     lib.mss_selective_scan_fwd.restype = ctypes.c_int
+    lib.mss_selective_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+    lib.mss_selective_scan_fwd_noalloc.restype = ctypes.c_int
     lib.mss_selective_state_update.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.mss_selective_state_update.restype = ctypes.c_int
     lib.mss_selective_scan_fwd_complex.argtypes = [ctypes.POINTER(ScanComplexArgs), _vp]

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "mss.h"
 #include "mss_internal.hpp"
@@ -227,37 +228,43 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
 constexpr int64_t kConvTargetWaves = 4096;
 constexpr int64_t kConvMinSeg = 64;
 
-}  // namespace
+// ---- device scratch of the no-allocation forward --------------------------
+// mss_selective_scan_fwd_noalloc keeps its time-segment carries and ragged-tail
+// hand-off in this array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy from the first call on it until the
+// process ends, and every call on that GPU shares it.  In host code `scratch`
+// only names the symbol: its device address comes from hipGetSymbolAddress,
+// once per device, and that address is what the kernels receive.
+constexpr size_t kScratchBytes = MSS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-extern "C" {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices] = {};
 
-int mss_abi_version(void) { return MSS_ABI_VERSION; }
-
-const char* mss_status_string(mss_status status) {
-  switch (status) {
-    case MSS_OK: return "ok";
-    case MSS_ERR_NULL_POINTER: return "a required pointer is NULL";
-    case MSS_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 1 and fit the grid; conv width 1..4)";
-    case MSS_ERR_BAD_STRIDE: return "invalid stride (negative, overlapping output, or a tile spans >= 2 GiB)";
-    case MSS_ERR_UNSUPPORTED_DTYPE: return "unsupported io dtype (expected MSS_F32 or MSS_BF16)";
-    case MSS_ERR_UNSUPPORTED_DSTATE: return "dstate must be between 1 and 16";
-    case MSS_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
-    case MSS_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or smaller than mss_selective_scan_workspace_size";
-    case MSS_ERR_ALIASING: return "an output overlaps an input";
-    case MSS_ERR_BAD_STRUCT: return "arguments struct is NULL, of the wrong size, or has reserved fields set";
-    case MSS_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
+// Device address of `scratch` on the device that `stream` belongs to.
+mss_status scratch_address(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return MSS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MSS_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MSS_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MSS_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return MSS_ERR_HIP;
+    g_scratch_addr[dev] = static_cast<char*>(ptr);
   }
-  return "unknown status";
+  *out = g_scratch_addr[dev];
+  return MSS_OK;
 }
 
-size_t mss_selective_scan_workspace_size(const mss_scan_args* a, mss_status* status) {
-  const mss_status st = check_shape(a);
-  if (status != nullptr) *status = st;
-  if (st != MSS_OK) return 0;
-  return make_plan(a).workspace;
-}
-
-mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
+// The scan forward.  noalloc: the workspace is this library's device array
+// `scratch` instead of the caller's (args->workspace must then be NULL).
+mss_status scan_fwd(const mss_scan_args* a, void* stream, bool noalloc) {
   mss_status st = check_shape(a);
   if (st != MSS_OK) return st;
   if (a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr || a->B == nullptr ||
@@ -309,7 +316,10 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
 
   const ScanPlan plan = make_plan(a);
   mss::ScanPtrs p{};
-  if (plan.workspace > 0) {
+  if (noalloc) {
+    if (a->workspace != nullptr || a->workspace_bytes != 0) return MSS_ERR_BAD_STRUCT;
+    if (plan.workspace > kScratchBytes) return MSS_ERR_SCRATCH_LIMIT;
+  } else if (plan.workspace > 0) {
     if (a->workspace == nullptr || a->workspace_bytes < plan.workspace)
       return MSS_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned(a->workspace, 256)) return MSS_ERR_MISALIGNED;
@@ -318,13 +328,6 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
     for (const Extent& e : ins)
       if (overlaps(ew, e)) return MSS_ERR_ALIASING;
     if (overlaps(ew, eo) || overlaps(ew, ef) || overlaps(ew, ecs)) return MSS_ERR_ALIASING;
-    char* ws = static_cast<char*>(a->workspace);
-    if (plan.agg_bytes > 0) {
-      p.agg = reinterpret_cast<float2*>(ws);
-      p.carry = reinterpret_cast<float*>(ws + plan.agg_bytes);
-    }
-    if (plan.tail_bytes > 0)
-      p.tail_h0 = reinterpret_cast<float*>(ws + plan.agg_bytes + plan.carry_bytes);
   }
   mss::ScanShape s = plan.shape;
   // A dimension of size 1 is never stepped, so its stride is free: use 1.
@@ -386,12 +389,68 @@ mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
   // that is not a whole number of vectors gets an element-wise tail pass.
   s.use_vec = s.vec_ok && (xt || a->dim % V == 0) && (bt || a->dstate % V == 0);
   if (s.use_vec && (xt || bt)) s.t_stop = static_cast<int>(a->seqlen / V * V);
+  if (s.use_vec) s.nseg = std::max(1, (s.t_stop + s.seg_len - 1) / s.seg_len);
+  // Every argument check has passed: the first HIP call of this entry point
+  // may come next (the scratch array's address, once per device).
+  if (plan.workspace > 0) {
+    char* ws = static_cast<char*>(a->workspace);
+    if (noalloc) {
+      const mss_status sst = scratch_address(static_cast<hipStream_t>(stream), &ws);
+      if (sst != MSS_OK) return sst;
+    }
+    if (plan.agg_bytes > 0) {
+      p.agg = reinterpret_cast<float2*>(ws);
+      p.carry = reinterpret_cast<float*>(ws + plan.agg_bytes);
+    }
+    if (plan.tail_bytes > 0)
+      p.tail_h0 = reinterpret_cast<float*>(ws + plan.agg_bytes + plan.carry_bytes);
+  }
   if (s.use_vec && s.t_stop < s.seqlen && s.t_stop > 0 && p.tail_h0 == nullptr)
     return MSS_ERR_WORKSPACE_TOO_SMALL;  // unreachable: the plan reserves it
-  if (s.use_vec) s.nseg = std::max(1, (s.t_stop + s.seg_len - 1) / s.seg_len);
   const hipError_t e = mss::launch_scan(s, p, a->io_dtype == MSS_BF16, xt, bt,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mss_abi_version(void) { return MSS_ABI_VERSION; }
+
+const char* mss_status_string(mss_status status) {
+  switch (status) {
+    case MSS_OK: return "ok";
+    case MSS_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MSS_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 1 and fit the grid; conv width 1..4)";
+    case MSS_ERR_BAD_STRIDE: return "invalid stride (negative, overlapping output, or a tile spans >= 2 GiB)";
+    case MSS_ERR_UNSUPPORTED_DTYPE: return "unsupported io dtype (expected MSS_F32 or MSS_BF16)";
+    case MSS_ERR_UNSUPPORTED_DSTATE: return "dstate must be between 1 and 16";
+    case MSS_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
+    case MSS_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or smaller than mss_selective_scan_workspace_size";
+    case MSS_ERR_ALIASING: return "an output overlaps an input";
+    case MSS_ERR_BAD_STRUCT: return "arguments struct is NULL, of the wrong size, or has reserved fields set";
+    case MSS_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
+    case MSS_ERR_SCRATCH_LIMIT:
+      return "the shape needs more device scratch than the no-allocation forward holds "
+             "(MSS_NOALLOC_SCRATCH_BYTES); use mss_selective_scan_fwd with a workspace";
+  }
+  return "unknown status";
+}
+
+size_t mss_selective_scan_workspace_size(const mss_scan_args* a, mss_status* status) {
+  const mss_status st = check_shape(a);
+  if (status != nullptr) *status = st;
+  if (st != MSS_OK) return 0;
+  return make_plan(a).workspace;
+}
+
+mss_status mss_selective_scan_fwd(const mss_scan_args* a, void* stream) {
+  return scan_fwd(a, stream, /*noalloc=*/false);
+}
+
+mss_status mss_selective_scan_fwd_noalloc(const mss_scan_args* a, void* stream) {
+  return scan_fwd(a, stream, /*noalloc=*/true);
 }
 
 mss_status mss_selective_state_update(const mss_step_args* a, void* stream) {

@@ -196,6 +196,59 @@ def test_scan_workspace_checks():
     assert call_scan(a) == code("MSS_ERR_ALIASING")
 
 
+def call_scan_noalloc(a):
+    return _lib.lib().mss_selective_scan_fwd_noalloc(ctypes.byref(a) if a is not None else None,
+                                                     None)
+
+
+NOALLOC_CASES = {k: v for k, v in SCAN_CASES.items() if k != "no_workspace"}
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+@pytest.mark.parametrize("case", sorted(NOALLOC_CASES))
+def test_scan_noalloc_argument_checks(case):
+    """The no-allocation forward runs every check of the forward, before any
+    HIP call (including the scratch-address lookup)."""
+    fn, expect = NOALLOC_CASES[case]
+    a = None if fn is None else _mut_scan(fn)
+    assert call_scan_noalloc(a) == code(expect)
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+def test_scan_noalloc_workspace_and_scratch_limit():
+    # a workspace passed to the no-allocation entry point is a usage error
+    a = scan_args(ws=True)
+    assert call_scan_noalloc(a) == code("MSS_ERR_BAD_STRUCT")
+    a = scan_args(ws=False)
+    a.workspace_bytes = 64
+    assert call_scan_noalloc(a) == code("MSS_ERR_BAD_STRUCT")
+    # a ragged length over more channels than the scratch holds a state
+    # hand-off for: rejected before any HIP call
+    dim = _lib.MSS_NOALLOC_SCRATCH_BYTES // (16 * 4) + 8
+    a = scan_args(batch=1, dim=dim, seqlen=3, ws=False)
+    st = ctypes.c_int(-1)
+    need = _lib.lib().mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    assert st.value == 0 and need > _lib.MSS_NOALLOC_SCRATCH_BYTES
+    assert call_scan_noalloc(a) == code("MSS_ERR_SCRATCH_LIMIT")
+
+
+def test_noalloc_scratch_covers_every_segmented_shape():
+    """Time segments are planned only below 2048 channel tiles (16384
+    channels): their carries, plus a ragged-tail hand-off, fit the scratch for
+    every such shape (the worst cases of the segment count are swept)."""
+    lib = _lib.lib()
+    st = ctypes.c_int(-1)
+    worst = 0
+    for channels in (8, 64, 256, 1024, 1536, 4096, 16376):
+        for seqlen in (3, 4097, 65539, 1 << 20, (1 << 30) - 1):
+            a = _lib.new_scan_args()
+            a.batch, a.dim, a.seqlen, a.dstate = 1, channels, seqlen, 16
+            n = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+            assert st.value == 0
+            worst = max(worst, n)
+    assert 0 < worst <= _lib.MSS_NOALLOC_SCRATCH_BYTES
+
+
 def step_args():
     a = _lib.new_step_args()
     a.io_dtype = _lib.MSS_F32
