@@ -73,12 +73,11 @@ __device__ static inline float silu(float z) {
   return z * __builtin_amdgcn_rcpf(den);
 }
 
-// Sum over the eight state groups of one channel (lanes c + 8g) of four
-// per-step partial sums.  The two swap-and-add levels sum over lane bits 5 and
-// 4 and leave step {0, 2, 1, 3}[row] in 16-lane row `row`; a DPP rotation by 8
-// within the row adds lane bit 3.  Both lanes c and c + 8 of a row end with
-// the same total.
-__device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
+// Sum over four of the eight state groups of one channel (lanes c + 8g) of
+// four per-step partial sums.  The two swap-and-add levels sum over lane bits
+// 5 and 4 and leave step {0, 2, 1, 3}[row] in 16-lane row `row`: lane c + 8h
+// of the row holds the sum over the groups g with g % 2 == h.
+__device__ inline float reduce_groups_half(float y0, float y1, float y2, float y3) {
   const auto s01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y0), __float_as_uint(y1),
                                                     false, false);
   const auto s23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y2), __float_as_uint(y3),
@@ -87,7 +86,13 @@ __device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
   const float p23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
   const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(p01), __float_as_uint(p23),
                                                   false, false);
-  const float w = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// The same over all eight groups: a DPP rotation by 8 within the row adds the
+// two halves, so lanes c and c + 8 of a row end with the same total.
+__device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
+  const float w = reduce_groups_half(y0, y1, y2, y3);
   // row_ror:8 -- lane i of a row reads lane (i + 8) mod 16
   return w + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(w), 0x128, 0xF, 0xF,
                                                         false));

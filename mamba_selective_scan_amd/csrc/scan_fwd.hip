@@ -25,10 +25,12 @@
 //   S  per step and state one exp2, two multiplies and two FMAs, all on plain
 //      VGPR operands: each lane reads the B and C of its two states from LDS
 //      four steps at a time.  The partial sums C.h of the eight state groups
-//      of a channel meet through v_permlane32_swap, v_permlane16_swap and one
-//      DPP row rotation; two swap-and-add levels reduce four steps at once;
-//   O  the totals go through LDS back to the load layout, where the skip term
-//      and the gate are applied and the output is stored.
+//      of a channel meet through v_permlane32_swap and v_permlane16_swap:
+//      two swap-and-add levels reduce four steps at once to two half sums
+//      (over the groups of each parity);
+//   O  the half sums go through LDS back to the load layout, where they are
+//      added, the skip term and the gate are applied and the output is
+//      stored.
 // For t-fast data every phase is wave-local: there is no workgroup barrier,
 // so waves drift apart and memory waits of one wave overlap the recurrence
 // of others.  The d-fast vector path exchanges its loads and stores between
@@ -544,27 +546,53 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   const float* p_c0 = s_bc + (AGG ? 0 : (kMaxState + 2 * sg) * kT);
   const float* p_dd = s_dd + sc * kDdPitch;
   // The group reduction leaves step {0, 2, 1, 3}[row] of each block in row
-  // `row` = lane / 16.  The total of step t replaces delta_t in s_dd: the
-  // block has read it, and later blocks read other steps.
+  // `row` = lane / 16, as two sums over four state groups each: lane c + 8h
+  // of the row holds the sum over the groups of parity h.  The two sums of
+  // step t replace (delta_t, delta_t * u_t) in s_dd -- the block has read
+  // them, and later blocks read other steps -- and the output phase adds
+  // them (the same sum, in the same order, as a cross-lane add here).
   const int row = lane >> 4;
   const int y_step = row == 1 ? 2 : (row == 2 ? 1 : row);
-  float* p_y = s_dd + sc * kDdPitch + 2 * y_step;
+  float* p_y = s_dd + sc * kDdPitch + 2 * y_step + ((lane >> 3) & 1);
 
   // Chunk states (main pass only): the state entering logical step t when t
   // is a multiple of kStateChunk, written by the lane for its two states.
+  // Vector passes start every chunk on a multiple of kT, so only the blocks
+  // at t4 = 0 and t4 = kStateChunk can record, and there the record is one
+  // buffer store whose offset falls outside the range when the state is not
+  // wanted: no branch in the block, so the next block's LDS reads can be
+  // issued ahead.
   const int64_t cs_row = static_cast<int64_t>(b) * s.dim + d;
   const int64_t cs_plane = static_cast<int64_t>(s.batch) * s.dim;
-  auto record_state = [&](int t) __attribute__((always_inline)) {
-    if (!AGG && chunk_states != nullptr && (t & (kStateChunk - 1)) == 0 && t < t_end && dvalid)
-      *reinterpret_cast<float2*>(chunk_states +
-                                 ((t / kStateChunk) * cs_plane + cs_row) * kMaxState +
-                                 sg * kStatesPerLane) = make_float2(h[0], h[1]);
+  const bool has_cs = !AGG && chunk_states != nullptr;
+  const uint32_t cs_off = static_cast<uint32_t>((sc * kMaxState + sg * kStatesPerLane) * 4);
+  auto record_state = [&](int t, int t4) __attribute__((always_inline)) {
+    if constexpr (AGG) {
+      return;
+    } else if constexpr (VEC) {
+      static_assert(kT % kStateChunk == 0, "chunks start on chunk-state boundaries");
+      if (t4 % kStateChunk != 0) return;
+      const int64_t tile0 =
+          (static_cast<int64_t>(t / kStateChunk) * cs_plane + static_cast<int64_t>(b) * s.dim +
+           d0) * kMaxState;
+      void* base = has_cs ? static_cast<void*>(chunk_states + tile0) : static_cast<void*>(out);
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, has_cs ? kRsrcRange : 0,
+                                                        kRsrcFlags);
+      const u32x2 w = {__float_as_uint(h[0]), __float_as_uint(h[1])};
+      __builtin_amdgcn_raw_buffer_store_b64(w, rs, (dvalid && t < t_end) ? cs_off : kOffNone, 0,
+                                            0);
+    } else {
+      if (has_cs && (t & (kStateChunk - 1)) == 0 && t < t_end && dvalid)
+        *reinterpret_cast<float2*>(chunk_states +
+                                   ((t / kStateChunk) * cs_plane + cs_row) * kMaxState +
+                                   sg * kStatesPerLane) = make_float2(h[0], h[1]);
+    }
   };
 
   // One block of 4 steps: the scan of this lane's two states and, outside
   // the AGG pass, one state-group reduction of C.h.
   auto scan_block = [&](int t4, int t0, int nb) __attribute__((always_inline)) {
-    record_state(t0 + t4);
+    record_state(t0 + t4, t4);
     const int col = (((t4 >> 2) ^ sg) & 7) << 2;
     const float* pb = p_b0 + nb * kBcSize;
     const float* pd = p_dd + nb * kWg * kDdSize;
@@ -596,7 +624,7 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
         y[k] = fmaf(cs1[k], h[1], cs0[k] * h[0]);
       }
-      p_y[nb * kWg * kDdSize + 2 * t4] = reduce_groups(y[0], y[1], y[2], y[3]);
+      p_y[nb * kWg * kDdSize + 2 * t4] = reduce_groups_half(y[0], y[1], y[2], y[3]);
     }
   };
   // The main pass unrolls the blocks: the swizzled B/C offsets become
@@ -619,13 +647,16 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         const float* p = s_dd + xa * kDdPitch + 8 * xb;
         const f4 v0 = lds_f4(p), v1 = lds_f4(p + 4);
         const f4 sk = lds_f4(s_skip + xa * kSkipPitch + 4 * xb);
-        y[0] = v0.x + sk.x;
-        y[1] = v0.z + sk.y;
-        y[2] = v1.x + sk.z;
-        y[3] = v1.z + sk.w;
+        y[0] = (v0.x + v0.y) + sk.x;
+        y[1] = (v0.z + v0.w) + sk.y;
+        y[2] = (v1.x + v1.y) + sk.z;
+        y[3] = (v1.z + v1.w) + sk.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) y[j] = *e_dd(nb, j) + (COOP ? skr[j] : *e_sk(nb, j));
+        for (int j = 0; j < kPerThread; ++j) {
+          const float2 pair = *reinterpret_cast<const float2*>(e_dd(nb, j));
+          y[j] = (pair.x + pair.y) + (COOP ? skr[j] : *e_sk(nb, j));
+        }
       }
       if (has_z) {
 #pragma unroll

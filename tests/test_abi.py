@@ -162,6 +162,10 @@ SCAN_CASES = {
     "out_overlap": (lambda a: a.out_stride.__setitem__(1, 0), "MSS_ERR_BAD_STRIDE"),
     "tile_2gib": (lambda a: a.u_stride.__setitem__(1, 1 << 27), "MSS_ERR_BAD_STRIDE"),
     "misaligned_u": (lambda a: setattr(a, "u", fake(0) + 2), "MSS_ERR_MISALIGNED"),
+    # bf16 elements must be 2-byte aligned (a 4-byte misaligned bf16 view is
+    # legal and runs the element-wise instantiation; see the GPU parity tests)
+    "misaligned_bf16": (lambda a: (setattr(a, "io_dtype", _lib.MSS_BF16),
+                                   setattr(a, "B", fake(3) + 1)), "MSS_ERR_MISALIGNED"),
     "misaligned_final": (lambda a: setattr(a, "final_state", fake(9) + 1), "MSS_ERR_MISALIGNED"),
     "out_is_u": (lambda a: setattr(a, "out", fake(0)), "MSS_ERR_ALIASING"),
     "final_in_z": (lambda a: setattr(a, "final_state", fake(6) + 64), "MSS_ERR_ALIASING"),

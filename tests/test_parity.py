@@ -176,6 +176,63 @@ def test_views_into_padded_buffers(mss, layout):
     check(f"padded views {layout} final", to_np(fin), ref_fin, 1e-4)
 
 
+def _run_pair(mss, a, b):
+    """Run the forward on two argument dicts; both results, synchronised."""
+    import torch
+    ra = mss.selective_scan_fwd(a["u"], a["delta_raw"], a["A_log"], a["B"], a["C"], D=a["D"],
+                                z=a["z"], dt_bias=a["dt_bias"], return_final_state=True)
+    rb = mss.selective_scan_fwd(b["u"], b["delta_raw"], b["A_log"], b["B"], b["C"], D=b["D"],
+                                z=b["z"], dt_bias=b["dt_bias"], return_final_state=True)
+    torch.cuda.synchronize()
+    return ra, rb
+
+
+def _odd_pitch(t):
+    """The same [B, X, L] values as a view into a buffer one step wider (the
+    row pitch becomes odd)."""
+    import torch
+    wide = torch.zeros(t.shape[0], t.shape[1], t.shape[2] + 1, dtype=t.dtype, device=t.device)
+    wide[:, :, :t.shape[2]] = t
+    return wide[:, :, :t.shape[2]]
+
+
+@pytest.mark.parametrize("case", ["bf16_odd_pitch", "channel_last_dim102", "nfast_bc_dstate5"])
+def test_elementwise_equals_vector_path(mss, case):
+    """Layouts whose 4-element vectors are not whole run the element-wise
+    instantiation of the same kernel: the result is bit for bit the vector
+    path's on the same values."""
+    import torch
+    note(f"element-wise vs vector path: {case}")
+    if case == "bf16_odd_pitch":
+        # bf16 rows of odd pitch: 8-byte vectors would not be 4-byte aligned
+        dx = to_torch(generate(2, 96, 1000, 16, seed=31), device(), "bf16")
+        ev = dict(dx)
+        for k in ("u", "delta_raw", "z", "B", "C"):
+            ev[k] = _odd_pitch(dx[k])
+        assert ev["u"].stride(1) % 2 == 1
+        (out_v, fin_v), (out_e, fin_e) = _run_pair(mss, dx, ev)
+    elif case == "channel_last_dim102":
+        # 104 channels take the vector path, 102 (not a whole number of
+        # 4-channel vectors) the element-wise one; the first 102 channels must
+        # agree (the same 13 channel tiles, the same time segments)
+        big = to_torch(generate(1, 104, 3000, 16, "bld", seed=32), device(), "f32")
+        small = {k: (v[:, :102] if k in ("u", "delta_raw", "z") else
+                     v[:102] if k in ("A_log", "D", "dt_bias") else v) for k, v in big.items()}
+        (out_v, fin_v), (out_e, fin_e) = _run_pair(mss, big, small)
+        out_v, fin_v = out_v[:, :102], fin_v[:, :102]
+    else:
+        # dstate 5 with B, C stored [B, L, N] (n-fast, not whole vectors of
+        # states) against the same values stored [B, N, L]
+        dx = to_torch(generate(2, 80, 700, 5, seed=33), device(), "f32")
+        nf = dict(dx)
+        for k in ("B", "C"):
+            nf[k] = dx[k].transpose(1, 2).contiguous().transpose(1, 2)
+        assert nf["B"].stride(1) == 1
+        (out_v, fin_v), (out_e, fin_e) = _run_pair(mss, dx, nf)
+    assert torch.equal(out_v, out_e), "outputs differ"
+    assert torch.equal(fin_v, fin_e), "final states differ"
+
+
 def test_no_unit_stride_axis_is_rejected(mss):
     import torch
     from mamba_selective_scan_amd import MssError
@@ -216,7 +273,10 @@ def test_softplus_upper_range(mss, io, big_bias, layout):
 
 # ------------------------------------------------------------ full workloads
 
-def _sampled_workload(mss, wname, io, k, seed=0):
+def _sampled_workload(mss, wname, io, k, seed=0, whole_row=None):
+    """The full workload on the GPU in the launch configuration bench.py
+    times; the oracle on k sampled channels (whole sequences), and with
+    ``whole_row`` on every channel of that batch row as well."""
     import torch
     w = WORKLOADS[wname]
     note(f"{wname} {io}: generating inputs")
@@ -233,14 +293,21 @@ def _sampled_workload(mss, wname, io, k, seed=0):
     tol = tol_for(io)
     check(f"{wname} {io} out (sampled)", got_out, ref_out, tol)
     check(f"{wname} {io} final (sampled)", got_fin, ref_fin, tol)
+    if whole_row is not None:
+        b = whole_row
+        note(f"{wname} {io}: oracle on all {w.dim} channels of batch row {b}")
+        row = [(b, d) for d in range(w.dim)]
+        ref_out, ref_fin = oracle.scan_channels(dx, row)
+        check(f"{wname} {io} out (row {b}, every channel)", to_np(out[b]), ref_out, tol)
+        check(f"{wname} {io} final (row {b}, every channel)", to_np(fin[b]), ref_fin, tol)
 
 
 def test_mamba2p8b_layer_fp32_sampled(mss):
-    _sampled_workload(mss, "mamba2p8b_layer", "f32", 96)
+    _sampled_workload(mss, "mamba2p8b_layer", "f32", 96, whole_row=5)
 
 
 def test_mamba2p8b_layer_bf16_sampled(mss):
-    _sampled_workload(mss, "mamba2p8b_layer", "bf16", 96)
+    _sampled_workload(mss, "mamba2p8b_layer", "bf16", 96, whole_row=3)
 
 
 def test_audio_channel_last_sampled(mss):
