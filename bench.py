@@ -75,7 +75,8 @@ KERNEL_SOURCES = {
                "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
     "scan_complex": ["mamba_selective_scan_amd/csrc/scan_cplx.hip",
                      "mamba_selective_scan_amd/csrc/mss_device.hpp",
-                     "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
+                     "mamba_selective_scan_amd/csrc/mss_internal.hpp",
+                     "mamba_selective_scan_amd/csrc/mss_cplx.hpp"],
     "scan_bwd": ["mamba_selective_scan_amd/csrc/scan_bwd.hip",
                  "mamba_selective_scan_amd/csrc/mss_device.hpp",
                  "mamba_selective_scan_amd/csrc/mss_internal.hpp"],
@@ -401,6 +402,7 @@ def main_conv(args):
         conv()
         if not args.no_step:
             decode()
+    settle(conv, args.settle_seconds)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -524,6 +526,7 @@ def main_bwd(args):
 
     for _ in range(args.warmup):
         bwd()
+    settle(bwd, args.settle_seconds)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -751,14 +754,18 @@ def main_complex(args):
     dx = complex_to_torch(x, dev)
     out = torch.empty_like(dx["u"])
     fin = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.complex64, device=dev)
+    ws = torch.empty(max(mss.scan_complex_workspace_size(dx["u"], dx["A_log"]), 1),
+                     dtype=torch.uint8, device=dev)
 
     def run():
         mss.selective_scan_fwd_complex(dx["u"], dx["delta_raw"], dx["A_log"], dx["A_imag"],
                                        dx["B"], dx["C"], D=dx["D"], z=dx["z"],
-                                       dt_bias=dx["dt_bias"], out=out, final_state=fin)
+                                       dt_bias=dx["dt_bias"], out=out, final_state=fin,
+                                       workspace=ws)
 
     for _ in range(args.warmup):
         run()
+    settle(run, args.settle_seconds)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

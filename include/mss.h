@@ -118,7 +118,7 @@
 extern "C" {
 #endif
 
-#define MSS_ABI_VERSION 4
+#define MSS_ABI_VERSION 5
 
 /* Chunk states: the state entering every MSS_STATE_CHUNK-step chunk of
  * logical time, fp32, laid out [ceil(L / MSS_STATE_CHUNK)][b][d][MSS_MAX_DSTATE]
@@ -418,11 +418,23 @@ typedef struct mss_scan_complex_args {
 
     int32_t delta_softplus;      /* nonzero: delta = softplus(delta_raw + dt_bias)       */
     int32_t reserved1;           /* must be 0                                            */
+
+    void *workspace;             /* device scratch, 256-byte aligned, of at least        */
+    size_t workspace_bytes;      /* mss_selective_scan_fwd_complex_workspace_size bytes  */
+                                 /* (may be 0)                                           */
 } mss_scan_complex_args;
 
+/* Bytes of device workspace mss_selective_scan_fwd_complex needs.  It is 0
+ * unless the shape has few channels (fewer than 512 tiles of 16) and is cut
+ * into time segments, whose complex state carries it holds.  Depends only on
+ * the shapes.  Returns 0 and sets *status (if non-NULL) on invalid shapes. */
+size_t mss_selective_scan_fwd_complex_workspace_size(const mss_scan_complex_args *args,
+                                                     mss_status *status);
+
 /* Selective-scan forward with complex A (operation 6 at the top of this
- * file).  The same checks and errors as mss_selective_scan_fwd; no workspace.
- * out and final_state must not overlap any input or each other. */
+ * file).  The same checks and errors as mss_selective_scan_fwd, and the same
+ * workspace rules.  out and final_state must not overlap any input or each
+ * other. */
 mss_status mss_selective_scan_fwd_complex(const mss_scan_complex_args *args, void *stream);
 
 /* Bytes of device workspace mss_selective_scan_bwd needs: the states entering

@@ -34,7 +34,8 @@ from ._lib import MSS_MAX_DSTATE, MssError
 
 __all__ = ["selective_scan_fwd", "selective_scan_fwd_noalloc", "selective_state_update", "scan_workspace_size",
            "causal_conv1d_fwd", "causal_conv1d_update", "selective_scan_bwd",
-           "scan_bwd_workspace_size", "selective_scan", "MssError", "MSS_MAX_DSTATE",
+           "scan_bwd_workspace_size", "selective_scan", "selective_scan_fwd_complex",
+           "scan_complex_workspace_size", "MssError", "MSS_MAX_DSTATE",
            "library_path"]
 
 
@@ -231,9 +232,22 @@ def selective_scan_fwd_noalloc(u, delta_raw, A_log, B, C, D=None, z=None, dt_bia
                               chunk_states=chunk_states, _noalloc=True)
 
 
+def scan_complex_workspace_size(u, A_log) -> int:
+    """Workspace bytes selective_scan_fwd_complex needs for u [B, D, L] and
+    A_log [D, N] (0 unless the shape is cut into time segments)."""
+    a = _lib.new_scan_complex_args()
+    a.batch, a.dim, a.seqlen = u.shape
+    a.dstate = A_log.shape[1]
+    st = ctypes.c_int(0)
+    n = _lib.lib().mss_selective_scan_fwd_complex_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    _lib.check(st.value)
+    return int(n)
+
+
 def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None, dt_bias=None, *,
                                delta_softplus=True, initial_state=None,
-                               return_final_state=False, out=None, final_state=None):
+                               return_final_state=False, out=None, final_state=None,
+                               workspace=None):
     """Selective-scan forward with complex A = -exp(A_log) + i A_imag, ordered on
     torch's current stream.
 
@@ -241,6 +255,8 @@ def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None
     complex64 [B, N, L] (any strides); initial_state, final_state: complex64
     [B, D, N] contiguous.  Returns ``out`` (fp32, the real part of C . h plus
     D u, gated), or ``(out, final_state)`` when ``return_final_state``.
+    ``workspace`` (uint8, at least scan_complex_workspace_size bytes) may be
+    supplied to avoid its allocation.
     """
     torch = _torch()
     lib = _lib.lib()
@@ -291,6 +307,14 @@ def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None
     a.out, a.out_stride = _ptr(out), _strides(out, 3)
     a.final_state = _ptr(final_state)
     a.delta_softplus = 1 if delta_softplus else 0
+    st = ctypes.c_int(0)
+    need = lib.mss_selective_scan_fwd_complex_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    _lib.check(st.value)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.mss_selective_scan_fwd_complex(ctypes.byref(a), _stream_handle(dev)))
     return (out, final_state) if return_final_state else out
 

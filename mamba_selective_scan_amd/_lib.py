@@ -13,7 +13,7 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmss.so")
 
-MSS_ABI_VERSION = 4
+MSS_ABI_VERSION = 5
 MSS_MAX_DSTATE = 16
 MSS_STATE_CHUNK = 16
 MSS_MAX_CONV_WIDTH = 4
@@ -43,7 +43,7 @@ EXPORTS = ("mss_abi_version", "mss_status_string", "mss_selective_scan_workspace
            "mss_selective_scan_fwd", "mss_selective_state_update", "mss_causal_conv1d_fwd",
            "mss_causal_conv1d_update", "mss_selective_scan_bwd_workspace_size",
            "mss_selective_scan_bwd", "mss_selective_scan_fwd_complex",
-           "mss_selective_scan_fwd_noalloc")
+           "mss_selective_scan_fwd_noalloc", "mss_selective_scan_fwd_complex_workspace_size")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -187,6 +187,7 @@ class ScanComplexArgs(ctypes.Structure):
         ("out", _vp), ("out_stride", _i64 * 3),
         ("final_state", _vp),
         ("delta_softplus", _i32), ("reserved1", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -230,6 +231,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mss_selective_state_update.restype = ctypes.c_int
     lib.mss_selective_scan_fwd_complex.argtypes = [ctypes.POINTER(ScanComplexArgs), _vp]
     lib.mss_selective_scan_fwd_complex.restype = ctypes.c_int
+    lib.mss_selective_scan_fwd_complex_workspace_size.argtypes = [
+        ctypes.POINTER(ScanComplexArgs), ctypes.POINTER(ctypes.c_int)]
+    lib.mss_selective_scan_fwd_complex_workspace_size.restype = ctypes.c_size_t
     lib.mss_selective_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs),
                                                           ctypes.POINTER(ctypes.c_int)]
     lib.mss_selective_scan_bwd_workspace_size.restype = ctypes.c_size_t

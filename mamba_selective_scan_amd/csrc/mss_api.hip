@@ -11,6 +11,7 @@
 
 #include "mss.h"
 #include "mss_internal.hpp"
+#include "mss_cplx.hpp"
 
 namespace {
 
@@ -227,6 +228,55 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
 // holds about this many waves.
 constexpr int64_t kConvTargetWaves = 4096;
 constexpr int64_t kConvMinSeg = 64;
+
+// Complex-A forward: shapes with fewer channel tiles (16 channels each) than
+// kCxSplitBelow are cut into time segments, as many as bring the grid to about
+// kCxTargetWgs workgroups (four 4-wave workgroups per CU).
+constexpr int64_t kCxSplitBelow = 512;
+constexpr int64_t kCxTargetWgs = 1024;
+
+mss_status check_cplx_shape(const mss_scan_complex_args* a) {
+  if (a == nullptr || a->struct_size != sizeof(mss_scan_complex_args) || a->reserved0 != 0 ||
+      a->reserved1 != 0)
+    return MSS_ERR_BAD_STRUCT;
+  if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->batch > kMaxDim || a->dim > kMaxDim ||
+      a->seqlen > kMaxSeqlen || a->batch * a->dim > kMaxDim)
+    return MSS_ERR_BAD_SHAPE;
+  if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
+  const int64_t tiles = (a->dim + mss::kCxCh - 1) / mss::kCxCh;
+  if (a->batch * tiles > 0x7FFFFFFFll) return MSS_ERR_BAD_SHAPE;
+  return MSS_OK;
+}
+
+struct CplxPlan {
+  mss::CplxShape shape;
+  size_t agg_bytes = 0, carry_bytes = 0, workspace = 0;
+};
+
+CplxPlan make_cplx_plan(const mss_scan_complex_args* a) {
+  CplxPlan p;
+  mss::CplxShape& s = p.shape;
+  s.batch = static_cast<int>(a->batch);
+  s.dim = static_cast<int>(a->dim);
+  s.seqlen = static_cast<int>(a->seqlen);
+  s.dstate = static_cast<int>(a->dstate);
+  s.softplus = a->delta_softplus ? 1 : 0;
+  s.tiles = static_cast<int>((a->dim + mss::kCxCh - 1) / mss::kCxCh);
+  const int64_t total = a->batch * s.tiles;
+  const int64_t chunks = (a->seqlen + mss::kCxT - 1) / mss::kCxT;
+  int64_t nseg = 1;
+  if (total < kCxSplitBelow) nseg = std::max<int64_t>(1, std::min<int64_t>(kCxTargetWgs / total, chunks));
+  const int64_t seg_chunks = (chunks + nseg - 1) / nseg;
+  s.seg_len = static_cast<int>(seg_chunks * mss::kCxT);
+  s.nseg = static_cast<int>((a->seqlen + s.seg_len - 1) / s.seg_len);
+  s.nchan_pad = total * mss::kCxCh;
+  if (s.nseg > 1) {
+    p.agg_bytes = round_up(static_cast<size_t>(s.nseg - 1) * s.nchan_pad * kMaxState * sizeof(float4), 256);
+    p.carry_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float2), 256);
+  }
+  p.workspace = p.agg_bytes + p.carry_bytes;
+  return p;
+}
 
 // ---- device scratch of the no-allocation forward --------------------------
 // mss_selective_scan_fwd_noalloc keeps its time-segment carries and ragged-tail
@@ -693,16 +743,17 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
 }
 
+size_t mss_selective_scan_fwd_complex_workspace_size(const mss_scan_complex_args* a,
+                                                     mss_status* status) {
+  const mss_status st = check_cplx_shape(a);
+  if (status != nullptr) *status = st;
+  if (st != MSS_OK) return 0;
+  return make_cplx_plan(a).workspace;
+}
+
 mss_status mss_selective_scan_fwd_complex(const mss_scan_complex_args* a, void* stream) {
-  if (a == nullptr || a->struct_size != sizeof(mss_scan_complex_args) || a->reserved0 != 0 ||
-      a->reserved1 != 0)
-    return MSS_ERR_BAD_STRUCT;
-  if (a->batch < 1 || a->dim < 1 || a->seqlen < 1 || a->batch > kMaxDim || a->dim > kMaxDim ||
-      a->seqlen > kMaxSeqlen || a->batch * a->dim > kMaxDim)
-    return MSS_ERR_BAD_SHAPE;
-  if (a->dstate < 1 || a->dstate > MSS_MAX_DSTATE) return MSS_ERR_UNSUPPORTED_DSTATE;
-  const int64_t tiles = (a->dim + mss::kCxCh - 1) / mss::kCxCh;
-  if (a->batch * tiles > 0xFFFFFFFFll) return MSS_ERR_BAD_SHAPE;
+  const mss_status sst = check_cplx_shape(a);
+  if (sst != MSS_OK) return sst;
   if (a->u == nullptr || a->delta_raw == nullptr || a->A_log == nullptr || a->A_imag == nullptr ||
       a->B == nullptr || a->C == nullptr || a->out == nullptr)
     return MSS_ERR_NULL_POINTER;
@@ -741,14 +792,19 @@ mss_status mss_selective_scan_fwd_complex(const mss_scan_complex_args* a, void* 
   for (const Extent& e : ins)
     if (overlaps(eo, e) || overlaps(ef, e)) return MSS_ERR_ALIASING;
   if (overlaps(eo, ef)) return MSS_ERR_ALIASING;
+  const CplxPlan plan = make_cplx_plan(a);
+  if (plan.workspace > 0) {
+    if (a->workspace == nullptr || a->workspace_bytes < plan.workspace)
+      return MSS_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(a->workspace, 256)) return MSS_ERR_MISALIGNED;
+    const Extent ew{reinterpret_cast<uintptr_t>(a->workspace),
+                    reinterpret_cast<uintptr_t>(a->workspace) + plan.workspace, true};
+    for (const Extent& e : ins)
+      if (overlaps(ew, e)) return MSS_ERR_ALIASING;
+    if (overlaps(ew, eo) || overlaps(ew, ef)) return MSS_ERR_ALIASING;
+  }
 
-  mss::CplxShape s{};
-  s.batch = static_cast<int>(a->batch);
-  s.dim = static_cast<int>(a->dim);
-  s.seqlen = static_cast<int>(a->seqlen);
-  s.dstate = static_cast<int>(a->dstate);
-  s.softplus = a->delta_softplus ? 1 : 0;
-  s.tiles = static_cast<int>(tiles);
+  mss::CplxShape s = plan.shape;
   std::memcpy(s.su, a->u_stride, sizeof(s.su));
   std::memcpy(s.sd, a->delta_stride, sizeof(s.sd));
   std::memcpy(s.so, a->out_stride, sizeof(s.so));
@@ -770,6 +826,11 @@ mss_status mss_selective_scan_fwd_complex(const mss_scan_complex_args* a, void* 
   p.h0 = static_cast<const float2*>(a->initial_state);
   p.out = a->out;
   p.final_state = static_cast<float2*>(a->final_state);
+  if (plan.workspace > 0) {
+    char* ws = static_cast<char*>(a->workspace);
+    p.agg = reinterpret_cast<float4*>(ws);
+    p.carry = reinterpret_cast<float2*>(ws + plan.agg_bytes);
+  }
   const hipError_t e = mss::launch_scan_complex(s, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
 }

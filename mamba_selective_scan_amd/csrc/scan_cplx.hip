@@ -25,8 +25,21 @@
 //      land in LDS;
 //   O  out = (y + D u) silu(z), one store per element.
 // The state never leaves the registers.  Lanes past dstate hold zeros.
+//
+// Few channels with a long sequence leave most of the GPU idle (16 channels
+// per workgroup), so such shapes are cut into time segments, as the real
+// forward does ("mamba-metal", section "チャンク間 running prefix"): an
+// aggregate pass (AGG) walks every segment but the last from a zero state
+// and records, per (channel, state), the segment's pair (prod_t a_t, h_end);
+// carry_cplx_kernel composes the pairs in order with the pair operator
+// (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) in complex arithmetic; the main
+// pass starts every segment from its carry.  The product of the decays is
+// exp(A sum_t delta_t): its modulus comes from the sum of the deltas, and its
+// phase from the per-step turns accumulated modulo one turn (a sum of the
+// deltas times Im(A) would lose the phase to rounding over long segments).
 #include "mss_device.hpp"
 #include "mss_internal.hpp"
+#include "mss_cplx.hpp"
 
 namespace mss {
 namespace {
@@ -57,30 +70,52 @@ __device__ inline float row_sum16_x4(float v0, float v1, float v2, float v3, int
 }
 constexpr int kCxPer = kCxCh * kCxT / kCxThreads;  // elements per lane in E and O (2)
 
+constexpr int kXcds = 8;  // MI355X: 8 accelerator dies
+
+template <bool AGG>
 __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, CplxPtrs p) {
   __shared__ float2 s_B[kMaxState][kCxT + 1];
-  __shared__ float2 s_C[kMaxState][kCxT + 1];
+  __shared__ float2 s_C[AGG ? 1 : kMaxState][kCxT + 1];
   __shared__ float2 s_dd[kCxCh][kCxT + 1];  // (delta, delta * u)
-  __shared__ float s_y[kCxCh][kCxT + 1];
+  __shared__ float s_y[AGG ? 1 : kCxCh][kCxT + 1];
 
   const int tid = threadIdx.x;
-  const int b = static_cast<int>(blockIdx.x / s.tiles);
-  const int d0 = static_cast<int>(blockIdx.x % s.tiles) * kCxCh;
+  // Workgroups are dispatched round-robin over the XCDs; renumber them so
+  // that each XCD takes a contiguous range of tiles (tiles of one batch row
+  // share B and C in that XCD's L2).  Tile i of a pass is channel tile i % T
+  // of time segment i / T.
+  const int nwg = static_cast<int>(gridDim.x), lin = static_cast<int>(blockIdx.x);
+  const int xcd = lin % kXcds, per_xcd = nwg / kXcds, extra = nwg % kXcds;
+  const int logical = xcd * per_xcd + min(xcd, extra) + lin / kXcds;
+  const int T = s.batch * s.tiles;
+  const int tile = logical % T, seg = logical / T;
+  const int b = tile / s.tiles;
+  const int d0 = (tile % s.tiles) * kCxCh;
+  const int t_begin = seg * s.seg_len;
+  const int t_end = min(s.seqlen, t_begin + s.seg_len);
 
   // scan role: lane (c, n) = (tid / 16, tid % 16)
   const int c = tid >> 4, n = tid & (kMaxState - 1);
   const int d = d0 + c;
   const bool active = d < s.dim && n < s.dstate;
+  const int64_t ws_row = (static_cast<int64_t>(tile) * kCxCh + c) * kMaxState + n;
   float ar2 = 0.0f, ai = 0.0f, hr = 0.0f, hi = 0.0f;
   if (active) {
     ar2 = -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e;  // Re(A) log2 e
     ai = p.A_imag[d * s.sAi[0] + n * s.sAi[1]] * kInv2Pi;      // Im(A) in turns
-    if (p.h0 != nullptr) {
-      const float2 v = p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
-      hr = v.x;
-      hi = v.y;
+    if (!AGG) {
+      if (seg > 0) {
+        const float2 v = p.carry[static_cast<int64_t>(seg) * s.nchan_pad * kMaxState + ws_row];
+        hr = v.x;
+        hi = v.y;
+      } else if (p.h0 != nullptr) {
+        const float2 v = p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
+        hr = v.x;
+        hi = v.y;
+      }
     }
   }
+  float sum_delta = 0.0f, turns_acc = 0.0f;  // AGG: the segment's sum of delta, turns mod 1
 
   // element role: element e = tid + kCxThreads j of the 16 x kCxT tile is
   // (row e / kCxT, step e % kCxT); rows are channels for u, delta, z, out
@@ -98,19 +133,20 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
     eskip[j] = (ok && p.D != nullptr) ? p.D[dd] : 0.0f;
   }
 
-  for (int t0 = 0; t0 < s.seqlen; t0 += kCxT) {
+  for (int t0 = t_begin; t0 < t_end; t0 += kCxT) {
     float eu[kCxPer];
     // ---- E ----
 #pragma unroll
     for (int j = 0; j < kCxPer; ++j) {
       const int t = t0 + estep[j];
-      const bool tin = t < s.seqlen;
+      const bool tin = t < t_end;
       const int ns = erow[j];
       const bool bok = tin && ns < s.dstate;
       s_B[ns][estep[j]] =
           bok ? p.B[b * s.sB[0] + ns * s.sB[1] + t * s.sB[2]] : make_float2(0.0f, 0.0f);
-      s_C[ns][estep[j]] =
-          bok ? p.C[b * s.sC[0] + ns * s.sC[1] + t * s.sC[2]] : make_float2(0.0f, 0.0f);
+      if constexpr (!AGG)
+        s_C[ns][estep[j]] =
+            bok ? p.C[b * s.sC[0] + ns * s.sC[1] + t * s.sC[2]] : make_float2(0.0f, 0.0f);
       const int dd = d0 + erow[j];
       const bool xok = tin && dd < s.dim;
       float dl = 0.0f, uv = 0.0f;
@@ -131,7 +167,6 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
       for (int i = 0; i < 4; ++i) {
         const float2 dd = s_dd[c][t4 + i];
         const float2 bb = s_B[n][t4 + i];
-        const float2 cc = s_C[n][t4 + i];
         const float turns = __builtin_amdgcn_fractf(dd.x * ai);
         const float m = fast_exp2(dd.x * ar2);
         const float a_r = m * __builtin_amdgcn_cosf(turns);
@@ -140,33 +175,97 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
         const float ni = fmaf(a_r, hi, fmaf(a_i, hr, dd.y * bb.y));
         hr = nr;
         hi = ni;
-        yv[i] = fmaf(cc.x, hr, -cc.y * hi);
+        if constexpr (AGG) {
+          sum_delta += dd.x;
+          turns_acc = __builtin_amdgcn_fractf(turns_acc + turns);
+        } else {
+          const float2 cc = s_C[n][t4 + i];
+          yv[i] = fmaf(cc.x, hr, -cc.y * hi);
+        }
       }
-      const float y = row_sum16_x4(yv[0], yv[1], yv[2], yv[3], n);
-      if ((n & 3) == 0) s_y[c][t4 + (n >> 2)] = y;
+      if constexpr (!AGG) {
+        const float y = row_sum16_x4(yv[0], yv[1], yv[2], yv[3], n);
+        if ((n & 3) == 0) s_y[c][t4 + (n >> 2)] = y;
+      }
     }
     __syncthreads();
+    if constexpr (AGG) continue;  // the next chunk's E phase follows the barrier
     // ---- O ----
 #pragma unroll
     for (int j = 0; j < kCxPer; ++j) {
       const int t = t0 + estep[j];
       const int dd = d0 + erow[j];
-      if (t < s.seqlen && dd < s.dim) {
+      if (t < t_end && dd < s.dim) {
         float y = fmaf(eskip[j], eu[j], s_y[erow[j]][estep[j]]);
         if (p.z != nullptr) y *= silu(p.z[b * s.sz[0] + dd * s.sz[1] + t * s.sz[2]]);
         p.out[b * s.so[0] + dd * s.so[1] + t * s.so[2]] = y;
       }
     }
   }
-  if (active && p.final_state != nullptr)
+  if constexpr (AGG) {
+    // (prod_t a_t, h from zero) of the segment; lanes outside the tensors
+    // record the identity pair ((1, 0), (0, 0))
+    const float m = fast_exp2(ar2 * sum_delta);
+    p.agg[static_cast<int64_t>(seg) * s.nchan_pad * kMaxState + ws_row] =
+        make_float4(m * __builtin_amdgcn_cosf(turns_acc), m * __builtin_amdgcn_sinf(turns_acc),
+                    hr, hi);
+  } else if (active && p.final_state != nullptr && seg == s.nseg - 1) {
     p.final_state[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] = make_float2(hr, hi);
+  }
+}
+
+// carry[k] = complex state entering segment k: carry[0] = h0 (or 0),
+// carry[k+1] = P[k] carry[k] + H[k].  One lane per (channel, state); the
+// aggregates do not depend on the chain, so they are loaded kCarryBatch
+// segments at a time ahead of the multiply-adds.
+__global__ __launch_bounds__(256) void carry_cplx_kernel(CplxShape s, const float4* __restrict__ agg,
+                                                         const float2* __restrict__ h0,
+                                                         float2* __restrict__ carry) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= s.nchan_pad * kMaxState) return;
+  const int n = static_cast<int>(idx % kMaxState);
+  const int64_t row = idx / kMaxState;
+  const int64_t per_b = static_cast<int64_t>(s.tiles) * kCxCh;
+  const int b = static_cast<int>(row / per_b);
+  const int d = static_cast<int>(row % per_b);
+  const int64_t sstride = s.nchan_pad * kMaxState;
+  float cr = 0.0f, ci = 0.0f;
+  if (h0 != nullptr && d < s.dim && n < s.dstate) {
+    const float2 v = h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
+    cr = v.x;
+    ci = v.y;
+  }
+  for (int base = 0; base + 1 < s.nseg; base += kCarryBatch) {
+    float4 a[kCarryBatch];
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {  // past the last aggregate: the identity
+      const float4 v = agg[min(base + j, s.nseg - 2) * sstride + idx];
+      a[j] = base + j + 1 < s.nseg ? v : make_float4(1.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      const float nr = fmaf(a[j].x, cr, fmaf(-a[j].y, ci, a[j].z));
+      const float ni = fmaf(a[j].x, ci, fmaf(a[j].y, cr, a[j].w));
+      cr = nr;
+      ci = ni;
+      if (base + j + 1 < s.nseg) carry[(base + j + 1) * sstride + idx] = make_float2(cr, ci);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_scan_complex(const CplxShape& s, const CplxPtrs& p, hipStream_t stream) {
-  const unsigned wgs = static_cast<unsigned>(static_cast<int64_t>(s.batch) * s.tiles);
-  scan_cplx_kernel<<<dim3(wgs), dim3(kCxThreads), 0, stream>>>(s, p);
+  const unsigned tiles = static_cast<unsigned>(static_cast<int64_t>(s.batch) * s.tiles);
+  if (s.nseg > 1) {
+    scan_cplx_kernel<true><<<dim3(tiles * static_cast<unsigned>(s.nseg - 1)), dim3(kCxThreads), 0,
+                             stream>>>(s, p);
+    const int64_t lanes = s.nchan_pad * kMaxState;
+    carry_cplx_kernel<<<dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0, stream>>>(
+        s, p.agg, p.h0, p.carry);
+  }
+  scan_cplx_kernel<false><<<dim3(tiles * static_cast<unsigned>(s.nseg)), dim3(kCxThreads), 0,
+                            stream>>>(s, p);
   return hipGetLastError();
 }
 

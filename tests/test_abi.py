@@ -512,7 +512,39 @@ CPLX_CASES = {
     "out_is_u": (lambda a: setattr(a, "out", fake(0)), "MSS_ERR_ALIASING"),
     "final_on_C": (lambda a: setattr(a, "final_state", fake(5) + 64), "MSS_ERR_ALIASING"),
     "final_on_out": (lambda a: setattr(a, "final_state", fake(10) + 64), "MSS_ERR_ALIASING"),
+    # this shape (6 tiles of 16 channels) is cut into time segments: it needs
+    # a workspace, 256-byte aligned and clear of every tensor
+    "no_workspace": (lambda a: None, "MSS_ERR_WORKSPACE_TOO_SMALL"),
+    "workspace_short": (lambda a: (setattr(a, "workspace", fake(12)),
+                                   setattr(a, "workspace_bytes", _cplx_ws(a) - 1)),
+                        "MSS_ERR_WORKSPACE_TOO_SMALL"),
+    "workspace_misaligned": (lambda a: (setattr(a, "workspace", fake(12) + 64),
+                                        setattr(a, "workspace_bytes", _cplx_ws(a))),
+                             "MSS_ERR_MISALIGNED"),
+    "workspace_on_u": (lambda a: (setattr(a, "workspace", fake(0)),
+                                  setattr(a, "workspace_bytes", _cplx_ws(a))), "MSS_ERR_ALIASING"),
 }
+
+
+def _cplx_ws(a):
+    st = ctypes.c_int(-1)
+    n = _lib.lib().mss_selective_scan_fwd_complex_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    assert st.value == 0
+    return n
+
+
+def test_complex_workspace_size_depends_on_shape_only():
+    a = _lib.new_scan_complex_args()
+    a.batch, a.dim, a.seqlen, a.dstate = 8, 5120, 4096, 16
+    assert _cplx_ws(a) == 0                 # 2560 tiles: no time segments
+    a.batch, a.dim, a.seqlen = 1, 256, 220500
+    n = _cplx_ws(a)                          # 16 tiles: 64 segments of complex carries
+    assert n >= 63 * 256 * 16 * 16 + 64 * 256 * 16 * 8
+    a.dstate = 0
+    st = ctypes.c_int(-1)
+    assert _lib.lib().mss_selective_scan_fwd_complex_workspace_size(ctypes.byref(a),
+                                                                    ctypes.byref(st)) == 0
+    assert st.value == _lib.STATUS_CODE["MSS_ERR_UNSUPPORTED_DSTATE"]
 
 
 @pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")

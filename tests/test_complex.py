@@ -138,6 +138,52 @@ def test_mamba2p8b_layer_sampled(mss):
     check("complex 2.8b sampled final", _cnp(fin[:, ci]), r_fin, TOL)
 
 
+def test_long_sequence_time_split(mss):
+    """Few channels, a long ragged sequence: 3 tiles of 16 channels cut into
+    hundreds of time segments (aggregates, complex carries, main pass),
+    started from an initial state, against the oracle element by element."""
+    _case(mss, "time split 48 x 20011", 1, 48, 20011, h0=True)
+
+
+def test_time_split_channel_last_random_a(mss):
+    """The segmented path on channel-last data with A_log ~ N(0, 1) (slow and
+    fast decays, so carries reach far), a ragged length and dstate 13."""
+    import torch
+    x = generate_complex(2, 40, 3001, 13, "bld", seed=21)
+    rng = np.random.default_rng(21)
+    x["A_log"] = rng.standard_normal(x["A_log"].shape).astype(np.float32)
+    dx = complex_to_torch(x, device())
+    init = _h0(2, 40, 13)
+    note("complex time split, channel-last, random A_log")
+    out, fin = _run(mss, dx, init)
+    torch.cuda.synchronize()
+    r_out, r_fin = _ref(dx, init)
+    check("complex split bld random A out", to_np(out), r_out, TOL)
+    check("complex split bld random A final", _cnp(fin), r_fin, TOL)
+
+
+def test_audio_channel_last_sampled(mss):
+    """The audio-length channel-last shape (1 x 220500 x 256, 16 tiles, so 64
+    time segments) in full on the GPU; sampled channels against the oracle."""
+    import torch
+    w = WORKLOADS["audio_channel_last"]
+    note("complex audio channel-last")
+    dx = complex_to_torch(generate_complex(w.batch, w.dim, w.seqlen, w.dstate, w.layout, seed=13),
+                          device())
+    assert mss.scan_complex_workspace_size(dx["u"], dx["A_log"]) > 0
+    out, fin = _run(mss, dx)
+    torch.cuda.synchronize()
+    chans = np.array([0, 15, 16, 100, 200, w.dim - 1])
+    ci = torch.as_tensor(chans, device=device())
+    sub = dict(dx, u=dx["u"][:, ci], delta_raw=dx["delta_raw"][:, ci], z=dx["z"][:, ci],
+               A_log=dx["A_log"][ci], A_imag=dx["A_imag"][ci], D=dx["D"][ci],
+               dt_bias=dx["dt_bias"][ci])
+    note(f"complex audio: oracle on {len(chans)} channels")
+    r_out, r_fin = _ref(sub)
+    check("complex audio sampled out", to_np(out[:, ci]), r_out, TOL)
+    check("complex audio sampled final", _cnp(fin[:, ci]), r_fin, TOL)
+
+
 def test_real_case_matches_real_kernel(mss):
     """Im(A) = 0 with real B, C: the complex kernel and the real forward kernel
     (separate code) agree."""
