@@ -110,8 +110,15 @@ __device__ inline uint32_t chunk_off(const BwdShape& s, const int64_t* st, int64
   return static_cast<uint32_t>((row * st[1] + tl * st[2]) * es);
 }
 
+// Cache policy of buffer accesses to data that this pass writes or reads
+// exactly once (its gradient outputs, the dB/dC partials, the checkpoints):
+// the non-temporal bit, so that these lines leave L2 first and the input lines
+// that the next chunk reuses (a 16-step chunk is half of a 128-byte line of
+// [B,D,L] data) stay.
+constexpr int kStream = 2;
+
 // Two adjacent elements of one row through a buffer descriptor, the one at
-// the lower address first.
+// the lower address first (stores are streaming).
 template <typename IO>
 struct pair_io;
 template <>
@@ -126,7 +133,7 @@ struct pair_io<float> {
     u32x2 v;
     v[0] = __float_as_uint(lo);
     v[1] = __float_as_uint(hi);
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStream);
   }
 };
 template <>
@@ -139,9 +146,25 @@ struct pair_io<bf16_t> {
   __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float lo, float hi) {
     __builtin_amdgcn_raw_buffer_store_b32(
         static_cast<uint32_t>(bf16_bits(lo)) | (static_cast<uint32_t>(bf16_bits(hi)) << 16), r, off,
-        0, 0);
+        0, kStream);
   }
 };
+
+// One element, streaming (stores of once-written outputs, loads of
+// once-read checkpoints).
+template <typename IO>
+__device__ inline void store_stream(float y, __amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ inline void store_stream<float>(float y, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), r, off, 0, kStream);
+}
+template <>
+__device__ inline void store_stream<bf16_t>(float y, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(y), r, off, 0, kStream);
+}
+__device__ inline float load_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStream));
+}
 
 // A tensor's row (b, row0) as the loop keeps it: its base address and the
 // bytes per time step (32-bit: tiles span less than 2 GiB), three scalar
@@ -766,7 +789,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
         p.ckpt + (static_cast<int64_t>(q) * ck_plane + ck_row0) * kMaxState, 0, kRsrcRange,
         kRsrcFlags);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) rck[k] = buf_one<float>::load(r_ck, qok ? o_ck[k] : kOffNone, 0);
+    for (int k = 0; k < 2; ++k) rck[k] = load_stream(r_ck, qok ? o_ck[k] : kOffNone);
   };
   // The workgroup's dB / dC partial of chunk q (the thread's B/C tile
   // positions): the sum over the waves of their reduction rows.
@@ -780,7 +803,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
       for (int ww = 0; ww < kBwdWaves; ++ww) sum += red[ww * kRedSize + r * kBwdT + tt];
       if ((r & 15) < s.dstate && t < s.seqlen)
-        p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t] = sum;
+        __builtin_nontemporal_store(
+            sum, &p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) *
+                                s.seqlen + t]);
     }
   };
 
@@ -926,9 +951,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const bool ok = t0 + 2 * sg + e < s.seqlen;
-        buf_one<IO>::store(o_du_v[e], r_du, ok ? o_du[e] : kOffNone, 0);
-        buf_one<IO>::store(o_ddr_v[e], r_ddr, ok ? o_ddr[e] : kOffNone, 0);
-        if (has_dz) buf_one<IO>::store(o_dz_v[e], r_dz, ok ? o_dz[e] : kOffNone, 0);
+        store_stream<IO>(o_du_v[e], r_du, ok ? o_du[e] : kOffNone);
+        store_stream<IO>(o_ddr_v[e], r_ddr, ok ? o_ddr[e] : kOffNone);
+        if (has_dz) store_stream<IO>(o_dz_v[e], r_dz, ok ? o_dz[e] : kOffNone);
       }
     }
   }
@@ -998,7 +1023,8 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
   const int n = is_c ? j - s.dstate : j;
   const int r = is_c ? kMaxState + n : n;
   const float sum = ordered_sum(s.tiles, [&](int tile) {
-    return p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t];
+    return __builtin_nontemporal_load(
+        &p.part_bc[((static_cast<int64_t>(b) * s.tiles + tile) * 2 * kMaxState + r) * s.seqlen + t]);
   });
   if (is_c)
     io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + tstore(s, t) * s.sdC[2], sum);
