@@ -100,3 +100,41 @@ def test_shape_beyond_scratch_is_rejected(mss):
     assert e.value.name == "MSS_ERR_SCRATCH_LIMIT"
     torch.cuda.synchronize()
     assert not out.any()
+
+
+def test_graph_capture_and_replay(mss):
+    """The callers this entry point is for record it: captured once in a HIP
+    graph (after a first eager call on the device), then replayed with new
+    inputs copied into the recorded buffers and unrelated eager work between
+    the replays; every replay equals the eager workspace forward bit for bit."""
+    import torch
+    note("noalloc graph capture")
+    shape = (1, 256, 999)  # time segments and a ragged tail: the scratch holds both
+    sets = [to_torch(generate(*shape, 16, seed=s), device(), "f32") for s in (11, 12, 13)]
+    static = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in sets[0].items()}
+    out = torch.empty_like(static["u"])
+    fin = torch.empty(shape[0], shape[1], 16, device=device())
+    args = lambda d: (d["u"], d["delta_raw"], d["A_log"], d["B"], d["C"])  # noqa: E731
+    kw = lambda d: dict(D=d["D"], z=d["z"], dt_bias=d["dt_bias"])  # noqa: E731
+    mss.selective_scan_fwd_noalloc(*args(static), **kw(static), out=out, final_state=fin)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        mss.selective_scan_fwd_noalloc(*args(static), **kw(static), out=out, final_state=fin)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        src = sets[rep % len(sets)]
+        for k in ("u", "delta_raw", "z", "B", "C", "A_log", "D", "dt_bias"):
+            static[k].copy_(src[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_fin = mss.selective_scan_fwd(*args(src), **kw(src), return_final_state=True)
+        # unrelated eager work on the same GPU between replays
+        mss.selective_scan_fwd_noalloc(*args(sets[2]), **kw(sets[2]),
+                                       out=torch.empty_like(sets[2]["u"]))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {rep}: out differs"
+        assert torch.equal(fin, ref_fin), f"replay {rep}: final state differs"
