@@ -86,9 +86,10 @@
  *    u / delta_raw / z / out as (b, d, t), B / C as (b, n, t), A_log as (d, n).
  *    For the scan forward, u, delta_raw, z and out must share a unit-stride
  *    axis, t or d (for example [B,D,L] or channel-last [B,L,D] buffers), and
- *    B and C must share one, t or n; the conv1d and the backward accept any
- *    non-negative strides.  Other strides are free (views into larger
- *    buffers are fine).
+ *    B and C must share one, t or n, unless both have time stride 0
+ *    (time-invariant B and C, any state stride: the forward then holds them
+ *    in registers); the conv1d and the backward accept any non-negative
+ *    strides.  Other strides are free (views into larger buffers are fine).
  *    A dimension of size 1 may have any stride.  D, dt_bias and the states
  *    are contiguous.
  *  - io_dtype selects the element type of u, delta_raw, z, B, C and out

@@ -395,7 +395,11 @@ mss_status scan_fwd(const mss_scan_args* a, void* stream, bool noalloc) {
   const bool x_dfast = s.su[1] == 1 && s.sd[1] == 1 && s.sz[1] == 1 && s.so[1] == 1;
   const bool bc_tfast = s.sB[2] == 1 && s.sC[2] == 1;
   const bool bc_nfast = s.sB[1] == 1 && s.sC[1] == 1;
-  if (!(x_tfast || x_dfast) || !(bc_tfast || bc_nfast)) return MSS_ERR_BAD_STRIDE;
+  // Time-invariant B/C (time stride 0; a length-1 time axis has stride 1
+  // after norm_strides): the vector pass holds them in registers, so their
+  // state stride is free.
+  s.bc_const = s.sB[2] == 0 && s.sC[2] == 0;
+  if (!(x_tfast || x_dfast) || !(bc_tfast || bc_nfast || s.bc_const)) return MSS_ERR_BAD_STRIDE;
   const bool xt = x_tfast;
   const bool bt = bc_tfast;
   const int V = vec_elems(a->io_dtype);
@@ -437,7 +441,7 @@ mss_status scan_fwd(const mss_scan_args* a, void* stream, bool noalloc) {
   // Vectors along the unit-stride axes need the channel count (for
   // d-fast data) and dstate (for n-fast B/C) to be whole vectors; a time axis
   // that is not a whole number of vectors gets an element-wise tail pass.
-  s.use_vec = s.vec_ok && (xt || a->dim % V == 0) && (bt || a->dstate % V == 0);
+  s.use_vec = s.vec_ok && (xt || a->dim % V == 0) && (bt || s.bc_const || a->dstate % V == 0);
   if (s.use_vec && (xt || bt)) s.t_stop = static_cast<int>(a->seqlen / V * V);
   if (s.use_vec) s.nseg = std::max(1, (s.t_stop + s.seg_len - 1) / s.seg_len);
   // Every argument check has passed: the first HIP call of this entry point

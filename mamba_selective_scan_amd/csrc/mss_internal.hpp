@@ -40,6 +40,7 @@ struct ScanShape {
   int use_vec;          // the vector pass runs (else everything is element-wise)
   int t_first, t_stop;  // this pass covers time steps [t_first, t_stop)
   int reverse;          // logical step tau is storage step seqlen-1-tau
+  int bc_const;         // B and C have time stride 0 (time-invariant)
 };
 
 struct StepShape {

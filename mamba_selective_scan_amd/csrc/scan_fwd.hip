@@ -151,9 +151,13 @@ constexpr int kWavesPerSimd = (VEC && (XT || BT || sizeof(IO) == 2)) ? 5 : 4;
 template <bool XT>
 constexpr int kWavesPerWg = XT ? 1 : 4;
 
-template <typename IO, bool XT, bool BT, bool AGG, bool VEC, bool REV>
+// LTI: B and C do not depend on t (time stride 0, the time-invariant case of
+// createcentury's reading, "主要な最適化テクニック": the kIsVariableB/C
+// switches).  Each lane then holds the B and C of its two states in registers
+// for the whole segment: no B/C loads, LDS stores or LDS reads per chunk.
+template <typename IO, bool XT, bool BT, bool AGG, bool VEC, bool REV, bool LTI>
 __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_waves_per_eu(
-    kWavesPerSimd<IO, VEC, XT, BT>, 8))) void scan_kernel(
+    kWavesPerSimd<IO, VEC, XT, BT || LTI>, 8))) void scan_kernel(
     ScanShape s, const IO* __restrict__ u, const IO* __restrict__ delta_raw,
     const float* __restrict__ A_log, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
     const float* __restrict__ Dskip, const IO* __restrict__ z,
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   // LDS buffers alternate with the chunk's parity.
   constexpr bool COOP = !XT && VEC;
   constexpr int kBufs = COOP ? 2 : 1;
-  constexpr int kBcSize = (AGG ? kMaxState : kBcRows) * kT;
+  constexpr int kBcSize = LTI ? 4 : (AGG ? kMaxState : kBcRows) * kT;
   constexpr int kDdSize = kCh * kDdPitch;
   constexpr int kSkipSize = (AGG || COOP) ? 4 : kCh * kSkipPitch;  // COOP keeps D*u in registers
   constexpr int kChanSpan = COOP ? kWg * kCh : kCh;  // channels whose dt_bias, D sit in s_chan
@@ -246,6 +250,19 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     h[k] = h_init;
   }
   float sum_delta = 0.0f;
+  // LTI: B (and C outside the AGG pass) of the lane's two states
+  float b_lti[kStatesPerLane] = {}, c_lti[kStatesPerLane] = {};
+  if constexpr (LTI) {
+#pragma unroll
+    for (int k = 0; k < kStatesPerLane; ++k) {
+      const int n = sg * kStatesPerLane + k;
+      if (n < s.dstate) {
+        b_lti[k] = io_traits<IO>::load(Bm + static_cast<int64_t>(b) * s.sB[0] + n * s.sB[1]);
+        if constexpr (!AGG)
+          c_lti[k] = io_traits<IO>::load(Cm + static_cast<int64_t>(b) * s.sC[0] + n * s.sC[1]);
+      }
+    }
+  }
 
   // ---- chunk memory access ------------------------------------------------
   // All global traffic uses raw buffer loads/stores: a per-chunk descriptor
@@ -364,8 +381,8 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   struct ZBuf {
     float z[kPerThread];
   };
-  constexpr int kBcLoads = COOP ? 1 : (AGG ? 2 : 4);  // the AGG pass needs no C
-  float bcb[kBcLoads * kVec];  // B/C of the next chunk
+  constexpr int kBcLoads = LTI ? 0 : (COOP ? 1 : (AGG ? 2 : 4));  // the AGG pass needs no C
+  float bcb[kBcLoads > 0 ? kBcLoads * kVec : 1];  // B/C of the next chunk
 
   // Loads of one x-tensor.  VEC: one vector (wholly in or out of the valid
   // region); else element by element.
@@ -403,7 +420,9 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   const int cb_n = BT ? kCh * (wave & 1) + (lane >> 3) : 4 * (lane & 3);
   const int cb_t = BT ? 4 * (lane & 7) : 16 * (wave & 1) + (lane >> 2);
   auto issue_bc_loads = [&](int t0, int lim) __attribute__((always_inline)) {
-    if constexpr (COOP) {
+    if constexpr (LTI) {
+      return;
+    } else if constexpr (COOP) {
       const int64_t* st = cb_c ? s.sC : s.sB;
       const auto rs = rsrc(cb_c ? Cm : Bm, st, 0, t0);
       const int ts = REV ? (BT ? kT - kVec - cb_t : kT - 1 - cb_t) : cb_t;
@@ -492,7 +511,9 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
           *e_sk(nb, j) = sk[j];
       }
     }
-    if constexpr (COOP) {
+    if constexpr (LTI) {
+      // B and C stay in registers
+    } else if constexpr (COOP) {
       // one vector per lane into the workgroup's shared B/C buffer (n-fast:
       // the two-index form of the non-cooperative path below)
       float* const sbc = s_bc_all + nb * kBcSize;
@@ -596,8 +617,8 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     const int col = (((t4 >> 2) ^ sg) & 7) << 2;
     const float* pb = p_b0 + nb * kBcSize;
     const float* pd = p_dd + nb * kWg * kDdSize;
-    const f4 b0 = lds_f4(pb + col);
-    const f4 b1 = lds_f4(pb + kT + col);
+    const f4 b0 = LTI ? f4{b_lti[0], b_lti[0], b_lti[0], b_lti[0]} : lds_f4(pb + col);
+    const f4 b1 = LTI ? f4{b_lti[1], b_lti[1], b_lti[1], b_lti[1]} : lds_f4(pb + kT + col);
     const f4 dd01 = lds_f4(pd + 2 * t4);
     const f4 dd23 = lds_f4(pd + 2 * t4 + 4);
     const float dls[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
@@ -613,8 +634,8 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
       sum_delta += (dls[0] + dls[1]) + (dls[2] + dls[3]);
     } else {
       const float* pc = p_c0 + nb * kBcSize;
-      const f4 c0 = lds_f4(pc + col);
-      const f4 c1 = lds_f4(pc + kT + col);
+      const f4 c0 = LTI ? f4{c_lti[0], c_lti[0], c_lti[0], c_lti[0]} : lds_f4(pc + col);
+      const f4 c1 = LTI ? f4{c_lti[1], c_lti[1], c_lti[1], c_lti[1]} : lds_f4(pc + kT + col);
       const float cs0[4] = {c0.x, c0.y, c0.z, c0.w};
       const float cs1[4] = {c1.x, c1.y, c1.z, c1.w};
       float y[4];
@@ -787,7 +808,7 @@ __global__ __launch_bounds__(256) void carry_kernel(ScanShape s, const float2* _
   }
 }
 
-template <typename IO, bool XT, bool BT, bool VEC, bool REV>
+template <typename IO, bool XT, bool BT, bool VEC, bool REV, bool LTI>
 static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, float* final_state,
                         hipStream_t stream) {
   constexpr int kWg = kWavesPerWg<XT>;
@@ -807,37 +828,44 @@ static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, 
   const IO* z = static_cast<const IO*>(p.z);
   IO* out = static_cast<IO*>(p.out);
   if (s.nseg > 1) {
-    scan_kernel<IO, XT, BT, true, VEC, REV><<<wgs(s.nseg - 1), block, 0, stream>>>(
+    scan_kernel<IO, XT, BT, true, VEC, REV, LTI><<<wgs(s.nseg - 1), block, 0, stream>>>(
         s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
         nullptr);
     const int64_t n = s.nchan_pad * kMaxState;
     carry_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream>>>(
         s, p.agg, h0, p.carry);
   }
-  scan_kernel<IO, XT, BT, false, VEC, REV><<<wgs(s.nseg), block, 0, stream>>>(
+  scan_kernel<IO, XT, BT, false, VEC, REV, LTI><<<wgs(s.nseg), block, 0, stream>>>(
       s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
       p.chunk_states);
 }
 
 // The vector pass covers [0, s.t_stop); when s.t_stop < seqlen it exports its
 // state to p.tail_h0 and an element-wise pass covers the remaining steps.
+// Time-invariant B/C (s.bc_const) take the LTI instantiation on the vector
+// pass; the element-wise passes read them through their zero time stride.
 template <typename IO, bool XT, bool BT, bool REV>
 static hipError_t launch_dir(const ScanShape& s, const ScanPtrs& p, hipStream_t stream) {
   if (!s.use_vec) {
-    launch_pass<IO, XT, BT, false, REV>(s, p, p.h0, p.final_state, stream);
+    launch_pass<IO, XT, BT, false, REV, false>(s, p, p.h0, p.final_state, stream);
     return hipGetLastError();
   }
   const bool tail = s.t_stop < s.seqlen;
-  if (s.t_stop > 0)
-    launch_pass<IO, XT, BT, true, REV>(s, p, p.h0, tail ? p.tail_h0 : p.final_state, stream);
+  float* const vec_final = tail ? p.tail_h0 : p.final_state;
+  if (s.t_stop > 0) {
+    if (s.bc_const && !BT)
+      launch_pass<IO, XT, false, true, REV, true>(s, p, p.h0, vec_final, stream);
+    else
+      launch_pass<IO, XT, BT, true, REV, false>(s, p, p.h0, vec_final, stream);
+  }
   if (tail) {
     ScanShape t = s;
     t.t_first = s.t_stop;
     t.t_stop = s.seqlen;
     t.nseg = 1;
     t.seg_len = s.seqlen - s.t_stop;
-    launch_pass<IO, XT, BT, false, REV>(t, p, s.t_stop > 0 ? p.tail_h0 : p.h0, p.final_state,
-                                        stream);
+    launch_pass<IO, XT, BT, false, REV, false>(t, p, s.t_stop > 0 ? p.tail_h0 : p.h0,
+                                               p.final_state, stream);
   }
   return hipGetLastError();
 }

@@ -220,11 +220,12 @@ def slice_time(inputs: dict, start: int, stop: int) -> dict:
 
 def algorithmic_bytes(batch: int, dim: int, seqlen: int, dstate: int, io_bytes: int,
                       final_state: bool = False, has_z: bool = True, has_D: bool = True,
-                      has_dt_bias: bool = True) -> int:
-    """Bytes the forward must move: each input read once, each output written once."""
+                      has_dt_bias: bool = True, bc_time_invariant: bool = False) -> int:
+    """Bytes the forward must move: each input read once, each output written once.
+    Time-invariant B and C are one [batch, dstate] value each."""
     per_bdl = 3 + int(has_z)          # u, delta_raw, out (+ z)
     n = batch * dim * seqlen * per_bdl * io_bytes
-    n += 2 * batch * seqlen * dstate * io_bytes   # B, C
+    n += 2 * batch * (1 if bc_time_invariant else seqlen) * dstate * io_bytes   # B, C
     n += dim * dstate * 4                          # A_log
     n += dim * 4 * (int(has_D) + int(has_dt_bias))
     if final_state:

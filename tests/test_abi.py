@@ -188,6 +188,22 @@ def test_scan_argument_checks(case):
 
 
 @pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
+def test_scan_bc_layout_checks():
+    """B and C need a shared unit-stride axis (t or n) unless both are
+    time-invariant (time stride 0), which takes any state stride."""
+    a = scan_args(ws=True)
+    a.B_stride[2] = a.C_stride[2] = 3
+    assert call_scan(a) == code("MSS_ERR_BAD_STRIDE")
+    a = scan_args(ws=True)
+    a.B_stride[2] = 0  # B time-invariant with state stride seqlen, C per step
+    assert call_scan(a) == code("MSS_ERR_BAD_STRIDE")
+    a = scan_args(ws=True)
+    a.B_stride[2] = a.C_stride[2] = 0  # both time-invariant, state stride seqlen
+    # every argument check passes; only the launch fails (no device here)
+    assert call_scan(a) == code("MSS_ERR_HIP")
+
+
+@pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer checks run only where no GPU is present")
 def test_scan_workspace_checks():
     a = scan_args(ws=True)
     a.workspace_bytes -= 1

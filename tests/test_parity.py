@@ -140,6 +140,81 @@ def test_time_invariant_B_C(mss, shared_batch, seqlen):
     check(f"time-invariant B/C L={seqlen} final", to_np(fin), ref_fin, 1e-4)
 
 
+def _lti_inputs(batch, dim, seqlen, dstate, layout, io, seed, source="expand"):
+    """A workload with B and C replaced by [batch, dstate] values broadcast
+    along time (stride-0 views): of a [batch, dstate] tensor ("expand", state
+    stride 1) or of the workload's own first step ("slice", the state stride of
+    its layout: seqlen for [B,N,L])."""
+    import torch
+    x = generate(batch, dim, seqlen, dstate, layout, seed=seed)
+    dx = to_torch(x, device(), io)
+    g = torch.Generator().manual_seed(seed + 5)
+    for k in ("B", "C"):
+        if source == "slice":
+            dx[k] = dx[k][:, :, :1].expand(batch, dstate, seqlen)
+        else:
+            base = torch.randn(batch, dstate, generator=g).to(device(), dx["u"].dtype)
+            dx[k] = base[:, :, None].expand(batch, dstate, seqlen)
+    return dx
+
+
+def _materialised(t, layout):
+    """The same values with a real time axis, in the workload's B/C layout."""
+    if layout == "bld":
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+    return t.contiguous()
+
+
+@pytest.mark.parametrize("source", ["expand", "slice"])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+def test_time_invariant_register_path_equals_materialised(mss, layout, io, reverse, source):
+    """Time-invariant B/C take the vector pass that holds B and C in registers;
+    the same values materialised along time take the path through LDS.  Both
+    do the same arithmetic in the same order, so the results are bitwise equal.
+    The length leaves a ragged tail for the element-wise pass."""
+    import torch
+    batch, dim, seqlen, N = 2, 96, 1002, 16
+    note(f"LTI vs materialised: {layout} {io} reverse={reverse} L={seqlen} {source}")
+    dx = _lti_inputs(batch, dim, seqlen, N, layout, io, seed=21, source=source)
+    dm = dict(dx)
+    for k in ("B", "C"):
+        dm[k] = _materialised(dx[k], layout)
+        assert dx[k].stride()[2] == 0 and dm[k].stride()[2] != 0
+    res = []
+    for d_in in (dx, dm):
+        res.append(mss.selective_scan_fwd(
+            d_in["u"], d_in["delta_raw"], d_in["A_log"], d_in["B"], d_in["C"], D=d_in["D"],
+            z=d_in["z"], dt_bias=d_in["dt_bias"], reverse=reverse, return_final_state=True))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]), "outputs differ"
+    assert torch.equal(res[0][1], res[1][1]), "final states differ"
+    if not reverse:
+        ref_out, ref_fin = oracle_full(dx)
+        check(f"LTI {layout} {io} out", to_np(res[0][0]), ref_out, tol_for(io))
+        check(f"LTI {layout} {io} final", to_np(res[0][1]), ref_fin, tol_for(io))
+
+
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+def test_time_invariant_split_h0_odd_dstate(mss, layout):
+    """Few channels and a long sequence with time-invariant B/C: aggregate
+    pass, carries and main pass all hold B and C in registers, from an initial
+    state.  dstate 5 is not a whole number of 4-element vectors, which the
+    register path does not need."""
+    import torch
+    batch, dim, seqlen, N = 1, 64, 20000, 5
+    note(f"LTI split+h0 {layout} B={batch} D={dim} L={seqlen} N={N}")
+    dx = _lti_inputs(batch, dim, seqlen, N, layout, "f32", seed=33)
+    g = torch.Generator().manual_seed(34)
+    init = torch.randn(batch, dim, N, generator=g).to(device())
+    out, fin = run_gpu(mss, dx, initial_state=init)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle_full(dx, initial_state=init)
+    check(f"LTI split {layout} out", to_np(out), ref_out, 1e-4)
+    check(f"LTI split {layout} final", to_np(fin), ref_fin, 1e-4)
+
+
 @pytest.mark.parametrize("layout", ["bdl", "bld"])
 def test_views_into_padded_buffers(mss, layout):
     """Views with offsets and padded row strides (the unit-stride axis kept)."""
