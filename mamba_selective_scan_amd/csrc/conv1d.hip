@@ -65,8 +65,7 @@ struct vec16<bf16_t> {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(bf16_bits(v[2 * i])) |
-             (static_cast<uint32_t>(bf16_bits(v[2 * i + 1])) << 16);
+      w[i] = bf16x2_bits(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };

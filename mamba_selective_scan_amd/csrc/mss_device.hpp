@@ -27,13 +27,17 @@ struct io_traits<float> {
   __device__ static inline void store(float* p, float v) { *p = v; }
 };
 
-// fp32 -> bf16 bit pattern, rounded to nearest with ties to even; a NaN stays
-// a quiet NaN.
+// fp32 -> bf16 bit patterns on gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32): round to nearest with ties to even (the default
+// rounding mode), subnormals kept, a NaN stays a NaN.  The pair form converts
+// two values with one instruction.
 __device__ static inline uint16_t bf16_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+__device__ static inline uint32_t bf16x2_bits(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <>

@@ -144,9 +144,7 @@ struct pair_io<bf16_t> {
     hi = __uint_as_float(v & 0xffff0000u);
   }
   __device__ static inline void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float lo, float hi) {
-    __builtin_amdgcn_raw_buffer_store_b32(
-        static_cast<uint32_t>(bf16_bits(lo)) | (static_cast<uint32_t>(bf16_bits(hi)) << 16), r, off,
-        0, kStream);
+    __builtin_amdgcn_raw_buffer_store_b32(bf16x2_bits(lo, hi), r, off, 0, kStream);
   }
 };
 

@@ -106,8 +106,7 @@ struct vec_io<bf16_t> {
     u32x2 w;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      w[j] = static_cast<uint32_t>(bf16_bits(y[2 * j])) |
-             (static_cast<uint32_t>(bf16_bits(y[2 * j + 1])) << 16);
+      w[j] = bf16x2_bits(y[2 * j], y[2 * j + 1]);
     __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, 0);
   }
   __device__ static inline float load_one(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {

@@ -95,6 +95,28 @@ def test_channel_permutation(mss):
     assert torch.equal(a[:, perm], b) and torch.equal(fa[:, perm], fb)
 
 
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+def test_bf16_io_is_the_fp32_path_rounded(mss, layout):
+    """bf16 I/O loads its values exactly into fp32, computes in fp32 and
+    rounds only the output.  On the same (bf16-representable) values, the fp32
+    path's output rounded to nearest even by torch is therefore the bf16
+    path's output, bit for bit, and the fp32 final states are equal.  This
+    pins the library's output rounding against an independent one.  The even
+    length keeps the bf16 vector path and leaves a ragged tail."""
+    import torch
+    note(f"bf16 == rounded fp32 ({layout})")
+    dx16 = to_torch(generate(2, 96, 1002, 16, layout, seed=8), device(), "bf16")
+    dx32 = dict(dx16)
+    for k in ("u", "delta_raw", "z", "B", "C"):
+        dx32[k] = dx16[k].to(torch.float32)  # dense views keep their strides
+        assert dx32[k].stride() == dx16[k].stride()
+    a16, f16 = _run(mss, dx16)
+    a32, f32 = _run(mss, dx32)
+    torch.cuda.synchronize()
+    assert torch.equal(f16, f32), "final states differ"
+    assert torch.equal(a16, a32.to(torch.bfloat16)), "bf16 output is not the rounded fp32 output"
+
+
 def test_argument_errors_with_real_tensors(mss):
     """Argument checks on real device tensors: rejected before any launch."""
     import torch
