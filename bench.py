@@ -60,9 +60,9 @@ HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 PEAK_SCLK_MHZ = 2400.0
 # VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instructions per
-# second without packed fp32 (which the build disables).  The backward and
-# complex lines weight a transcendental (exp2, log2, rcp, sin, cos) as 4 slots
-# (the ISA's quarter rate); the forward line counts one slot per instruction.
+# second without packed fp32 (which the build disables).  Every line counts one
+# slot per instruction, transcendentals included: mixed with FMAs as in these
+# kernels, a v_exp_f32 costs about one FMA slot (measured).
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
@@ -486,17 +486,19 @@ def main_conv(args):
     return 0
 
 
-def bwd_valu_slots_per_element(dstate: int) -> int:
-    """Algorithmic VALU slots per (b, d, t) element of the backward.
+def bwd_valu_instr_per_element(dstate: int) -> int:
+    """VALU instructions per (b, d, t) element that the backward's arithmetic
+    needs, every instruction one issue slot (as valu_instr_per_element).
 
-    Per state: the decay exp2 (4) and Delta*A2; the forward state (Delta*u*B,
-    the h FMA) needed by dC and dA; the adjoint G (FMA), its dC and dB terms,
-    the B.G sum, G*h_prev*a (2), the dA and A.(...) sums, g*a: 15 slots.
-    Per element: softplus (15) and its derivative sigmoid (exp2, rcp, 2 ops:
-    10); dy = dout*silu(z) (12); y = C.h + D*u for dz (1) and silu'(z) (4
-    ops) times dout*y (2); du and ddelta_raw (3); the dD and ddt_bias sums (2).
+    Per state: the decay exp2 and Delta*A2; the forward state (Delta*u*B, the
+    h FMA) needed by dC and dA; the adjoint G (FMA), its dC and dB terms, the
+    B.G sum, G*a (the next adjoint) and G*a*h_prev, the dA and A.(...) sums:
+    12.  Per element: softplus (9) and its derivative sigmoid (exp2, rcp and 2
+    ops: 4); dy = dout*silu(z) (6); y = C.h + D*u for dz (1) and silu'(z) (4
+    ops) times dout*y (2); du and ddelta_raw (3); the dD and ddt_bias sums
+    (2): 31.
     """
-    return dstate * 15 + 15 + 10 + 12 + 1 + 4 + 2 + 3 + 2
+    return dstate * 12 + 9 + 4 + 6 + 1 + 4 + 2 + 3 + 2
 
 
 def main_bwd(args):
@@ -587,7 +589,7 @@ def main_bwd(args):
     alg_bytes = ne * 7 * io_bytes + 4 * nbc * io_bytes           # u, dr, z, dout; du, ddr, dz; B, C, dB, dC
     alg_bytes += 2 * w.dim * (w.dstate + 2) * 4                  # A_log, D, dt_bias and their grads
     alg_bytes += 3 * w.batch * w.dim * w.dstate * 4              # h0, dfinal, dh0
-    slots = ne * bwd_valu_slots_per_element(w.dstate)
+    slots = ne * bwd_valu_instr_per_element(w.dstate)
     achieved_gbs = alg_bytes / (mean_ms * 1e-3) / 1e9
     achieved_slots = slots / (mean_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash("scan_bwd")
@@ -618,11 +620,12 @@ def main_bwd(args):
             "kernel": "selective-scan bwd (checkpoint, reverse, reduce passes) on the current stream",
             "achieved": round(achieved_slots, 3),
             "peak": round(VALU_PEAK_TSLOTS, 3),
-            "unit": "T VALU lane-slots/s",
+            "unit": "T VALU lane-instructions/s",
             "frac": round(achieved_slots / VALU_PEAK_TSLOTS, 4),
             "traffic": traffic,
-            "algorithmic_slots": slots,
-            "slots_per_element": bwd_valu_slots_per_element(w.dstate),
+            "algorithmic_instr": slots,
+            "instr_per_element": bwd_valu_instr_per_element(w.dstate),
+            "peak_what": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz, one instruction per lane-slot",
             "hbm": {"achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_bytes},
             "event_us_mean": round(mean_ms * 1e3, 2),
@@ -678,15 +681,16 @@ def bwd_cpu_baseline(x, w, io_bytes, alg_bytes, target_s):
     }
 
 
-def complex_valu_slots_per_element(dstate: int) -> int:
-    """Algorithmic VALU slots per (b, d, t) element of the complex-A forward.
+def complex_valu_instr_per_element(dstate: int) -> int:
+    """VALU instructions per (b, d, t) element that the complex-A forward's
+    arithmetic needs, every instruction one issue slot.
 
-    Per state: exp2, sin and cos (4 each); delta*Re(A) and delta*Im(A); the
-    modulus times cos and sin; the complex multiply-add h = a h + delta u B
-    (delta u times Re and Im of B, then two FMAs per component); Re(C h) (a
-    multiply and an FMA): 24.  Per element as the real forward: 31.
+    Per state: exp2, sin and cos; delta*Re(A) and delta*Im(A); the modulus
+    times cos and sin; the complex multiply-add h = a h + delta u B (delta u
+    times Re and Im of B, then two FMAs per component); Re(C h) (a multiply
+    and an FMA): 15.  Per element as the real forward: 19.
     """
-    return dstate * 24 + 31
+    return dstate * 15 + 19
 
 
 def complex_cpu_baseline(x, target_s):
@@ -780,7 +784,7 @@ def main_complex(args):
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(ms) / len(ms)
     alg = complex_algorithmic_bytes(w.batch, w.dim, w.seqlen, w.dstate)
-    slots = w.elems * complex_valu_slots_per_element(w.dstate)
+    slots = w.elems * complex_valu_instr_per_element(w.dstate)
     gbs = alg / (mean_ms * 1e-3) / 1e9
     tslots = slots / (mean_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash("scan_complex")
@@ -811,11 +815,12 @@ def main_complex(args):
             "kernel": "scan_cplx_kernel (mss_selective_scan_fwd_complex) on the current stream",
             "achieved": round(tslots, 3),
             "peak": round(VALU_PEAK_TSLOTS, 3),
-            "unit": "T VALU lane-slots/s",
+            "unit": "T VALU lane-instructions/s",
             "frac": round(tslots / VALU_PEAK_TSLOTS, 4),
             "traffic": traffic,
-            "algorithmic_slots": slots,
-            "slots_per_element": complex_valu_slots_per_element(w.dstate),
+            "algorithmic_instr": slots,
+            "instr_per_element": complex_valu_instr_per_element(w.dstate),
+            "peak_what": "256 CU x 4 SIMD x 16 lanes x 2.4 GHz, one instruction per lane-slot",
             "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg},
             "event_us_mean": round(mean_ms * 1e3, 2),

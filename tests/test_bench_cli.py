@@ -45,6 +45,8 @@ def test_valu_instructions_per_element():
     # 5 per state-step (exp2, two multiplies, two FMAs) and 19 per element
     assert bench.valu_instr_per_element(16) == 99
     assert bench.valu_instr_per_element(16, softplus=False, has_z=False) == 84
+    assert bench.bwd_valu_instr_per_element(16) == 223
+    assert bench.complex_valu_instr_per_element(16) == 259
 
 
 def test_cold_cache_sets():
