@@ -231,9 +231,10 @@ constexpr int64_t kConvMinSeg = 64;
 
 // Complex-A forward: shapes with fewer channel tiles (16 channels each) than
 // kCxSplitBelow are cut into time segments, as many as bring the grid to about
-// kCxTargetWgs workgroups (four 4-wave workgroups per CU).
+// kCxTargetWgs workgroups: five 4-wave workgroups per CU, as many as the
+// kernel's registers (up to 100 with the chunk loads in flight) let a CU hold.
 constexpr int64_t kCxSplitBelow = 512;
-constexpr int64_t kCxTargetWgs = 1024;
+constexpr int64_t kCxTargetWgs = 1280;
 
 mss_status check_cplx_shape(const mss_scan_complex_args* a) {
   if (a == nullptr || a->struct_size != sizeof(mss_scan_complex_args) || a->reserved0 != 0 ||

@@ -17,7 +17,9 @@
 // (row_sum16_x4).  Time is walked in
 // chunks of kCxT steps:
 //   E  B and C of the chunk (16 states x kCxT steps, shared by the 16
-//      channels) and, per element, (delta, delta u) into LDS;
+//      channels) and, per element, (delta, delta u) into LDS, from registers
+//      loaded during the previous chunk (u, delta_raw, z, B and C of chunk
+//      c+1 are in flight while chunk c is scanned);
 //   S  each lane walks the chunk: the complex decay from exp2, and from the
 //      hardware sin / cos of the fractional turns delta Im(A) / 2 pi (the
 //      fraction keeps v_sin / v_cos inside their input range); one complex
@@ -72,7 +74,9 @@ constexpr int kCxPer = kCxCh * kCxT / kCxThreads;  // elements per lane in E and
 
 constexpr int kXcds = 8;  // MI355X: 8 accelerator dies
 
-template <bool AGG>
+// XR / BR: u, delta_raw (z, out) / B, C have unit stride along their rows
+// (channels / states), and their elements are read rows-fastest.
+template <bool AGG, bool XR, bool BR>
 __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, CplxPtrs p) {
   __shared__ float2 s_B[kMaxState][kCxT + 1];
   __shared__ float2 s_C[AGG ? 1 : kMaxState][kCxT + 1];
@@ -117,47 +121,66 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
   }
   float sum_delta = 0.0f, turns_acc = 0.0f;  // AGG: the segment's sum of delta, turns mod 1
 
-  // element role: element e = tid + kCxThreads j of the 16 x kCxT tile is
-  // (row e / kCxT, step e % kCxT); rows are channels for u, delta, z, out
-  // and states for B, C
-  int erow[kCxPer], estep[kCxPer];
+  // element roles: element e = tid + kCxThreads j of the 16-row x kCxT-step
+  // tile; rows are channels for u, delta, z, out and states for B, C.  Steps
+  // run fastest over the lanes when the data has unit stride along time;
+  // rows run fastest when it has unit stride along them (channel-last
+  // activations, n-fast B/C), so that 16 lanes read one step's 16 adjacent
+  // channels or states instead of 16 separate lines.
+  int erow[kCxPer], estep[kCxPer], brow[kCxPer], bstep[kCxPer];
   float ebias[kCxPer], eskip[kCxPer];
 #pragma unroll
   for (int j = 0; j < kCxPer; ++j) {
     const int e = tid + kCxThreads * j;
-    erow[j] = e / kCxT;
-    estep[j] = e % kCxT;
+    erow[j] = XR ? e % kCxCh : e / kCxT;
+    estep[j] = XR ? e / kCxCh : e % kCxT;
+    brow[j] = BR ? e % kMaxState : e / kCxT;
+    bstep[j] = BR ? e / kMaxState : e % kCxT;
     const int dd = d0 + erow[j];
     const bool ok = dd < s.dim;
     ebias[j] = (ok && p.dt_bias != nullptr) ? p.dt_bias[dd] : 0.0f;
     eskip[j] = (ok && p.D != nullptr) ? p.D[dd] : 0.0f;
   }
 
+  // The raw inputs of a chunk, loaded one chunk ahead of use: the loads of
+  // chunk c+1 are in flight while chunk c is scanned.
+  float2 rb[kCxPer], rc[kCxPer];
+  float rx[kCxPer], ru[kCxPer], rz[kCxPer];
+  auto load_chunk = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kCxPer; ++j) {
+      const int tb = t0 + bstep[j];
+      const int ns = brow[j];
+      const bool bok = tb < t_end && ns < s.dstate;
+      rb[j] = bok ? p.B[b * s.sB[0] + ns * s.sB[1] + tb * s.sB[2]] : make_float2(0.0f, 0.0f);
+      rc[j] = (!AGG && bok) ? p.C[b * s.sC[0] + ns * s.sC[1] + tb * s.sC[2]]
+                            : make_float2(0.0f, 0.0f);
+      const int t = t0 + estep[j];
+      const int dd = d0 + erow[j];
+      const bool xok = t < t_end && dd < s.dim;
+      rx[j] = xok ? p.delta_raw[b * s.sd[0] + dd * s.sd[1] + t * s.sd[2]] : 0.0f;
+      ru[j] = xok ? p.u[b * s.su[0] + dd * s.su[1] + t * s.su[2]] : 0.0f;
+      rz[j] = (!AGG && xok && p.z != nullptr) ? p.z[b * s.sz[0] + dd * s.sz[1] + t * s.sz[2]]
+                                             : 0.0f;
+    }
+  };
+  load_chunk(t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += kCxT) {
-    float eu[kCxPer];
+    float eu[kCxPer], ez[kCxPer];
     // ---- E ----
 #pragma unroll
     for (int j = 0; j < kCxPer; ++j) {
+      ez[j] = rz[j];
+      s_B[brow[j]][bstep[j]] = rb[j];
+      if constexpr (!AGG) s_C[brow[j]][bstep[j]] = rc[j];
       const int t = t0 + estep[j];
-      const bool tin = t < t_end;
-      const int ns = erow[j];
-      const bool bok = tin && ns < s.dstate;
-      s_B[ns][estep[j]] =
-          bok ? p.B[b * s.sB[0] + ns * s.sB[1] + t * s.sB[2]] : make_float2(0.0f, 0.0f);
-      if constexpr (!AGG)
-        s_C[ns][estep[j]] =
-            bok ? p.C[b * s.sC[0] + ns * s.sC[1] + t * s.sC[2]] : make_float2(0.0f, 0.0f);
-      const int dd = d0 + erow[j];
-      const bool xok = tin && dd < s.dim;
-      float dl = 0.0f, uv = 0.0f;
-      if (xok) {
-        const float x = p.delta_raw[b * s.sd[0] + dd * s.sd[1] + t * s.sd[2]] + ebias[j];
-        dl = s.softplus ? softplus(x) : x;
-        uv = p.u[b * s.su[0] + dd * s.su[1] + t * s.su[2]];
-      }
-      eu[j] = uv;
-      s_dd[erow[j]][estep[j]] = make_float2(dl, dl * uv);
+      const bool xok = t < t_end && d0 + erow[j] < s.dim;
+      const float x = rx[j] + ebias[j];
+      const float dl = xok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      eu[j] = ru[j];
+      s_dd[erow[j]][estep[j]] = make_float2(dl, dl * ru[j]);
     }
+    load_chunk(t0 + kCxT);
     __syncthreads();
     // ---- S ----
 #pragma unroll 2
@@ -197,7 +220,7 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
       const int dd = d0 + erow[j];
       if (t < t_end && dd < s.dim) {
         float y = fmaf(eskip[j], eu[j], s_y[erow[j]][estep[j]]);
-        if (p.z != nullptr) y *= silu(p.z[b * s.sz[0] + dd * s.sz[1] + t * s.sz[2]]);
+        if (p.z != nullptr) y *= silu(ez[j]);
         p.out[b * s.so[0] + dd * s.so[1] + t * s.so[2]] = y;
       }
     }
@@ -253,19 +276,29 @@ __global__ __launch_bounds__(256) void carry_cplx_kernel(CplxShape s, const floa
   }
 }
 
-}  // namespace
-
-hipError_t launch_scan_complex(const CplxShape& s, const CplxPtrs& p, hipStream_t stream) {
+template <bool XR, bool BR>
+void launch_complex_passes(const CplxShape& s, const CplxPtrs& p, hipStream_t stream) {
   const unsigned tiles = static_cast<unsigned>(static_cast<int64_t>(s.batch) * s.tiles);
   if (s.nseg > 1) {
-    scan_cplx_kernel<true><<<dim3(tiles * static_cast<unsigned>(s.nseg - 1)), dim3(kCxThreads), 0,
-                             stream>>>(s, p);
+    scan_cplx_kernel<true, XR, BR><<<dim3(tiles * static_cast<unsigned>(s.nseg - 1)),
+                                     dim3(kCxThreads), 0, stream>>>(s, p);
     const int64_t lanes = s.nchan_pad * kMaxState;
     carry_cplx_kernel<<<dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0, stream>>>(
         s, p.agg, p.h0, p.carry);
   }
-  scan_cplx_kernel<false><<<dim3(tiles * static_cast<unsigned>(s.nseg)), dim3(kCxThreads), 0,
-                            stream>>>(s, p);
+  scan_cplx_kernel<false, XR, BR><<<dim3(tiles * static_cast<unsigned>(s.nseg)), dim3(kCxThreads),
+                                    0, stream>>>(s, p);
+}
+
+}  // namespace
+
+hipError_t launch_scan_complex(const CplxShape& s, const CplxPtrs& p, hipStream_t stream) {
+  const bool xr = s.su[1] == 1 && s.sd[1] == 1;
+  const bool br = s.sB[1] == 1 && s.sC[1] == 1;
+  if (xr && br) launch_complex_passes<true, true>(s, p, stream);
+  else if (xr) launch_complex_passes<true, false>(s, p, stream);
+  else if (br) launch_complex_passes<false, true>(s, p, stream);
+  else launch_complex_passes<false, false>(s, p, stream);
   return hipGetLastError();
 }
 

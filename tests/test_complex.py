@@ -113,6 +113,40 @@ def test_channel_last(mss):
     _case(mss, "bld", 2, 64, 77, layout="bld", h0=True)
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_layouts_bitwise_equal(mss, split):
+    """The element roles of the load phase follow the layouts (steps fastest
+    for unit time stride, channels or states fastest for unit row stride), but
+    each (channel, state) lane does the same arithmetic in the same order:
+    the four combinations of [B,D,L] / [B,L,D] activations and [B,N,L] /
+    [B,L,N] B and C give bitwise equal results, equal to the oracle.  The
+    split case (few channels, long sequence) takes the time segments."""
+    import torch
+    batch, dim, seqlen = (1, 32, 4000) if split else (2, 48, 333)
+    note(f"complex layout combinations split={split}")
+    dx = complex_to_torch(generate_complex(batch, dim, seqlen, 16, "bdl", seed=17), device())
+    init = _h0(batch, dim, 16, seed=9)
+
+    def layout(t, rows_fast):
+        return t.transpose(1, 2).contiguous().transpose(1, 2) if rows_fast else t.contiguous()
+
+    res = []
+    for x_rows in (False, True):
+        for b_rows in (False, True):
+            q = dict(dx)
+            for k in ("u", "delta_raw", "z"):
+                q[k] = layout(dx[k], x_rows)
+            for k in ("B", "C"):
+                q[k] = layout(dx[k], b_rows)
+            res.append(_run(mss, q, init))
+    torch.cuda.synchronize()
+    for out, fin in res[1:]:
+        assert torch.equal(out, res[0][0]) and torch.equal(fin, res[0][1])
+    r_out, r_fin = _ref(dx, init)
+    check("complex layouts out", to_np(res[0][0]), r_out, TOL)
+    check("complex layouts final", _cnp(res[0][1]), r_fin, TOL)
+
+
 def test_mamba130m_layer_full(mss):
     w = WORKLOADS["mamba130m_layer"]
     _case(mss, "130m layer", w.batch, w.dim, w.seqlen, w.dstate)
