@@ -214,7 +214,8 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
   s.nseg = (s.nchunk + s.seg_chunks - 1) / s.seg_chunks;
   // checkpoints in the chunk-state layout (unused when the caller passes them)
   p.ckpt_bytes = round_up(static_cast<size_t>(s.nchunk) * a->batch * a->dim * kMaxState * sizeof(float), 256);
-  p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * a->seqlen * sizeof(float), 256);
+  p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * s.nchunk *
+                            mss::kBwdT * sizeof(float), 256);
   p.chan_bytes = round_up(static_cast<size_t>(s.nseg) * a->batch * a->dim * (kMaxState + 2) * sizeof(float), 256);
   if (s.nseg > 1) {
     p.agg_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float4), 256);

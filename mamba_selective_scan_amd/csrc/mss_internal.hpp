@@ -188,7 +188,8 @@ struct BwdPtrs {
   float* dh0;
   // workspace
   float* ckpt;       // [nchunk][batch][dim][kMaxState] state entering each chunk (chunk states)
-  float* part_bc;    // [batch][tiles][2 * kMaxState][seqlen] per-workgroup dB, dC sums
+  float* part_bc;    // [batch][nchunk][tiles][2 * kMaxState][kBwdT] per-workgroup dB, dC sums:
+                     // one workgroup's chunk is 2 KB in one place
   float* part_chan;  // [nseg][batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
   float4* agg;       // [nseg][nchan_pad][kMaxState] per segment (prod a, h from 0, g from 0, -)
   float* carry_h;    // [nseg][nchan_pad][kMaxState] state entering each segment

@@ -233,6 +233,20 @@ def test_channel_last_layout(mss):
     _run_and_check(mss, "bld", _problem(2, 64, 200, 16, layout="bld", h0=True, dfinal=True))
 
 
+@pytest.mark.parametrize("case", [
+    (1, 50, 3000, "f32"),   # time segments, a partly empty 32-channel block
+    (2, 40, 333, "bf16"),   # bf16, partly empty block, ragged chunk
+    (8, 3072, 48, "f32"),   # 768 (row, block) pairs: no time segments
+])
+def test_channel_last_cooperative_rows(mss, case):
+    """Channel-last inputs: the reverse walk's workgroups load whole rows of
+    their 32-channel blocks and hand each element to the wave that scans it."""
+    batch, dim, seqlen, io = case
+    _run_and_check(mss, f"bld coop {case}",
+                   _problem(batch, dim, seqlen, 16, layout="bld", io=io, h0=True, dfinal=True),
+                   io=io)
+
+
 @pytest.mark.parametrize("seqlen", [200, 201])
 def test_bf16(mss, seqlen):
     # an even length moves the step pairs as one 32-bit access; an odd one

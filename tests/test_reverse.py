@@ -92,15 +92,19 @@ def test_bidirectional_sum(mss):
     check("bidirectional sum", to_np(both), f + r[:, :, ::-1], 1e-4)
 
 
-@pytest.mark.parametrize("shape", [(2, 72, 100), (1, 64, 1500)])
-def test_reverse_backward(mss, shape):
+@pytest.mark.parametrize("shape,layout", [((2, 72, 100), "bdl"), ((1, 64, 1500), "bdl"),
+                                          ((1, 40, 1500), "bld")])
+def test_reverse_backward(mss, shape, layout):
     import torch
     batch, dim, seqlen = shape
-    note(f"reverse bwd {shape}")
-    x = generate(batch, dim, seqlen, 16, seed=23, a_log="normal")
+    note(f"reverse bwd {shape} {layout}")
+    x = generate(batch, dim, seqlen, 16, layout, seed=23, a_log="normal")
     dx = to_torch(x, device(), "f32")
     g = torch.Generator().manual_seed(5)
-    dout = torch.randn(batch, dim, seqlen, generator=g).to(device())
+    dout = torch.randn(batch, dim, seqlen, generator=g)
+    if layout == "bld":
+        dout = dout.transpose(1, 2).contiguous().transpose(1, 2)
+    dout = dout.to(device())
     h0 = torch.randn(batch, dim, 16, generator=g).to(device())
     dfin = torch.randn(batch, dim, 16, generator=g).to(device())
     got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dout,
