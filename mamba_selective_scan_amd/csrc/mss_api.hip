@@ -202,6 +202,7 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
   s.dstate = static_cast<int>(a->dstate);
   s.softplus = a->delta_softplus ? 1 : 0;
   s.nchunk = static_cast<int>((a->seqlen + mss::kBwdT - 1) / mss::kBwdT);
+  s.npair = (s.nchunk + 1) / 2;
   s.tiles = static_cast<int>((a->dim + mss::kBwdCh - 1) / mss::kBwdCh);
   s.nchan_pad = a->batch * s.tiles * mss::kBwdCh;
   s.reverse = a->reverse;
@@ -214,7 +215,7 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
   s.nseg = (s.nchunk + s.seg_chunks - 1) / s.seg_chunks;
   // checkpoints in the chunk-state layout (unused when the caller passes them)
   p.ckpt_bytes = round_up(static_cast<size_t>(s.nchunk) * a->batch * a->dim * kMaxState * sizeof(float), 256);
-  p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * s.nchunk *
+  p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * s.npair * 2 *
                             mss::kBwdT * sizeof(float), 256);
   p.chan_bytes = round_up(static_cast<size_t>(s.nseg) * a->batch * a->dim * (kMaxState + 2) * sizeof(float), 256);
   if (s.nseg > 1) {

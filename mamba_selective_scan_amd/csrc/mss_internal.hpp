@@ -147,6 +147,7 @@ struct BwdShape {
   int batch, dim, seqlen, dstate;
   int softplus;
   int nchunk;         // ceil(seqlen / kBwdT)
+  int npair;          // ceil(nchunk / 2)
   int tiles;          // ceil(dim / kBwdCh) workgroups per batch row
   int nseg;           // time segments (each seg_chunks chunks; the last may be shorter)
   int seg_chunks;
@@ -188,8 +189,8 @@ struct BwdPtrs {
   float* dh0;
   // workspace
   float* ckpt;       // [nchunk][batch][dim][kMaxState] state entering each chunk (chunk states)
-  float* part_bc;    // [batch][nchunk][tiles][2 * kMaxState][kBwdT] per-workgroup dB, dC sums:
-                     // one workgroup's chunk is 2 KB in one place
+  float* part_bc;    // [batch][npair][tiles][2 * kMaxState][2 kBwdT] per-workgroup dB, dC sums:
+                     // a workgroup's two chunks of a pair fill 128-byte row pieces, 4 KB in one place
   float* part_chan;  // [nseg][batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
   float4* agg;       // [nseg][nchan_pad][kMaxState] per segment (prod a, h from 0, g from 0, -)
   float* carry_h;    // [nseg][nchan_pad][kMaxState] state entering each segment

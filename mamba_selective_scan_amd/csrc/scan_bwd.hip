@@ -802,8 +802,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
       for (int ww = 0; ww < kBwdWaves; ++ww) sum += red[ww * kRedSize + r * kBwdT + tt];
       if ((r & 15) < s.dstate && t < s.seqlen)
         __builtin_nontemporal_store(
-            sum, &p.part_bc[(((static_cast<int64_t>(b) * s.nchunk + q) * s.tiles + tile) *
-                                 2 * kMaxState + r) * kBwdT + tt]);
+            sum, &p.part_bc[(((static_cast<int64_t>(b) * s.npair + (q >> 1)) * s.tiles + tile) *
+                                 2 * kMaxState + r) * (2 * kBwdT) + (q & 1) * kBwdT + tt]);
     }
   };
 
@@ -1022,8 +1022,8 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
   const int r = is_c ? kMaxState + n : n;
   const float sum = ordered_sum(s.tiles, [&](int tile) {
     return __builtin_nontemporal_load(
-        &p.part_bc[(((static_cast<int64_t>(b) * s.nchunk + t / kBwdT) * s.tiles + tile) * 2 *
-                        kMaxState + r) * kBwdT + t % kBwdT]);
+        &p.part_bc[(((static_cast<int64_t>(b) * s.npair + t / (2 * kBwdT)) * s.tiles + tile) * 2 *
+                        kMaxState + r) * (2 * kBwdT) + t % (2 * kBwdT)]);
   });
   if (is_c)
     io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + tstore(s, t) * s.sdC[2], sum);
