@@ -435,10 +435,11 @@ def test_bwd_workspace_size():
     n = lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st))
     assert st.value == 0
     # the reverse walk takes 32-channel tiles: checkpoints 7 chunks x 2*3*32 padded
-    # channels x 16 states; partials 2 rows x 3 tiles x 32 x 100 steps; per-row sums
-    # 2 x 96 x 18 (each rounded up to 256 B)
+    # channels x 16 states; partials 2 rows x 4 chunk pairs (32 steps each, the
+    # 100 steps rounded up) x 3 tiles x 32; per-row sums 2 x 96 x 18 (each
+    # rounded up to 256 B)
     r = lambda v: (v + 255) // 256 * 256
-    assert n == r(7 * 2 * 96 * 16 * 4) + r(2 * 3 * 32 * 100 * 4) + r(2 * 96 * 18 * 4)
+    assert n == r(7 * 2 * 96 * 16 * 4) + r(2 * 4 * 3 * 32 * 32 * 4) + r(2 * 96 * 18 * 4)
     a.dstate = 0
     assert lib.mss_selective_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(st)) == 0
     assert st.value == code("MSS_ERR_UNSUPPORTED_DSTATE")
