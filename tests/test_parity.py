@@ -186,10 +186,12 @@ def test_time_invariant_register_path_equals_materialised(mss, layout, io, rever
     for d_in in (dx, dm):
         res.append(mss.selective_scan_fwd(
             d_in["u"], d_in["delta_raw"], d_in["A_log"], d_in["B"], d_in["C"], D=d_in["D"],
-            z=d_in["z"], dt_bias=d_in["dt_bias"], reverse=reverse, return_final_state=True))
+            z=d_in["z"], dt_bias=d_in["dt_bias"], reverse=reverse, return_final_state=True,
+            return_chunk_states=True))
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0]), "outputs differ"
     assert torch.equal(res[0][1], res[1][1]), "final states differ"
+    assert torch.equal(res[0][2], res[1][2]), "chunk states differ"
     if not reverse:
         ref_out, ref_fin = oracle_full(dx)
         check(f"LTI {layout} {io} out", to_np(res[0][0]), ref_out, tol_for(io))
