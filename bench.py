@@ -249,7 +249,7 @@ def load_traffic(workload: str, io: str, src_hash: str, op: str = "scan"):
     return rec.get("traffic_bytes_per_launch")
 
 
-def graph_us(fn, reps: int, inner: int = 1) -> float:
+def graph_us(fn, reps: int, inner: int = 1, settle_seconds: float = 0.2) -> float:
     """Mean GPU time per call of fn: fn recorded `inner` times in one HIP graph,
     the graph replayed `reps` times between two events, so no host launch
     cost enters (what a caller that records its loop sees)."""
@@ -266,6 +266,9 @@ def graph_us(fn, reps: int, inner: int = 1) -> float:
             fn()
     g.replay()
     torch.cuda.synchronize()
+    # the capture left the GPU idle: replay untimed until the clock is back
+    # at its sustained value, as the eager steps were timed
+    settle(g.replay, settle_seconds)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
@@ -423,8 +426,10 @@ def main_conv(args):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(ms) / len(ms)
-    conv_graph_us = graph_us(conv, reps=max(5, min(200, int(20e3 / (mean_ms * 1e3)))))
-    dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64)
+    conv_graph_us = graph_us(conv, reps=max(5, min(200, int(20e3 / (mean_ms * 1e3)))),
+                             settle_seconds=min(args.settle_seconds, 0.3))
+    dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64,
+                                                        settle_seconds=min(args.settle_seconds, 0.3))
     fwd_bytes = conv_algorithmic_bytes(w.batch, w.dim, w.seqlen, width, io_bytes)
     fwd_bytes += w.batch * w.dim * (width - 1) * io_bytes          # exported window
     step_b = 0 if args.no_step else (2 * w.batch * w.dim * (width - 1) * io_bytes
@@ -972,8 +977,10 @@ def main(argv=None):
             wev[i][1].record(stream)
         torch.cuda.synchronize()
         warm_us = sum(a.elapsed_time(b) for a, b in wev) / args.steps * 1e3
-    scan_graph_us = graph_us(scan, reps=max(5, min(200, int(20e3 / (scan_ms_mean * 1e3)))))
-    dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64)
+    scan_graph_us = graph_us(scan, reps=max(5, min(200, int(20e3 / (scan_ms_mean * 1e3)))),
+                             settle_seconds=min(args.settle_seconds, 0.3))
+    dec_graph_us = None if args.no_step else graph_us(decode, reps=10, inner=64,
+                                                        settle_seconds=min(args.settle_seconds, 0.3))
     # the clock while the timed steps ran, else while the settling launches ran
     sclk = timed_clock.mean if len(timed_clock.vals) >= 3 else settled.mean
     sclk_src = None if sclk is None else SCLK_SOURCE + (

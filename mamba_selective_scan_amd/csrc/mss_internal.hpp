@@ -24,6 +24,14 @@ constexpr int kPerThread = kCh * kT / kThreads;      // 4 tile elements per lane
 
 // Carry kernels (time segments): aggregates loaded per batch of segments.
 constexpr int kCarryBatch = 16;
+// The forward's carry workgroup cuts the chain of nseg - 1 aggregates into
+// ranges of at most kCarryBatch segments (when that takes at most kCarryWaves
+// waves), one wave each.
+constexpr int kCarryWaves = 16;
+inline int carry_waves(int nseg) {
+  const int w = (nseg - 1 + kCarryBatch - 1) / kCarryBatch;
+  return w < 1 ? 1 : (w > kCarryWaves ? kCarryWaves : w);
+}
 
 // Sizes and element strides (logical order) of one scan call.  Pointers are
 // passed as separate kernel arguments so they can carry __restrict__.
