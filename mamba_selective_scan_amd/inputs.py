@@ -105,6 +105,43 @@ def generate(batch: int, dim: int, seqlen: int, dstate: int, layout: str = "bdl"
             "A_log": A_log, "D": D, "dt_bias": dt_bias, "layout": layout}
 
 
+def generate_device(batch: int, dim: int, seqlen: int, dstate: int, layout: str = "bdl",
+                    seed: int = 0, device="cuda") -> dict:
+    """The recipe of ``generate`` drawn on ``device`` with torch's generator,
+    for problems too large to draw on the host and copy over (tensors of many
+    GiB).  The distributions are the same; the random stream is torch's
+    (u, delta_raw, z, B, C drawn in that order from one generator seeded with
+    ``seed``), not numpy's.  The small per-channel parameters (dt_bias,
+    A_log = log(n + 1), D = 1) come from ``generate``'s own rules, dt from a
+    numpy stream seeded with ``seed``.  Returns float32 torch tensors in
+    logical index order, as views over the storage layout."""
+    import torch
+
+    if layout not in ("bdl", "bld"):
+        raise ValueError("layout must be 'bdl' or 'bld'")
+    g = torch.Generator(device=device).manual_seed(seed)
+    if layout == "bdl":
+        x_shape, bc_shape = (batch, dim, seqlen), (batch, dstate, seqlen)
+    else:
+        x_shape, bc_shape = (batch, seqlen, dim), (batch, seqlen, dstate)
+
+    def draw(shape, scale=1.0):
+        a = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            a.mul_(scale)
+        return a if layout == "bdl" else a.transpose(1, 2)
+
+    out = {"u": draw(x_shape), "delta_raw": draw(x_shape, 0.1), "z": draw(x_shape),
+           "B": draw(bc_shape), "C": draw(bc_shape)}
+    rng = np.random.default_rng(seed)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), size=dim))
+    out["dt_bias"] = torch.from_numpy(np.log(np.expm1(dt)).astype(np.float32)).to(device)
+    a_log = np.tile(np.log(np.arange(1, dstate + 1, dtype=np.float64)), (dim, 1))
+    out["A_log"] = torch.from_numpy(a_log.astype(np.float32)).to(device)
+    out["D"] = torch.ones(dim, device=device, dtype=torch.float32)
+    return out
+
+
 def softplus_range_delta(batch: int, dim: int, seqlen: int, seed: int = 0,
                          big_bias: bool = False) -> tuple:
     """(delta_raw [batch, dim, seqlen], dt_bias [dim]) float32 whose sum
