@@ -5,12 +5,13 @@ A [2, 4096, 280000] float32 tensor holds 2.29e9 elements (more than 2^31) in
 every 32-bit wrap point of both.  The kernels address memory through 64-bit
 tile or row bases plus 32-bit offsets inside a tile; these tests run that
 arithmetic where a 32-bit product would wrap: the scan forward in both layouts
-(with time segments: the shape has 1024 channel tiles), the backward and the
-conv.  Sampled channels, the first and last of each batch row among them, are
-compared over their whole sequences with the oracle at the fp32 tolerance.
+(with time segments: the shape has 1024 channel tiles), the backward, the
+complex-A forward and the conv.  Sampled channels, the first and last of each
+batch row among them, are compared over their whole sequences with the oracle
+at the fp32 tolerance.
 Inputs are drawn on the device (``generate_device``: the workload recipe with
-torch's generator).  Device memory: about 40 GB for the forward and the conv,
-85 GB for the backward, released after each test.
+torch's generator).  Device memory: about 40 GB for the forward, the complex
+forward and the conv, 85 GB for the backward, released after each test.
 """
 
 import numpy as np
@@ -89,6 +90,40 @@ def test_backward_past_32bit_offsets(mss, fresh_memory):
         check(f"large backward {k}", to_np(got[k][:, ci]), ref[k], TOL)
     for k in ("dA_log", "dD", "ddt_bias"):
         check(f"large backward {k}", to_np(got[k][ci]), ref[k], TOL)
+
+
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+def test_complex_forward_past_32bit_offsets(mss, fresh_memory, layout):
+    """Complex B and C with unit complex variance and A_imag = pi n, as the
+    complex workload recipe has them, drawn on the device."""
+    import torch
+    note(f"large complex forward: B={BATCH} D={DIM} L={SEQLEN} N={DSTATE} {layout} f32")
+    x = generate_device(BATCH, DIM, SEQLEN, DSTATE, layout, seed=6, device=device())
+    g = torch.Generator(device=device()).manual_seed(66)
+    half = 0.5 ** 0.5
+    for k in ("B", "C"):
+        shape = (BATCH, DSTATE, SEQLEN) if layout == "bdl" else (BATCH, SEQLEN, DSTATE)
+        re = torch.randn(shape, generator=g, device=device()) * half
+        im = torch.randn(shape, generator=g, device=device()) * half
+        c = torch.complex(re, im)
+        x[k] = c if layout == "bdl" else c.transpose(1, 2)
+    a_imag = torch.pi * torch.arange(DSTATE, device=device(), dtype=torch.float32)
+    x["A_imag"] = a_imag.expand(DIM, DSTATE).contiguous()
+    out, fin = mss.selective_scan_fwd_complex(x["u"], x["delta_raw"], x["A_log"], x["A_imag"],
+                                              x["B"], x["C"], D=x["D"], z=x["z"],
+                                              dt_bias=x["dt_bias"], return_final_state=True)
+    torch.cuda.synchronize()
+    for b in range(BATCH):
+        ds = [d for bb, d in CHANNELS if bb == b]
+        ci = torch.as_tensor(ds, device=device())
+        row = slice(b, b + 1)
+        cnp = lambda t: t.detach().to("cpu", torch.complex128).numpy()  # noqa: E731
+        r_out, r_fin = oracle.scan_fwd_complex(
+            x["u"][row, ci], x["delta_raw"][row, ci], x["A_log"][ci], x["A_imag"][ci],
+            cnp(x["B"][row]), cnp(x["C"][row]), D=x["D"][ci], z=x["z"][row, ci],
+            dt_bias=x["dt_bias"][ci])
+        check(f"large complex {layout} row {b} out", to_np(out[row, ci]), r_out, TOL)
+        check(f"large complex {layout} row {b} final", cnp(fin[row, ci]), r_fin, TOL)
 
 
 @pytest.mark.parametrize("layout", ["bdl", "bld"])
