@@ -33,6 +33,84 @@ inline int carry_waves(int nseg) {
   return w < 1 ? 1 : (w > kCarryWaves ? kCarryWaves : w);
 }
 
+// Links of a linear chain c_{k+1} = P_k c_k + H_k: a real link is (P, H)
+// acting on a float, a complex one (Re P, Im P, Re H, Im H) acting on
+// (Re c, Im c).  link_then(acc, a) is the link acc followed by a.
+__device__ inline float link_apply(float2 a, float c) { return fmaf(a.x, c, a.y); }
+__device__ inline float2 link_then(float2 acc, float2 a) {
+  return make_float2(acc.x * a.x, fmaf(a.x, acc.y, a.y));
+}
+__device__ inline float2 link_identity(float2) { return make_float2(1.0f, 0.0f); }
+__device__ inline float2 link_apply(float4 a, float2 c) {
+  return make_float2(fmaf(a.x, c.x, fmaf(-a.y, c.y, a.z)), fmaf(a.x, c.y, fmaf(a.y, c.x, a.w)));
+}
+__device__ inline float4 link_then(float4 acc, float4 a) {
+  const float2 P = link_apply(make_float4(a.x, a.y, 0.0f, 0.0f), make_float2(acc.x, acc.y));
+  const float2 H = link_apply(a, make_float2(acc.z, acc.w));
+  return make_float4(P.x, P.y, H.x, H.y);
+}
+__device__ inline float4 link_identity(float4) { return make_float4(1.0f, 0.0f, 0.0f, 0.0f); }
+
+// A chain c_{k+1} = link_k(c_k) over links k = 0 .. nlink - 1 from c_0,
+// walked by the waves of one workgroup in ranges (the links compose
+// associatively), one lane per chain in every wave: a wave composes its range
+// into one link, loading its links kCarryBatch at a time ahead of the
+// arithmetic; the ranges' links meet in LDS (xch, a slot per wave and lane);
+// each wave walks its range again from the value entering it.  link(k)
+// returns link k for any k in [0, nlink), also in a lane whose chain is not
+// valid (its loads must stay in bounds there); put(k, c) receives c_{k+1}
+// and is called in valid lanes only.  nlink >= 1.  Every thread of the
+// workgroup calls it (it holds a barrier), in a workgroup of
+// 64 x carry_waves(nlink + 1) threads.
+template <typename Pair, typename Val, typename Link, typename Put>
+__device__ inline void walk_chain_in_ranges(int nlink, Val c, bool valid, Pair (*xch)[64],
+                                            Link link, Put put) {
+  const int lane = static_cast<int>(threadIdx.x) % 64;
+  const int w = static_cast<int>(threadIdx.x) / 64;
+  const int nw = static_cast<int>(blockDim.x) / 64;
+  const int per = (nlink + nw - 1) / nw;
+  const int s0 = min(w * per, nlink);
+  const int s1 = min(s0 + per, nlink);
+  const Pair one = link_identity(Pair{});
+  auto load_batch = [&](Pair (&a)[kCarryBatch], int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {  // past the range: the identity
+      const bool in = base + j < s1;
+      const Pair v = link(in ? base + j : 0);
+      a[j] = in ? v : one;
+    }
+  };
+  Pair first[kCarryBatch];
+  load_batch(first, s0);
+  Pair acc = one;
+#pragma unroll
+  for (int j = 0; j < kCarryBatch; ++j) acc = link_then(acc, first[j]);
+  for (int base = s0 + kCarryBatch; base < s1; base += kCarryBatch) {
+    Pair a[kCarryBatch];
+    load_batch(a, base);
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) acc = link_then(acc, a[j]);
+  }
+  xch[w][lane] = acc;
+  __syncthreads();
+  for (int k = 0; k < w; ++k) c = link_apply(xch[k][lane], c);
+  if (!valid) return;
+#pragma unroll
+  for (int j = 0; j < kCarryBatch; ++j) {
+    c = link_apply(first[j], c);
+    if (s0 + j < s1) put(s0 + j, c);
+  }
+  for (int base = s0 + kCarryBatch; base < s1; base += kCarryBatch) {
+    Pair a[kCarryBatch];
+    load_batch(a, base);
+#pragma unroll
+    for (int j = 0; j < kCarryBatch; ++j) {
+      c = link_apply(a[j], c);
+      if (base + j < s1) put(base + j, c);
+    }
+  }
+}
+
 // Sizes and element strides (logical order) of one scan call.  Pointers are
 // passed as separate kernel arguments so they can carry __restrict__.
 struct ScanShape {
@@ -147,6 +225,7 @@ hipError_t launch_conv_step(const ConvStepShape& s, const ConvStepPtrs& p, bool 
 // chunks of kBwdT steps, the last chunk first.  Four-wave workgroups at up
 // to 168 VGPRs and 46 KB of LDS put three workgroups on a CU.
 constexpr int kBwdT = kStateChunk;  // a backward chunk is one chunk-state interval
+constexpr int kBcSteps = 4;          // dB/dC sum: consecutive steps per thread
 constexpr int kBwdWaves = 4;
 constexpr int kBwdCh = kCh * kBwdWaves;  // 32
 constexpr int kBwdThreads = 64 * kBwdWaves;

@@ -407,49 +407,43 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
 }
 
 // State entering each segment (forward) and adjoint reaching each segment's
-// last state (backward), one lane per (padded channel row, state).
-__global__ __launch_bounds__(256) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= s.nchan_pad * kMaxState) return;
-  const int n = static_cast<int>(idx % kMaxState);
-  const int64_t row = idx / kMaxState;
+// last state (backward), one lane per (padded channel row, state); each chain
+// is walked in ranges of segments, one wave each (walk_chain_in_ranges).
+__global__ __launch_bounds__(64 * kCarryWaves) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
+  __shared__ float2 xch[kCarryWaves][64];
+  const int64_t sstride = s.nchan_pad * kMaxState;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x % 64;
+  const bool valid = idx < sstride;
+  const int64_t ic = valid ? idx : 0;
+  const int n = static_cast<int>(ic % kMaxState);
+  const int64_t row = ic / kMaxState;
   const int64_t per_b = static_cast<int64_t>(s.tiles) * kBwdCh;
   const int b = static_cast<int>(row / per_b);
   const int d = static_cast<int>(row % per_b);
-  const bool active = d < s.dim && n < s.dstate;
-  const int64_t sstride = s.nchan_pad * kMaxState;
-  float h = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
-  p.carry_h[idx] = h;
-  // the aggregates do not depend on the chains: load kCarryBatch segments
-  // ahead of the multiply-adds (one memory latency per batch)
-  for (int base = 0; base + 1 < s.nseg; base += kCarryBatch) {
-    float2 a[kCarryBatch];
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      const float4 v = p.agg[min(base + j, s.nseg - 2) * sstride + idx];
-      a[j] = base + j + 1 < s.nseg ? make_float2(v.x, v.y) : make_float2(1.0f, 0.0f);
-    }
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      h = fmaf(a[j].x, h, a[j].y);
-      if (base + j + 1 < s.nseg) p.carry_h[(base + j + 1) * sstride + idx] = h;
-    }
-  }
-  float g = (active && p.dfinal != nullptr) ? p.dfinal[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
-  p.carry_g[(s.nseg - 1) * sstride + idx] = g;
-  for (int top = s.nseg - 1; top > 0; top -= kCarryBatch) {
-    float2 a[kCarryBatch];
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      const float4 v = p.agg[max(top - j, 1) * sstride + idx];
-      a[j] = top - j > 0 ? make_float2(v.x, v.z) : make_float2(1.0f, 0.0f);
-    }
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      g = fmaf(a[j].x, g, a[j].y);
-      if (top - j > 0) p.carry_g[(top - j - 1) * sstride + idx] = g;
-    }
-  }
+  const bool active = valid && d < s.dim && n < s.dstate;
+  const int64_t ch = (static_cast<int64_t>(b) * s.dim + d) * s.dstate + n;
+  // the state entering each segment, forward over the segments
+  const float h = (active && p.h0 != nullptr) ? p.h0[ch] : 0.0f;
+  if (valid) p.carry_h[idx] = h;
+  walk_chain_in_ranges(
+      s.nseg - 1, h, valid, xch,
+      [&](int k) {
+        const float4 v = p.agg[k * sstride + ic];
+        return make_float2(v.x, v.y);
+      },
+      [&](int k, float c) { p.carry_h[(k + 1) * sstride + idx] = c; });
+  __syncthreads();  // xch is used again
+  // the adjoint reaching each segment's end, backward over the segments:
+  // link k is segment nseg - 1 - k
+  const float g = (active && p.dfinal != nullptr) ? p.dfinal[ch] : 0.0f;
+  if (valid) p.carry_g[(s.nseg - 1) * sstride + idx] = g;
+  walk_chain_in_ranges(
+      s.nseg - 1, g, valid, xch,
+      [&](int k) {
+        const float4 v = p.agg[(s.nseg - 1 - k) * sstride + ic];
+        return make_float2(v.x, v.z);
+      },
+      [&](int k, float c) { p.carry_g[(s.nseg - 2 - k) * sstride + idx] = c; });
 }
 
 // ---------------------------------------------------------------- pass 1 ---
@@ -1007,28 +1001,67 @@ __device__ inline float ordered_sum(int n, F f) {
   return sum;
 }
 
-// dB / dC[b, n, t] = sum over the row's workgroups of their partials.
-template <typename IO>
+// dB / dC[b, n, t] = sum over the row's workgroups of their partials, added
+// in tile order.  A thread sums four consecutive steps of one state: they are
+// adjacent in a partial row (a pair of chunks holds 2 kBwdT steps), so each
+// tile's terms arrive as one 16-byte load, and the four sums keep the order
+// of a one-step sum.  NF (outputs with unit state stride, as channel-last B
+// and C give them): a wave takes 8 states x 32 steps (8 lanes per state,
+// each loading 16 bytes of the state's 128-byte partial row), and the two
+// waves of a state-half pair cover all 16 states of those steps, so that the
+// stores fill whole runs of the output instead of one 4-byte word per 64
+// bytes, and every load still reads whole partial rows.
+static_assert((2 * kBwdT) % kBcSteps == 0, "a thread's steps lie in one partial row");
+template <typename IO, bool NF>
 __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
-  const int64_t n_items = static_cast<int64_t>(s.batch) * 2 * s.dstate * s.seqlen;
+  const int nq = (s.seqlen + kBcSteps - 1) / kBcSteps;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n_items) return;
-  const int t = static_cast<int>(i % s.seqlen);
-  const int64_t rest = i / s.seqlen;
-  const int j = static_cast<int>(rest % (2 * s.dstate));
-  const int b = static_cast<int>(rest / (2 * s.dstate));
-  const bool is_c = j >= s.dstate;
-  const int n = is_c ? j - s.dstate : j;
+  int t0, n, b;
+  bool is_c;
+  if constexpr (NF) {  // i = (((b * 2 + is_c) * nqb + qb) * 2 + n_hi) * 64 + q_lo * 8 + n_lo
+    constexpr int kQ = 2 * kBwdT / kBcSteps;  // step quads per partial row: 8
+    const int nqb = (nq + kQ - 1) / kQ;
+    if (i >= static_cast<int64_t>(s.batch) * 2 * nqb * 2 * 64) return;
+    const int lane = static_cast<int>(i % 64);
+    const int64_t rest = i / 64;
+    n = (lane % 8) + 8 * static_cast<int>(rest % 2);
+    const int q = static_cast<int>((rest / 2) % nqb) * kQ + lane / 8;
+    if (n >= s.dstate || q >= nq) return;
+    t0 = q * kBcSteps;
+    is_c = (rest / 2 / nqb) % 2 != 0;
+    b = static_cast<int>(rest / 2 / nqb / 2);
+  } else {  // i = ((b * 2 * dstate) + j) * nq + q
+    if (i >= static_cast<int64_t>(s.batch) * 2 * s.dstate * nq) return;
+    t0 = static_cast<int>(i % nq) * kBcSteps;
+    const int64_t rest = i / nq;
+    const int j = static_cast<int>(rest % (2 * s.dstate));
+    b = static_cast<int>(rest / (2 * s.dstate));
+    is_c = j >= s.dstate;
+    n = is_c ? j - s.dstate : j;
+  }
   const int r = is_c ? kMaxState + n : n;
-  const float sum = ordered_sum(s.tiles, [&](int tile) {
-    return __builtin_nontemporal_load(
-        &p.part_bc[(((static_cast<int64_t>(b) * s.npair + t / (2 * kBwdT)) * s.tiles + tile) * 2 *
-                        kMaxState + r) * (2 * kBwdT) + t % (2 * kBwdT)]);
-  });
-  if (is_c)
-    io_traits<IO>::store(static_cast<IO*>(p.dC) + b * s.sdC[0] + n * s.sdC[1] + tstore(s, t) * s.sdC[2], sum);
-  else
-    io_traits<IO>::store(static_cast<IO*>(p.dB) + b * s.sdB[0] + n * s.sdB[1] + tstore(s, t) * s.sdB[2], sum);
+  using v4 = float __attribute__((ext_vector_type(4)));
+  constexpr int64_t kTileStride = 2 * kMaxState * 2 * kBwdT;  // floats between tiles
+  const float* row = p.part_bc +
+      (((static_cast<int64_t>(b) * s.npair + t0 / (2 * kBwdT)) * s.tiles) * 2 * kMaxState + r) *
+          (2 * kBwdT) + t0 % (2 * kBwdT);
+  v4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t0b = 0; t0b < s.tiles; t0b += kSumBatch) {
+    v4 v[kSumBatch];
+#pragma unroll
+    for (int k = 0; k < kSumBatch; ++k)
+      v[k] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4*>(row + min(t0b + k, s.tiles - 1) * kTileStride));
+#pragma unroll
+    for (int k = 0; k < kSumBatch; ++k)
+      if (t0b + k < s.tiles) sum += v[k];
+  }
+  IO* out = static_cast<IO*>(is_c ? p.dC : p.dB) + b * (is_c ? s.sdC[0] : s.sdB[0]) +
+            n * (is_c ? s.sdC[1] : s.sdB[1]);
+  const int64_t st = is_c ? s.sdC[2] : s.sdB[2];
+#pragma unroll
+  for (int e = 0; e < kBcSteps; ++e)
+    if (t0 + e < s.seqlen) io_traits<IO>::store(out + tstore(s, t0 + e) * st, sum[e]);
 }
 
 // ---------------------------------------------------------------- pass 4 ---
@@ -1081,7 +1114,8 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
   if (s.nseg > 1) {
     launch_agg<IO>(s, p, stream, static_cast<unsigned>(waves));
     const int64_t nc = s.nchan_pad * kMaxState;
-    carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
+    carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 63) / 64)), dim3(64 * carry_waves(s.nseg)),
+                       0, stream>>>(s, p);
   }
   // chunk states recorded by the forward replace the checkpoint pass
   if (s.states_given == 0) {
@@ -1100,8 +1134,17 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
     bwd_kernel<IO, true><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
   else
     bwd_kernel<IO, false><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
-  const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * s.dstate * s.seqlen;
-  reduce_bc_kernel<IO><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream>>>(s, p);
+  const int64_t nq = (s.seqlen + kBcSteps - 1) / kBcSteps;
+  if (s.sdB[1] == 1 && s.sdB[2] != 1) {
+    constexpr int kQ = 2 * kBwdT / kBcSteps;
+    const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * ((nq + kQ - 1) / kQ) * 2 * 64;
+    reduce_bc_kernel<IO, true><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0,
+                                 stream>>>(s, p);
+  } else {
+    const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * s.dstate * nq;
+    reduce_bc_kernel<IO, false><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0,
+                                  stream>>>(s, p);
+  }
   const int64_t nch = static_cast<int64_t>(s.dim) * (kMaxState + 2);
   finalize_kernel<<<dim3(static_cast<unsigned>((nch + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   return hipGetLastError();

@@ -39,6 +39,8 @@
 // exp(A sum_t delta_t): its modulus comes from the sum of the deltas, and its
 // phase from the per-step turns accumulated modulo one turn (a sum of the
 // deltas times Im(A) would lose the phase to rounding over long segments).
+#include <algorithm>
+
 #include "mss_device.hpp"
 #include "mss_internal.hpp"
 #include "mss_cplx.hpp"
@@ -239,41 +241,31 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
 
 // carry[k] = complex state entering segment k: carry[0] = h0 (or 0),
 // carry[k+1] = P[k] carry[k] + H[k].  One lane per (channel, state); the
-// aggregates do not depend on the chain, so they are loaded kCarryBatch
-// segments at a time ahead of the multiply-adds.
-__global__ __launch_bounds__(256) void carry_cplx_kernel(CplxShape s, const float4* __restrict__ agg,
-                                                         const float2* __restrict__ h0,
-                                                         float2* __restrict__ carry) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= s.nchan_pad * kMaxState) return;
-  const int n = static_cast<int>(idx % kMaxState);
-  const int64_t row = idx / kMaxState;
-  const int64_t per_b = static_cast<int64_t>(s.tiles) * kCxCh;
-  const int b = static_cast<int>(row / per_b);
-  const int d = static_cast<int>(row % per_b);
+// chain is walked in ranges of segments, one wave each
+// (walk_chain_in_ranges), at most kCarryWavesCx waves: a range held in
+// registers is kCarryBatch complex links, 64 registers, and 16 waves per
+// workgroup would leave 128 registers per lane.
+constexpr int kCarryWavesCx = 8;
+__global__ __launch_bounds__(64 * kCarryWavesCx) void carry_cplx_kernel(
+    CplxShape s, const float4* __restrict__ agg, const float2* __restrict__ h0,
+    float2* __restrict__ carry) {
+  __shared__ float4 xch[kCarryWavesCx][64];
   const int64_t sstride = s.nchan_pad * kMaxState;
-  float cr = 0.0f, ci = 0.0f;
-  if (h0 != nullptr && d < s.dim && n < s.dstate) {
-    const float2 v = h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
-    cr = v.x;
-    ci = v.y;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x % 64;
+  const bool valid = idx < sstride;
+  const int64_t ic = valid ? idx : 0;
+  float2 c = make_float2(0.0f, 0.0f);
+  if (valid && h0 != nullptr) {
+    const int n = static_cast<int>(idx % kMaxState);
+    const int64_t row = idx / kMaxState;
+    const int64_t per_b = static_cast<int64_t>(s.tiles) * kCxCh;
+    const int b = static_cast<int>(row / per_b);
+    const int d = static_cast<int>(row % per_b);
+    if (d < s.dim && n < s.dstate) c = h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
   }
-  for (int base = 0; base + 1 < s.nseg; base += kCarryBatch) {
-    float4 a[kCarryBatch];
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {  // past the last aggregate: the identity
-      const float4 v = agg[min(base + j, s.nseg - 2) * sstride + idx];
-      a[j] = base + j + 1 < s.nseg ? v : make_float4(1.0f, 0.0f, 0.0f, 0.0f);
-    }
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      const float nr = fmaf(a[j].x, cr, fmaf(-a[j].y, ci, a[j].z));
-      const float ni = fmaf(a[j].x, ci, fmaf(a[j].y, cr, a[j].w));
-      cr = nr;
-      ci = ni;
-      if (base + j + 1 < s.nseg) carry[(base + j + 1) * sstride + idx] = make_float2(cr, ci);
-    }
-  }
+  walk_chain_in_ranges(
+      s.nseg - 1, c, valid, xch, [&](int k) { return agg[k * sstride + ic]; },
+      [&](int k, float2 v) { carry[(k + 1) * sstride + idx] = v; });
 }
 
 template <bool XR, bool BR>
@@ -283,7 +275,8 @@ void launch_complex_passes(const CplxShape& s, const CplxPtrs& p, hipStream_t st
     scan_cplx_kernel<true, XR, BR><<<dim3(tiles * static_cast<unsigned>(s.nseg - 1)),
                                      dim3(kCxThreads), 0, stream>>>(s, p);
     const int64_t lanes = s.nchan_pad * kMaxState;
-    carry_cplx_kernel<<<dim3(static_cast<unsigned>((lanes + 255) / 256)), dim3(256), 0, stream>>>(
+    carry_cplx_kernel<<<dim3(static_cast<unsigned>((lanes + 63) / 64)),
+                        dim3(64 * std::min(carry_waves(s.nseg), kCarryWavesCx)), 0, stream>>>(
         s, p.agg, p.h0, p.carry);
   }
   scan_cplx_kernel<false, XR, BR><<<dim3(tiles * static_cast<unsigned>(s.nseg)), dim3(kCxThreads),

@@ -773,57 +773,19 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
 
 // carry[s] = state entering segment s, from the segment aggregates:
 //   carry[0] = h0 (or 0),  carry[s+1] = P[s] * carry[s] + H[s].
-// The pair operator is associative, so the chain is cut into ranges of
-// segments, one wave each, with one lane per (channel, state) in every wave.
-// A wave composes its range into one pair, the ranges' pairs meet in LDS, and
-// each wave walks its range again from the state entering it.  The aggregates
-// do not depend on the chain, so a wave loads kCarryBatch of them ahead of the
-// multiply-adds: a range of at most kCarryBatch segments costs one memory
-// latency, held in registers for the second walk (a 256-channel sequence in
-// 128 segments has only 4096 lanes, and had walked its 127 aggregates in
-// eight dependent batches).
+// One lane per (channel, state); the chain of nseg - 1 aggregates is walked in
+// ranges of at most kCarryBatch segments, one wave each (walk_chain_in_ranges):
+// one memory latency per call.  (A 256-channel sequence in 128 segments has
+// only 4096 chains, and had walked its 127 aggregates in eight dependent
+// batches.)
 __global__ __launch_bounds__(kThreads * kCarryWaves) void carry_kernel(
     ScanShape s, const float2* __restrict__ agg, const float* __restrict__ h0,
     float* __restrict__ carry) {
-  __shared__ float2 range_pair[kCarryWaves][kThreads];
-  const int lane = static_cast<int>(threadIdx.x) % kThreads;
-  const int w = static_cast<int>(threadIdx.x) / kThreads;
-  const int nw = static_cast<int>(blockDim.x) / kThreads;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + lane;
-  const bool valid = idx < s.nchan_pad * kMaxState;
+  __shared__ float2 xch[kCarryWaves][kThreads];
   const int64_t sstride = s.nchan_pad * kMaxState;  // idx = row * kMaxState + n
-  const int nagg = s.nseg - 1;
-  const int per = (nagg + nw - 1) / nw;
-  const int s0 = min(w * per, nagg);
-  const int s1 = min(s0 + per, nagg);
-  auto load_batch = [&](float2 (&a)[kCarryBatch], int base) {
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {  // past the range: the identity (1, 0)
-      const bool in = valid && base + j < s1;
-      const float2 v = agg[static_cast<int64_t>(in ? base + j : 0) * sstride + (valid ? idx : 0)];
-      a[j] = in ? v : make_float2(1.0f, 0.0f);
-    }
-  };
-  // the range's pair: (P, H) with carry_out = P * carry_in + H
-  float2 first[kCarryBatch];
-  load_batch(first, s0);
-  float P = 1.0f, H = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kCarryBatch; ++j) {
-    H = fmaf(first[j].x, H, first[j].y);
-    P *= first[j].x;
-  }
-  for (int base = s0 + kCarryBatch; base < s1; base += kCarryBatch) {
-    float2 a[kCarryBatch];
-    load_batch(a, base);
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      H = fmaf(a[j].x, H, a[j].y);
-      P *= a[j].x;
-    }
-  }
-  range_pair[w][lane] = make_float2(P, H);
-  __syncthreads();
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x % kThreads;
+  const bool valid = idx < sstride;
+  const int64_t ic = valid ? idx : 0;
   float c = 0.0f;
   if (valid && h0 != nullptr) {
     const int n = static_cast<int>(idx % kMaxState);
@@ -833,22 +795,9 @@ __global__ __launch_bounds__(kThreads * kCarryWaves) void carry_kernel(
     const int d = static_cast<int>(row % per_b);
     if (d < s.dim && n < s.dstate) c = h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
   }
-  for (int k = 0; k < w; ++k) c = fmaf(range_pair[k][lane].x, c, range_pair[k][lane].y);
-  if (!valid) return;
-#pragma unroll
-  for (int j = 0; j < kCarryBatch; ++j) {
-    c = fmaf(first[j].x, c, first[j].y);
-    if (s0 + j < s1) carry[(s0 + j + 1) * sstride + idx] = c;
-  }
-  for (int base = s0 + kCarryBatch; base < s1; base += kCarryBatch) {
-    float2 a[kCarryBatch];
-    load_batch(a, base);
-#pragma unroll
-    for (int j = 0; j < kCarryBatch; ++j) {
-      c = fmaf(a[j].x, c, a[j].y);
-      if (base + j < s1) carry[(base + j + 1) * sstride + idx] = c;
-    }
-  }
+  walk_chain_in_ranges(
+      s.nseg - 1, c, valid, xch, [&](int k) { return agg[k * sstride + ic]; },
+      [&](int k, float v) { carry[(k + 1) * sstride + idx] = v; });
 }
 
 template <typename IO, bool XT, bool BT, bool VEC, bool REV, bool LTI>
