@@ -178,6 +178,24 @@ struct BwdPlan {
 // chunks.
 constexpr int64_t kBwdSplitBelow = 768;
 constexpr int64_t kBwdMinSegChunks = 8;
+// The segment aggregate pass runs one wave per (row, 8 channels, segment),
+// three per SIMD at the split above, where its registers (about 80 with the
+// forward's chunk states given, 100 without) leave room for six or five: it
+// then cuts every segment into parts, as many as bring its grid to that many
+// waves (the carry pass composes the parts), with parts of at least
+// kBwdMinSegChunks chunks (shorter ones lost more to the longer carry chain
+// than they gained: the 130m-layer shape, 8-chunk segments).  The count is a
+// power of two, so that the carry pass finds segment boundaries with a mask.
+constexpr int64_t kBwdAggWavesGiven = 6 * 1024;
+constexpr int64_t kBwdAggWavesFull = 5 * 1024;
+int bwd_agg_split(const mss::BwdShape& s, bool states_given) {
+  const int64_t base = static_cast<int64_t>(s.batch) * s.tiles * mss::kBwdWaves * s.nseg;
+  const int64_t k = std::min<int64_t>((states_given ? kBwdAggWavesGiven : kBwdAggWavesFull) / base,
+                                      s.seg_chunks / kBwdMinSegChunks);
+  int split = 1;
+  while (2 * split <= k) split *= 2;
+  return split;
+}
 
 mss_status check_bwd_shape(const mss_scan_bwd_args* a) {
   if (a == nullptr || a->struct_size != sizeof(mss_scan_bwd_args) || (a->reverse & ~1) != 0)
@@ -223,8 +241,12 @@ BwdPlan make_bwd_plan(const mss_scan_bwd_args* a) {
   p.bc_bytes = round_up(static_cast<size_t>(a->batch) * s.tiles * 2 * kMaxState * s.npair * 2 *
                             mss::kBwdT * sizeof(float), 256);
   p.chan_bytes = round_up(static_cast<size_t>(s.nseg) * a->batch * a->dim * (kMaxState + 2) * sizeof(float), 256);
+  s.agg_split = 1;
   if (s.nseg > 1) {
-    p.agg_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float4), 256);
+    // sized for the larger split, so that the workspace does not depend on
+    // whether the forward's chunk states are passed
+    const int split = std::max(bwd_agg_split(s, true), bwd_agg_split(s, false));
+    p.agg_bytes = round_up(static_cast<size_t>(s.nseg) * split * s.nchan_pad * kMaxState * sizeof(float4), 256);
     p.carry_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float), 256);
   }
   p.workspace = p.ckpt_bytes + p.bc_bytes + p.chan_bytes + p.agg_bytes + 2 * p.carry_bytes;
@@ -742,6 +764,7 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
     p.ckpt = const_cast<float*>(a->chunk_states);
     s.states_given = 1;
   }
+  if (s.nseg > 1) s.agg_split = bwd_agg_split(s, s.states_given != 0);
   p.part_bc = reinterpret_cast<float*>(ws + plan.ckpt_bytes);
   p.part_chan = reinterpret_cast<float*>(ws + plan.ckpt_bytes + plan.bc_bytes);
   if (plan.agg_bytes > 0) {

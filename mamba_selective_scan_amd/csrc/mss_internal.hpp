@@ -238,6 +238,7 @@ struct BwdShape {
   int tiles;          // ceil(dim / kBwdCh) workgroups per batch row
   int nseg;           // time segments (each seg_chunks chunks; the last may be shorter)
   int seg_chunks;
+  int agg_split;      // the aggregate pass cuts each segment into this many parts (a power of 2)
   int64_t nchan_pad;  // batch * tiles * kBwdCh: rows of the checkpoint array
   int64_t su[3], sd[3], sz[3], sdo[3];      // u, delta_raw, z, dout: (b, d, t)
   int64_t sdu[3], sddr[3], sdz[3];          // du, ddelta_raw, dz
@@ -279,7 +280,8 @@ struct BwdPtrs {
   float* part_bc;    // [batch][npair][tiles][2 * kMaxState][2 kBwdT] per-workgroup dB, dC sums:
                      // a workgroup's two chunks of a pair fill 128-byte row pieces, 4 KB in one place
   float* part_chan;  // [nseg][batch][dim][kMaxState + 2] per-row dA_log, dD, ddt_bias
-  float4* agg;       // [nseg][nchan_pad][kMaxState] per segment (prod a, h from 0, g from 0, -)
+  float4* agg;       // [nseg * agg_split][nchan_pad][kMaxState] per segment part
+                     // (prod a, h from 0, g from 0, -)
   float* carry_h;    // [nseg][nchan_pad][kMaxState] state entering each segment
   float* carry_g;    // [nseg][nchan_pad][kMaxState] adjoint reaching each segment's last state
 };

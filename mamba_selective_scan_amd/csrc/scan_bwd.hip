@@ -246,8 +246,10 @@ __device__ inline int group_step(int lane) {
 }
 
 // ---------------------------------------------------------------- pass 0 ---
-// Segment aggregates, walking each segment forward from zero: per state
-// P = prod a_t, H = the state reached, Z = sum_t (prod_(r<=t) a_r) dy_t C_t.
+// Segment aggregates, walking each part of a segment (s.agg_split parts of
+// ceil(seg_chunks / agg_split) chunks; trailing parts may be empty) forward
+// from zero: per state P = prod a_t, H = the state reached,
+// Z = sum_t (prod_(r<=t) a_r) dy_t C_t.
 // WITH_H: also the forward aggregate H, which only the checkpoint pass
 // needs (forward chunk states given: no checkpoint pass, H is skipped).
 // PAIR: u, delta_raw, dout, z as pairs of adjacent steps (s.pairs); BCQ: B
@@ -259,9 +261,10 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   const int lane = threadIdx.x;
   const int64_t groups8 = static_cast<int64_t>(s.tiles) * kBwdWaves;
   const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
-  const int64_t row_seg = logical / groups8;
-  const int b = static_cast<int>(row_seg / s.nseg);
-  const int seg = static_cast<int>(row_seg % s.nseg);
+  const int64_t row_part = logical / groups8;
+  const int nparts = s.nseg * s.agg_split;
+  const int b = static_cast<int>(row_part / nparts);
+  const int part = static_cast<int>(row_part % nparts);
   const int dg = static_cast<int>(logical % groups8) * kCh;
   const int sg = lane >> 3, sc = lane & 7;
   const int d = dg + sc;
@@ -281,8 +284,11 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   const IO* zz = static_cast<const IO*>(p.z);
   const IO* dout = static_cast<const IO*>(p.dout);
   const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
-  const int q_begin = seg * s.seg_chunks;
-  const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
+  const int part_chunks = (s.seg_chunks + s.agg_split - 1) / s.agg_split;
+  const int seg_begin = part / s.agg_split * s.seg_chunks;
+  const int seg_end = min(s.nchunk, seg_begin + s.seg_chunks);
+  const int q_begin = min(seg_end, seg_begin + part % s.agg_split * part_chunks);
+  const int q_end = min(seg_end, q_begin + part_chunks);
   constexpr int64_t es = sizeof(IO);
   // Raw inputs go through buffer descriptors with loop-invariant offsets
   // (out-of-range ones read 0), one chunk ahead of use: B and C, lane covers
@@ -402,13 +408,16 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    p.agg[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] =
+    p.agg[(static_cast<int64_t>(part) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] =
         make_float4(P[k], H[k], Z[k], 0.0f);
 }
 
 // State entering each segment (forward) and adjoint reaching each segment's
-// last state (backward), one lane per (padded channel row, state); each chain
-// is walked in ranges of segments, one wave each (walk_chain_in_ranges).
+// last state (backward), one lane per (padded channel row, state).  Each
+// chain runs over the segment parts of the aggregate pass and is walked in
+// ranges, one wave each (walk_chain_in_ranges); the values at segment
+// boundaries are kept.
+template <bool SPLIT>  // s.agg_split > 1
 __global__ __launch_bounds__(64 * kCarryWaves) void carry_bwd_kernel(BwdShape s, BwdPtrs p) {
   __shared__ float2 xch[kCarryWaves][64];
   const int64_t sstride = s.nchan_pad * kMaxState;
@@ -422,28 +431,37 @@ __global__ __launch_bounds__(64 * kCarryWaves) void carry_bwd_kernel(BwdShape s,
   const int d = static_cast<int>(row % per_b);
   const bool active = valid && d < s.dim && n < s.dstate;
   const int64_t ch = (static_cast<int64_t>(b) * s.dim + d) * s.dstate + n;
-  // the state entering each segment, forward over the segments
+  const int ks = SPLIT ? s.agg_split : 1;  // a power of two: boundaries by mask and shift
+  const int ks_log2 = SPLIT ? __builtin_ctz(static_cast<unsigned>(ks)) : 0;
+  const int nparts = s.nseg * ks;
+  // the state entering each part, forward over the parts: link k is part k
   const float h = (active && p.h0 != nullptr) ? p.h0[ch] : 0.0f;
   if (valid) p.carry_h[idx] = h;
   walk_chain_in_ranges(
-      s.nseg - 1, h, valid, xch,
+      nparts - 1, h, valid, xch,
       [&](int k) {
         const float4 v = p.agg[k * sstride + ic];
         return make_float2(v.x, v.y);
       },
-      [&](int k, float c) { p.carry_h[(k + 1) * sstride + idx] = c; });
+      [&](int k, float c) {  // c enters part k + 1
+        if (!SPLIT || ((k + 1) & (ks - 1)) == 0)
+          p.carry_h[((k + 1) >> ks_log2) * sstride + idx] = c;
+      });
   __syncthreads();  // xch is used again
-  // the adjoint reaching each segment's end, backward over the segments:
-  // link k is segment nseg - 1 - k
+  // the adjoint reaching each part's end, backward over the parts: link k is
+  // part nparts - 1 - k
   const float g = (active && p.dfinal != nullptr) ? p.dfinal[ch] : 0.0f;
   if (valid) p.carry_g[(s.nseg - 1) * sstride + idx] = g;
   walk_chain_in_ranges(
-      s.nseg - 1, g, valid, xch,
+      nparts - 1, g, valid, xch,
       [&](int k) {
-        const float4 v = p.agg[(s.nseg - 1 - k) * sstride + ic];
+        const float4 v = p.agg[(nparts - 1 - k) * sstride + ic];
         return make_float2(v.x, v.z);
       },
-      [&](int k, float c) { p.carry_g[(s.nseg - 2 - k) * sstride + idx] = c; });
+      [&](int k, float c) {  // c reaches the end of part nparts - 2 - k
+        const int q = nparts - 2 - k;
+        if (!SPLIT || (q & (ks - 1)) == ks - 1) p.carry_g[(q >> ks_log2) * sstride + idx] = c;
+      });
 }
 
 // ---------------------------------------------------------------- pass 1 ---
@@ -1112,10 +1130,14 @@ template <typename IO>
 hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream) {
   const int64_t waves = static_cast<int64_t>(s.batch) * s.nseg * s.tiles * kBwdWaves;
   if (s.nseg > 1) {
-    launch_agg<IO>(s, p, stream, static_cast<unsigned>(waves));
+    launch_agg<IO>(s, p, stream, static_cast<unsigned>(waves * s.agg_split));
     const int64_t nc = s.nchan_pad * kMaxState;
-    carry_bwd_kernel<<<dim3(static_cast<unsigned>((nc + 63) / 64)), dim3(64 * carry_waves(s.nseg)),
-                       0, stream>>>(s, p);
+    const dim3 grid(static_cast<unsigned>((nc + 63) / 64));
+    const dim3 block(64 * carry_waves(s.nseg * s.agg_split));
+    if (s.agg_split > 1)
+      carry_bwd_kernel<true><<<grid, block, 0, stream>>>(s, p);
+    else
+      carry_bwd_kernel<false><<<grid, block, 0, stream>>>(s, p);
   }
   // chunk states recorded by the forward replace the checkpoint pass
   if (s.states_given == 0) {

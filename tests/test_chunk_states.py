@@ -146,3 +146,39 @@ def test_bwd_with_chunk_states(mss, shape, reverse):
         # the two differ only by the rounding of the states: the forward's
         # time segments compose their states in another order
         check(f"bwd with vs without chunk states {shape} {k}", to_np(v), to_np(without[k]), 1e-4)
+
+
+@pytest.mark.parametrize("shape,layout", [((1, 384, 32768), "bdl"), ((1, 256, 39700), "bld")])
+def test_bwd_with_chunk_states_split_aggregates(mss, shape, layout):
+    """Few channels, long segments and the forward's chunk states given: the
+    backward's segment aggregate pass cuts every segment into two parts (384
+    channels x 32768 steps: 64 segments of 32 chunks; 256 channel-last
+    channels x 39700 steps: 96 segments of 26 chunks, the last one of 12
+    chunks, whose second part is empty, and a ragged last chunk).  Every
+    gradient against the oracle."""
+    import torch
+    batch, dim, seqlen = shape
+    note(f"bwd split aggregates: B={batch} D={dim} L={seqlen} {layout}")
+    # (the recorded states are checked against oracle prefixes at the shorter
+    # lengths above; that check grows with the square of the length)
+    dx = to_torch(generate(batch, dim, seqlen, 16, layout, seed=3), device())
+    init = torch.randn(batch, dim, 16, generator=torch.Generator().manual_seed(4)).to(device())
+    _, states = mss.selective_scan_fwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                       D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                       initial_state=init, return_chunk_states=True)
+    g = torch.Generator().manual_seed(12)
+    dout = torch.randn(batch, dim, seqlen, generator=g)
+    if layout == "bld":
+        dout = dout.transpose(1, 2).contiguous().transpose(1, 2)
+    dout = dout.to(device())
+    dfin = torch.randn(batch, dim, 16, generator=g).to(device())
+    got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dout,
+                                 D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], initial_state=init,
+                                 dfinal_state=dfin, chunk_states=states)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dout,
+                          D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], h0=init, dfinal=dfin)
+    names = {"du": "du", "ddelta_raw": "ddelta_raw", "dB": "dB", "dC": "dC", "dz": "dz",
+             "dA_log": "dA_log", "dD": "dD", "ddt_bias": "ddt_bias", "dinitial_state": "dh0"}
+    for k, v in got.items():
+        check(f"bwd split aggregates {shape} {layout} {k}", to_np(v), ref[names[k]], 1e-4)
