@@ -520,7 +520,10 @@ def main_bwd(args):
     x = generate(w.batch, w.dim, w.seqlen, w.dstate, w.layout, seed=args.seed)
     dx = to_torch(x, dev, args.io)
     g = torch.Generator().manual_seed(args.seed + 1)
-    dout = torch.randn(w.batch, w.dim, w.seqlen, generator=g).to(device=dev, dtype=dx["u"].dtype)
+    dout = torch.randn(w.batch, w.dim, w.seqlen, generator=g)
+    if w.layout == "bld":  # the gradient of out has out's (u's) layout
+        dout = dout.transpose(1, 2).contiguous().transpose(1, 2)
+    dout = dout.to(device=dev, dtype=dx["u"].dtype)
     h0 = torch.randn(w.batch, w.dim, w.dstate, generator=g).to(dev)
     dfin = torch.randn(w.batch, w.dim, w.dstate, generator=g).to(dev)
     ws = torch.empty(mss.scan_bwd_workspace_size(dx["u"], dx["A_log"]), dtype=torch.uint8,

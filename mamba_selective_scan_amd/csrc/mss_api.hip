@@ -735,6 +735,25 @@ mss_status mss_selective_scan_bwd(const mss_scan_bwd_args* a, void* stream) {
     s.bquads = quad_rows(a->B, a->B_stride) ? 1 : 0;
     s.bcquads = (s.bquads && quad_rows(a->C, a->C_stride)) ? 1 : 0;
   }
+  // Channel pairs and state quads (channel-last data) for the segment
+  // aggregates: every (b, t) row starts on a pair (quad) boundary and holds
+  // whole pairs (quads).
+  {
+    const void* xp[] = {a->u, a->delta_raw, a->dout, a->z};
+    const int64_t* xst[] = {a->u_stride, a->delta_stride, a->dout_stride, a->z_stride};
+    bool ok = a->dim % 2 == 0;
+    for (int i = 0; i < 4 && ok; ++i) {
+      if (xp[i] == nullptr) continue;
+      ok = xst[i][1] == 1 && aligned(xp[i], 2 * es) && (a->batch == 1 || xst[i][0] % 2 == 0) &&
+           xst[i][2] % 2 == 0;
+    }
+    s.dpairs = ok ? 1 : 0;
+    auto nquad_rows = [&](const void* ptr, const int64_t* st) {
+      return a->dstate % 4 == 0 && st[1] == 1 && aligned(ptr, 4 * es) &&
+             (a->batch == 1 || st[0] % 4 == 0) && st[2] % 4 == 0;
+    };
+    s.nquads = (nquad_rows(a->B, a->B_stride) && nquad_rows(a->C, a->C_stride)) ? 1 : 0;
+  }
   char* ws = static_cast<char*>(a->workspace);
   mss::BwdPtrs p{};
   p.u = a->u;

@@ -252,9 +252,16 @@ __device__ inline int group_step(int lane) {
 // Z = sum_t (prod_(r<=t) a_r) dy_t C_t.
 // WITH_H: also the forward aggregate H, which only the checkpoint pass
 // needs (forward chunk states given: no checkpoint pass, H is skipped).
-// PAIR: u, delta_raw, dout, z as pairs of adjacent steps (s.pairs); BCQ: B
-// and C as 4-step vectors (s.bcquads).
-template <typename IO, bool WITH_H, bool PAIR, bool BCQ>
+// XM: how u, delta_raw, dout, z are read: kXScalar element by element,
+// kXStepPairs as pairs of adjacent steps (s.pairs), kXChanPairs as pairs of
+// adjacent channels (s.dpairs, channel-last data).  BM: B and C element by
+// element (kBScalar), as 4-step vectors (kBStepQuads, s.bcquads) or as
+// 4-state vectors (kBStateQuads, s.nquads).  The vector forms need fewer
+// load instructions; with element loads the channel-last audio shape kept
+// the texture units about as busy as the ALUs.
+enum { kXScalar = 0, kXStepPairs = 1, kXChanPairs = 2 };
+enum { kBScalar = 0, kBStepQuads = 1, kBStateQuads = 2 };
+template <typename IO, bool WITH_H, int XM, int BM>
 __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
   __shared__ __attribute__((aligned(16))) float s_el[kCh * kElPitch];
@@ -283,7 +290,6 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   const IO* dr = static_cast<const IO*>(p.delta_raw);
   const IO* zz = static_cast<const IO*>(p.z);
   const IO* dout = static_cast<const IO*>(p.dout);
-  const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
   const int part_chunks = (s.seg_chunks + s.agg_split - 1) / s.agg_split;
   const int seg_begin = part / s.agg_split * s.seg_chunks;
   const int seg_end = min(s.nchunk, seg_begin + s.seg_chunks);
@@ -291,26 +297,41 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   const int q_end = min(seg_end, q_begin + part_chunks);
   constexpr int64_t es = sizeof(IO);
   // Raw inputs go through buffer descriptors with loop-invariant offsets
-  // (out-of-range ones read 0), one chunk ahead of use: B and C, lane covers
-  // rows lane / 4 and 16 + lane / 4 at steps 4 (lane % 4) .. + 3; u,
-  // delta_raw, dout, z, lane (c, j) steps 2j, 2j+1 of channel c.
-  const int bn = lane >> 2, bt0 = (lane & 3) * 4;
+  // (out-of-range ones read 0), one chunk ahead of use.  B and C: lane
+  // covers rows lane / 4 and 16 + lane / 4 at steps 4 (lane % 4) .. + 3, or
+  // (kBStateQuads) states 4 (lane % 4) .. + 3 of step lane / 4.  u,
+  // delta_raw, dout, z: lane (c, j) covers steps 2j, 2j+1 of channel c, or
+  // (kXChanPairs) channels 2 (lane % 4), +1 of step lane / 4.
+  const int bn = BM == kBStateQuads ? (lane & 3) * 4 : lane >> 2;  // first state
+  const int bt0 = BM == kBStateQuads ? lane >> 2 : (lane & 3) * 4;  // first step
+  const int xc = XM == kXChanPairs ? 2 * (lane & 3) : sc;            // first channel
+  const int xt = XM == kXChanPairs ? lane >> 2 : 2 * sg;             // first step
   uint32_t o_b[4], o_c[4], o_u[2], o_dr[2], o_do[2], o_z[2];
-  // (BCQ / PAIR use slot 0 only: the vector's or pair's lower address, which
-  // holds its first step in forward time and its last in reverse time)
+  // (the vector and pair forms use slot 0 only: the lower address, which
+  // holds a step vector's first step in forward time and its last in reverse
+  // time)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tt = BCQ ? bt0 + (s.reverse ? 3 : 0) : bt0 + i;
+    const int tt = BM == kBStepQuads ? bt0 + (s.reverse ? 3 : 0) : (BM == kBStateQuads ? bt0 : bt0 + i);
     o_b[i] = chunk_off(s, s.sB, es, bn, tt);
     o_c[i] = chunk_off(s, s.sC, es, bn, tt);
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int tt = PAIR ? 2 * sg + (s.reverse ? 1 : 0) : 2 * sg + e;
-    o_u[e] = chunk_off(s, s.su, es, sc, tt);
-    o_dr[e] = chunk_off(s, s.sd, es, sc, tt);
-    o_do[e] = chunk_off(s, s.sdo, es, sc, tt);
-    o_z[e] = chunk_off(s, s.sz, es, sc, tt);
+    const int tt = XM == kXStepPairs ? xt + (s.reverse ? 1 : 0) : (XM == kXChanPairs ? xt : xt + e);
+    o_u[e] = chunk_off(s, s.su, es, xc, tt);
+    o_dr[e] = chunk_off(s, s.sd, es, xc, tt);
+    o_do[e] = chunk_off(s, s.sdo, es, xc, tt);
+    o_z[e] = chunk_off(s, s.sz, es, xc, tt);
+  }
+  // the channels of the lane's two elements: dt_bias and validity
+  float bias[2];
+  bool xvalid[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int de = dg + xc + (XM == kXChanPairs ? e : 0);
+    xvalid[e] = de < s.dim;
+    bias[e] = (xvalid[e] && p.dt_bias != nullptr) ? p.dt_bias[de] : 0.0f;
   }
   float rb[4], rc[4], ru[2], rx[2], rgo[2], rz[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
@@ -318,7 +339,7 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     const bool qin = q < q_end;
     const auto rs_b = chunk_rsrc(s, Bm, s.sB, es, b, 0, t0, true, Bm);
     const auto rs_c = chunk_rsrc(s, Cm, s.sC, es, b, 0, t0, true, Cm);
-    if constexpr (BCQ) {
+    if constexpr (BM == kBStepQuads) {
       // length a multiple of 4: a vector is wholly inside or past the sequence
       const bool ok = qin && bn < s.dstate && t0 + bt0 < s.seqlen;
       float vb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vc[4];
@@ -328,6 +349,17 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
       for (int i = 0; i < 4; ++i) {
         rb[i] = s.reverse ? vb[3 - i] : vb[i];
         rc[i] = s.reverse ? vc[3 - i] : vc[i];
+      }
+    } else if constexpr (BM == kBStateQuads) {
+      // dstate a multiple of 4: a vector is wholly inside or past the states
+      const bool ok = qin && bn < s.dstate && t0 + bt0 < s.seqlen;
+      float vb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vc[4];
+      if constexpr (WITH_H) quad_io<IO>::load(rs_b, ok ? o_b[0] : kOffNone, vb);
+      quad_io<IO>::load(rs_c, ok ? o_c[0] : kOffNone, vc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rb[i] = vb[i];
+        rc[i] = vc[i];
       }
     } else {
 #pragma unroll
@@ -341,14 +373,16 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     const auto rs_dr = chunk_rsrc(s, dr, s.sd, es, b, dg, t0, true, u);
     const auto rs_do = chunk_rsrc(s, dout, s.sdo, es, b, dg, t0, true, u);
     const auto rs_z = chunk_rsrc(s, zz, s.sz, es, b, dg, t0, has_z, u);
-    if constexpr (PAIR) {
-      // even length: a pair is wholly inside or past the sequence
-      const bool ok = qin && dvalid && t0 + 2 * sg < s.seqlen;
+    if constexpr (XM != kXScalar) {
+      // even length (dim): a pair is wholly inside or past the sequence (the
+      // channels)
+      const bool ok = qin && xvalid[0] && t0 + xt < s.seqlen;
+      const bool swap = XM == kXStepPairs && s.reverse;
       auto pair = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[2]) {
         float lo, hi;
         pair_io<IO>::load(r, ok ? off : kOffNone, lo, hi);
-        v[0] = s.reverse ? hi : lo;
-        v[1] = s.reverse ? lo : hi;
+        v[0] = swap ? hi : lo;
+        v[1] = swap ? lo : hi;
       };
       pair(rs_u, o_u[0], ru);
       pair(rs_dr, o_dr[0], rx);
@@ -370,17 +404,20 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     const int t0 = q * kBwdT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s_bc[bn * kBcPitch + bt0 + i] = rb[i];
-      s_bc[(kMaxState + bn) * kBcPitch + bt0 + i] = rc[i];
+      const int r = BM == kBStateQuads ? bn + i : bn;
+      const int t = BM == kBStateQuads ? bt0 : bt0 + i;
+      s_bc[r * kBcPitch + t] = rb[i];
+      s_bc[(kMaxState + r) * kBcPitch + t] = rc[i];
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int tt = 2 * sg + e;
-      const bool ok = dvalid && t0 + tt < s.seqlen;
-      const float x = rx[e] + bias;
+      const int c = XM == kXChanPairs ? xc + e : xc;
+      const int tt = XM == kXChanPairs ? xt : xt + e;
+      const bool ok = xvalid[e] && t0 + tt < s.seqlen;
+      const float x = rx[e] + bias[e];
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
       const float dy = has_z ? rgo[e] * silu(rz[e]) : rgo[e];
-      *reinterpret_cast<f4*>(s_el + sc * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
+      *reinterpret_cast<f4*>(s_el + c * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
     }
     load_chunk(q + 1);
     __builtin_amdgcn_wave_barrier();
@@ -1101,20 +1138,24 @@ __global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
   }
 }
 
-template <typename IO, bool WITH_H, bool PAIR>
-void launch_agg_q(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
-  if (s.bcquads)
-    agg_kernel<IO, WITH_H, PAIR, true><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+template <typename IO, bool WITH_H, int XM>
+void launch_agg_b(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
+  if (s.nquads)
+    agg_kernel<IO, WITH_H, XM, kBStateQuads><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+  else if (s.bcquads)
+    agg_kernel<IO, WITH_H, XM, kBStepQuads><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
   else
-    agg_kernel<IO, WITH_H, PAIR, false><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+    agg_kernel<IO, WITH_H, XM, kBScalar><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
 }
 
 template <typename IO, bool WITH_H>
 void launch_agg_p(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
   if (s.pairs)
-    launch_agg_q<IO, WITH_H, true>(s, p, stream, waves);
+    launch_agg_b<IO, WITH_H, kXStepPairs>(s, p, stream, waves);
+  else if (s.dpairs)
+    launch_agg_b<IO, WITH_H, kXChanPairs>(s, p, stream, waves);
   else
-    launch_agg_q<IO, WITH_H, false>(s, p, stream, waves);
+    launch_agg_b<IO, WITH_H, kXScalar>(s, p, stream, waves);
 }
 
 // Forward aggregate H only without the forward's chunk states.
