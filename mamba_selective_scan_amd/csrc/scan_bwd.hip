@@ -253,13 +253,11 @@ __device__ inline int group_step(int lane) {
 // WITH_H: also the forward aggregate H, which only the checkpoint pass
 // needs (forward chunk states given: no checkpoint pass, H is skipped).
 // XM: how u, delta_raw, dout, z are read: kXScalar element by element,
-// kXStepPairs as pairs of adjacent steps (s.pairs), kXChanPairs as pairs of
-// adjacent channels (s.dpairs, channel-last data).  BM: B and C element by
-// element (kBScalar), as 4-step vectors (kBStepQuads, s.bcquads) or as
-// 4-state vectors (kBStateQuads, s.nquads).  The vector forms need fewer
-// load instructions; with element loads the channel-last audio shape kept
-// the texture units about as busy as the ALUs.
-enum { kXScalar = 0, kXStepPairs = 1, kXChanPairs = 2 };
+// kXStepPairs as pairs of adjacent steps (s.pairs); channel-last data takes
+// agg_coop_kernel.  BM: B and C element by element (kBScalar), as 4-step
+// vectors (kBStepQuads, s.bcquads) or as 4-state vectors (kBStateQuads,
+// s.nquads).
+enum { kXScalar = 0, kXStepPairs = 1 };
 enum { kBScalar = 0, kBStepQuads = 1, kBStateQuads = 2 };
 template <typename IO, bool WITH_H, int XM, int BM>
 __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
@@ -300,12 +298,9 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   // (out-of-range ones read 0), one chunk ahead of use.  B and C: lane
   // covers rows lane / 4 and 16 + lane / 4 at steps 4 (lane % 4) .. + 3, or
   // (kBStateQuads) states 4 (lane % 4) .. + 3 of step lane / 4.  u,
-  // delta_raw, dout, z: lane (c, j) covers steps 2j, 2j+1 of channel c, or
-  // (kXChanPairs) channels 2 (lane % 4), +1 of step lane / 4.
+  // delta_raw, dout, z: lane (c, j) covers steps 2j, 2j+1 of channel c.
   const int bn = BM == kBStateQuads ? (lane & 3) * 4 : lane >> 2;  // first state
   const int bt0 = BM == kBStateQuads ? lane >> 2 : (lane & 3) * 4;  // first step
-  const int xc = XM == kXChanPairs ? 2 * (lane & 3) : sc;            // first channel
-  const int xt = XM == kXChanPairs ? lane >> 2 : 2 * sg;             // first step
   uint32_t o_b[4], o_c[4], o_u[2], o_dr[2], o_do[2], o_z[2];
   // (the vector and pair forms use slot 0 only: the lower address, which
   // holds a step vector's first step in forward time and its last in reverse
@@ -318,21 +313,13 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int tt = XM == kXStepPairs ? xt + (s.reverse ? 1 : 0) : (XM == kXChanPairs ? xt : xt + e);
-    o_u[e] = chunk_off(s, s.su, es, xc, tt);
-    o_dr[e] = chunk_off(s, s.sd, es, xc, tt);
-    o_do[e] = chunk_off(s, s.sdo, es, xc, tt);
-    o_z[e] = chunk_off(s, s.sz, es, xc, tt);
+    const int tt = XM == kXStepPairs ? 2 * sg + (s.reverse ? 1 : 0) : 2 * sg + e;
+    o_u[e] = chunk_off(s, s.su, es, sc, tt);
+    o_dr[e] = chunk_off(s, s.sd, es, sc, tt);
+    o_do[e] = chunk_off(s, s.sdo, es, sc, tt);
+    o_z[e] = chunk_off(s, s.sz, es, sc, tt);
   }
-  // the channels of the lane's two elements: dt_bias and validity
-  float bias[2];
-  bool xvalid[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int de = dg + xc + (XM == kXChanPairs ? e : 0);
-    xvalid[e] = de < s.dim;
-    bias[e] = (xvalid[e] && p.dt_bias != nullptr) ? p.dt_bias[de] : 0.0f;
-  }
+  const float bias = (dvalid && p.dt_bias != nullptr) ? p.dt_bias[d] : 0.0f;
   float rb[4], rc[4], ru[2], rx[2], rgo[2], rz[2];
   auto load_chunk = [&](int q) __attribute__((always_inline)) {
     const int t0 = q * kBwdT;
@@ -373,16 +360,14 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     const auto rs_dr = chunk_rsrc(s, dr, s.sd, es, b, dg, t0, true, u);
     const auto rs_do = chunk_rsrc(s, dout, s.sdo, es, b, dg, t0, true, u);
     const auto rs_z = chunk_rsrc(s, zz, s.sz, es, b, dg, t0, has_z, u);
-    if constexpr (XM != kXScalar) {
-      // even length (dim): a pair is wholly inside or past the sequence (the
-      // channels)
-      const bool ok = qin && xvalid[0] && t0 + xt < s.seqlen;
-      const bool swap = XM == kXStepPairs && s.reverse;
+    if constexpr (XM == kXStepPairs) {
+      // even length: a pair is wholly inside or past the sequence
+      const bool ok = qin && dvalid && t0 + 2 * sg < s.seqlen;
       auto pair = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[2]) {
         float lo, hi;
         pair_io<IO>::load(r, ok ? off : kOffNone, lo, hi);
-        v[0] = swap ? hi : lo;
-        v[1] = swap ? lo : hi;
+        v[0] = s.reverse ? hi : lo;
+        v[1] = s.reverse ? lo : hi;
       };
       pair(rs_u, o_u[0], ru);
       pair(rs_dr, o_dr[0], rx);
@@ -411,13 +396,12 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int c = XM == kXChanPairs ? xc + e : xc;
-      const int tt = XM == kXChanPairs ? xt : xt + e;
-      const bool ok = xvalid[e] && t0 + tt < s.seqlen;
-      const float x = rx[e] + bias[e];
+      const int tt = 2 * sg + e;
+      const bool ok = dvalid && t0 + tt < s.seqlen;
+      const float x = rx[e] + bias;
       const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
       const float dy = has_z ? rgo[e] * silu(rz[e]) : rgo[e];
-      *reinterpret_cast<f4*>(s_el + c * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
+      *reinterpret_cast<f4*>(s_el + sc * kElPitch + 4 * tt) = f4{dl, dl * ru[e], dy, 0.0f};
     }
     load_chunk(q + 1);
     __builtin_amdgcn_wave_barrier();
@@ -442,6 +426,127 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
       }
     }
     __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    p.agg[(static_cast<int64_t>(part) * s.nchan_pad + chan_row) * kMaxState + 2 * sg + k] =
+        make_float4(P[k], H[k], Z[k], 0.0f);
+}
+
+// The aggregate pass for channel-last u, delta_raw, dout, z (s.dpairs): one
+// workgroup of kBwdWaves waves per (row, segment part, 32-channel tile),
+// with the scan roles of agg_kernel in each wave.  The workgroup loads the
+// tile's inputs together: thread (t, j) = (tid / 16, tid % 16) reads
+// channels 2j, 2j+1 of step t of each tensor, so that 16 threads cover one
+// 128-byte row of 32 channels, and B and C once for the tile (thread
+// (t, n) = (tid / 16, tid % 16)).  The inputs are staged in LDS,
+// double-buffered by chunk parity, so that one barrier per chunk orders every
+// shared access.  (One wave per 8 channels read a quarter of each row, and
+// the four waves that share a row ran in workgroups on different CUs.)
+template <typename IO, bool WITH_H>
+__global__ __launch_bounds__(kBwdThreads) void agg_coop_kernel(BwdShape s, BwdPtrs p) {
+  __shared__ __attribute__((aligned(16))) float s_bc[2][2 * kMaxState * kBcPitch];
+  __shared__ __attribute__((aligned(16))) float s_el[2][kBwdCh * kElPitch];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
+  const int tile = static_cast<int>(logical % s.tiles);
+  const int64_t row_part = logical / s.tiles;
+  const int nparts = s.nseg * s.agg_split;
+  const int b = static_cast<int>(row_part / nparts);
+  const int part = static_cast<int>(row_part % nparts);
+  // scan role: lane (c, g) of wave w, states 2g, 2g+1 of channel 8w + c of the tile
+  const int sg = lane >> 3, sc = lane & 7;
+  const int d0 = tile * kBwdCh;
+  const int d = d0 + w * kCh + sc;
+  const bool dvalid = d < s.dim;
+  const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
+  const bool has_z = p.z != nullptr;
+  float A2[2], H[2] = {0.0f, 0.0f}, P[2] = {1.0f, 1.0f}, Z[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int n = 2 * sg + k;
+    A2[k] = (dvalid && n < s.dstate) ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e : 0.0f;
+  }
+  const IO* Bm = static_cast<const IO*>(p.B);
+  const IO* Cm = static_cast<const IO*>(p.C);
+  const IO* u = static_cast<const IO*>(p.u);
+  const IO* dr = static_cast<const IO*>(p.delta_raw);
+  const IO* zz = static_cast<const IO*>(p.z);
+  const IO* dout = static_cast<const IO*>(p.dout);
+  const int part_chunks = (s.seg_chunks + s.agg_split - 1) / s.agg_split;
+  const int seg_begin = part / s.agg_split * s.seg_chunks;
+  const int seg_end = min(s.nchunk, seg_begin + s.seg_chunks);
+  const int q_begin = min(seg_end, seg_begin + part % s.agg_split * part_chunks);
+  const int q_end = min(seg_end, q_begin + part_chunks);
+  constexpr int64_t es = sizeof(IO);
+  // load role: step lt of the chunk, channels lc, lc + 1 of the tile, state ln
+  const int lt = tid >> 4, lc = 2 * (tid & 15), ln = tid & 15;
+  const bool xv = d0 + lc < s.dim;  // dim is even: the pair is wholly in or out
+  const uint32_t o_u = chunk_off(s, s.su, es, lc, lt);
+  const uint32_t o_dr = chunk_off(s, s.sd, es, lc, lt);
+  const uint32_t o_do = chunk_off(s, s.sdo, es, lc, lt);
+  const uint32_t o_z = chunk_off(s, s.sz, es, lc, lt);
+  const uint32_t o_b = chunk_off(s, s.sB, es, ln, lt);
+  const uint32_t o_c = chunk_off(s, s.sC, es, ln, lt);
+  float bias[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) bias[e] = (xv && p.dt_bias != nullptr) ? p.dt_bias[d0 + lc + e] : 0.0f;
+  float ru[2], rx[2], rgo[2], rz[2], rb = 0.0f, rc = 0.0f;
+  auto load_chunk = [&](int q) __attribute__((always_inline)) {
+    const int t0 = q * kBwdT;
+    const bool tin = q < q_end && t0 + lt < s.seqlen;
+    const bool ok = tin && xv;
+    pair_io<IO>::load(chunk_rsrc(s, u, s.su, es, b, d0, t0, true, u), ok ? o_u : kOffNone, ru[0], ru[1]);
+    pair_io<IO>::load(chunk_rsrc(s, dr, s.sd, es, b, d0, t0, true, u), ok ? o_dr : kOffNone, rx[0],
+                      rx[1]);
+    pair_io<IO>::load(chunk_rsrc(s, dout, s.sdo, es, b, d0, t0, true, u), ok ? o_do : kOffNone,
+                      rgo[0], rgo[1]);
+    pair_io<IO>::load(chunk_rsrc(s, zz, s.sz, es, b, d0, t0, has_z, u), ok ? o_z : kOffNone, rz[0],
+                      rz[1]);
+    const bool bok = tin && ln < s.dstate;
+    if constexpr (WITH_H)
+      rb = buf_one<IO>::load(chunk_rsrc(s, Bm, s.sB, es, b, 0, t0, true, Bm), bok ? o_b : kOffNone, 0);
+    rc = buf_one<IO>::load(chunk_rsrc(s, Cm, s.sC, es, b, 0, t0, true, Cm), bok ? o_c : kOffNone, 0);
+  };
+  load_chunk(q_begin);
+  for (int q = q_begin; q < q_end; ++q) {
+    const int t0 = q * kBwdT;
+    float* bc = s_bc[(q - q_begin) & 1];
+    float* el = s_el[(q - q_begin) & 1];
+    bc[ln * kBcPitch + lt] = rb;
+    bc[(kMaxState + ln) * kBcPitch + lt] = rc;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const bool ok = xv && t0 + lt < s.seqlen;
+      const float x = rx[e] + bias[e];
+      const float dl = ok ? (s.softplus ? softplus(x) : x) : 0.0f;
+      const float dy = has_z ? rgo[e] * silu(rz[e]) : rgo[e];
+      *reinterpret_cast<f4*>(el + (lc + e) * kElPitch + 4 * lt) = f4{dl, dl * ru[e], dy, 0.0f};
+    }
+    load_chunk(q + 1);
+    __syncthreads();
+    const float* wel = el + w * kCh * kElPitch;
+#pragma unroll
+    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
+      const f4 b0 = ld4(bc + (2 * sg) * kBcPitch + t4);
+      const f4 b1 = ld4(bc + (2 * sg + 1) * kBcPitch + t4);
+      const f4 c0 = ld4(bc + (kMaxState + 2 * sg) * kBcPitch + t4);
+      const f4 c1 = ld4(bc + (kMaxState + 2 * sg + 1) * kBcPitch + t4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f4 dd = ld4(wel + sc * kElPitch + 4 * (t4 + i));
+        const float bk[2] = {f4_at(b0, i), f4_at(b1, i)};
+        const float ck[2] = {f4_at(c0, i), f4_at(c1, i)};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float a = fast_exp2(dd.x * A2[k]);
+          if constexpr (WITH_H) H[k] = fmaf(a, H[k], dd.y * bk[k]);
+          P[k] *= a;
+          Z[k] = fmaf(P[k], dd.z * ck[k], Z[k]);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k)
@@ -1153,7 +1258,7 @@ void launch_agg_p(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsig
   if (s.pairs)
     launch_agg_b<IO, WITH_H, kXStepPairs>(s, p, stream, waves);
   else if (s.dpairs)
-    launch_agg_b<IO, WITH_H, kXChanPairs>(s, p, stream, waves);
+    agg_coop_kernel<IO, WITH_H><<<dim3(waves / kBwdWaves), dim3(kBwdThreads), 0, stream>>>(s, p);
   else
     launch_agg_b<IO, WITH_H, kXScalar>(s, p, stream, waves);
 }
