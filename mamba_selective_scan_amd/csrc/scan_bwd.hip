@@ -764,6 +764,136 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   }
 }
 
+// The checkpoint pass for channel-last data (s.dpairs): one workgroup of
+// kBwdWaves waves per (row, segment, 32-channel tile), each wave walking its
+// 8 channels as in ckpt_kernel.  The workgroup loads a block of two chunks
+// together: thread (t, j) = (tid / 16, tid % 16) reads channels 2j, 2j+1 of
+// steps t and t + 16 of u and delta_raw (16 threads per 128-byte row of 32
+// channels), and B at states tid % 16 of the same steps.  The block is staged
+// in LDS, double-buffered by block parity, one barrier per block.
+template <typename IO>
+__global__ __launch_bounds__(kBwdThreads) void ckpt_coop_kernel(BwdShape s, BwdPtrs p) {
+  __shared__ __attribute__((aligned(16))) float s_b[2][kMaxState * kCkBPitch];
+  __shared__ __attribute__((aligned(16))) float s_dd[2][kBwdCh * kCkDdPitch];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int64_t logical = xcd_order(blockIdx.x, gridDim.x);
+  const int tile = static_cast<int>(logical % s.tiles);
+  const int64_t row_seg = logical / s.tiles;
+  const int b = static_cast<int>(row_seg / s.nseg);
+  const int seg = static_cast<int>(row_seg % s.nseg);
+  // walk role: lane (c, g) of wave w, states 2g, 2g+1 of channel 8w + c of the tile
+  const int sg = lane >> 3, sc = lane & 7;
+  const int d0 = tile * kBwdCh;
+  const int dg = d0 + w * kCh;
+  const int d = dg + sc;
+  const bool dvalid = d < s.dim;
+  const int64_t chan_row = static_cast<int64_t>(b) * s.tiles * kBwdCh + d;
+  float A2[2], h[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int n = 2 * sg + k;
+    const bool active = dvalid && n < s.dstate;
+    A2[k] = active ? -expf(p.A_log[d * s.sA[0] + n * s.sA[1]]) * kLog2e : 0.0f;
+    if (s.nseg > 1)
+      h[k] = p.carry_h[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + n];
+    else
+      h[k] = (active && p.h0 != nullptr) ? p.h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n] : 0.0f;
+  }
+  const int q_begin = seg * s.seg_chunks;
+  const int q_end = min(s.nchunk, q_begin + s.seg_chunks);
+  constexpr int64_t es = sizeof(IO);
+  // load role: steps lt, lt + 16 of the block, channels lc, lc + 1, state ln
+  const int lt = tid >> 4, lc = 2 * (tid & 15), ln = tid & 15;
+  const bool xv = d0 + lc < s.dim;  // dim is even: the pair is wholly in or out
+  uint32_t o_u[2], o_dr[2], o_b[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    o_u[v] = chunk_off<kCkSpan>(s, s.su, es, lc, lt + 16 * v);
+    o_dr[v] = chunk_off<kCkSpan>(s, s.sd, es, lc, lt + 16 * v);
+    o_b[v] = chunk_off<kCkSpan>(s, s.sB, es, ln, lt + 16 * v);
+  }
+  float bias[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) bias[e] = (xv && p.dt_bias != nullptr) ? p.dt_bias[d0 + lc + e] : 0.0f;
+  // checkpoints in the chunk-state layout [q][batch][dim][kMaxState]
+  const uint32_t o_ck =
+      dvalid ? static_cast<uint32_t>((sc * kMaxState + 2 * sg) * sizeof(float)) : kOffNone;
+  const int64_t ck_row0 = static_cast<int64_t>(b) * s.dim + dg;  // wave-uniform
+  const int64_t ck_plane = static_cast<int64_t>(s.batch) * s.dim;
+  float ru[2][2], rx[2][2], rb[2];
+  auto load_block = [&](int q) __attribute__((always_inline)) {
+    const int t0 = q * kBwdT;
+    const auto r_b = chunk_rsrc<kCkSpan>(s, p.B, s.sB, es, b, 0, t0, true, p.u);
+    const auto r_u = chunk_rsrc<kCkSpan>(s, p.u, s.su, es, b, d0, t0, true, p.u);
+    const auto r_dr = chunk_rsrc<kCkSpan>(s, p.delta_raw, s.sd, es, b, d0, t0, true, p.u);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const bool tin = q < q_end && t0 + lt + 16 * v < s.seqlen;
+      pair_io<IO>::load(r_u, (tin && xv) ? o_u[v] : kOffNone, ru[v][0], ru[v][1]);
+      pair_io<IO>::load(r_dr, (tin && xv) ? o_dr[v] : kOffNone, rx[v][0], rx[v][1]);
+      rb[v] = buf_one<IO>::load(r_b, (tin && ln < s.dstate) ? o_b[v] : kOffNone, 0);
+    }
+  };
+  // Walk the 16 steps of chunk q from LDS step c0 of the block, recording the
+  // state entering it.
+  auto walk_chunk = [&](const float* sb, const float* sdd, int q, int c0)
+      __attribute__((always_inline)) {
+    store2(h[0], h[1],
+           __builtin_amdgcn_make_buffer_rsrc(
+               p.ckpt + (static_cast<int64_t>(q) * ck_plane + ck_row0) * kMaxState, 0,
+               kRsrcRange, kRsrcFlags),
+           o_ck);
+#pragma unroll
+    for (int t4 = 0; t4 < kBwdT; t4 += 4) {
+      const f4 b0 = ld4(sb + (2 * sg) * kCkBPitch + c0 + t4);
+      const f4 b1 = ld4(sb + (2 * sg + 1) * kCkBPitch + c0 + t4);
+      const f4 dd01 = ld4(sdd + sc * kCkDdPitch + 2 * (c0 + t4));
+      const f4 dd23 = ld4(sdd + sc * kCkDdPitch + 2 * (c0 + t4) + 4);
+      const float dl[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
+      const float du[4] = {dd01.y, dd01.w, dd23.y, dd23.w};
+      float a0[4], a1[4], x0[4], x1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a0[i] = fast_exp2(dl[i] * A2[0]);
+        a1[i] = fast_exp2(dl[i] * A2[1]);
+        x0[i] = du[i] * f4_at(b0, i);
+        x1[i] = du[i] * f4_at(b1, i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[0] = fmaf(a0[i], h[0], x0[i]);
+        h[1] = fmaf(a1[i], h[1], x1[i]);
+      }
+    }
+  };
+  load_block(q_begin);
+  for (int q = q_begin; q < q_end; q += 2) {
+    const int t0 = q * kBwdT;
+    float* sb = s_b[((q - q_begin) >> 1) & 1];
+    float* sdd = s_dd[((q - q_begin) >> 1) & 1];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int tt = lt + 16 * v;
+      sb[ln * kCkBPitch + tt] = rb[v];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool ok = xv && t0 + tt < s.seqlen;
+        const float x = rx[v][e] + bias[e];
+        const float sp = s.softplus ? softplus(x) : x;
+        const float dl = ok ? sp : 0.0f;
+        *reinterpret_cast<float2*>(sdd + (lc + e) * kCkDdPitch + 2 * tt) =
+            make_float2(dl, dl * ru[v][e]);
+      }
+    }
+    load_block(q + 2);
+    __syncthreads();
+    const float* wdd = sdd + w * kCh * kCkDdPitch;
+    walk_chunk(sb, wdd, q, 0);
+    if (q + 1 < q_end) walk_chunk(sb, wdd, q + 1, kBwdT);
+  }
+}
+
 // ---------------------------------------------------------------- pass 2 ---
 // PAIR: the lane's two elements (steps 2j, 2j+1 of its channel) are one
 // 2-element access per tensor (s.pairs).
@@ -1288,7 +1418,10 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
   // chunk states recorded by the forward replace the checkpoint pass
   if (s.states_given == 0) {
     const dim3 grid(static_cast<unsigned>(waves));
-    if (s.quads && s.bquads)
+    if (s.dpairs)
+      ckpt_coop_kernel<IO><<<dim3(static_cast<unsigned>(waves / kBwdWaves)), dim3(kBwdThreads), 0,
+                             stream>>>(s, p);
+    else if (s.quads && s.bquads)
       ckpt_kernel<IO, true, true><<<grid, dim3(64), 0, stream>>>(s, p);
     else if (s.quads)
       ckpt_kernel<IO, true, false><<<grid, dim3(64), 0, stream>>>(s, p);
