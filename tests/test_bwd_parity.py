@@ -239,12 +239,41 @@ def test_channel_last_layout(mss):
     (8, 3072, 48, "f32"),   # 768 (row, block) pairs: no time segments
 ])
 def test_channel_last_cooperative_rows(mss, case):
-    """Channel-last inputs: the reverse walk's workgroups load whole rows of
-    their 32-channel blocks and hand each element to the wave that scans it."""
+    """Channel-last inputs: with time segments, the aggregate and checkpoint
+    passes' workgroups load whole 128-byte rows of their 32-channel tiles and
+    stage them in LDS for the waves that walk them."""
     batch, dim, seqlen, io = case
     _run_and_check(mss, f"bld coop {case}",
                    _problem(batch, dim, seqlen, 16, layout="bld", io=io, h0=True, dfinal=True),
                    io=io)
+
+
+@pytest.mark.parametrize("dstate,io,states", [(5, "f32", False), (3, "f32", True),
+                                               (16, "bf16", True), (8, "bf16", False)])
+def test_channel_last_segments_small_dstate_and_states(mss, dstate, io, states):
+    """Channel-last, time segments (1 x 80 x 1900: 3 tiles, the last half
+    empty, 14 segments), with dstate below 16 (B, C element by element when it
+    is not a multiple of 4, 4-state vectors when it is; dB and dC summed with
+    lanes past dstate idle) and with or without the forward's chunk states
+    (the aggregate pass without H)."""
+    import torch
+    dx = _problem(1, 80, 1900, dstate, layout="bld", io=io, h0=True, dfinal=True)
+    kw = {}
+    if states:
+        _, kw["chunk_states"] = mss.selective_scan_fwd(
+            dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], D=dx["D"], z=dx["z"],
+            dt_bias=dx["dt_bias"], initial_state=dx["h0"], return_chunk_states=True)
+    note(f"bwd bld segments N={dstate} {io} states={states}")
+    got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
+                                 dx["dout"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                 initial_state=dx["h0"], dfinal_state=dx["dfinal"], **kw)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dx["dout"],
+                          D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], h0=dx["h0"],
+                          dfinal=dx["dfinal"])
+    for k, v in got.items():
+        check(f"bwd bld segments N={dstate} {io} states={states} {k}", to_np(v),
+              ref[ORACLE_NAME[k]], TOL[io])
 
 
 @pytest.mark.parametrize("seqlen", [200, 201])
