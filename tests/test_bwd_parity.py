@@ -248,22 +248,25 @@ def test_channel_last_cooperative_rows(mss, case):
                    io=io)
 
 
-@pytest.mark.parametrize("dstate,io,states", [(5, "f32", False), (3, "f32", True),
-                                               (16, "bf16", True), (8, "bf16", False)])
-def test_channel_last_segments_small_dstate_and_states(mss, dstate, io, states):
+@pytest.mark.parametrize("dstate,io,states,dim", [(5, "f32", False, 80), (3, "f32", True, 80),
+                                                   (16, "bf16", True, 80), (8, "bf16", False, 80),
+                                                   (16, "f32", False, 77), (16, "f32", True, 77)])
+def test_channel_last_segments_small_dstate_and_states(mss, dstate, io, states, dim):
     """Channel-last, time segments (1 x 80 x 1900: 3 tiles, the last half
     empty, 14 segments), with dstate below 16 (B, C element by element when it
     is not a multiple of 4, 4-state vectors when it is; dB and dC summed with
     lanes past dstate idle) and with or without the forward's chunk states
-    (the aggregate pass without H)."""
+    (the aggregate pass without H).  An odd channel count (77) cannot move
+    channel pairs: the one-wave aggregate and checkpoint passes with element
+    loads."""
     import torch
-    dx = _problem(1, 80, 1900, dstate, layout="bld", io=io, h0=True, dfinal=True)
+    dx = _problem(1, dim, 1900, dstate, layout="bld", io=io, h0=True, dfinal=True)
     kw = {}
     if states:
         _, kw["chunk_states"] = mss.selective_scan_fwd(
             dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], D=dx["D"], z=dx["z"],
             dt_bias=dx["dt_bias"], initial_state=dx["h0"], return_chunk_states=True)
-    note(f"bwd bld segments N={dstate} {io} states={states}")
+    note(f"bwd bld segments D={dim} N={dstate} {io} states={states}")
     got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"],
                                  dx["dout"], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
                                  initial_state=dx["h0"], dfinal_state=dx["dfinal"], **kw)
@@ -272,7 +275,7 @@ def test_channel_last_segments_small_dstate_and_states(mss, dstate, io, states):
                           D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], h0=dx["h0"],
                           dfinal=dx["dfinal"])
     for k, v in got.items():
-        check(f"bwd bld segments N={dstate} {io} states={states} {k}", to_np(v),
+        check(f"bwd bld segments D={dim} N={dstate} {io} states={states} {k}", to_np(v),
               ref[ORACLE_NAME[k]], TOL[io])
 
 
