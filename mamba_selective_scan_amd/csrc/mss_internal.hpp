@@ -251,10 +251,11 @@ struct BwdShape {
               // (unit time stride, length and strides multiples of 4)
   int bquads;  // ... and B too (the same conditions on B)
   int bcquads;  // B and C both meet them: the segment aggregates read B, C as 4-step vectors
-  int dpairs;   // the segment aggregates read u, delta_raw, dout, z as pairs of adjacent
-                // channels (unit channel stride, even dim and strides)
-  int nquads;   // ... and B, C as 4-state vectors (unit state stride, dstate and strides
-                // multiples of 4)
+  int dpairs;   // channel-last data: the segment aggregate and checkpoint passes run in
+                // 4-wave workgroups per 32-channel tile and read u, delta_raw, dout, z as
+                // pairs of adjacent channels (unit channel stride, even dim and strides)
+  int nquads;   // the one-wave segment aggregate pass reads B, C as 4-state vectors (unit
+                // state stride, dstate and strides multiples of 4)
   int states_given;  // ckpt holds chunk states recorded by the forward: no checkpoint pass
 };
 
