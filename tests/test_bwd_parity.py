@@ -248,6 +248,19 @@ def test_channel_last_cooperative_rows(mss, case):
                    io=io)
 
 
+@pytest.mark.parametrize("batch,dim,seqlen,io,with_z", [
+    (2, 96, 130, "f32", False),   # no z: no dz rows to store
+    (3, 34, 45, "bf16", True),    # a 2-channel last tile, odd batch, ragged chunk
+])
+def test_channel_last_gradient_rows(mss, batch, dim, seqlen, io, with_z):
+    """Channel-last inputs and gradients without z (no dz rows), and with a last
+    32-channel tile that holds 2 channels, an odd batch and a ragged chunk."""
+    _run_and_check(mss, f"bld rows B={batch} D={dim} L={seqlen} {io} z={with_z}",
+                   _problem(batch, dim, seqlen, 16, layout="bld", io=io, with_z=with_z,
+                            h0=True, dfinal=True),
+                   io=io)
+
+
 @pytest.mark.parametrize("dstate,io,states,dim", [(5, "f32", False, 80), (3, "f32", True, 80),
                                                    (16, "bf16", True, 80), (8, "bf16", False, 80),
                                                    (16, "f32", False, 77), (16, "f32", True, 77)])

@@ -93,7 +93,7 @@ def test_bidirectional_sum(mss):
 
 
 @pytest.mark.parametrize("shape,layout", [((2, 72, 100), "bdl"), ((1, 64, 1500), "bdl"),
-                                          ((1, 40, 1500), "bld")])
+                                          ((1, 40, 1500), "bld"), ((2, 48, 333), "bld")])
 def test_reverse_backward(mss, shape, layout):
     import torch
     batch, dim, seqlen = shape
