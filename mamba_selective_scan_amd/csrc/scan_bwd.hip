@@ -14,7 +14,10 @@
 // The training backward is what the pages list as not yet written
 // ("mamba-metal: Apple Silicon で Mamba を動かす", section "残り課題").
 // Every kernel works in logical time; in reverse time (s.reverse) logical
-// step t reads and writes storage step L-1-t.
+// step t reads and writes storage step L-1-t.  The aggregate, checkpoint and
+// reverse-walk passes take the direction as a template argument (REV ==
+// s.reverse), so that the order of the steps inside a loaded vector is fixed
+// at compile time rather than chosen per element.
 //
 // Passes:
 //   0. (few channels, long sequences) the sequence is cut into time segments
@@ -259,7 +262,7 @@ __device__ inline int group_step(int lane) {
 // s.nquads).
 enum { kXScalar = 0, kXStepPairs = 1 };
 enum { kBScalar = 0, kBStepQuads = 1, kBStateQuads = 2 };
-template <typename IO, bool WITH_H, int XM, int BM>
+template <typename IO, bool WITH_H, int XM, int BM, bool REV>
 __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2 * kMaxState * kBcPitch];
   __shared__ __attribute__((aligned(16))) float s_el[kCh * kElPitch];
@@ -307,13 +310,13 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
   // time)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tt = BM == kBStepQuads ? bt0 + (s.reverse ? 3 : 0) : (BM == kBStateQuads ? bt0 : bt0 + i);
+    const int tt = BM == kBStepQuads ? bt0 + (REV ? 3 : 0) : (BM == kBStateQuads ? bt0 : bt0 + i);
     o_b[i] = chunk_off(s, s.sB, es, bn, tt);
     o_c[i] = chunk_off(s, s.sC, es, bn, tt);
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int tt = XM == kXStepPairs ? 2 * sg + (s.reverse ? 1 : 0) : 2 * sg + e;
+    const int tt = XM == kXStepPairs ? 2 * sg + (REV ? 1 : 0) : 2 * sg + e;
     o_u[e] = chunk_off(s, s.su, es, sc, tt);
     o_dr[e] = chunk_off(s, s.sd, es, sc, tt);
     o_do[e] = chunk_off(s, s.sdo, es, sc, tt);
@@ -334,8 +337,8 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
       quad_io<IO>::load(rs_c, ok ? o_c[0] : kOffNone, vc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        rb[i] = s.reverse ? vb[3 - i] : vb[i];
-        rc[i] = s.reverse ? vc[3 - i] : vc[i];
+        rb[i] = REV ? vb[3 - i] : vb[i];
+        rc[i] = REV ? vc[3 - i] : vc[i];
       }
     } else if constexpr (BM == kBStateQuads) {
       // dstate a multiple of 4: a vector is wholly inside or past the states
@@ -366,8 +369,8 @@ __global__ __launch_bounds__(64) void agg_kernel(BwdShape s, BwdPtrs p) {
       auto pair = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[2]) {
         float lo, hi;
         pair_io<IO>::load(r, ok ? off : kOffNone, lo, hi);
-        v[0] = s.reverse ? hi : lo;
-        v[1] = s.reverse ? lo : hi;
+        v[0] = REV ? hi : lo;
+        v[1] = REV ? lo : hi;
       };
       pair(rs_u, o_u[0], ru);
       pair(rs_dr, o_dr[0], rx);
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(64 * kCarryWaves) void carry_bwd_kernel(BwdShape s,
 // ---------------------------------------------------------------- pass 1 ---
 // QUAD: u and delta_raw are read as 4-step vectors (s.quads); BQUAD: B as
 // well (s.bquads).
-template <typename IO, bool QUAD, bool BQUAD>
+template <typename IO, bool QUAD, bool BQUAD, bool REV>
 __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   __shared__ __attribute__((aligned(16))) float s_b[kMaxState * kCkBPitch];
   __shared__ __attribute__((aligned(16))) float s_dd[kCh * kCkDdPitch];
@@ -651,13 +654,13 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
   for (int i = 0; i < 8; ++i) {
     // BQUAD: slots 0 and 4 hold the two vectors' lower addresses (steps
     // 8k and 8k+4 forward, 8k+3 and 8k+7 reversed)
-    const int tt = BQUAD ? (lane & 3) * 8 + (i & 4) + (s.reverse ? 3 : 0) : (lane & 3) * 8 + i;
+    const int tt = BQUAD ? (lane & 3) * 8 + (i & 4) + (REV ? 3 : 0) : (lane & 3) * 8 + i;
     o_b[i] = bn < s.dstate ? chunk_off<kCkSpan>(s, s.sB, es, bn, tt) : kOffNone;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     // QUAD: slot 0 holds the vector's lower address: step 4j forward, 4j+3 reversed
-    const int tt = QUAD ? 4 * sg + (s.reverse ? 3 : 0) : 4 * sg + e;
+    const int tt = QUAD ? 4 * sg + (REV ? 3 : 0) : 4 * sg + e;
     o_u[e] = dvalid ? chunk_off<kCkSpan>(s, s.su, es, sc, tt) : kOffNone;
     o_dr[e] = dvalid ? chunk_off<kCkSpan>(s, s.sd, es, sc, tt) : kOffNone;
   }
@@ -681,7 +684,7 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
         const bool ok = qok && t0 + (lane & 3) * 8 + 4 * v < s.seqlen;
         quad_io<IO>::load(r_b, ok ? o_b[4 * v] : kOffNone, vb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rb[4 * v + e] = s.reverse ? vb[3 - e] : vb[e];
+        for (int e = 0; e < 4; ++e) rb[4 * v + e] = REV ? vb[3 - e] : vb[e];
       }
     } else {
 #pragma unroll
@@ -696,8 +699,8 @@ __global__ __launch_bounds__(64) void ckpt_kernel(BwdShape s, BwdPtrs p) {
       quad_io<IO>::load(r_dr, ok ? o_dr[0] : kOffNone, vx);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        ru[e] = s.reverse ? vu[3 - e] : vu[e];
-        rx[e] = s.reverse ? vx[3 - e] : vx[e];
+        ru[e] = REV ? vu[3 - e] : vu[e];
+        rx[e] = REV ? vx[3 - e] : vx[e];
       }
     } else {
 #pragma unroll
@@ -897,7 +900,7 @@ __global__ __launch_bounds__(kBwdThreads) void ckpt_coop_kernel(BwdShape s, BwdP
 // ---------------------------------------------------------------- pass 2 ---
 // PAIR: the lane's two elements (steps 2j, 2j+1 of its channel) are one
 // 2-element access per tensor (s.pairs).
-template <typename IO, bool PAIR>
+template <typename IO, bool PAIR, bool REV>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_kernel(BwdShape s, BwdPtrs p) {
   // One LDS block, B/C first and the reduction rows next, so that the rows
   // addressed with per-lane bases plus a step offset stay within reach of the
@@ -981,7 +984,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
   const RowBase rb_C = row_base(Cm, s.sC, es, b, 0, true, u);
   // lowest storage step of the chunk starting at logical step t0
   auto chunk_ts = [&](int t0) __attribute__((always_inline)) {
-    return s.reverse ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : static_cast<int64_t>(t0);
+    return REV ? static_cast<int64_t>(s.seqlen) - kBwdT - t0 : static_cast<int64_t>(t0);
   };
   auto tile_off = [&](const int64_t* st, int row, int tt) __attribute__((always_inline)) {
     return chunk_off(s, st, es, row, tt);
@@ -994,7 +997,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
   uint32_t o_u[2], o_dr[2], o_do[2], o_z[2], o_du[2], o_ddr[2], o_dz[2], o_ck[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int tt = PAIR ? 2 * sg + (s.reverse ? 1 : 0) : 2 * sg + e;
+    const int tt = PAIR ? 2 * sg + (REV ? 1 : 0) : 2 * sg + e;
     o_u[e] = dvalid ? tile_off(s.su, sc, tt) : kOffNone;
     o_dr[e] = dvalid ? tile_off(s.sd, sc, tt) : kOffNone;
     o_do[e] = dvalid ? tile_off(s.sdo, sc, tt) : kOffNone;
@@ -1050,8 +1053,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
           __attribute__((always_inline)) {
         float lo, hi;
         pair_io<IO>::load(r, ok ? off : kOffNone, lo, hi);
-        x[0] = s.reverse ? hi : lo;
-        x[1] = s.reverse ? lo : hi;
+        x[0] = REV ? hi : lo;
+        x[1] = REV ? lo : hi;
       };
       ld2(r_u, o_u[0], ru);
       ld2(r_dr, o_dr[0], rx);
@@ -1224,7 +1227,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
       const bool ok = t0 + 2 * sg < s.seqlen;
       auto st2 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[2])
           __attribute__((always_inline)) {
-        pair_io<IO>::store(r, ok ? off : kOffNone, s.reverse ? x[1] : x[0], s.reverse ? x[0] : x[1]);
+        pair_io<IO>::store(r, ok ? off : kOffNone, REV ? x[1] : x[0], REV ? x[0] : x[1]);
       };
       st2(r_du, o_du[0], o_du_v);
       st2(r_ddr, o_ddr[0], o_ddr_v);
@@ -1373,40 +1376,40 @@ __global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
   }
 }
 
-template <typename IO, bool WITH_H, int XM>
+template <typename IO, bool WITH_H, int XM, bool REV>
 void launch_agg_b(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
   if (s.nquads)
-    agg_kernel<IO, WITH_H, XM, kBStateQuads><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+    agg_kernel<IO, WITH_H, XM, kBStateQuads, REV><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
   else if (s.bcquads)
-    agg_kernel<IO, WITH_H, XM, kBStepQuads><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+    agg_kernel<IO, WITH_H, XM, kBStepQuads, REV><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
   else
-    agg_kernel<IO, WITH_H, XM, kBScalar><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
+    agg_kernel<IO, WITH_H, XM, kBScalar, REV><<<dim3(waves), dim3(64), 0, stream>>>(s, p);
 }
 
-template <typename IO, bool WITH_H>
+template <typename IO, bool WITH_H, bool REV>
 void launch_agg_p(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
   if (s.pairs)
-    launch_agg_b<IO, WITH_H, kXStepPairs>(s, p, stream, waves);
+    launch_agg_b<IO, WITH_H, kXStepPairs, REV>(s, p, stream, waves);
   else if (s.dpairs)
     agg_coop_kernel<IO, WITH_H><<<dim3(waves / kBwdWaves), dim3(kBwdThreads), 0, stream>>>(s, p);
   else
-    launch_agg_b<IO, WITH_H, kXScalar>(s, p, stream, waves);
+    launch_agg_b<IO, WITH_H, kXScalar, REV>(s, p, stream, waves);
 }
 
 // Forward aggregate H only without the forward's chunk states.
-template <typename IO>
+template <typename IO, bool REV>
 void launch_agg(const BwdShape& s, const BwdPtrs& p, hipStream_t stream, unsigned waves) {
   if (s.states_given)
-    launch_agg_p<IO, false>(s, p, stream, waves);
+    launch_agg_p<IO, false, REV>(s, p, stream, waves);
   else
-    launch_agg_p<IO, true>(s, p, stream, waves);
+    launch_agg_p<IO, true, REV>(s, p, stream, waves);
 }
 
-template <typename IO>
+template <typename IO, bool REV>
 hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream) {
   const int64_t waves = static_cast<int64_t>(s.batch) * s.nseg * s.tiles * kBwdWaves;
   if (s.nseg > 1) {
-    launch_agg<IO>(s, p, stream, static_cast<unsigned>(waves * s.agg_split));
+    launch_agg<IO, REV>(s, p, stream, static_cast<unsigned>(waves * s.agg_split));
     const int64_t nc = s.nchan_pad * kMaxState;
     const dim3 grid(static_cast<unsigned>((nc + 63) / 64));
     const dim3 block(64 * carry_waves(s.nseg * s.agg_split));
@@ -1422,19 +1425,19 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
       ckpt_coop_kernel<IO><<<dim3(static_cast<unsigned>(waves / kBwdWaves)), dim3(kBwdThreads), 0,
                              stream>>>(s, p);
     else if (s.quads && s.bquads)
-      ckpt_kernel<IO, true, true><<<grid, dim3(64), 0, stream>>>(s, p);
+      ckpt_kernel<IO, true, true, REV><<<grid, dim3(64), 0, stream>>>(s, p);
     else if (s.quads)
-      ckpt_kernel<IO, true, false><<<grid, dim3(64), 0, stream>>>(s, p);
+      ckpt_kernel<IO, true, false, REV><<<grid, dim3(64), 0, stream>>>(s, p);
     else if (s.bquads)
-      ckpt_kernel<IO, false, true><<<grid, dim3(64), 0, stream>>>(s, p);
+      ckpt_kernel<IO, false, true, REV><<<grid, dim3(64), 0, stream>>>(s, p);
     else
-      ckpt_kernel<IO, false, false><<<grid, dim3(64), 0, stream>>>(s, p);
+      ckpt_kernel<IO, false, false, REV><<<grid, dim3(64), 0, stream>>>(s, p);
   }
   const int64_t wgs = static_cast<int64_t>(s.batch) * s.nseg * s.tiles;
   if (s.pairs)
-    bwd_kernel<IO, true><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
+    bwd_kernel<IO, true, REV><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
   else
-    bwd_kernel<IO, false><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
+    bwd_kernel<IO, false, REV><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
   const int64_t nq = (s.seqlen + kBcSteps - 1) / kBcSteps;
   if (s.sdB[1] == 1 && s.sdB[2] != 1) {
     constexpr int kQ = 2 * kBwdT / kBcSteps;
@@ -1454,7 +1457,9 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_scan_bwd(const BwdShape& s, const BwdPtrs& p, bool io_bf16, hipStream_t stream) {
-  return io_bf16 ? launch_bwd_t<bf16_t>(s, p, stream) : launch_bwd_t<float>(s, p, stream);
+  if (s.reverse)
+    return io_bf16 ? launch_bwd_t<bf16_t, true>(s, p, stream) : launch_bwd_t<float, true>(s, p, stream);
+  return io_bf16 ? launch_bwd_t<bf16_t, false>(s, p, stream) : launch_bwd_t<float, false>(s, p, stream);
 }
 
 }  // namespace mss
