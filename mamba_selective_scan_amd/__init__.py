@@ -70,6 +70,35 @@ def _need(t, name, ndim, dtype=None, device=None):
     return t
 
 
+def _need_gpu(t, name):
+    """The tensor that fixes a call's device must live on a GPU: the kernels
+    read and write every pointer from the device."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (torch device type 'cuda'), got {t.device}")
+
+
+def _workspace(t, device):
+    """A caller's workspace: contiguous uint8 on the call's device (its byte
+    count is passed on; the library checks it against what the call needs)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if t.dtype != torch.uint8 or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return t
+
+
+def _out_like(out, ref, name):
+    """A caller's output buffer for a decode step: the shape, dtype and device
+    of ``ref`` (any strides)."""
+    if tuple(out.shape) != tuple(ref.shape) or out.dtype != ref.dtype or out.device != ref.device:
+        raise ValueError(f"out must match {name} in shape, dtype and device")
+    return out
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -102,6 +131,7 @@ def _stream_handle(device):
 def _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
                delta_softplus, reverse=False):
     torch = _torch()
+    _need_gpu(u, "u")
     dev = u.device
     _need(u, "u", 3)
     bsz, dim, seqlen = u.shape
@@ -208,7 +238,7 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
         _lib.check(st.value)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
-        a.workspace = _ptr(workspace)
+        a.workspace = _ptr(_workspace(workspace, u.device))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
         _lib.check(lib.mss_selective_scan_fwd(ctypes.byref(a), _stream_handle(u.device)))
     res = (out,) + ((final_state,) if return_final_state else ()) + \
@@ -260,6 +290,7 @@ def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None
     """
     torch = _torch()
     lib = _lib.lib()
+    _need_gpu(u, "u")
     dev = u.device
     _need(u, "u", 3, torch.float32, dev)
     bsz, dim, seqlen = u.shape
@@ -313,7 +344,7 @@ def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
-        a.workspace = _ptr(workspace)
+        a.workspace = _ptr(_workspace(workspace, dev))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.mss_selective_scan_fwd_complex(ctypes.byref(a), _stream_handle(dev)))
     return (out, final_state) if return_final_state else out
@@ -325,6 +356,7 @@ def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_
     returns out [B, D].  u, delta_raw, z are [B, D]; B, C are [B, N]."""
     torch = _torch()
     lib = _lib.lib()
+    _need_gpu(state, "state")
     dev = state.device
     _need(state, "state", 3, torch.float32, dev)
     if not state.is_contiguous():
@@ -346,8 +378,7 @@ def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_
         _need(z, "z", 2, dt, dev)
     _contig_f32(D, "D", (dim,), dev)
     _contig_f32(dt_bias, "dt_bias", (dim,), dev)
-    if out is None:
-        out = torch.empty_like(u)
+    out = torch.empty_like(u) if out is None else _out_like(out, u, "u")
     a = _lib.new_step_args()
     a.io_dtype = _io_dtype(u)
     a.batch, a.dim, a.dstate = bsz, dim, dstate
@@ -409,6 +440,7 @@ def causal_conv1d_fwd(x, weight, bias=None, *, activation="silu", initial_state=
     """
     torch = _torch()
     lib = _lib.lib()
+    _need_gpu(x, "x")
     dev = x.device
     _need(x, "x", 3)
     bsz, dim, seqlen = x.shape
@@ -447,6 +479,7 @@ def causal_conv1d_update(state, x, weight, bias=None, *, activation="silu", out=
     slides ``state`` [B, D, W-1] (x's dtype, contiguous) in place."""
     torch = _torch()
     lib = _lib.lib()
+    _need_gpu(x, "x")
     dev = x.device
     _need(x, "x", 2)
     bsz, dim = x.shape
@@ -456,8 +489,7 @@ def causal_conv1d_update(state, x, weight, bias=None, *, activation="silu", out=
     if activation not in _ACTIVATIONS:
         raise ValueError(f"activation must be 'silu' or None, got {activation!r}")
     _window(state, "state", (bsz, dim, width - 1), x.dtype, dev)
-    if out is None:
-        out = torch.empty_like(x)
+    out = torch.empty_like(x) if out is None else _out_like(out, x, "x")
     a = _lib.new_conv_step_args()
     a.io_dtype = _io_dtype(x)
     a.batch, a.dim, a.width = bsz, dim, width
@@ -547,7 +579,7 @@ def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=
     _lib.check(st.value)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    b.workspace = _ptr(workspace)
+    b.workspace = _ptr(_workspace(workspace, dev))
     b.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.mss_selective_scan_bwd(ctypes.byref(b), _stream_handle(dev)))
     return {k: v for k, v in g.items() if v is not None}
