@@ -128,6 +128,18 @@ def _stream_handle(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _launch(fn, args, device):
+    """Call a library entry point on torch's current stream of ``device``, with
+    ``device`` current: torch's default stream is HIP's null stream, which
+    stands for the current device's."""
+    torch = _torch()
+    if device.index is None or device.index == torch.cuda.current_device():
+        _lib.check(fn(ctypes.byref(args), _stream_handle(device)))
+        return
+    with torch.cuda.device(device):
+        _lib.check(fn(ctypes.byref(args), _stream_handle(device)))
+
+
 def _scan_args(u, delta_raw, A_log, B, C, D, z, dt_bias, initial_state, out, final_state,
                delta_softplus, reverse=False):
     torch = _torch()
@@ -231,7 +243,7 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
     if _noalloc:
         if workspace is not None:
             raise ValueError("the no-allocation forward takes no workspace")
-        _lib.check(lib.mss_selective_scan_fwd_noalloc(ctypes.byref(a), _stream_handle(u.device)))
+        _launch(lib.mss_selective_scan_fwd_noalloc, a, u.device)
     else:
         st = ctypes.c_int(0)
         need = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
@@ -240,7 +252,7 @@ def selective_scan_fwd(u, delta_raw, A_log, B, C, D=None, z=None, dt_bias=None, 
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
         a.workspace = _ptr(_workspace(workspace, u.device))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
-        _lib.check(lib.mss_selective_scan_fwd(ctypes.byref(a), _stream_handle(u.device)))
+        _launch(lib.mss_selective_scan_fwd, a, u.device)
     res = (out,) + ((final_state,) if return_final_state else ()) + \
         ((chunk_states,) if return_chunk_states else ())
     return res if len(res) > 1 else out
@@ -346,7 +358,7 @@ def selective_scan_fwd_complex(u, delta_raw, A_log, A_imag, B, C, D=None, z=None
     if workspace is not None:
         a.workspace = _ptr(_workspace(workspace, dev))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
-    _lib.check(lib.mss_selective_scan_fwd_complex(ctypes.byref(a), _stream_handle(dev)))
+    _launch(lib.mss_selective_scan_fwd_complex, a, dev)
     return (out, final_state) if return_final_state else out
 
 
@@ -393,7 +405,7 @@ def selective_state_update(state, u, delta_raw, A_log, B, C, D=None, z=None, dt_
     a.dt_bias = _ptr(dt_bias)
     a.out, a.out_stride = _ptr(out), _strides(out, 2)
     a.delta_softplus = 1 if delta_softplus else 0
-    _lib.check(lib.mss_selective_state_update(ctypes.byref(a), _stream_handle(dev)))
+    _launch(lib.mss_selective_state_update, a, dev)
     return out
 
 
@@ -468,7 +480,7 @@ def causal_conv1d_fwd(x, weight, bias=None, *, activation="silu", initial_state=
     a.out, a.out_stride = _ptr(out), _strides(out, 3)
     a.final_state = _ptr(final_state)
     a.activation = _ACTIVATIONS[activation]
-    _lib.check(lib.mss_causal_conv1d_fwd(ctypes.byref(a), _stream_handle(dev)))
+    _launch(lib.mss_causal_conv1d_fwd, a, dev)
     if return_final_state:
         return out, final_state
     return out
@@ -499,7 +511,7 @@ def causal_conv1d_update(state, x, weight, bias=None, *, activation="silu", out=
     a.bias = _ptr(bias)
     a.out, a.out_stride = _ptr(out), _strides(out, 2)
     a.activation = _ACTIVATIONS[activation]
-    _lib.check(lib.mss_causal_conv1d_update(ctypes.byref(a), _stream_handle(dev)))
+    _launch(lib.mss_causal_conv1d_update, a, dev)
     return out
 
 
@@ -581,7 +593,7 @@ def selective_scan_bwd(u, delta_raw, A_log, B, C, dout, D=None, z=None, dt_bias=
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     b.workspace = _ptr(_workspace(workspace, dev))
     b.workspace_bytes = workspace.numel() * workspace.element_size()
-    _lib.check(lib.mss_selective_scan_bwd(ctypes.byref(b), _stream_handle(dev)))
+    _launch(lib.mss_selective_scan_bwd, b, dev)
     return {k: v for k, v in g.items() if v is not None}
 
 
