@@ -92,19 +92,24 @@ def test_bidirectional_sum(mss):
     check("bidirectional sum", to_np(both), f + r[:, :, ::-1], 1e-4)
 
 
-@pytest.mark.parametrize("shape,layout", [((2, 72, 100), "bdl"), ((1, 64, 1500), "bdl"),
-                                          ((1, 40, 1500), "bld"), ((2, 48, 333), "bld")])
-def test_reverse_backward(mss, shape, layout):
+@pytest.mark.parametrize("shape,layout,io", [
+    ((2, 72, 100), "bdl", "f32"), ((1, 64, 1500), "bdl", "f32"), ((1, 40, 1500), "bld", "f32"),
+    ((2, 48, 333), "bld", "f32"),
+    # bf16: step pairs and 4-step vectors, with and without time segments, and
+    # an odd length (element by element)
+    ((2, 72, 100), "bdl", "bf16"), ((1, 64, 1500), "bdl", "bf16"), ((1, 40, 1501), "bdl", "bf16"),
+    ((1, 64, 998), "bld", "bf16")])
+def test_reverse_backward(mss, shape, layout, io):
     import torch
     batch, dim, seqlen = shape
-    note(f"reverse bwd {shape} {layout}")
+    note(f"reverse bwd {shape} {layout} {io}")
     x = generate(batch, dim, seqlen, 16, layout, seed=23, a_log="normal")
-    dx = to_torch(x, device(), "f32")
+    dx = to_torch(x, device(), io)
     g = torch.Generator().manual_seed(5)
     dout = torch.randn(batch, dim, seqlen, generator=g)
     if layout == "bld":
         dout = dout.transpose(1, 2).contiguous().transpose(1, 2)
-    dout = dout.to(device())
+    dout = dout.to(device=device(), dtype=dx["u"].dtype)
     h0 = torch.randn(batch, dim, 16, generator=g).to(device())
     dfin = torch.randn(batch, dim, 16, generator=g).to(device())
     got = mss.selective_scan_bwd(dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dout,
@@ -120,4 +125,4 @@ def test_reverse_backward(mss, shape, layout):
         r = ref[names[k]]
         if k in ("du", "ddelta_raw", "dB", "dC", "dz"):
             r = r[:, :, ::-1]
-        check(f"reverse bwd {shape} {k}", to_np(v), r, 1e-4)
+        check(f"reverse bwd {shape} {io} {k}", to_np(v), r, TOL[io])
