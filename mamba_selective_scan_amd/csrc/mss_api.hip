@@ -208,11 +208,14 @@ mss_status check_bwd_shape(const mss_scan_bwd_args* a) {
   const int64_t tiles = (a->dim + mss::kBwdCh - 1) / mss::kBwdCh;
   if (a->batch * tiles * mss::kBwdWaves > 0xFFFFFFFFll) return MSS_ERR_BAD_SHAPE;
   // the dB/dC sum's grid: 256-thread blocks over batch x 2 x 16 states x
-  // the step quads of whole partial rows (written as a division: the product
-  // of the largest allowed sizes overflows)
+  // the step quads of whole partial rows, then the parameter sums' blocks
+  // (written as a division: the product of the largest allowed sizes
+  // overflows)
   const int64_t row_steps = 2 * mss::kBwdT;
   const int64_t quads = (a->seqlen + row_steps - 1) / row_steps * (row_steps / mss::kBcSteps);
-  if (a->batch > (int64_t{0xFFFFFFFF} * 256) / (2 * mss::kMaxState * quads)) return MSS_ERR_BAD_SHAPE;
+  const int64_t fin_blocks = (a->dim * (mss::kMaxState + 2) + 255) / 256;
+  if (a->batch > ((int64_t{0xFFFFFFFF} - fin_blocks) * 256) / (2 * mss::kMaxState * quads))
+    return MSS_ERR_BAD_SHAPE;
   return MSS_OK;
 }
 

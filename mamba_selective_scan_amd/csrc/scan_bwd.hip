@@ -48,8 +48,8 @@
 //           into one partial per workgroup and step;
 //        O  du and ddelta_raw per element.
 //   3. reduce_bc_kernel: dB and dC as sums of the workgroup partials, in a
-//      fixed order (deterministic).
-//   4. finalize_kernel: dA_log, dD and ddt_bias summed over the batch rows.
+//      fixed order (deterministic); the same launch's last blocks sum
+//      dA_log, dD and ddt_bias over the batch rows and segments.
 #include "mss_device.hpp"
 #include "mss_internal.hpp"
 
@@ -1305,8 +1305,34 @@ __device__ inline float ordered_sum(int n, F f) {
 // stores fill whole runs of the output instead of one 4-byte word per 64
 // bytes, and every load still reads whole partial rows.
 static_assert((2 * kBwdT) % kBcSteps == 0, "a thread's steps lie in one partial row");
+// dA_log, dD and ddt_bias: element i of [dim][kMaxState + 2], the sum over
+// batch rows and segments of the reverse walk's per-channel partials.
+__device__ inline void finalize_sums(const BwdShape& s, const BwdPtrs& p, int64_t i) {
+  if (i >= static_cast<int64_t>(s.dim) * (kMaxState + 2)) return;
+  const int d = static_cast<int>(i / (kMaxState + 2));
+  const int j = static_cast<int>(i % (kMaxState + 2));
+  if (j < kMaxState && j >= s.dstate) return;
+  const float sum = ordered_sum(s.nseg * s.batch, [&](int r) {
+    return p.part_chan[(static_cast<int64_t>(r) * s.dim + d) * (kMaxState + 2) + j];
+  });
+  if (j < kMaxState)
+    p.dA_log[static_cast<int64_t>(d) * s.dstate + j] = sum;
+  else if (j == kMaxState) {
+    if (p.dD != nullptr) p.dD[d] = sum;
+  } else if (p.ddt_bias != nullptr) {
+    p.ddt_bias[d] = sum;
+  }
+}
+
+// Blocks [0, bc_blocks) sum dB and dC; the blocks after them run
+// finalize_sums (one launch for both, which read only the reverse walk's
+// partials).
 template <typename IO, bool NF>
-__global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
+__global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p, unsigned bc_blocks) {
+  if (blockIdx.x >= bc_blocks) {
+    finalize_sums(s, p, static_cast<int64_t>(blockIdx.x - bc_blocks) * blockDim.x + threadIdx.x);
+    return;
+  }
   const int nq = (s.seqlen + kBcSteps - 1) / kBcSteps;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   int t0, n, b;
@@ -1355,25 +1381,6 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(BwdShape s, BwdPtrs p) {
 #pragma unroll
   for (int e = 0; e < kBcSteps; ++e)
     if (t0 + e < s.seqlen) io_traits<IO>::store(out + tstore(s, t0 + e) * st, sum[e]);
-}
-
-// ---------------------------------------------------------------- pass 4 ---
-__global__ __launch_bounds__(256) void finalize_kernel(BwdShape s, BwdPtrs p) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= static_cast<int64_t>(s.dim) * (kMaxState + 2)) return;
-  const int d = static_cast<int>(i / (kMaxState + 2));
-  const int j = static_cast<int>(i % (kMaxState + 2));
-  if (j < kMaxState && j >= s.dstate) return;
-  const float sum = ordered_sum(s.nseg * s.batch, [&](int r) {
-    return p.part_chan[(static_cast<int64_t>(r) * s.dim + d) * (kMaxState + 2) + j];
-  });
-  if (j < kMaxState)
-    p.dA_log[static_cast<int64_t>(d) * s.dstate + j] = sum;
-  else if (j == kMaxState) {
-    if (p.dD != nullptr) p.dD[d] = sum;
-  } else if (p.ddt_bias != nullptr) {
-    p.ddt_bias[d] = sum;
-  }
 }
 
 template <typename IO, bool WITH_H, int XM, bool REV>
@@ -1439,18 +1446,19 @@ hipError_t launch_bwd_t(const BwdShape& s, const BwdPtrs& p, hipStream_t stream)
   else
     bwd_kernel<IO, false, REV><<<dim3(static_cast<unsigned>(wgs)), dim3(kBwdThreads), 0, stream>>>(s, p);
   const int64_t nq = (s.seqlen + kBcSteps - 1) / kBcSteps;
+  const int64_t fin_blocks = (static_cast<int64_t>(s.dim) * (kMaxState + 2) + 255) / 256;
   if (s.sdB[1] == 1 && s.sdB[2] != 1) {
     constexpr int kQ = 2 * kBwdT / kBcSteps;
     const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * ((nq + kQ - 1) / kQ) * 2 * 64;
-    reduce_bc_kernel<IO, true><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0,
-                                 stream>>>(s, p);
+    const unsigned bc_blocks = static_cast<unsigned>((nbc + 255) / 256);
+    reduce_bc_kernel<IO, true><<<dim3(static_cast<unsigned>(bc_blocks + fin_blocks)), dim3(256), 0,
+                                 stream>>>(s, p, bc_blocks);
   } else {
     const int64_t nbc = static_cast<int64_t>(s.batch) * 2 * s.dstate * nq;
-    reduce_bc_kernel<IO, false><<<dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0,
-                                  stream>>>(s, p);
+    const unsigned bc_blocks = static_cast<unsigned>((nbc + 255) / 256);
+    reduce_bc_kernel<IO, false><<<dim3(static_cast<unsigned>(bc_blocks + fin_blocks)), dim3(256), 0,
+                                  stream>>>(s, p, bc_blocks);
   }
-  const int64_t nch = static_cast<int64_t>(s.dim) * (kMaxState + 2);
-  finalize_kernel<<<dim3(static_cast<unsigned>((nch + 255) / 256)), dim3(256), 0, stream>>>(s, p);
   return hipGetLastError();
 }
 
