@@ -143,6 +143,67 @@ def test_long_sequence(mss):
         check(f"bwd long {k}", to_np(v), ref[ORACLE_NAME[k]], TOL["f32"])
 
 
+def _oracle_bwd_in_channel_groups(dx, groups=8):
+    """The oracle backward over every channel, run on channel groups in
+    threads (the oracle's C call releases the GIL).  Channels are independent
+    except through dB and dC, which sum over them: the groups' dB and dC are
+    added (in fp64), every other gradient comes from its channel's group."""
+    from concurrent.futures import ThreadPoolExecutor
+    oracle.load()
+    host = {k: (None if dx.get(k) is None else to_np(dx[k]))
+            for k in ("u", "delta_raw", "A_log", "B", "C", "dout", "D", "z", "dt_bias", "h0",
+                      "dfinal")}
+    dim = host["u"].shape[1]
+    edges = np.linspace(0, dim, groups + 1).astype(int)
+
+    def run(i):
+        c = slice(edges[i], edges[i + 1])
+        opt = lambda k, ax: None if host[k] is None else (host[k][:, c] if ax else host[k][c])  # noqa: E731
+        return oracle.scan_bwd(host["u"][:, c], host["delta_raw"][:, c], host["A_log"][c],
+                               host["B"], host["C"], host["dout"][:, c], D=opt("D", 0),
+                               z=opt("z", 1), dt_bias=opt("dt_bias", 0), h0=opt("h0", 1),
+                               dfinal=opt("dfinal", 1))
+
+    with ThreadPoolExecutor(groups) as pool:
+        parts = list(pool.map(run, range(groups)))
+    ref = {}
+    for k in parts[0]:
+        if parts[0][k] is None:
+            ref[k] = None
+        elif k in ("dB", "dC"):
+            ref[k] = sum(p[k] for p in parts)
+        else:
+            ref[k] = np.concatenate([p[k] for p in parts], axis=0 if k in ("dA_log", "dD",
+                                                                           "ddt_bias") else 1)
+    return ref
+
+
+@pytest.mark.parametrize("wname", ["mamba130m_layer", "long_handoff", "audio_channel_last"])
+def test_few_channel_workloads_full(mss, wname):
+    """The few-channel workloads at their full shapes, in the launch
+    configuration bench.py times (time segments; the aggregate pass in parts
+    when the forward's chunk states are given; channel-last rows on the audio
+    shape), with initial state and final-state gradient: the standalone
+    backward and the backward reading the forward's chunk states, every
+    gradient of every channel against the oracle."""
+    import torch
+    w = WORKLOADS[wname]
+    dx = _problem(w.batch, w.dim, w.seqlen, w.dstate, layout=w.layout, h0=True, dfinal=True)
+    note(f"bwd full {wname}: B={w.batch} D={w.dim} L={w.seqlen} {w.layout}")
+    args = (dx["u"], dx["delta_raw"], dx["A_log"], dx["B"], dx["C"], dx["dout"])
+    kw = dict(D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"], initial_state=dx["h0"],
+              dfinal_state=dx["dfinal"])
+    standalone = mss.selective_scan_bwd(*args, **kw)
+    _, states = mss.selective_scan_fwd(*args[:5], D=dx["D"], z=dx["z"], dt_bias=dx["dt_bias"],
+                                       initial_state=dx["h0"], return_chunk_states=True)
+    with_states = mss.selective_scan_bwd(*args, **kw, chunk_states=states)
+    torch.cuda.synchronize()
+    ref = _oracle_bwd_in_channel_groups(dx)
+    for name, got in (("standalone", standalone), ("with chunk states", with_states)):
+        for k, v in got.items():
+            check(f"bwd full {wname} {name} {k}", to_np(v), ref[ORACLE_NAME[k]], TOL["f32"])
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_mamba2p8b_layer_full(mss, io):
     """The 2.8b layer shape (8 x 5120 x 4096) in the launch configuration
