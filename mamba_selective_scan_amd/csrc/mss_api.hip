@@ -28,6 +28,15 @@ constexpr int64_t kMaxSeqlen = int64_t{1} << 30;  // time indices, padded, stay 
 // The plan depends only on the shape, so results do not depend on the device.
 constexpr int64_t kSplitBelowTiles = 2048;
 constexpr int64_t kTargetTiles = 4096;
+// The aggregate pass (every segment but the last, no C, z or output) needs
+// about 60 VGPRs, so eight of its waves fit a SIMD where the main pass holds
+// four or five.  It cuts every segment into parts, as many as bring its grid
+// to at most kAggWaves waves (counting whole 32-channel blocks, so that both
+// layouts get the same plan), with parts of at least kAggMinPartChunks
+// chunks and at most mss::kMaxAggSplit parts; the carry pass composes the
+// parts.
+constexpr int64_t kAggWaves = 8 * 1024;
+constexpr int64_t kAggMinPartChunks = 4;
 
 struct Extent {
   uintptr_t lo = 0, hi = 0;  // byte range [lo, hi)
@@ -136,13 +145,22 @@ ScanPlan make_plan(const mss_scan_args* a) {
   const int64_t seg_chunks = (chunks + nseg - 1) / nseg;
   s.seg_len = static_cast<int>(seg_chunks * kT);
   s.nseg = static_cast<int>((a->seqlen + s.seg_len - 1) / s.seg_len);
+  s.agg_split = 1;
+  if (s.nseg > 1) {
+    const int64_t blocks = a->batch * ((s.groups + 3) / 4) * 4 * (s.nseg - 1);
+    s.agg_split = static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>({kAggWaves / blocks, seg_chunks / kAggMinPartChunks,
+                              int64_t{mss::kMaxAggSplit}})));
+  }
+  s.part_len = static_cast<int>((seg_chunks + s.agg_split - 1) / s.agg_split * kT);
   s.nchan_pad = tiles * kCh;
   s.softplus = a->delta_softplus ? 1 : 0;
   s.reverse = a->reverse;
   s.t_first = 0;
   s.t_stop = s.seqlen;
   if (s.nseg > 1) {
-    p.agg_bytes = round_up(static_cast<size_t>(s.nseg - 1) * s.nchan_pad * kMaxState * sizeof(float2), 256);
+    p.agg_bytes = round_up(static_cast<size_t>(s.nseg - 1) * s.agg_split * s.nchan_pad *
+                               kMaxState * sizeof(float2), 256);
     p.carry_bytes = round_up(static_cast<size_t>(s.nseg) * s.nchan_pad * kMaxState * sizeof(float), 256);
   }
   // a sequence that does not end on a vector boundary ends with an

@@ -102,6 +102,16 @@ __device__ inline float reduce_groups(float y0, float y1, float y2, float y3) {
                                                         false));
 }
 
+// Sum over the eight state groups of one channel (lanes c + 8g) of one value
+// per lane, left in all eight lanes: a butterfly over lane bits 5, 4 and 3,
+// so every lane adds the same pairs (up to order) and ends with the same sum.
+__device__ inline float sum_over_groups(float v) {
+  v += __shfl_xor(v, 32, 64);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
 // Sum over the 16 lanes of a DPP row, left in every lane of the row (every
 // source lane of a row rotation is valid, so bound_ctrl changes nothing).
 __device__ inline float row_sum16(float v) {

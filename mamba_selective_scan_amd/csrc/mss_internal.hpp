@@ -117,6 +117,8 @@ struct ScanShape {
   int batch, dim, seqlen, dstate;
   int groups;           // ceil(dim / kCh)
   int nseg, seg_len;    // time segments (seg_len is a multiple of kT)
+  int agg_split;        // AGG pass: parts per segment, 1..kMaxAggSplit (the carry pass composes them)
+  int part_len;         // AGG pass: steps per part, a multiple of kT
   int64_t nchan_pad;    // batch * groups * kCh: rows of the workspace arrays
   int64_t su[3], sd[3], sz[3], so[3];  // u, delta_raw, z, out: (b, d, t)
   int64_t sB[3], sC[3];                // B, C: (b, n, t)
@@ -128,6 +130,8 @@ struct ScanShape {
   int reverse;          // logical step tau is storage step seqlen-1-tau
   int bc_const;         // B and C have time stride 0 (time-invariant)
 };
+
+constexpr int kMaxAggSplit = 2;
 
 struct StepShape {
   int batch, dim, dstate;

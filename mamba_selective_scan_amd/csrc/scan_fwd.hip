@@ -47,7 +47,9 @@
 // grid covers the GPU.  Segment s needs the state entering it.  A first pass
 // (AGG) runs every segment but the last from a zero state and records, per
 // (channel, state), the segment's pair aggregate (prod_t a_t, h_end): the
-// product is exp2(A2 * sum_t delta_t) since all a_t share A.  A carry pass
+// product is exp2(A2 * sum_t delta_t) since all a_t share A.  Its waves need
+// fewer registers than the main pass's, so it cuts each segment into
+// agg_split parts and records one aggregate per part.  A carry pass
 // composes the aggregates in order with (a2, b2) o (a1, b1) = (a2 a1,
 // a2 b1 + b2) ("mamba-metal", sections "Selective scan の本質" and
 // "チャンク間 running prefix"), and the main pass starts each segment from
@@ -172,7 +174,10 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   // workgroup.  The exchange takes two workgroup barriers per chunk, and the
   // LDS buffers alternate with the chunk's parity.
   constexpr bool COOP = !XT && VEC;
-  constexpr int kBufs = COOP ? 2 : 1;
+  // The AGG pass has no output phase: a chunk's second barrier already orders
+  // every read of its buffer before the next chunk's E phase writes it, so one
+  // buffer serves (half the LDS, which leaves room for eight waves per SIMD).
+  constexpr int kBufs = (COOP && !AGG) ? 2 : 1;
   constexpr int kBcSize = LTI ? 4 : (AGG ? kMaxState : kBcRows) * kT;
   constexpr int kDdSize = kCh * kDdPitch;
   constexpr int kSkipSize = (AGG || COOP) ? 4 : kCh * kSkipPitch;  // COOP keeps D*u in registers
@@ -199,15 +204,16 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   const int xcd = lin % kXcds;
   const int per_xcd = nwg / kXcds, extra = nwg % kXcds;
   const int logical = xcd * per_xcd + min(xcd, extra) + lin / kXcds;
-  const int pass_segs = AGG ? s.nseg - 1 : s.nseg;
-  int b, d0, seg, dx0;  // dx0: first channel of the x data the lane loads and stores
+  // The AGG pass walks part `link % agg_split` of segment `link / agg_split`.
+  const int pass_links = AGG ? (s.nseg - 1) * s.agg_split : s.nseg;
+  int b, d0, link, dx0;  // dx0: first channel of the x data the lane loads and stores
   bool tile_ok = true;  // COOP: the wave's tile lies inside the channel groups
   if constexpr (COOP) {
     const int quads = (s.groups + kWg - 1) / kWg;
     const int GQ = s.batch * quads;
-    if (logical >= GQ * pass_segs) return;  // uniform over the workgroup
+    if (logical >= GQ * pass_links) return;  // uniform over the workgroup
     const int gq = logical % GQ;
-    seg = logical / GQ;
+    link = logical / GQ;
     b = gq / quads;
     const int group = (gq - b * quads) * kWg + wave;
     tile_ok = group < s.groups;
@@ -216,15 +222,19 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   } else {
     const int G = s.batch * s.groups;
     const int tile = logical * kWg + wave;
-    if (tile >= G * pass_segs) return;  // the last workgroup's spare waves
+    if (tile >= G * pass_links) return;  // the last workgroup's spare waves
     const int g = tile % G;
-    seg = tile / G;
+    link = tile / G;
     b = g / s.groups;
     d0 = (g - b * s.groups) * kCh;
     dx0 = d0;
   }
-  const int t_begin = s.t_first + seg * s.seg_len;
-  const int t_end = min(s.t_stop, t_begin + s.seg_len);
+  const int seg = AGG ? link / s.agg_split : link;
+  const int seg_begin = s.t_first + seg * s.seg_len;
+  const int seg_end = min(s.t_stop, seg_begin + s.seg_len);
+  // (a trailing part may be empty: it walks no chunk and records (1, 0))
+  const int t_begin = AGG ? seg_begin + (link - seg * s.agg_split) * s.part_len : seg_begin;
+  const int t_end = AGG ? min(seg_end, t_begin + s.part_len) : seg_end;
   constexpr int64_t es = sizeof(IO);
 
   // ---- S-phase constants: lane = (state group sg, channel sc) ----
@@ -565,6 +575,11 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   const float* p_b0 = s_bc + (2 * sg) * kT;
   const float* p_c0 = s_bc + (AGG ? 0 : (kMaxState + 2 * sg) * kT);
   const float* p_dd = s_dd + sc * kDdPitch;
+  // The same B rows as byte offsets from the buffer start, for the AGG pass's
+  // rolled block loop: rows 2sg, 2sg+1 start 256 sg bytes in (bits 4..6 clear)
+  // and the swizzled column of block t4 / 4 flips bits 4..6 only, so one XOR
+  // per block gives the address: 256 sg + 16 ((t4 / 4) ^ (sg % 8)).
+  const uint32_t b_key = static_cast<uint32_t>(2 * sg * kT * 4 + ((sg & 7) << 4));
   // The group reduction leaves step {0, 2, 1, 3}[row] of each block in row
   // `row` = lane / 16, as two sums over four state groups each: lane c + 8h
   // of the row holds the sum over the groups of parity h.  The two sums of
@@ -614,10 +629,13 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   auto scan_block = [&](int t4, int t0, int nb) __attribute__((always_inline)) {
     record_state(t0 + t4, t4);
     const int col = (((t4 >> 2) ^ sg) & 7) << 2;
-    const float* pb = p_b0 + nb * kBcSize;
+    const float* pb = AGG ? reinterpret_cast<const float*>(
+                                reinterpret_cast<const char*>(s_bc + nb * kBcSize) +
+                                (b_key ^ static_cast<uint32_t>(t4 << 2)))
+                          : p_b0 + nb * kBcSize + col;
     const float* pd = p_dd + nb * kWg * kDdSize;
-    const f4 b0 = LTI ? f4{b_lti[0], b_lti[0], b_lti[0], b_lti[0]} : lds_f4(pb + col);
-    const f4 b1 = LTI ? f4{b_lti[1], b_lti[1], b_lti[1], b_lti[1]} : lds_f4(pb + kT + col);
+    const f4 b0 = LTI ? f4{b_lti[0], b_lti[0], b_lti[0], b_lti[0]} : lds_f4(pb);
+    const f4 b1 = LTI ? f4{b_lti[1], b_lti[1], b_lti[1], b_lti[1]} : lds_f4(pb + kT);
     const f4 dd01 = lds_f4(pd + 2 * t4);
     const f4 dd23 = lds_f4(pd + 2 * t4 + 4);
     const float dls[4] = {dd01.x, dd01.z, dd23.x, dd23.z};
@@ -630,7 +648,6 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
         h[0] = fmaf(fast_exp2(dls[k] * A2[0]), h[0], dus[k] * bs0[k]);
         h[1] = fmaf(fast_exp2(dls[k] * A2[1]), h[1], dus[k] * bs1[k]);
       }
-      sum_delta += (dls[0] + dls[1]) + (dls[2] + dls[3]);
     } else {
       const float* pc = p_c0 + nb * kBcSize;
       const f4 c0 = LTI ? f4{c_lti[0], c_lti[0], c_lti[0], c_lti[0]} : lds_f4(pc + col);
@@ -647,9 +664,14 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
       p_y[nb * kWg * kDdSize + 2 * t4] = reduce_groups_half(y[0], y[1], y[2], y[3]);
     }
   };
-  // The main pass unrolls the blocks: the swizzled B/C offsets become
-  // loop-invariant registers and the other LDS offsets immediates.  The AGG
-  // pass keeps a loop (unrolled, its LDS reads would all be hoisted).
+  // The blocks are unrolled: the swizzled B/C offsets become loop-invariant
+  // registers and the other LDS offsets immediates.  In the AGG pass a
+  // scheduling barrier keeps each block's LDS reads inside the block (hoisted
+  // together, they would hold eight blocks of operands in registers), and the
+  // segment's sum of delta is split over the lanes of a channel: lane (g, c)
+  // adds the four deltas of block g of every chunk (a lane reads them from
+  // s_dd like its scan does), and the eight partial sums meet once, at the
+  // segment end (sum_over_groups), instead of every lane adding all 32.
   auto phase_s = [&](int t0, int nb) __attribute__((always_inline)) {
     if constexpr (AGG) {
 #pragma unroll 1
@@ -657,6 +679,11 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     } else {
 #pragma unroll
       for (int t4 = 0; t4 < kT; t4 += 4) scan_block(t4, t0, nb);
+    }
+    if constexpr (AGG) {
+      const float* pg = p_dd + nb * kWg * kDdSize + 8 * sg;
+      const f4 d01 = lds_f4(pg), d23 = lds_f4(pg + 4);
+      sum_delta += (d01.x + d01.z) + (d23.x + d23.z);
     }
   };
 
@@ -718,11 +745,12 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
   // the output and input phases, so a wave whose scan is done gets to its
   // memory waits and load issue at once instead of queueing behind the scans
   // of older waves: loads leave earlier and have longer to arrive.
-  // COOP: chunk c uses LDS buffer nb = c % 2.  The first barrier publishes
-  // every wave's E(c) before any wave scans c; the second publishes every
-  // wave's totals of c before any wave reads them in O(c).  E(c+1) writes
-  // the other buffer, whose last readers (S(c-1), O(c-1)) all finished
-  // before the first barrier of c.
+  // COOP: chunk c uses LDS buffer nb = c % 2 (the AGG pass: buffer 0).  The
+  // first barrier publishes every wave's E(c) before any wave scans c; the
+  // second publishes every wave's totals of c before any wave reads them in
+  // O(c).  E(c+1) writes the other buffer, whose last readers (S(c-1),
+  // O(c-1)) all finished before the first barrier of c; with one buffer
+  // (AGG: no O phase) its last readers, S(c), finished before the second.
   auto chunk = [&](int c, int nb) __attribute__((always_inline)) {
     const int t0 = t_begin + c * kT;
     issue_bc_loads(t0 + kT, t_end);
@@ -734,7 +762,7 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     if constexpr (COOP) __syncthreads();
     phase_o(zb, t0, nb);
     issue_z_loads(zb, t0 + kT, t_end);
-    phase_e(in, t0 + kT, COOP ? nb ^ 1 : 0);
+    phase_e(in, t0 + kT, kBufs == 2 ? nb ^ 1 : 0);
   };
   if constexpr (COOP) {
     // Two chunks per iteration, so that the buffer index is a constant in
@@ -743,7 +771,7 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
     // unchanged, and its stores and chunk states are masked by t_end.
     for (int c = 0; c < nchunks; c += 2) {
       chunk(c, 0);
-      chunk(c + 1, 1);
+      chunk(c + 1, kBufs == 2 ? 1 : 0);
     }
   } else {
     for (int c = 0; c < nchunks; ++c) chunk(c, 0);
@@ -751,12 +779,13 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
 
   // ---- segment end ----
   if constexpr (AGG) {
+    const float seg_delta = sum_over_groups(sum_delta);
 #pragma unroll
     for (int k = 0; k < kStatesPerLane; ++k) {
       const int n = sg * kStatesPerLane + k;
-      const float prod_a = fast_exp2(A2[k] * sum_delta);
+      const float prod_a = fast_exp2(A2[k] * seg_delta);
       if (tile_ok)
-        agg[(static_cast<int64_t>(seg) * s.nchan_pad + chan_row) * kMaxState + n] =
+        agg[(static_cast<int64_t>(link) * s.nchan_pad + chan_row) * kMaxState + n] =
             make_float2(prod_a, h[k]);
     }
   } else {
@@ -772,12 +801,14 @@ __global__ __launch_bounds__(kThreads * kWavesPerWg<XT>) __attribute__((amdgpu_w
 }
 
 // carry[s] = state entering segment s, from the segment aggregates:
-//   carry[0] = h0 (or 0),  carry[s+1] = P[s] * carry[s] + H[s].
-// One lane per (channel, state); the chain of nseg - 1 aggregates is walked in
-// ranges of at most kCarryBatch segments, one wave each (walk_chain_in_ranges):
+//   carry[0] = h0 (or 0),  carry[s+1] = P[s] * carry[s] + H[s],
+// where (P[s], H[s]) composes the agg_split part aggregates of segment s in
+// order.  One lane per (channel, state); the chain of nseg - 1 aggregates is
+// walked in ranges of at most kCarryBatch segments, one wave each (walk_chain_in_ranges):
 // one memory latency per call.  (A 256-channel sequence in 128 segments has
 // only 4096 chains, and had walked its 127 aggregates in eight dependent
 // batches.)
+template <int SPLIT>
 __global__ __launch_bounds__(kThreads * kCarryWaves) void carry_kernel(
     ScanShape s, const float2* __restrict__ agg, const float* __restrict__ h0,
     float* __restrict__ carry) {
@@ -795,8 +826,19 @@ __global__ __launch_bounds__(kThreads * kCarryWaves) void carry_kernel(
     const int d = static_cast<int>(row % per_b);
     if (d < s.dim && n < s.dstate) c = h0[(static_cast<int64_t>(b) * s.dim + d) * s.dstate + n];
   }
+  // Link k of the chain is segment k: its SPLIT (= agg_split) parts composed
+  // in order.  (SPLIT is a template argument: with a runtime count the
+  // compiler put each further part's load under a branch and waited for it
+  // there, one memory latency per link.)
   walk_chain_in_ranges(
-      s.nseg - 1, c, valid, xch, [&](int k) { return agg[k * sstride + ic]; },
+      s.nseg - 1, c, valid, xch,
+      [&](int k) {
+        const float2* a = agg + static_cast<int64_t>(k) * SPLIT * sstride + ic;
+        float2 l = a[0];
+#pragma unroll
+        for (int j = 1; j < SPLIT; ++j) l = link_then(l, a[j * sstride]);
+        return l;
+      },
       [&](int k, float v) { carry[(k + 1) * sstride + idx] = v; });
 }
 
@@ -820,12 +862,18 @@ static void launch_pass(const ScanShape& s, const ScanPtrs& p, const float* h0, 
   const IO* z = static_cast<const IO*>(p.z);
   IO* out = static_cast<IO*>(p.out);
   if (s.nseg > 1) {
-    scan_kernel<IO, XT, BT, true, VEC, REV, LTI><<<wgs(s.nseg - 1), block, 0, stream>>>(
+    const int links = (s.nseg - 1) * s.agg_split;
+    scan_kernel<IO, XT, BT, true, VEC, REV, LTI><<<wgs(links), block, 0, stream>>>(
         s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
         nullptr);
     const int64_t n = s.nchan_pad * kMaxState;
-    carry_kernel<<<dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)),
-                   dim3(kThreads * carry_waves(s.nseg)), 0, stream>>>(s, p.agg, h0, p.carry);
+    const dim3 cgrid(static_cast<unsigned>((n + kThreads - 1) / kThreads));
+    const dim3 cblock(kThreads * carry_waves(s.nseg));
+    static_assert(kMaxAggSplit == 2, "one carry instantiation per part count");
+    if (s.agg_split == 2)
+      carry_kernel<2><<<cgrid, cblock, 0, stream>>>(s, p.agg, h0, p.carry);
+    else
+      carry_kernel<1><<<cgrid, cblock, 0, stream>>>(s, p.agg, h0, p.carry);
   }
   scan_kernel<IO, XT, BT, false, VEC, REV, LTI><<<wgs(s.nseg), block, 0, stream>>>(
       s, u, dr, p.A_log, Bm, Cm, p.D, z, p.dt_bias, h0, out, final_state, p.agg, p.carry,
