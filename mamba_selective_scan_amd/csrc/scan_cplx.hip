@@ -201,7 +201,6 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
         hr = nr;
         hi = ni;
         if constexpr (AGG) {
-          sum_delta += dd.x;
           turns_acc = __builtin_amdgcn_fractf(turns_acc + turns);
         } else {
           const float2 cc = s_C[n][t4 + i];
@@ -212,6 +211,13 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
         const float y = row_sum16_x4(yv[0], yv[1], yv[2], yv[3], n);
         if ((n & 3) == 0) s_y[c][t4 + (n >> 2)] = y;
       }
+    }
+    if constexpr (AGG) {
+      // The segment's sum of delta, split over the channel's 16 lanes: lane n
+      // adds steps n and n + 16 of each chunk, and the row sums the partial
+      // sums at the segment end (every lane had added all 32 steps).
+      static_assert(kCxT == 2 * kMaxState, "two steps per lane and chunk");
+      sum_delta += s_dd[c][n].x + s_dd[c][n + kMaxState].x;
     }
     __syncthreads();
     if constexpr (AGG) continue;  // the next chunk's E phase follows the barrier
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(kCxThreads) void scan_cplx_kernel(CplxShape s, Cplx
   if constexpr (AGG) {
     // (prod_t a_t, h from zero) of the segment; lanes outside the tensors
     // record the identity pair ((1, 0), (0, 0))
-    const float m = fast_exp2(ar2 * sum_delta);
+    const float m = fast_exp2(ar2 * row_sum16(sum_delta));
     p.agg[static_cast<int64_t>(seg) * s.nchan_pad * kMaxState + ws_row] =
         make_float4(m * __builtin_amdgcn_cosf(turns_acc), m * __builtin_amdgcn_sinf(turns_acc),
                     hr, hi);

@@ -94,6 +94,35 @@ def test_workspace_size_depends_on_shape_only():
     assert st.value == _lib.STATUS_CODE["MSS_ERR_BAD_STRUCT"]
 
 
+@pytest.mark.parametrize("dim,seqlen,parts", [(8192, 1117, 2), (1536, 2048, 1), (256, 220500, 2),
+                                               (1536, 32768, 2)])
+def test_scan_workspace_holds_aggregate_parts(dim, seqlen, parts):
+    # Workspace = (nseg - 1) * parts aggregates (P, H) per padded channel and
+    # state, nseg carries, and a state hand-off when the length is not a
+    # multiple of 4.  The plan: segments fill 4096 waves of 8 channels; the
+    # aggregate pass cuts each into `parts` (at most 2) while its grid, in whole
+    # 32-channel blocks, stays at or below 8192 waves with parts of >= 4 chunks.
+    lib = _lib.lib()
+    a = _lib.new_scan_args()
+    a.batch, a.dim, a.seqlen, a.dstate = 1, dim, seqlen, 16
+    st = ctypes.c_int(-1)
+    n = lib.mss_selective_scan_workspace_size(ctypes.byref(a), ctypes.byref(st))
+    assert st.value == 0
+    tiles = (dim + 7) // 8
+    chunks = (seqlen + 31) // 32
+    nseg0 = max(1, min(4096 // tiles, chunks))
+    seg_chunks = -(-chunks // nseg0)
+    nseg = -(-seqlen // (seg_chunks * 32))
+    blocks = -(-tiles // 4) * 4 * (nseg - 1)
+    assert min(8192 // blocks, seg_chunks // 4, 2) == parts
+    pad = tiles * 8
+    up = lambda x: -(-x // 256) * 256
+    want = up((nseg - 1) * parts * pad * 16 * 8) + up(nseg * pad * 16 * 4)
+    if seqlen % 4:
+        want += up(dim * 16 * 4)
+    assert n == want
+
+
 # ----------------------------------------------------------- argument checks
 
 BASE = 0x7F0000000000

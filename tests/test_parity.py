@@ -114,6 +114,15 @@ def test_time_split_with_initial_state(mss):
     _full_case(mss, "split+h0", 1, 64, 20000, 16, h0=True)
 
 
+@pytest.mark.parametrize("layout", ["bdl", "bld"])
+def test_aggregate_pass_in_parts(mss, layout):
+    """1x8192x1117: four time segments of 9 chunks (the last one ragged), the
+    aggregate pass cut into parts of 5 and 4 chunks (8192 channels in four
+    segments fill only half of its eight waves per SIMD), started from h0,
+    with a ragged tail; both layouts against the oracle."""
+    _full_case(mss, f"aggregate parts {layout}", 1, 8192, 1117, 16, layout=layout, h0=True)
+
+
 @pytest.mark.parametrize("shared_batch", [False, True])
 @pytest.mark.parametrize("seqlen", [77, 4096])
 def test_time_invariant_B_C(mss, shared_batch, seqlen):
