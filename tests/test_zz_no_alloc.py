@@ -68,6 +68,14 @@ def test_sequence_of_layouts_and_dtypes(mss):
     assert _pair(mss, 1, 64, 515, seed=5) > 0
 
 
+def test_aggregate_parts(mss):
+    # 1x8192x1117: the aggregate pass in two parts per segment (its part
+    # aggregates fill the scratch), both layouts, then a smaller shape
+    assert _pair(mss, 1, 8192, 1117, seed=8, h0=True) > 0
+    assert _pair(mss, 1, 8192, 1117, layout="bld", seed=9) > 0
+    assert _pair(mss, 1, 256, 999, seed=10) > 0
+
+
 def test_reverse_time(mss):
     import torch
     note("noalloc reverse time")
